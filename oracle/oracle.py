@@ -1,0 +1,255 @@
+"""ctypes front end of the CPU oracle (liboracle.so, built from oracle.c).
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).  Marshals numpy
+arrays into the C functions; every number is computed in oracle.c.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_i64 = C.c_int64
+_dbl = C.c_double
+_vp = C.c_void_p
+
+
+class DecoderConfig(C.Structure):
+    _fields_ = [("n_layers", _i64), ("dim", _i64), ("n_heads", _i64), ("n_kv_heads", _i64),
+                ("head_dim", _i64), ("hidden", _i64), ("vocab", _i64), ("n_slots", _i64),
+                ("norm_eps", _dbl), ("rope_theta", _dbl)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [("attn_norm", _vp), ("ffn_norm", _vp), ("wq", _vp), ("wk", _vp), ("wv", _vp),
+                ("wo", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = C.CDLL(_LIB_PATH)
+        L.orc_fp16_to_double.restype = _dbl
+        L.orc_fp16_to_double.argtypes = [C.c_uint16]
+        L.orc_bf16_to_double.restype = _dbl
+        L.orc_bf16_to_double.argtypes = [C.c_uint16]
+        for name, args in {
+            "orc_fp16_to_double_array": [_vp, _i64, _vp],
+            "orc_bf16_to_double_array": [_vp, _i64, _vp],
+            "orc_q4_dequant": [_vp, _i64, _vp],
+            "orc_q4_gemv": [_vp, _vp, _vp, _i64, _i64],
+            "orc_q4_gemv_f64": [_vp, _vp, _vp, _i64, _i64],
+            "orc_q4_gemv_rows": [_vp, _vp, _vp, _i64, _vp, _i64],
+            "orc_q4_gemm": [_vp, _vp, _vp, _i64, _i64, _i64],
+            "orc_rmsnorm": [_vp, _vp, _i64, _dbl, _vp],
+            "orc_rope": [_vp, _i64, _i64, _i64, _dbl],
+            "orc_attn_probs": [_vp, _vp, _i64, _i64, _i64, _dbl, _vp],
+            "orc_gqa_attn": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _dbl, _vp],
+            "orc_swiglu": [_vp, _vp, _i64, _vp],
+            "orc_decoder_destroy": [_vp],
+            "orc_decoder_reset": [_vp],
+        }.items():
+            f = getattr(L, name)
+            f.restype = None
+            f.argtypes = args
+        L.orc_argmax_f32.restype = _i64
+        L.orc_argmax_f32.argtypes = [_vp, _i64]
+        L.orc_argmax_f64.restype = _i64
+        L.orc_argmax_f64.argtypes = [_vp, _i64]
+        L.orc_decoder_create.restype = _vp
+        L.orc_decoder_create.argtypes = [C.POINTER(DecoderConfig), _vp, _vp, C.POINTER(LayerWeights)]
+        L.orc_decoder_position.restype = _i64
+        L.orc_decoder_position.argtypes = [_vp]
+        L.orc_decoder_step.restype = _i64
+        L.orc_decoder_step.argtypes = [_vp, _i64, _vp]
+        L.orc_decoder_hidden.restype = C.POINTER(C.c_double)
+        L.orc_decoder_hidden.argtypes = [_vp]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_vp)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def fp16_to_double(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float64)
+    lib().orc_fp16_to_double_array(_p(h), h.size, _p(out))
+    return out
+
+
+def bf16_to_double(b) -> np.ndarray:
+    b = _c(b, np.uint16)
+    out = np.empty(b.shape, np.float64)
+    lib().orc_bf16_to_double_array(_p(b), b.size, _p(out))
+    return out
+
+
+def q4_dequant(blocks) -> np.ndarray:
+    """blocks: uint8 [..., 18*nb] -> float32 [nb*32] (flattened in block order)."""
+    b = _c(blocks, np.uint8)
+    nb = b.size // 18
+    out = np.empty(nb * 32, np.float32)
+    lib().orc_q4_dequant(_p(b), nb, _p(out))
+    return out
+
+
+def q4_gemv(w, x) -> np.ndarray:
+    """w: uint8 [n, k/32*18]; x: float32 [k] -> float64 [n]."""
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32)
+    k = x.size
+    n = w.size // ((k // 32) * 18)
+    y = np.empty(n, np.float64)
+    lib().orc_q4_gemv(_p(w), _p(x), _p(y), n, k)
+    return y
+
+
+def q4_gemv_f64(w, x) -> np.ndarray:
+    w = _c(w, np.uint8)
+    x = _c(x, np.float64)
+    k = x.size
+    n = w.size // ((k // 32) * 18)
+    y = np.empty(n, np.float64)
+    lib().orc_q4_gemv_f64(_p(w), _p(x), _p(y), n, k)
+    return y
+
+
+def q4_gemv_rows(w, x, rows) -> np.ndarray:
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32)
+    rows = _c(rows, np.int64)
+    y = np.empty(rows.size, np.float64)
+    lib().orc_q4_gemv_rows(_p(w), _p(x), _p(rows), rows.size, _p(y), x.size)
+    return y
+
+
+def q4_gemm(w, x_bf16) -> np.ndarray:
+    """w: uint8 [n, k/32*18]; x_bf16: uint16 [m, k] -> float64 [m, n]."""
+    w = _c(w, np.uint8)
+    x = _c(x_bf16, np.uint16)
+    m, k = x.shape
+    n = w.size // ((k // 32) * 18)
+    y = np.empty((m, n), np.float64)
+    lib().orc_q4_gemm(_p(w), _p(x), _p(y), m, n, k)
+    return y
+
+
+def rmsnorm(x, g, eps) -> np.ndarray:
+    x = _c(x, np.float64)
+    g = _c(g, np.float32)
+    out = np.empty_like(x)
+    lib().orc_rmsnorm(_p(x), _p(g), x.size, float(eps), _p(out))
+    return out
+
+
+def rope(x, n_heads, head_dim, pos, theta) -> np.ndarray:
+    x = np.array(x, dtype=np.float64, copy=True)
+    lib().orc_rope(_p(x), n_heads, head_dim, pos, float(theta))
+    return x
+
+
+def attn_probs(q, k, scale) -> np.ndarray:
+    """q: [hd]; k: [len, hd] -> p [len]."""
+    q = _c(q, np.float64)
+    k = _c(k, np.float64)
+    length, hd = k.shape
+    p = np.empty(length, np.float64)
+    lib().orc_attn_probs(_p(q), _p(k), length, hd, hd, float(scale), _p(p))
+    return p
+
+
+def gqa_attn(q, k, v, scale) -> np.ndarray:
+    """q: [n_q, hd]; k, v: [n_kv, len, hd] in chronological order -> out [n_q, hd]."""
+    q = _c(q, np.float64)
+    k = _c(k, np.float64)
+    v = _c(v, np.float64)
+    n_q, hd = q.shape
+    n_kv, length, _ = k.shape
+    out = np.empty((n_q, hd), np.float64)
+    lib().orc_gqa_attn(_p(q), _p(k), _p(v), n_q, n_kv, hd, length, float(scale), _p(out))
+    return out
+
+
+def swiglu(gate, up) -> np.ndarray:
+    gate = _c(gate, np.float64)
+    up = _c(up, np.float64)
+    out = np.empty_like(gate)
+    lib().orc_swiglu(_p(gate), _p(up), gate.size, _p(out))
+    return out
+
+
+def argmax_f32(v) -> int:
+    v = _c(v, np.float32)
+    return int(lib().orc_argmax_f32(_p(v), v.size))
+
+
+def argmax_f64(v) -> int:
+    v = _c(v, np.float64)
+    return int(lib().orc_argmax_f64(_p(v), v.size))
+
+
+class Decoder:
+    """Oracle decoder over host weights (as produced by the synthetic generator)."""
+
+    def __init__(self, shape, weights):
+        s = shape
+        self.shape = s
+        self._keep = []
+
+        def keep(a, dtype):
+            a = _c(a, dtype)
+            self._keep.append(a)
+            return _p(a)
+
+        self.cfg = DecoderConfig(s.n_layers, s.dim, s.n_heads, s.n_kv_heads, s.head_dim, s.hidden,
+                                 s.vocab, s.n_slots, s.norm_eps, s.rope_theta)
+        arr = (LayerWeights * s.n_layers)()
+        for i, L in enumerate(weights["layers"]):
+            arr[i] = LayerWeights(keep(L["attn_norm"], np.float32), keep(L["ffn_norm"], np.float32),
+                                  keep(L["wq"], np.uint8), keep(L["wk"], np.uint8), keep(L["wv"], np.uint8),
+                                  keep(L["wo"], np.uint8), keep(L["w_gate"], np.uint8),
+                                  keep(L["w_up"], np.uint8), keep(L["w_down"], np.uint8))
+        self._layers = arr
+        self._h = lib().orc_decoder_create(C.byref(self.cfg), keep(weights["tok_embd"], np.uint8),
+                                           keep(weights["out_norm"], np.float32), arr)
+
+    def step(self, token: int, want_logits: bool = True):
+        logits = np.empty(self.shape.vocab, np.float64) if want_logits else None
+        nxt = lib().orc_decoder_step(self._h, int(token), _p(logits) if want_logits else None)
+        return int(nxt), logits
+
+    def reset(self):
+        lib().orc_decoder_reset(self._h)
+
+    @property
+    def position(self) -> int:
+        return int(lib().orc_decoder_position(self._h))
+
+    def hidden(self) -> np.ndarray:
+        p = lib().orc_decoder_hidden(self._h)
+        return np.ctypeslib.as_array(p, shape=(self.shape.dim,)).copy()
+
+    def close(self):
+        if self._h:
+            lib().orc_decoder_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,486 @@
+"""Pins of the CPU oracle against things other than itself (closed forms, exhaustive
+checks against numpy/torch number handling, exact rational brute force, invariants and
+library routines on small inputs).  CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from streaming_speech_text_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def make_block(d_bits: int, qs) -> np.ndarray:
+    b = np.zeros(18, np.uint8)
+    b[0] = d_bits & 0xFF
+    b[1] = d_bits >> 8
+    b[2:] = np.asarray(qs, dtype=np.uint8)
+    return b
+
+
+def f32_bits(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+# ---------------------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------------------
+
+def test_fp16_decode_exhaustive(orc):
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.fp16_to_double(allh)
+    ref = allh.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zeros too
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp16_decode_closed_forms(orc):
+    assert orc.lib().orc_fp16_to_double(0x3C00) == 1.0
+    assert orc.lib().orc_fp16_to_double(0x0001) == 2.0 ** -24
+    assert orc.lib().orc_fp16_to_double(0x0400) == 2.0 ** -14
+    assert orc.lib().orc_fp16_to_double(0x7BFF) == 65504.0
+    assert orc.lib().orc_fp16_to_double(0xC000) == -2.0
+    assert math.copysign(1.0, orc.lib().orc_fp16_to_double(0x8000)) == -1.0
+    assert math.isinf(orc.lib().orc_fp16_to_double(0x7C00))
+
+
+def test_bf16_decode_exhaustive(orc):
+    allb = np.arange(65536, dtype=np.uint32)
+    got = orc.bf16_to_double(allb.astype(np.uint16))
+    ref = (allb << 16).astype(np.uint32).view(np.float32)
+    with np.errstate(invalid="ignore"):
+        ref = ref.astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_bf16_generator_rounding_matches_torch():
+    # the generator's bf16 rounding (input preparation) is round-to-nearest-even, as torch's
+    x = synth.normal_f32(synth.generator(99), (4096,))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(synth.bf16_bits(x), ref)
+
+
+# ---------------------------------------------------------------------------------------
+# Q4_0 dequantisation
+# ---------------------------------------------------------------------------------------
+
+def test_dequant_handbuilt_unit_scale(orc):
+    # d = 1.0; byte j: low nibble j, high nibble 15 - j
+    qs = [j | ((15 - j) << 4) for j in range(16)]
+    v = orc.q4_dequant(make_block(0x3C00, qs))
+    expect = [j - 8 for j in range(16)] + [7 - j for j in range(16)]
+    assert v.tolist() == [float(e) for e in expect]
+
+
+def test_dequant_handbuilt_extremes(orc):
+    # smallest subnormal scale: low nibbles 0 -> -8 * 2^-24, high nibbles 15 -> 7 * 2^-24
+    v = orc.q4_dequant(make_block(0x0001, [0xF0] * 16))
+    assert v[:16].tolist() == [-8 * 2.0 ** -24] * 16
+    assert v[16:].tolist() == [7 * 2.0 ** -24] * 16
+    # largest finite scale 65504: low 15 -> 7*65504, high 0 -> -8*65504
+    v = orc.q4_dequant(make_block(0x7BFF, [0x0F] * 16))
+    assert v[:16].tolist() == [458528.0] * 16
+    assert v[16:].tolist() == [-524032.0] * 16
+    # negative scale -0.5, code 8 everywhere -> (8-8) * -0.5 = -0.0 (sign kept)
+    v = orc.q4_dequant(make_block(0xB800, [0x88] * 16))
+    assert np.all(f32_bits(v) == 0x80000000)
+    # scale -0.0: (q-8) * -0 is -0 for q >= 8 and +0 for q < 8
+    qs = [j | (j << 4) for j in range(16)]
+    v = orc.q4_dequant(make_block(0x8000, qs))
+    sign = np.signbit(v[:16])
+    assert sign.tolist() == [j >= 8 for j in range(16)]
+    assert np.all(v == 0)
+
+
+def test_dequant_exhaustive_codes_and_finite_scales(orc):
+    # every finite fp16 scale with every code, in both nibble positions
+    dbits = np.array([h for h in range(65536) if ((h >> 10) & 31) != 31], dtype=np.uint16)
+    nb = dbits.size
+    blocks = np.zeros((nb, 18), np.uint8)
+    blocks[:, 0] = dbits & 0xFF
+    blocks[:, 1] = dbits >> 8
+    codes = np.arange(16, dtype=np.uint8)
+    blocks[:, 2:] = codes | ((15 - codes) << 4)
+    got = orc.q4_dequant(blocks).reshape(nb, 32)
+    d = dbits.view(np.float16).astype(np.float64)
+    lo = (codes.astype(np.float64) - 8)
+    hi = (15 - codes.astype(np.float64) - 8)
+    ref = np.concatenate([d[:, None] * lo[None, :], d[:, None] * hi[None, :]], axis=1)
+    # the exact products fit fp32 (at most 15 significant bits)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    assert np.array_equal(f32_bits(got), f32_bits(ref.astype(np.float32)))
+
+
+def test_dequant_round_trip(orc):
+    # bytes -> values -> re-encode with the block's own scale -> identical bytes
+    g = synth.generator(11)
+    blocks = synth.q4_matrix(g, 64, 32 * 8).reshape(-1, 18)
+    vals = orc.q4_dequant(blocks).reshape(-1, 32).astype(np.float64)
+    d = blocks[:, 0:2].copy().view("<f2").astype(np.float64).reshape(-1)
+    codes = np.rint(vals / d[:, None] + 8).astype(np.int64)
+    assert codes.min() >= 0 and codes.max() <= 15
+    re = np.zeros_like(blocks)
+    re[:, 0:2] = blocks[:, 0:2]
+    re[:, 2:] = (codes[:, :16] | (codes[:, 16:] << 4)).astype(np.uint8)
+    assert np.array_equal(re, blocks)
+    # grid values -> encode -> dequant -> identical values
+    codes2 = synth.generator(12).integers(0, 16, size=(64, 32))
+    d2 = np.full(64, 0.0078125)  # 2^-7, exact in fp16
+    enc = np.zeros((64, 18), np.uint8)
+    enc[:, 0:2] = d2.astype("<f2").view(np.uint8).reshape(64, 2)
+    enc[:, 2:] = (codes2[:, :16] | (codes2[:, 16:] << 4)).astype(np.uint8)
+    back = orc.q4_dequant(enc).reshape(64, 32)
+    assert np.array_equal(back.astype(np.float64), (codes2 - 8) * d2[:, None])
+
+
+# ---------------------------------------------------------------------------------------
+# GEMV / GEMM
+# ---------------------------------------------------------------------------------------
+
+def _np_dequant(w, n, k):
+    """Independent numpy dequantisation used only as a cross-check."""
+    b = np.ascontiguousarray(w).reshape(n, k // 32, 18)
+    d = b[:, :, 0:2].copy().view("<f2").astype(np.float64)[..., 0]
+    lo = (b[:, :, 2:] & 15).astype(np.float64) - 8
+    hi = (b[:, :, 2:] >> 4).astype(np.float64) - 8
+    return (np.concatenate([lo, hi], axis=2) * d[..., None]).reshape(n, k)
+
+
+def _dyadic_q4(g, n, k):
+    """Q4_0 matrix whose scales are powers of two (exact in fp16 and every partial sum)."""
+    w = synth.q4_matrix(g, n, k).reshape(n, k // 32, 18)
+    e = g.integers(-6, 2, size=(n, k // 32)).astype(np.float64)
+    w[:, :, 0:2] = (2.0 ** e).astype("<f2").view(np.uint8).reshape(n, k // 32, 2)
+    return w.reshape(n, -1)
+
+
+def test_gemv_exact_bruteforce_fractions(orc):
+    g = synth.generator(21)
+    for n, k in [(1, 32), (3, 64), (5, 96), (7, 160)]:
+        w = _dyadic_q4(g, n, k)
+        x = g.integers(-7, 8, size=k).astype(np.float32)
+        y = orc.q4_gemv(w, x)
+        b = w.reshape(n, k // 32, 18)
+        for r in range(n):
+            acc = Fraction(0)
+            for blk in range(k // 32):
+                d = Fraction(float(b[r, blk, 0:2].copy().view("<f2")[0]))
+                for j in range(16):
+                    lo = int(b[r, blk, 2 + j]) & 15
+                    hi = int(b[r, blk, 2 + j]) >> 4
+                    acc += (lo - 8) * d * Fraction(float(x[blk * 32 + j]))
+                    acc += (hi - 8) * d * Fraction(float(x[blk * 32 + j + 16]))
+            assert Fraction(y[r]) == acc
+
+
+def test_gemv_random_vs_numpy(orc):
+    g = synth.generator(22)
+    for n, k in [(37, 256), (64, 3072), (5, 9216), (300, 1280)]:
+        w = synth.q4_matrix(g, n, k)
+        x = synth.normal_f32(g, (k,))
+        y = orc.q4_gemv(w, x)
+        ref = _np_dequant(w, n, k) @ x.astype(np.float64)
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+        rows = np.array([0, n - 1, n // 2], np.int64)
+        assert np.array_equal(orc.q4_gemv_rows(w, x, rows), y[rows])
+
+
+def test_gemv_nonsquare_orientation(orc):
+    # W is [n][k]; a transposed reading would not even have the right length
+    g = synth.generator(23)
+    w = synth.q4_matrix(g, 3, 64)
+    x = np.zeros(64, np.float32)
+    x[40] = 1.0  # picks column 40: block 1, element 8 -> low nibble of byte 8
+    y = orc.q4_gemv(w, x)
+    b = w.reshape(3, 2, 18)
+    d = b[:, 1, 0:2].copy().view("<f2").astype(np.float64)[:, 0]
+    assert np.array_equal(y, ((b[:, 1, 2 + 8] & 15).astype(np.float64) - 8) * d)
+    x[:] = 0
+    x[63] = 1.0  # block 1, element 31 -> high nibble of byte 15
+    y = orc.q4_gemv(w, x)
+    assert np.array_equal(y, ((b[:, 1, 2 + 15] >> 4).astype(np.float64) - 8) * d)
+
+
+def test_gemm_exact_and_random(orc):
+    g = synth.generator(24)
+    # exact: dyadic scales, small-integer bf16 activations
+    m, n, k = 5, 7, 96
+    w = _dyadic_q4(g, n, k)
+    xi = g.integers(-9, 10, size=(m, k)).astype(np.float32)
+    y = orc.q4_gemm(w, synth.bf16_bits(xi))
+    wd = _np_dequant(w, n, k)
+    ref = np.array([[sum(Fraction(float(xi[r, i])) * Fraction(wd[c, i]) for i in range(k))
+                     for c in range(n)] for r in range(m)])
+    assert all(Fraction(y[r, c]) == ref[r, c] for r in range(m) for c in range(n))
+    # random bf16 activations vs numpy
+    m, n, k = 33, 40, 1280
+    w = synth.q4_matrix(g, n, k)
+    xb = synth.bf16_normal(g, (m, k))
+    y = orc.q4_gemm(w, xb)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.allclose(y, xf @ _np_dequant(w, n, k).T, rtol=1e-12, atol=1e-12)
+    # a single row equals the GEMV of that row
+    assert np.allclose(y[3], orc.q4_gemv(w, xf[3].astype(np.float32)), rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------------------------------
+# RMSNorm, RoPE, attention, SwiGLU, argmax
+# ---------------------------------------------------------------------------------------
+
+def test_rmsnorm_closed_form_and_torch(orc):
+    dim, eps = 3072, 1e-5
+    c = 0.37
+    out = orc.rmsnorm(np.full(dim, c), np.ones(dim, np.float32), eps)
+    assert np.allclose(out, c / math.sqrt(c * c + eps), rtol=1e-12, atol=0)
+    x = synth.normal_f32(synth.generator(31), (dim,)).astype(np.float64) * 3
+    gain = synth.uniform_f32(synth.generator(32), (dim,), 0.5, 1.5)
+    out = orc.rmsnorm(x, gain, eps)
+    ref = F.rms_norm(torch.from_numpy(x), (dim,), torch.from_numpy(gain.astype(np.float64)), eps).numpy()
+    assert np.allclose(out, ref, rtol=1e-13, atol=1e-14)
+    # unit gain: output RMS = sqrt(ms / (ms + eps))
+    o1 = orc.rmsnorm(x, np.ones(dim, np.float32), eps)
+    ms = np.mean(x * x)
+    assert abs(math.sqrt(np.mean(o1 * o1)) - math.sqrt(ms / (ms + eps))) < 1e-14
+
+
+def test_rope_identity_norms_and_complex(orc):
+    g = synth.generator(33)
+    nh, hd, theta = 4, 128, 1e6
+    x = g.standard_normal(nh * hd)
+    assert np.array_equal(orc.rope(x, nh, hd, 0, theta), x)
+    for pos in (1, 37, 8191, 123456):
+        y = orc.rope(x, nh, hd, pos, theta)
+        pn = (x.reshape(-1, 2) ** 2).sum(1)
+        assert np.allclose((y.reshape(-1, 2) ** 2).sum(1), pn, rtol=1e-13)
+        i = np.arange(hd // 2)
+        ang = pos * theta ** (-2.0 * i / hd)
+        z = (x[0::2] + 1j * x[1::2]).reshape(nh, hd // 2) * np.exp(1j * ang)[None, :]
+        ref = np.stack([z.real, z.imag], axis=-1).reshape(-1)
+        # angle = pos * freq: one ulp of freq moves the angle by about pos * 1e-16 rad
+        assert np.allclose(y, ref, rtol=0, atol=1e-13 * (1 + pos))
+
+
+def test_rope_relative_position(orc):
+    g = synth.generator(34)
+    hd = 128
+    q = g.standard_normal(hd)
+    k = g.standard_normal(hd)
+    for a, b, t in [(5, 2, 11), (100, 0, 900), (7, 7, 3)]:
+        lhs = orc.rope(q, 1, hd, a, 1e6) @ orc.rope(k, 1, hd, b, 1e6)
+        rhs = orc.rope(q, 1, hd, a + t, 1e6) @ orc.rope(k, 1, hd, b + t, 1e6)
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(lhs))
+
+
+def test_attention_probability_sums_and_special_cases(orc):
+    g = synth.generator(35)
+    hd, L = 128, 300
+    q = g.standard_normal(hd)
+    k = g.standard_normal((L, hd)) * 2
+    p = orc.attn_probs(q, k, 1 / math.sqrt(hd))
+    assert abs(p.sum() - 1.0) < 1e-12 and p.min() >= 0
+    # all-ones values -> every output is 1 (probabilities sum to one)
+    nq, nkv = 32, 8
+    qq = g.standard_normal((nq, hd))
+    kk = g.standard_normal((nkv, L, hd))
+    out = orc.gqa_attn(qq, kk, np.ones((nkv, L, hd)), 1 / math.sqrt(hd))
+    assert np.allclose(out, 1.0, rtol=0, atol=1e-12)
+    # one key -> its value exactly
+    v1 = g.standard_normal((nkv, 1, hd))
+    out = orc.gqa_attn(qq, kk[:, :1], v1, 0.1)
+    assert np.array_equal(out, np.repeat(v1[:, 0], nq // nkv, axis=0))
+    # all keys equal -> mean of the values
+    keq = np.repeat(kk[:, :1], L, axis=1)
+    vv = g.standard_normal((nkv, L, hd))
+    out = orc.gqa_attn(qq, keq, vv, 0.3)
+    assert np.allclose(out, np.repeat(vv.mean(1), nq // nkv, axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_vs_torch_sdpa_gqa(orc):
+    g = synth.generator(36)
+    for nq, nkv, hd, L in [(32, 8, 128, 77), (4, 4, 16, 5), (8, 2, 64, 513)]:
+        q = g.standard_normal((nq, hd))
+        k = g.standard_normal((nkv, L, hd))
+        v = g.standard_normal((nkv, L, hd))
+        sc = 1 / math.sqrt(hd)
+        out = orc.gqa_attn(q, k, v, sc)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q)[None, :, None, :], torch.from_numpy(k)[None],
+                                             torch.from_numpy(v)[None], scale=sc, enable_gqa=True)
+        assert np.allclose(out, ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_ring_order_invariance(orc):
+    # a ring with write index w holds the same set as the chronological list; any slot
+    # permutation gives the same attention output
+    g = synth.generator(37)
+    nq, nkv, hd, S, w = 8, 2, 32, 64, 23
+    q = g.standard_normal((nq, hd))
+    ring_k = g.standard_normal((nkv, S, hd))
+    ring_v = g.standard_normal((nkv, S, hd))
+    chrono = np.concatenate([np.arange(w, S), np.arange(0, w)])
+    a = orc.gqa_attn(q, ring_k[:, chrono], ring_v[:, chrono], 0.2)
+    b = orc.gqa_attn(q, ring_k, ring_v, 0.2)
+    perm = g.permutation(S)
+    c = orc.gqa_attn(q, ring_k[:, perm], ring_v[:, perm], 0.2)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-13) and np.allclose(a, c, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_group_mapping(orc):
+    # query head h must read KV head h // 4: put a distinct constant value in each KV head
+    nq, nkv, hd, L = 32, 8, 16, 9
+    g = synth.generator(38)
+    q = g.standard_normal((nq, hd))
+    k = g.standard_normal((nkv, L, hd))
+    v = np.repeat(np.arange(nkv, dtype=np.float64)[:, None, None], L, axis=1).repeat(hd, axis=2)
+    out = orc.gqa_attn(q, k, v, 0.25)
+    assert np.allclose(out[:, 0], np.arange(nq) // 4, atol=1e-12)
+
+
+def test_swiglu(orc):
+    z = np.array([0.0, 1.0, -1.0, 30.0, -30.0, 2.5])
+    u = np.array([3.0, 2.0, 2.0, 1.0, 1.0, -1.0])
+    out = orc.swiglu(z, u)
+    assert out[0] == 0.0
+    assert abs(out[3] - 30.0) < 1e-9 and abs(out[4]) < 1e-9
+    ref = (F.silu(torch.from_numpy(z)) * torch.from_numpy(u)).numpy()
+    assert np.allclose(out, ref, rtol=1e-15, atol=0)
+
+
+def test_argmax_ties_lowest_index(orc):
+    v = np.array([1.0, 3.0, -2.0, 3.0, 3.0], np.float32)
+    assert orc.argmax_f32(v) == 1 == int(np.argmax(v))
+    assert orc.argmax_f64(v.astype(np.float64)) == 1
+    v = synth.normal_f32(synth.generator(39), (131072,))
+    assert orc.argmax_f32(v) == int(np.argmax(v))
+    # the fp32 decision: two doubles that round to the same float tie at the lower index
+    d = np.array([1.0, 1.0 + 2.0 ** -40, 0.5])
+    assert orc.argmax_f64(d) == 1
+    assert orc.argmax_f32(d.astype(np.float32)) == 0
+
+
+# ---------------------------------------------------------------------------------------
+# whole decoder step: tiny configuration against an independent torch float64 composition
+# ---------------------------------------------------------------------------------------
+
+TINY = synth.DecoderShape(n_layers=2, dim=64, n_heads=4, n_kv_heads=2, head_dim=16, hidden=192,
+                          vocab=512, n_slots=16, norm_eps=1e-5, rope_theta=1e6)
+
+
+def _torch_decoder_reference(shape, weights, tokens):
+    """Second, independent composition from library routines (torch float64)."""
+    s = shape
+    t = torch.float64
+
+    def deq(w, n, k):
+        return torch.from_numpy(_np_dequant(w, n, k))
+
+    E = deq(weights["tok_embd"], s.vocab, s.dim)
+    layers = []
+    for L in weights["layers"]:
+        layers.append({
+            "an": torch.from_numpy(L["attn_norm"].astype(np.float64)),
+            "fn": torch.from_numpy(L["ffn_norm"].astype(np.float64)),
+            "wq": deq(L["wq"], s.n_heads * s.head_dim, s.dim),
+            "wk": deq(L["wk"], s.n_kv_heads * s.head_dim, s.dim),
+            "wv": deq(L["wv"], s.n_kv_heads * s.head_dim, s.dim),
+            "wo": deq(L["wo"], s.dim, s.n_heads * s.head_dim),
+            "wg": deq(L["w_gate"], s.hidden, s.dim),
+            "wu": deq(L["w_up"], s.hidden, s.dim),
+            "wd": deq(L["w_down"], s.dim, s.hidden),
+        })
+    on = torch.from_numpy(weights["out_norm"].astype(np.float64))
+    inv = 1.0 / (s.rope_theta ** (torch.arange(0, s.head_dim, 2, dtype=t) / s.head_dim))
+
+    def rope(x, nh, pos):
+        z = torch.view_as_complex(x.reshape(nh, s.head_dim // 2, 2).contiguous())
+        z = z * torch.polar(torch.ones_like(inv), pos * inv)[None, :]
+        return torch.view_as_real(z).reshape(-1)
+
+    cache = [([], []) for _ in layers]
+    outs = []
+    for pos, tok in enumerate(tokens):
+        h = E[tok].clone()
+        for li, L in enumerate(layers):
+            x = F.rms_norm(h, (s.dim,), L["an"], s.norm_eps)
+            q = rope(L["wq"] @ x, s.n_heads, pos)
+            k = rope(L["wk"] @ x, s.n_kv_heads, pos)
+            v = L["wv"] @ x
+            ks, vs = cache[li]
+            ks.append(k.reshape(s.n_kv_heads, s.head_dim))
+            vs.append(v.reshape(s.n_kv_heads, s.head_dim))
+            K = torch.stack(ks[-s.n_slots:], dim=1)[None]
+            V = torch.stack(vs[-s.n_slots:], dim=1)[None]
+            o = F.scaled_dot_product_attention(q.reshape(1, s.n_heads, 1, s.head_dim), K, V,
+                                               scale=1 / math.sqrt(s.head_dim), enable_gqa=True)
+            h = h + L["wo"] @ o.reshape(-1)
+            x = F.rms_norm(h, (s.dim,), L["fn"], s.norm_eps)
+            h = h + L["wd"] @ (F.silu(L["wg"] @ x) * (L["wu"] @ x))
+        logits = E @ F.rms_norm(h, (s.dim,), on, s.norm_eps)
+        outs.append(logits.numpy())
+    return outs
+
+
+def test_decoder_tiny_vs_torch_composition(orc):
+    w = synth.decoder_weights(41, TINY)
+    n_steps = 40  # window of 16 wraps twice
+    tokens = synth.generator(41, 9).integers(0, TINY.vocab, size=n_steps).tolist()
+    dec = orc.Decoder(TINY, w)
+    got = []
+    for tok in tokens:
+        nxt, lg = dec.step(tok)
+        got.append(lg)
+        assert nxt == int(np.argmax(lg.astype(np.float32)))
+    assert dec.position == n_steps
+    ref = _torch_decoder_reference(TINY, w, tokens)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, rtol=1e-10, atol=1e-10)
+    # reset restarts the sequence from position 0 with an empty window
+    dec.reset()
+    nxt, lg = dec.step(tokens[0])
+    assert dec.position == 1 and np.allclose(lg, ref[0], rtol=1e-10, atol=1e-10)
+    dec.close()
+
+
+def test_decoder_window_drop_matters(orc):
+    # with the window of 16, step 17 must differ from an unbounded-history reference
+    w = synth.decoder_weights(42, TINY)
+    tokens = synth.generator(42, 9).integers(0, TINY.vocab, size=20).tolist()
+    wide = synth.DecoderShape(**{**TINY.__dict__, "n_slots": 64})
+    a = orc.Decoder(TINY, w)
+    b = orc.Decoder(wide, w)
+    la = [a.step(t)[1] for t in tokens]
+    lb = [b.step(t)[1] for t in tokens]
+    for i in range(16):
+        assert np.array_equal(la[i], lb[i])
+    assert not np.allclose(la[17], lb[17])
+
+
+# ---------------------------------------------------------------------------------------
+# shapes against the figures the pages print
+# ---------------------------------------------------------------------------------------
+
+def test_page_figures_pin_shapes():
+    fig = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
+    s = synth.VOXTRAL_DECODER
+    assert s.vocab * s.dim * 4 == fig["embedding_table_f32_bytes"]["bytes"] == int(1.5 * 2 ** 30)
+    kv = s.n_layers * s.n_slots * 2 * s.n_kv_heads * s.head_dim * 4
+    assert 0.95 * fig["kv_cache_max_bytes"]["upper_bytes"] < kv <= fig["kv_cache_max_bytes"]["upper_bytes"]
+    assert s.n_slots == fig["kv_window_positions"]["value"]
+    d = fig["decoder"]
+    assert (s.n_layers, s.dim, s.n_heads, s.n_kv_heads) == (d["n_layers"], d["dim"], d["n_heads"], d["n_kv_heads"])
+    assert synth.DECODER_PREFIX == fig["decoder_prefix_positions"]["value"]
+    # the quantised decoder (all linears + tied table) stays under the whole Q4 model size
+    per_layer = sum(o * synth.q4_row_bytes(i) for o, i in synth.LAYER_LINEARS.values())
+    total = s.n_layers * per_layer + s.vocab * synth.q4_row_bytes(s.dim)
+    assert total < fig["q4_model_bytes"]["approx_bytes"]
+    assert synth.ENCODER_LINEARS[0][1] == fig["encoder"]["dim"]
