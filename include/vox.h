@@ -1,0 +1,143 @@
+/* vox.h - C ABI of the MI355X (gfx950) library for the per-token decoder step of the
+ * streaming Voxtral Mini 4B Realtime speech-to-text model.
+ *
+ * Source pages this interface follows:
+ *  [RS] "Mistral의 Voxtral Mini 4B Realtime 모델을 Rust로 구현해 브라우저에서 실행"
+ *       (GeekNews 26595): section 아키텍처 - the Q4 path stores every linear as GGUF Q4_0 and
+ *       fuses dequantisation into the matrix product in custom shaders; section 브라우저 실행을
+ *       위한 기술적 해결 - the embedding stays on the GPU as Q4 and one row is looked up per token.
+ *  [VC] "Mistral Voxtral Realtime 4B 음성 인식 모델의 순수 C 기반 CPU 전용 추론 구현"
+ *       (GeekNews 26608): section 모델 아키텍처 - decoder of 26 layers, width 3072, GQA with 32
+ *       query heads over 8 KV heads, encoder width 1280, vocabulary 131,072; section 주요 기능 -
+ *       a rolling KV cache over an 8192-position sliding window; section C API 구조 - a `vox_`
+ *       prefixed C API around an opaque stream handle; section 성능 벤치마크 - the whole decoder
+ *       token is one GPU submission.
+ *
+ * Conventions for every entry point:
+ *  - Buffer pointers are DEVICE pointers owned by the caller.  The library never allocates
+ *    device memory; callers size workspaces with the *_workspace queries.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only enqueue
+ *    work; results are ready when the caller synchronises the stream.
+ *  - Arguments are validated on the host before any device work; a failed check returns a
+ *    negative status and enqueues nothing.  vox_last_error() then holds a message.
+ *  - Launch failures return VOX_E_HIP.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this interface.
+ *  - GGUF Q4_0 weights: a matrix of n rows by k inputs is n*k/32 blocks of 18 bytes, row
+ *    major, k/32 consecutive blocks per row.  Block: bytes 0..1 = fp16 scale d
+ *    (little-endian); byte 2+j (j=0..15) low nibble = code of weight j, high nibble = code of
+ *    weight j+16; weight = (code - 8) * d.  k must be a positive multiple of 32.
+ */
+#ifndef VOX_H
+#define VOX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    VOX_OK = 0,
+    VOX_E_INVAL = -1,        /* bad argument: null pointer, size, aliasing, layout */
+    VOX_E_UNSUPPORTED = -2,  /* valid request outside what the kernels implement */
+    VOX_E_WORKSPACE = -3,    /* workspace or buffer too small */
+    VOX_E_HIP = -4           /* HIP runtime error while enqueuing */
+};
+
+/* Static description of a status code. */
+const char *vox_strerror(int status);
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char *vox_last_error(void);
+
+/* Q4_0 dequantisation ([RS] 아키텍처).  out[32*b + j] = (code_j - 8) * d_b for n_blocks blocks,
+ * fp32, bit-exact (every product is exactly representable).  w_q4: n_blocks*18 bytes, any
+ * alignment.  out: n_blocks*32 floats, must not overlap w_q4.  n_blocks == 0 is a no-op. */
+int vox_q4_dequant(const void *w_q4, int64_t n_blocks, float *out, void *stream);
+
+/* Q4_0 matrix-vector product with dequantisation fused into the product ([RS] 아키텍처):
+ * y[r] = sum_i W[r][i] * x[i], fp32 accumulation.  w_q4: n rows by k inputs (layout above);
+ * x: k floats; y: n floats, must not overlap x or w_q4.  n == 0 is a no-op.
+ * k % 32 != 0 or k <= 0 -> VOX_E_INVAL. */
+int vox_q4_gemv(const void *w_q4, const float *x, float *y, int64_t n, int64_t k, void *stream);
+
+/* Encoder-chunk linear Y = X * W^T with Q4_0 weights ([VC] 모델 아키텍처: encoder width 1280;
+ * [RS] 아키텍처: Q4_0 linears), on the matrix cores.  x_bf16: m rows by k, bf16 bit patterns,
+ * row major; w_q4: n rows by k; y: m by n fp32, row major, must not overlap the inputs.
+ * Products of the exact Q4 codes with bf16 activations, fp32 accumulation.
+ * m == 0 or n == 0 is a no-op.  k % 32 != 0 -> VOX_E_INVAL. */
+int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, int64_t m, int64_t n, int64_t k,
+                void *stream);
+
+/* Grouped-query decode attention of one token over a KV ring ([RS] 아키텍처 and [VC] 모델
+ * 아키텍처: query head h reads KV head h / (n_q_heads / n_kv_heads); [VC] 주요 기능: rolling
+ * window).  q: [n_q_heads][head_dim]; k_cache, v_cache: [n_kv_heads][n_slots][head_dim];
+ * out: [n_q_heads][head_dim]; all fp32.  Attends over ring slots [0, n_valid) - the set of
+ * cached positions, in any slot order:
+ *   s_t = scale * <q_h, K[g][t]>,  out_h = sum_t softmax(s)_t * V[g][t].
+ * workspace: at least vox_gqa_decode_attn_workspace(...) bytes of device memory, 16-byte
+ * aligned, contents irrelevant.  head_dim must be 128 and n_q_heads / n_kv_heads in
+ * {1, 2, 4, 8} (else VOX_E_UNSUPPORTED); 1 <= n_valid <= n_slots (else VOX_E_INVAL). */
+size_t vox_gqa_decode_attn_workspace(int n_q_heads, int n_kv_heads, int head_dim, int n_slots);
+int vox_gqa_decode_attn(const float *q, const float *k_cache, const float *v_cache, float *out,
+                        int n_q_heads, int n_kv_heads, int head_dim, int n_slots, int n_valid,
+                        float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Whole decoder step ([VC] 모델 아키텍처, 주요 기능, 성능 벤치마크).  Per token:
+ *   h = dequant(tok_embd[token]);
+ *   per layer: x = RMSNorm(h)*attn_norm; q,k,v = Wq x, Wk x, Wv x; RoPE(q, k) at the absolute
+ *   position (interleaved pairs); K/V written to ring slot pos % n_slots; grouped attention
+ *   over min(pos+1, n_slots) slots with scale 1/sqrt(head_dim); h += Wo o;
+ *   x = RMSNorm(h)*ffn_norm; h += Wdown (silu(Wgate x) * (Wup x));
+ *   logits = tok_embd * (RMSNorm(h)*out_norm)  (tied Q4_0 table as LM head);
+ *   token_out = first index of the largest logit; pos += 1.
+ * The whole step is captured once as a HIP graph and replayed, so a token costs one
+ * submission; position and token ids stay on the device between steps.
+ * ---------------------------------------------------------------------------------- */
+
+typedef struct vox_decoder vox_decoder_t;   /* opaque */
+
+typedef struct {
+    int n_layers, dim, n_heads, n_kv_heads, head_dim, hidden, vocab, n_slots;
+    float norm_eps, rope_theta;
+} vox_decoder_config;
+
+typedef struct {
+    const float *attn_norm, *ffn_norm;                          /* [dim] fp32 */
+    const void *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;     /* Q4_0 */
+} vox_layer_weights;
+
+typedef struct {
+    const void *tok_embd;                 /* Q4_0 [vocab][dim], embedding and LM head */
+    const float *out_norm;                /* [dim] */
+    const vox_layer_weights *layers;      /* host array of n_layers (copied at create) */
+} vox_decoder_weights;
+
+/* Sizes of the two caller-allocated device buffers: the KV ring
+ * ([n_layers][2][n_kv_heads][n_slots][head_dim] fp32) and the step scratch. */
+int vox_decoder_workspace(const vox_decoder_config *c, size_t *kv_bytes, size_t *scratch_bytes);
+
+/* Creates a decoder over caller-owned weights and buffers (which must outlive it and stay
+ * unchanged while work is in flight).  Supported shapes: dim, hidden and n_heads*head_dim
+ * multiples of 256 and at most 16384, head_dim 128, n_heads/n_kv_heads in {1,2,4,8}.
+ * Enqueues the clearing of the scratch counters on `stream`. */
+int vox_decoder_create(const vox_decoder_config *c, const vox_decoder_weights *w, void *kv,
+                       size_t kv_bytes, void *scratch, size_t scratch_bytes, void *stream,
+                       vox_decoder_t **out);
+/* Position back to 0 (the KV window is logically emptied). */
+int vox_decoder_reset(vox_decoder_t *d, void *stream);
+/* One token: reads token_in[0] (device int32 in [0, vocab)), writes token_out[0] (device
+ * int32) and, when logits is not NULL, logits[vocab] fp32.  token_out may equal token_in. */
+int vox_decoder_step(vox_decoder_t *d, const int32_t *token_in, int32_t *token_out, float *logits,
+                     void *stream);
+/* Number of steps taken since create/reset (the absolute position of the next token). */
+int vox_decoder_position(const vox_decoder_t *d, int64_t *pos);
+/* 1 (default): replay a captured HIP graph per step; 0: launch the kernels directly. */
+int vox_decoder_set_graph(vox_decoder_t *d, int enable);
+void vox_decoder_destroy(vox_decoder_t *d);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VOX_H */

@@ -1,0 +1,292 @@
+// gemv_core.h - Q4_0 matrix-vector product with dequantisation fused into the product.
+//
+// The quantised path of the Rust/Burn port ("Mistral의 Voxtral Mini 4B Realtime 모델을 Rust로
+// 구현해 브라우저에서 실행", GeekNews 26595, section 아키텍처) keeps every linear in GGUF Q4_0 and
+// fuses dequantisation into the matrix product; on the voxtral.c page ("Mistral Voxtral Realtime
+// 4B ... 순수 C 기반 CPU 전용 추론 구현", GeekNews 26608, section 성능 벤치마크) the decoder token
+// is bandwidth-heavy GPU work.  Here the product streams the 18-byte blocks from HBM once.
+//
+// Layout of the work (gfx950, wave64):
+//  * A workgroup owns tiles of R consecutive rows.  Rows are contiguous in memory, so a
+//    tile is one contiguous byte range (R * 9K/16 bytes, 16-byte aligned when K % 256 == 0)
+//    loaded with fully coalesced 16-byte loads into LDS.  The loads of the next tile are
+//    issued into registers before the current tile is computed (software pipelining), and
+//    workgroups loop over tiles (persistent grid sized to the occupancy of the chip).
+//  * Two consecutive blocks (36 bytes = 9 dwords, dword aligned) form a "pair".  Thread c of
+//    a row group owns pair column c for every row of the group: it holds the 64 activations
+//    of that column in registers for the whole kernel, reads its 9 dwords per row from LDS,
+//    unpacks the nibbles in registers and accumulates in fp32.
+//  * Per block: sum_j (code_j - 8) x_j = sum_j code_j x_j - 8 sum_j x_j; the second term is
+//    computed once per kernel.  High nibbles are masked in place (code*16) and the factor
+//    1/16 is folded into the block sum, so a nibble costs one mask share, one
+//    byte-to-float conversion and one FMA.
+//  * The K/64 partial sums of a row are combined through LDS in a fixed order (the result is
+//    deterministic run to run).
+#pragma once
+
+#include "vox_common.h"
+
+namespace vox {
+
+// Native 16-byte vector (HIP's uint4 is a union-based struct that keeps arrays of it out of
+// registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int K_, int NT_, int R_, int NPART_ = 1>
+struct GemvGeom {
+    static constexpr int K = K_;
+    static constexpr int NT = NT_;
+    static constexpr int R = R_;
+    static constexpr int NPART = NPART_;        // tile = NPART slices of R/NPART rows
+    static constexpr int NB = K / 32;           // Q4_0 blocks per row
+    static constexpr int RB = NB * 18;          // bytes per row
+    static constexpr int TR = K / 64;           // threads per row (one block pair each)
+    static constexpr int G = NT / TR;           // row groups per workgroup
+    static constexpr int RPP = R / NPART;       // rows per slice
+    static constexpr int TC = R * RB / 16;      // 16-byte chunks per tile
+    static constexpr int PC = RPP * RB / 16;    // 16-byte chunks per slice
+    static constexpr int CPT = (TC + NT - 1) / NT;
+    static_assert(K % 256 == 0, "rows must be 16-byte aligned");
+    static_assert(NT % 64 == 0 && NT % TR == 0, "workgroup must hold whole row groups");
+    static_assert(R % G == 0 && R % NPART == 0, "tile rows must split over the row groups");
+};
+
+// Byte j of v as a float: one v_cvt_f32_ubyte{j}.  Written as inline asm so that the
+// compiler cannot fold the nibble masks below into per-element bit-field extracts.
+__device__ __forceinline__ float ubyte_f(uint32_t v, int j)
+{
+    float r;
+    switch (j) {
+    case 0: asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v)); break;
+    case 1: asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v)); break;
+    case 2: asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v)); break;
+    default: asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v)); break;
+    }
+    return r;
+}
+
+// Sum over one block of (code - 8) * x, without the scale.  qs: the 16 code bytes;
+// x: the block's 32 activations; neg8sum = -8 * sum(x).
+__device__ __forceinline__ float q4_block_dot(const uint32_t (&qs)[4], const float *x, float neg8sum)
+{
+    float lo_acc = neg8sum;
+    float hi_acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = qs[i] & 0x0F0F0F0Fu;   // codes of weights 4i .. 4i+3
+        const uint32_t hi = qs[i] & 0xF0F0F0F0u;   // 16 * codes of weights 16+4i .. 16+4i+3
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo_acc = fmaf(ubyte_f(lo, j), x[4 * i + j], lo_acc);
+            hi_acc = fmaf(ubyte_f(hi, j), x[16 + 4 * i + j], hi_acc);
+        }
+    }
+    return fmaf(hi_acc, 0.0625f, lo_acc);
+}
+
+// Dot product of one block pair (9 dwords as stored) with its 64 activations.
+// dword 0 = d0 | codes0[0..1]; dwords 1..3 = codes0[2..13]; dword 4 = codes0[14..15] | d1;
+// dwords 5..8 = codes1[0..15].
+__device__ __forceinline__ float q4_pair_dot(const uint32_t (&D)[9], const float (&x)[64], float n8a,
+                                             float n8b)
+{
+    const uint32_t q0[4] = {(D[0] >> 16) | (D[1] << 16), (D[1] >> 16) | (D[2] << 16),
+                            (D[2] >> 16) | (D[3] << 16), (D[3] >> 16) | (D[4] << 16)};
+    const uint32_t q1[4] = {D[5], D[6], D[7], D[8]};
+    const float d0 = half_bits_to_float(D[0]);
+    const float d1 = half_bits_to_float(D[4] >> 16);
+    const float s0 = q4_block_dot(q0, x, n8a);
+    const float s1 = q4_block_dot(q1, x + 32, n8b);
+    return fmaf(d0, s0, d1 * s1);
+}
+
+// Per-kernel prologue result: the thread's 64 activations and the two -8*sum terms.
+struct PairX {
+    float x[64];
+    float n8a, n8b;
+
+    __device__ __forceinline__ void finish()
+    {
+        float a = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            a += x[j];
+            b += x[32 + j];
+        }
+        n8a = -8.0f * a;
+        n8b = -8.0f * b;
+    }
+};
+
+// Workgroup-wide sum of one float per thread, taken in a fixed order (thread 0 first).
+// `buf` holds at least NT floats of LDS.  All threads return the same value.
+template <int NT>
+__device__ __forceinline__ float block_sum_ordered(float v, float *buf, int count)
+{
+    buf[threadIdx.x] = v;
+    __syncthreads();
+    float s = 0.0f;
+    for (int i = 0; i < count; ++i)
+        s += buf[i];
+    __syncthreads();
+    return s;
+}
+
+// Issues the 16-byte loads of tile t into the thread's prefetch registers.
+template <class Gm, class Policy>
+__device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT])
+{
+    const uint8_t *base[Gm::NPART];
+    int valid_chunks[Gm::NPART];
+#pragma unroll
+    for (int p = 0; p < Gm::NPART; ++p) {
+        int rows_valid;
+        base[p] = P.slice(t, p, rows_valid);
+        valid_chunks[p] = rows_valid * (Gm::RB / 16);
+    }
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < Gm::CPT; ++i) {
+        const int ch = tid + i * Gm::NT;
+        const int p = Gm::NPART == 1 ? 0 : (ch < Gm::PC ? 0 : 1);
+        const int off = ch - p * Gm::PC;
+        if (ch < Gm::TC && off < valid_chunks[p])
+            pf[i] = *reinterpret_cast<const u32x4 *>(base[p] + (size_t)off * 16);
+    }
+}
+
+// The tile pipeline shared by every Q4_0 GEMV flavour.  Policy supplies:
+//   load_x(c, PairX&, float* lds_scratch)  prologue (may synchronise the workgroup)
+//   num_tiles()                            tiles of R rows
+//   slice(tile, part, &rows_valid)         base pointer of slice `part` of the tile
+//   epilogue(tile, const float* rowsum)    consume the R row sums (all threads call it)
+//   finish(float* lds_scratch)             after the last tile (all threads call it)
+template <class Gm, class Policy>
+__device__ __forceinline__ void gemv_tiles(Policy &P)
+{
+    __shared__ u32x4 tile[Gm::TC];
+    __shared__ float red[Gm::R * Gm::TR > Gm::NT ? Gm::R * Gm::TR : Gm::NT];
+    __shared__ float rowsum[Gm::R];
+
+    const int tid = threadIdx.x;
+    const int c = tid % Gm::TR;
+    const int g = tid / Gm::TR;
+
+    PairX px;
+    P.load_x(c, px, red);
+    px.finish();
+
+    const int ntiles = P.num_tiles();
+    u32x4 pf[Gm::CPT];
+
+    int t = blockIdx.x;
+    if (t < ntiles)
+        gemv_fetch<Gm>(P, t, pf);
+    for (; t < ntiles; t += gridDim.x) {
+#pragma unroll
+        for (int i = 0; i < Gm::CPT; ++i) {
+            const int ch = tid + i * Gm::NT;
+            if (ch < Gm::TC)
+                tile[ch] = pf[i];
+        }
+        __syncthreads();
+        if (t + (int)gridDim.x < ntiles)
+            gemv_fetch<Gm>(P, t + gridDim.x, pf);   // next tile's loads stay in flight during the compute
+
+        const uint32_t *lds32 = reinterpret_cast<const uint32_t *>(tile);
+#pragma unroll
+        for (int j = 0; j < Gm::R / Gm::G; ++j) {
+            const int rr = g + j * Gm::G;
+            const uint32_t *p = lds32 + rr * (Gm::RB / 4) + 9 * c;
+            uint32_t D[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i)
+                D[i] = p[i];
+            red[rr * Gm::TR + c] = q4_pair_dot(D, px.x, px.n8a, px.n8b);
+        }
+        __syncthreads();
+        if (tid < Gm::R) {
+            const float4 *r4 = reinterpret_cast<const float4 *>(red + tid * Gm::TR);
+            float s = 0.0f;
+#pragma unroll 4
+            for (int i = 0; i < Gm::TR / 4; ++i) {
+                const float4 v = r4[i];
+                s += v.x;
+                s += v.y;
+                s += v.z;
+                s += v.w;
+            }
+            rowsum[tid] = s;
+        }
+        __syncthreads();
+        P.epilogue(t, rowsum);
+    }
+    P.finish(red);
+}
+
+// ---------------------------------------------------------------------------------------
+// Prologues
+// ---------------------------------------------------------------------------------------
+
+// x read from a global fp32 vector.
+__device__ __forceinline__ void load_x_plain(const float *__restrict__ xg, int c, PairX &px)
+{
+    const float4 *x4 = reinterpret_cast<const float4 *>(xg + 64 * c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float4 v = x4[i];
+        px.x[4 * i + 0] = v.x;
+        px.x[4 * i + 1] = v.y;
+        px.x[4 * i + 2] = v.z;
+        px.x[4 * i + 3] = v.w;
+    }
+}
+
+// RMSNorm of the residual stream h (dim = 64 * TR) with gain g, eps inside the root:
+// x = h / sqrt(mean(h^2) + eps) * g.  The sum of squares is taken in a fixed order.
+template <int NT, int TR>
+__device__ __forceinline__ void rmsnorm_x(PairX &px, const float *__restrict__ gain, int c, float eps,
+                                          float *lds)
+{
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        ss = fmaf(px.x[j], px.x[j], ss);
+    const float tot = block_sum_ordered<NT>(ss, lds, TR);
+    const float inv = 1.0f / sqrtf(tot / (float)(64 * TR) + eps);
+    const float4 *g4 = reinterpret_cast<const float4 *>(gain + 64 * c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float4 gv = g4[i];
+        px.x[4 * i + 0] = px.x[4 * i + 0] * inv * gv.x;
+        px.x[4 * i + 1] = px.x[4 * i + 1] * inv * gv.y;
+        px.x[4 * i + 2] = px.x[4 * i + 2] * inv * gv.z;
+        px.x[4 * i + 3] = px.x[4 * i + 3] * inv * gv.w;
+    }
+}
+
+// Dequantise block pair c of one Q4_0 row (global memory) into 64 floats: (code - 8) * d.
+__device__ __forceinline__ void dequant_pair_global(const uint8_t *__restrict__ row, int c, float (&out)[64])
+{
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(row + 36 * c);
+    uint32_t D[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+        D[i] = p[i];
+    const uint32_t q0[4] = {(D[0] >> 16) | (D[1] << 16), (D[1] >> 16) | (D[2] << 16),
+                            (D[2] >> 16) | (D[3] << 16), (D[3] >> 16) | (D[4] << 16)};
+    const float d0 = half_bits_to_float(D[0]);
+    const float d1 = half_bits_to_float(D[4] >> 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            out[4 * i + j] = (float)((int)((q0[i] >> (8 * j)) & 15u) - 8) * d0;
+            out[16 + 4 * i + j] = (float)((int)((q0[i] >> (8 * j + 4)) & 15u) - 8) * d0;
+            out[32 + 4 * i + j] = (float)((int)((D[5 + i] >> (8 * j)) & 15u) - 8) * d1;
+            out[48 + 4 * i + j] = (float)((int)((D[5 + i] >> (8 * j + 4)) & 15u) - 8) * d1;
+        }
+    }
+}
+
+}  // namespace vox

@@ -1,0 +1,276 @@
+// gqa_attn.h - grouped-query decode attention of one token over a KV ring (split-K).
+//
+// Pages: the decoder uses GQA with 32 query heads over 8 KV heads (voxtral.c page "Mistral
+// Voxtral Realtime 4B 음성 인식 모델의 순수 C 기반 CPU 전용 추론 구현", GeekNews 26608, section
+// 모델 아키텍처; Rust port page, GeekNews 26595, section 아키텍처) and keeps a rolling KV cache
+// over an 8192-position sliding window (GeekNews 26608, section 주요 기능).
+//
+// For query head h of group g = h / GROUP:  s_t = scale * <q_h, K[g][t]>,
+// p = softmax(s) over the live slots, out_h = sum_t p_t V[g][t].
+//
+// MI355X mapping: eight KV heads cannot fill 256 compute units, so the live window is split
+// into S chunks (grid = S x n_kv_heads).  A workgroup streams its chunk of K and V for one
+// KV head once and serves all GROUP query heads of that head from the same loads.  Inside
+// the chunk it walks 64-position sub-chunks with an online softmax (running max and sum);
+// it writes a partial (max, sum, unnormalised output) and the partials are merged in a
+// fixed order, either by a second kernel or by the last workgroup of the head to finish.
+#pragma once
+
+#include "vox_common.h"
+
+namespace vox {
+
+constexpr int ATTN_HD = 128;          // head size handled by the kernels
+constexpr int ATTN_SUB = 64;          // positions per online-softmax sub-chunk
+constexpr int ATTN_MIN_CHUNK = 32;    // do not split below this many positions
+constexpr int ATTN_PART = 132;        // floats per partial: m, l, 2 pad, o[128]
+
+__host__ __device__ inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// Split plan for n_valid live slots with at most `s_max` chunks.  Every chunk is non-empty.
+struct AttnPlan {
+    int splits, chunk;
+};
+
+__host__ __device__ inline AttnPlan attn_plan(int n_valid, int s_max)
+{
+    int s = ceil_div_i(n_valid, ATTN_MIN_CHUNK);
+    if (s > s_max)
+        s = s_max;
+    if (s < 1)
+        s = 1;
+    const int chunk = ceil_div_i(n_valid, s);
+    return AttnPlan{ceil_div_i(n_valid, chunk), chunk};
+}
+
+// Most chunks a ring of n_slots may be split into.
+__host__ __device__ inline int attn_split_cap(int n_slots)
+{
+    int c = ceil_div_i(n_slots, 64);
+    return c < 1 ? 1 : (c > 128 ? 128 : c);
+}
+
+struct AttnArgs {
+    const float *q;          // [n_q][128]
+    const float *kc, *vc;    // [n_kv][n_slots][128]
+    float *out;              // [n_q][128]
+    float *part;             // [n_kv][s_cap][GROUP][ATTN_PART]
+    uint32_t *ticket;        // [n_kv] arrival counters (fused merge only); left at zero
+    const int64_t *pos;      // when set: n_valid = min(*pos + 1, n_slots)
+    int n_slots, n_valid, s_cap;
+    float scale;
+};
+
+template <int GROUP>
+__device__ __forceinline__ void attn_merge(const AttnArgs &a, int g, int nsplit, float *lds)
+{
+    // lds: at least 2 * nsplit + 8 floats
+    float *wts = lds;             // exp(m_s - M)
+    float *red = lds + nsplit;    // scratch
+    const int tid = threadIdx.x;
+    for (int h = 0; h < GROUP; ++h) {
+        const float *p0 = a.part + ((size_t)g * a.s_cap * GROUP + h) * ATTN_PART;
+        const size_t sstride = (size_t)GROUP * ATTN_PART;
+        // max of the partial maxima (fixed order: one thread walks the splits)
+        if (tid == 0) {
+            float M = -INFINITY;
+            for (int s = 0; s < nsplit; ++s)
+                M = fmaxf(M, p0[s * sstride]);
+            float L = 0.0f;
+            for (int s = 0; s < nsplit; ++s) {
+                const float w = __expf(p0[s * sstride] - M);
+                wts[s] = w;
+                L = fmaf(w, p0[s * sstride + 1], L);
+            }
+            red[0] = 1.0f / L;
+        }
+        __syncthreads();
+        if (tid < ATTN_HD) {
+            float o = 0.0f;
+            for (int s = 0; s < nsplit; ++s)
+                o = fmaf(wts[s], p0[s * sstride + 4 + tid], o);
+            a.out[((size_t)g * GROUP + h) * ATTN_HD + tid] = o * red[0];
+        }
+        __syncthreads();
+    }
+}
+
+template <int GROUP, bool FUSED_MERGE>
+__device__ __forceinline__ void attn_chunk(const AttnArgs &a)
+{
+    __shared__ float sc[GROUP][ATTN_SUB];            // scores, then weights, of a sub-chunk
+    __shared__ float alpha_s[GROUP];                 // rescale of the running sums
+    __shared__ float ored[4][GROUP][ATTN_HD];        // per-wave partial outputs
+    __shared__ float ml[GROUP][2];
+    __shared__ int last_flag;
+
+    const int g = blockIdx.y;
+    const int s = blockIdx.x;
+    int nv = a.n_valid;
+    if (a.pos) {
+        const int64_t p = *a.pos + 1;
+        nv = p < a.n_slots ? (int)p : a.n_slots;
+    }
+    const AttnPlan plan = attn_plan(nv, gridDim.x);
+    if (s >= plan.splits)
+        return;
+    const int t0 = s * plan.chunk;
+    const int t1 = min(nv, t0 + plan.chunk);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int pslot = lane >> 4;     // score phase: 4 positions per wave, 16 lanes each
+    const int seg = lane & 15;       // 8 dims per lane
+
+    const float *kbase = a.kc + (size_t)g * a.n_slots * ATTN_HD;
+    const float *vbase = a.vc + (size_t)g * a.n_slots * ATTN_HD;
+
+    float qv[GROUP][8];
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        const float4 *q4 = reinterpret_cast<const float4 *>(a.q + ((size_t)g * GROUP + h) * ATTN_HD + 8 * seg);
+        const float4 u = q4[0], v = q4[1];
+        qv[h][0] = u.x; qv[h][1] = u.y; qv[h][2] = u.z; qv[h][3] = u.w;
+        qv[h][4] = v.x; qv[h][5] = v.y; qv[h][6] = v.z; qv[h][7] = v.w;
+    }
+
+    float m_run[GROUP], l_run[GROUP];
+    float2 acc[GROUP];
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.0f;
+        acc[h] = make_float2(0.0f, 0.0f);
+    }
+
+    for (int base = t0; base < t1; base += ATTN_SUB) {
+        // issue the K and V loads of the whole sub-chunk first
+        float4 kr[4][2];
+        float2 vr[16];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int t = base + it * 16 + wave * 4 + pslot;
+            if (t < t1) {
+                const float4 *k4 = reinterpret_cast<const float4 *>(kbase + (size_t)t * ATTN_HD + 8 * seg);
+                kr[it][0] = k4[0];
+                kr[it][1] = k4[1];
+            } else {
+                kr[it][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+                kr[it][1] = kr[it][0];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = base + wave + 4 * i;
+            vr[i] = t < t1 ? *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane)
+                           : make_float2(0.0f, 0.0f);
+        }
+        // scores
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int p = it * 16 + wave * 4 + pslot;
+            const float kk[8] = {kr[it][0].x, kr[it][0].y, kr[it][0].z, kr[it][0].w,
+                                 kr[it][1].x, kr[it][1].y, kr[it][1].z, kr[it][1].w};
+#pragma unroll
+            for (int h = 0; h < GROUP; ++h) {
+                float d = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    d = fmaf(qv[h][i], kk[i], d);
+                d += __shfl_xor(d, 8, 64);
+                d += __shfl_xor(d, 4, 64);
+                d += __shfl_xor(d, 2, 64);
+                d += __shfl_xor(d, 1, 64);
+                if (seg == 0)
+                    sc[h][p] = (base + p < t1) ? d * a.scale : -INFINITY;
+            }
+        }
+        __syncthreads();
+        // online softmax update: one wave per query head
+        for (int h = wave; h < GROUP; h += 4) {
+            const float v = sc[h][lane];
+            const float mx = wave_max(v);
+            const float m_new = fmaxf(m_run[h], mx);
+            const float e = (v == -INFINITY) ? 0.0f : __expf(v - m_new);
+            const float sum = wave_sum(e);
+            sc[h][lane] = e;
+            const float al = (m_run[h] == -INFINITY) ? 0.0f : __expf(m_run[h] - m_new);
+            if (lane == 0)
+                alpha_s[h] = al;
+            l_run[h] = fmaf(l_run[h], al, sum);
+            m_run[h] = m_new;
+        }
+        __syncthreads();
+        // weighted values: wave w takes positions w, w+4, ...; lane owns dims 2*lane, 2*lane+1
+#pragma unroll
+        for (int h = 0; h < GROUP; ++h) {
+            const float al = alpha_s[h];
+            acc[h].x *= al;
+            acc[h].y *= al;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int p = wave + 4 * i;
+#pragma unroll
+            for (int h = 0; h < GROUP; ++h) {
+                const float w = sc[h][p];
+                acc[h].x = fmaf(w, vr[i].x, acc[h].x);
+                acc[h].y = fmaf(w, vr[i].y, acc[h].y);
+            }
+        }
+        __syncthreads();
+    }
+
+    // combine the four waves' partial outputs
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        ored[wave][h][2 * lane] = acc[h].x;
+        ored[wave][h][2 * lane + 1] = acc[h].y;
+    }
+    for (int h = wave; h < GROUP; h += 4) {
+        if (lane == 0) {
+            ml[h][0] = m_run[h];
+            ml[h][1] = l_run[h];
+        }
+    }
+    __syncthreads();
+
+    if (plan.splits == 1) {
+        for (int i = tid; i < GROUP * ATTN_HD; i += 256) {
+            const int h = i / ATTN_HD, d = i % ATTN_HD;
+            const float o = ((ored[0][h][d] + ored[1][h][d]) + ored[2][h][d]) + ored[3][h][d];
+            a.out[((size_t)g * GROUP + h) * ATTN_HD + d] = o / ml[h][1];
+        }
+        return;
+    }
+
+    float *mypart = a.part + ((size_t)g * a.s_cap + s) * GROUP * ATTN_PART;
+    for (int i = tid; i < GROUP * ATTN_HD; i += 256) {
+        const int h = i / ATTN_HD, d = i % ATTN_HD;
+        mypart[h * ATTN_PART + 4 + d] = ((ored[0][h][d] + ored[1][h][d]) + ored[2][h][d]) + ored[3][h][d];
+    }
+    if (tid < GROUP) {
+        mypart[tid * ATTN_PART + 0] = ml[tid][0];
+        mypart[tid * ATTN_PART + 1] = ml[tid][1];
+    }
+    if (!FUSED_MERGE)
+        return;
+
+    // last workgroup of this KV head merges the partials
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = atomicAdd(&a.ticket[g], 1u);
+        last_flag = (prev == (uint32_t)plan.splits - 1);
+    }
+    __syncthreads();
+    if (!last_flag)
+        return;
+    __threadfence();
+    attn_merge<GROUP>(a, g, plan.splits, &ored[0][0][0]);
+    if (tid == 0)
+        a.ticket[g] = 0u;   // ready for the next launch
+}
+
+}  // namespace vox
