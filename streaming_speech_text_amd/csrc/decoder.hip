@@ -1,0 +1,743 @@
+// decoder.hip - the per-token decoder step of streaming Voxtral Mini 4B Realtime.
+//
+// Pages: voxtral.c page ("Mistral Voxtral Realtime 4B 음성 인식 모델의 순수 C 기반 CPU 전용 추론
+// 구현", GeekNews 26608): section 모델 아키텍처 - LLM decoder of 26 layers, width 3072, GQA 32 query
+// heads / 8 KV heads, "Ministral-3 based" (read as a Llama-style pre-norm block with RMSNorm,
+// rotary positions and a SwiGLU feed-forward); section 주요 기능 - rolling KV cache with an
+// 8192-position window; section 성능 벤치마크 - the whole token is one GPU submission.  Rust port
+// page ("Mistral의 Voxtral Mini 4B Realtime 모델을 Rust로 구현해 브라우저에서 실행", GeekNews 26595):
+// section 아키텍처 - GGUF Q4_0 linears with dequantisation fused into the product; section 브라우저
+// 실행을 위한 기술적 해결 - the embedding stays on the GPU as Q4 and one row is used per token.
+//
+// One step = 4 kernels per layer + 1:
+//   qkv    RMSNorm prologue (layer 0: from the token's embedding row), Q/K/V Q4_0 GEMV over one
+//          concatenated row space, RoPE on q and k, k and v written to ring slot pos % n_slots
+//   attn   split-K grouped attention over min(pos+1, n_slots) slots; the last workgroup of a
+//          KV head merges the partials
+//   o      Q4_0 GEMV of the attention output, added into the residual stream
+//   ffn    RMSNorm prologue, gate and up rows in the same tile, silu(gate) * up
+//   down   Q4_0 GEMV, added into the residual stream
+//   head   final RMSNorm, tied Q4_0 table as LM head, logits (optional) and a device-wide
+//          argmax; the last workgroup writes the token, clears the argmax state and advances pos
+// The sequence is captured once into a HIP graph and replayed per token.
+#include <math.h>
+#include <stdlib.h>
+
+#include <new>
+#include <vector>
+
+#include "gemv_core.h"
+#include "gqa_attn.h"
+#include "vox_host.h"
+
+namespace vox {
+
+struct DecCtl {
+    int64_t pos;                  // absolute position of the next token
+    unsigned long long argmax;    // packed (logit, index) key of the running argmax
+    uint32_t lm_ticket;           // LM-head workgroups finished
+    uint32_t pad;
+    uint32_t attn_ticket[64];     // per KV head: attention workgroups finished
+};
+
+// ---------------------------------------------------------------------------------------
+// policies for the shared Q4_0 tile pipeline (gemv_core.h)
+// ---------------------------------------------------------------------------------------
+
+struct QkvArgs {
+    const uint8_t *wq, *wk, *wv;
+    int qrows, kvrows;
+    const float *h;              // residual stream (layers >= 1)
+    float *h_out;                // layer 0: receives the embedding row
+    const uint8_t *emb;
+    const int32_t *tok;
+    int vocab;
+    const float *gain;
+    float eps;
+    float *q_out, *kc, *vc;      // q [qrows]; this layer's K, V rings [n_kv][n_slots][128]
+    const DecCtl *ctl;
+    int n_slots;
+    float rope_theta;
+};
+
+template <class Gm, bool EMBED>
+struct QkvPolicy {
+    QkvArgs a;
+
+    __host__ __device__ static int tiles(const QkvArgs &a) { return (a.qrows + 2 * a.kvrows) / Gm::R; }
+
+    __device__ void load_x(int c, PairX &px, float *lds)
+    {
+        if (EMBED) {
+            int t = *a.tok;
+            t = t < 0 ? 0 : (t >= a.vocab ? a.vocab - 1 : t);
+            dequant_pair_global(a.emb + (size_t)t * Gm::RB, c, px.x);
+            if (blockIdx.x == 0 && threadIdx.x < Gm::TR) {
+                float4 *o = reinterpret_cast<float4 *>(a.h_out + 64 * c);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    o[i] = make_float4(px.x[4 * i], px.x[4 * i + 1], px.x[4 * i + 2], px.x[4 * i + 3]);
+            }
+        } else {
+            load_x_plain(a.h, c, px);
+        }
+        rmsnorm_x<Gm::NT, Gm::TR>(px, a.gain, c, a.eps, lds);
+    }
+    __device__ int num_tiles() const { return tiles(a); }
+    __device__ const uint8_t *slice(int t, int, int &rows_valid) const
+    {
+        rows_valid = Gm::R;
+        int r0 = t * Gm::R;
+        if (r0 < a.qrows)
+            return a.wq + (size_t)r0 * Gm::RB;
+        r0 -= a.qrows;
+        if (r0 < a.kvrows)
+            return a.wk + (size_t)r0 * Gm::RB;
+        return a.wv + (size_t)(r0 - a.kvrows) * Gm::RB;
+    }
+    __device__ void epilogue(int t, const float *rs)
+    {
+        const int tid = threadIdx.x;
+        if (tid >= Gm::R / 2)
+            return;
+        const int r0 = t * Gm::R + 2 * tid;
+        float y0 = rs[2 * tid], y1 = rs[2 * tid + 1];
+        const int64_t pos = a.ctl->pos;
+        const int region = r0 < a.qrows ? 0 : (r0 < a.qrows + a.kvrows ? 1 : 2);
+        if (region < 2) {
+            // rotary position: pair i of the head turns by pos * theta^(-2i/128) (angle in fp64)
+            const int i = (r0 % ATTN_HD) / 2;
+            const double ang = (double)pos * pow((double)a.rope_theta, -2.0 * (double)i / (double)ATTN_HD);
+            double sn, cs;
+            sincos(ang, &sn, &cs);
+            const float c = (float)cs, s = (float)sn;
+            const float u = y0 * c - y1 * s;
+            const float v = y0 * s + y1 * c;
+            y0 = u;
+            y1 = v;
+        }
+        if (region == 0) {
+            a.q_out[r0] = y0;
+            a.q_out[r0 + 1] = y1;
+        } else {
+            const int rr = r0 - a.qrows - (region == 2 ? a.kvrows : 0);
+            const int slot = (int)(pos % a.n_slots);
+            float *dst = (region == 1 ? a.kc : a.vc) + ((size_t)(rr / ATTN_HD) * a.n_slots + slot) * ATTN_HD +
+                         rr % ATTN_HD;
+            dst[0] = y0;
+            dst[1] = y1;
+        }
+    }
+    __device__ void finish(float *) {}
+};
+
+struct ResidualArgs {
+    const uint8_t *w;
+    const float *x;
+    float *h;
+    int n;
+};
+
+// y = W x added into the residual stream h (attention output projection, FFN down).
+template <class Gm>
+struct ResidualPolicy {
+    ResidualArgs a;
+
+    __host__ __device__ static int tiles(const ResidualArgs &a) { return a.n / Gm::R; }
+    __device__ void load_x(int c, PairX &px, float *) { load_x_plain(a.x, c, px); }
+    __device__ int num_tiles() const { return tiles(a); }
+    __device__ const uint8_t *slice(int t, int, int &rows_valid) const
+    {
+        rows_valid = Gm::R;
+        return a.w + (size_t)t * Gm::R * Gm::RB;
+    }
+    __device__ void epilogue(int t, const float *rs)
+    {
+        const int tid = threadIdx.x;
+        if (tid < Gm::R)
+            a.h[t * Gm::R + tid] += rs[tid];
+    }
+    __device__ void finish(float *) {}
+};
+
+struct GateUpArgs {
+    const uint8_t *wg, *wu;
+    int n;                  // hidden width
+    const float *h, *gain;
+    float eps;
+    float *act;
+};
+
+// act = silu(Wg x) * (Wu x) with x = RMSNorm(h) * gain; a tile holds R/2 gate rows then the
+// matching R/2 up rows.
+template <class Gm>
+struct GateUpPolicy {
+    GateUpArgs a;
+
+    __host__ __device__ static int tiles(const GateUpArgs &a) { return a.n / (Gm::R / 2); }
+    __device__ void load_x(int c, PairX &px, float *lds)
+    {
+        load_x_plain(a.h, c, px);
+        rmsnorm_x<Gm::NT, Gm::TR>(px, a.gain, c, a.eps, lds);
+    }
+    __device__ int num_tiles() const { return tiles(a); }
+    __device__ const uint8_t *slice(int t, int part, int &rows_valid) const
+    {
+        rows_valid = Gm::R / 2;
+        return (part == 0 ? a.wg : a.wu) + (size_t)t * (Gm::R / 2) * Gm::RB;
+    }
+    __device__ void epilogue(int t, const float *rs)
+    {
+        const int tid = threadIdx.x;
+        if (tid < Gm::R / 2)
+            a.act[t * (Gm::R / 2) + tid] = silu(rs[tid]) * rs[Gm::R / 2 + tid];
+    }
+    __device__ void finish(float *) {}
+};
+
+struct LmHeadArgs {
+    const uint8_t *emb;
+    int vocab;
+    const float *h, *gain;
+    float eps;
+    float *logits;          // may be null
+    DecCtl *ctl;
+    int32_t *tok_out;
+};
+
+template <class Gm>
+struct LmHeadPolicy {
+    LmHeadArgs a;
+    unsigned long long best;
+
+    __host__ __device__ static int tiles(const LmHeadArgs &a) { return (a.vocab + Gm::R - 1) / Gm::R; }
+    __device__ void load_x(int c, PairX &px, float *lds)
+    {
+        best = 0ull;
+        load_x_plain(a.h, c, px);
+        rmsnorm_x<Gm::NT, Gm::TR>(px, a.gain, c, a.eps, lds);
+    }
+    __device__ int num_tiles() const { return tiles(a); }
+    __device__ const uint8_t *slice(int t, int, int &rows_valid) const
+    {
+        const int r0 = t * Gm::R;
+        rows_valid = a.vocab - r0 < Gm::R ? a.vocab - r0 : Gm::R;
+        return a.emb + (size_t)r0 * Gm::RB;
+    }
+    __device__ void epilogue(int t, const float *rs)
+    {
+        const int tid = threadIdx.x;
+        const int r = t * Gm::R + tid;
+        if (tid < Gm::R && r < a.vocab) {
+            const float v = rs[tid];
+            if (a.logits)
+                a.logits[r] = v;
+            const unsigned long long k = argmax_key(v, (uint32_t)r);
+            best = k > best ? k : best;
+        }
+    }
+    __device__ void finish(float *lds)
+    {
+        __shared__ unsigned long long keys[Gm::R];
+        __shared__ int last;
+        const int tid = threadIdx.x;
+        if (tid < Gm::R)
+            keys[tid] = best;
+        __syncthreads();
+        if (tid == 0) {
+            unsigned long long m = 0ull;
+            for (int i = 0; i < Gm::R; ++i)
+                m = keys[i] > m ? keys[i] : m;
+            atomicMax(&a.ctl->argmax, m);
+            __threadfence();
+            const uint32_t prev = atomicAdd(&a.ctl->lm_ticket, 1u);
+            last = prev == gridDim.x - 1;
+        }
+        __syncthreads();
+        if (tid == 0 && last) {
+            // every workgroup's atomicMax happened before its ticket: the key is final
+            __threadfence();
+            const unsigned long long key = atomicMax(&a.ctl->argmax, 0ull);
+            a.tok_out[0] = (int32_t)argmax_key_index(key);
+            a.ctl->argmax = 0ull;
+            a.ctl->lm_ticket = 0u;
+            a.ctl->pos = a.ctl->pos + 1;
+            __threadfence();
+        }
+    }
+};
+
+template <class Gm, class Policy>
+__global__ __launch_bounds__(Gm::NT) void dec_gemv_kernel(Policy P)
+{
+    gemv_tiles<Gm>(P);
+}
+
+template <int GROUP>
+__global__ __launch_bounds__(256) void dec_attn_kernel(AttnArgs a)
+{
+    attn_chunk<GROUP, true>(a);
+}
+
+__global__ void dec_reset_kernel(DecCtl *ctl)
+{
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        ctl->pos = 0;
+        ctl->argmax = 0ull;
+        ctl->lm_ticket = 0u;
+        ctl->pad = 0u;
+    }
+    if (tid < 64)
+        ctl->attn_ticket[tid] = 0u;
+}
+
+// ---------------------------------------------------------------------------------------
+// host dispatch: widths are compile-time in the kernels
+// ---------------------------------------------------------------------------------------
+
+template <int K>
+constexpr int nt_for()
+{
+    return K == 1024 ? 128 : K == 2048 ? 128 : K == 3072 ? 192 : K == 4096 ? 256 : 576;
+}
+
+template <int K, int R, int NPART = 1>
+using DGeom = GemvGeom<K, nt_for<K>(), R, NPART>;
+
+template <class Gm, class Policy, class Args>
+static int launch_gemv(const Args &args, hipStream_t s, const char *what)
+{
+    static int occ = 0;
+    if (occ <= 0) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, dec_gemv_kernel<Gm, Policy>, Gm::NT, 0) != hipSuccess ||
+            v < 1)
+            v = 1;
+        occ = v;
+    }
+    const int ntiles = Policy::tiles(args);
+    const int cap = occ * cu_count();
+    const int grid = ntiles < cap ? ntiles : cap;
+    Policy P{args};
+    hipLaunchKernelGGL((dec_gemv_kernel<Gm, Policy>), dim3(grid > 0 ? grid : 1), dim3(Gm::NT), 0, s, P);
+    return check_launch(what);
+}
+
+// R choices: the group count G (= NT / (K/64)) must divide R.
+template <int K>
+constexpr int min_rows()
+{
+    return nt_for<K>() / (K / 64);
+}
+
+template <int K, bool EMBED>
+static int run_qkv(const QkvArgs &a, int R, hipStream_t s)
+{
+    if (R == 16)
+        return launch_gemv<DGeom<K, 16>, QkvPolicy<DGeom<K, 16>, EMBED>>(a, s, "decoder qkv");
+    return launch_gemv<DGeom<K, 8>, QkvPolicy<DGeom<K, 8>, EMBED>>(a, s, "decoder qkv");
+}
+
+template <int K>
+static int run_residual(const ResidualArgs &a, int R, hipStream_t s)
+{
+    if (R == 16)
+        return launch_gemv<DGeom<K, 16>, ResidualPolicy<DGeom<K, 16>>>(a, s, "decoder residual gemv");
+    if (R == 8 || min_rows<K>() > 4)
+        return launch_gemv<DGeom<K, 8>, ResidualPolicy<DGeom<K, 8>>>(a, s, "decoder residual gemv");
+    if constexpr (min_rows<K>() <= 4)
+        return launch_gemv<DGeom<K, 4>, ResidualPolicy<DGeom<K, 4>>>(a, s, "decoder residual gemv");
+    return VOX_E_UNSUPPORTED;
+}
+
+template <int K>
+static int run_gateup(const GateUpArgs &a, int R, hipStream_t s)
+{
+    if (R == 16)
+        return launch_gemv<DGeom<K, 16, 2>, GateUpPolicy<DGeom<K, 16, 2>>>(a, s, "decoder gate/up");
+    return launch_gemv<DGeom<K, 8, 2>, GateUpPolicy<DGeom<K, 8, 2>>>(a, s, "decoder gate/up");
+}
+
+template <int K>
+static int run_lmhead(const LmHeadArgs &a, int R, hipStream_t s)
+{
+    if (R == 16)
+        return launch_gemv<DGeom<K, 16>, LmHeadPolicy<DGeom<K, 16>>>(a, s, "decoder lm head");
+    return launch_gemv<DGeom<K, 8>, LmHeadPolicy<DGeom<K, 8>>>(a, s, "decoder lm head");
+}
+
+static bool model_width(int k) { return k == 1024 || k == 3072; }
+static bool attn_width(int k) { return k == 1024 || k == 4096; }
+static bool ffn_width(int k) { return k == 2048 || k == 9216; }
+
+// Tile height for n row-tiles-worth of work: tall tiles when there are plenty, otherwise short
+// ones so that every compute unit gets work.
+static int pick_r(int64_t rows, int min_r)
+{
+    const int64_t cu = cu_count();
+    if (rows >= 16 * 4 * cu)
+        return 16;
+    if (rows >= 8 * 2 * cu || min_r > 4)
+        return 8;
+    return 4;
+}
+
+struct Layout {
+    size_t ctl, h, q, o, act, part, total;
+};
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static Layout scratch_layout(const vox_decoder_config &c)
+{
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const int group = c.n_heads / c.n_kv_heads;
+    L.ctl = take(sizeof(DecCtl));
+    L.h = take((size_t)c.dim * 4);
+    L.q = take((size_t)c.n_heads * c.head_dim * 4);
+    L.o = take((size_t)c.n_heads * c.head_dim * 4);
+    L.act = take((size_t)c.hidden * 4);
+    L.part = take((size_t)c.n_kv_heads * attn_split_cap(c.n_slots) * group * ATTN_PART * 4);
+    L.total = off;
+    return L;
+}
+
+static size_t kv_bytes_for(const vox_decoder_config &c)
+{
+    return (size_t)c.n_layers * 2 * c.n_kv_heads * c.n_slots * c.head_dim * sizeof(float);
+}
+
+static int check_config(const vox_decoder_config *c)
+{
+    if (!c)
+        return fail(VOX_E_INVAL, "decoder: null config");
+    if (c->n_layers < 1 || c->dim < 1 || c->n_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 || c->hidden < 1 ||
+        c->vocab < 1 || c->n_slots < 1)
+        return fail(VOX_E_INVAL, "decoder: every size must be positive");
+    if (c->n_heads % c->n_kv_heads)
+        return fail(VOX_E_INVAL, "decoder: n_heads must be a multiple of n_kv_heads");
+    if (!(c->norm_eps >= 0.0f) || !(c->rope_theta > 0.0f))
+        return fail(VOX_E_INVAL, "decoder: need norm_eps >= 0 and rope_theta > 0");
+    const int group = c->n_heads / c->n_kv_heads;
+    if (c->head_dim != ATTN_HD || (group != 1 && group != 2 && group != 4 && group != 8) || c->n_kv_heads > 64)
+        return fail(VOX_E_UNSUPPORTED, "decoder: needs head_dim 128, n_heads/n_kv_heads in {1,2,4,8}, n_kv_heads <= 64");
+    if (!model_width(c->dim) || !attn_width(c->n_heads * c->head_dim) || !ffn_width(c->hidden))
+        return fail(VOX_E_UNSUPPORTED,
+                    "decoder: widths (dim %d, heads*head_dim %d, hidden %d) must be (3072|1024, 4096|1024, 9216|2048)",
+                    c->dim, c->n_heads * c->head_dim, c->hidden);
+    if (c->n_slots > (1 << 24) || c->vocab > (1 << 28))
+        return fail(VOX_E_UNSUPPORTED, "decoder: n_slots or vocab too large");
+    return VOX_OK;
+}
+
+}  // namespace vox
+
+using namespace vox;
+
+struct vox_decoder {
+    vox_decoder_config c;
+    std::vector<vox_layer_weights> layers;
+    const uint8_t *tok_embd;
+    const float *out_norm;
+    float *kv;
+    uint8_t *scratch;
+    Layout lay;
+    DecCtl *ctl;
+    float *h, *q, *o, *act, *part;
+    int group, s_cap;
+    int r_qkv, r_o, r_ffn, r_down, r_head;
+    int64_t host_pos;
+    bool use_graph;
+    hipStream_t cap_stream;
+    hipGraphExec_t graphs[16];
+    const int32_t *g_in;
+    int32_t *g_out;
+    float *g_logits;
+};
+
+namespace vox {
+
+static int attn_bucket(const vox_decoder *d, int64_t pos)
+{
+    const int64_t nv64 = pos + 1 < d->c.n_slots ? pos + 1 : d->c.n_slots;
+    const int splits = attn_plan((int)nv64, d->s_cap).splits;
+    int b = 0;
+    while ((1 << b) < splits)
+        ++b;
+    return b;   // grid width 1 << b, capped at s_cap at launch
+}
+
+template <int GROUP>
+static int launch_attn(const AttnArgs &a, int width, int n_kv, hipStream_t s)
+{
+    hipLaunchKernelGGL(dec_attn_kernel<GROUP>, dim3(width, n_kv), dim3(256), 0, s, a);
+    return check_launch("decoder attention");
+}
+
+static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out, float *logits, int bucket,
+                        hipStream_t s)
+{
+    const vox_decoder_config &c = d->c;
+    const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    const size_t ring = (size_t)c.n_kv_heads * c.n_slots * c.head_dim;
+    int width = 1 << bucket;
+    if (width > d->s_cap)
+        width = d->s_cap;
+    int st = VOX_OK;
+    for (int l = 0; l < c.n_layers && !st; ++l) {
+        const vox_layer_weights &L = d->layers[l];
+        float *kc = d->kv + (size_t)(2 * l) * ring;
+        float *vc = d->kv + (size_t)(2 * l + 1) * ring;
+
+        QkvArgs qa{};
+        qa.wq = (const uint8_t *)L.wq;
+        qa.wk = (const uint8_t *)L.wk;
+        qa.wv = (const uint8_t *)L.wv;
+        qa.qrows = qd;
+        qa.kvrows = kvd;
+        qa.h = d->h;
+        qa.h_out = d->h;
+        qa.emb = d->tok_embd;
+        qa.tok = tok_in;
+        qa.vocab = c.vocab;
+        qa.gain = L.attn_norm;
+        qa.eps = c.norm_eps;
+        qa.q_out = d->q;
+        qa.kc = kc;
+        qa.vc = vc;
+        qa.ctl = d->ctl;
+        qa.n_slots = c.n_slots;
+        qa.rope_theta = c.rope_theta;
+        if (c.dim == 3072)
+            st = l == 0 ? run_qkv<3072, true>(qa, d->r_qkv, s) : run_qkv<3072, false>(qa, d->r_qkv, s);
+        else
+            st = l == 0 ? run_qkv<1024, true>(qa, d->r_qkv, s) : run_qkv<1024, false>(qa, d->r_qkv, s);
+        if (st)
+            break;
+
+        AttnArgs aa{};
+        aa.q = d->q;
+        aa.kc = kc;
+        aa.vc = vc;
+        aa.out = d->o;
+        aa.part = d->part;
+        aa.ticket = d->ctl->attn_ticket;
+        aa.pos = &d->ctl->pos;
+        aa.n_slots = c.n_slots;
+        aa.n_valid = 0;
+        aa.s_cap = d->s_cap;
+        aa.scale = 1.0f / sqrtf((float)c.head_dim);
+        switch (d->group) {
+        case 1: st = launch_attn<1>(aa, width, c.n_kv_heads, s); break;
+        case 2: st = launch_attn<2>(aa, width, c.n_kv_heads, s); break;
+        case 4: st = launch_attn<4>(aa, width, c.n_kv_heads, s); break;
+        default: st = launch_attn<8>(aa, width, c.n_kv_heads, s); break;
+        }
+        if (st)
+            break;
+
+        ResidualArgs oa{(const uint8_t *)L.wo, d->o, d->h, c.dim};
+        st = qd == 4096 ? run_residual<4096>(oa, d->r_o, s) : run_residual<1024>(oa, d->r_o, s);
+        if (st)
+            break;
+
+        GateUpArgs ga{(const uint8_t *)L.w_gate, (const uint8_t *)L.w_up, c.hidden, d->h, L.ffn_norm, c.norm_eps,
+                      d->act};
+        st = c.dim == 3072 ? run_gateup<3072>(ga, d->r_ffn, s) : run_gateup<1024>(ga, d->r_ffn, s);
+        if (st)
+            break;
+
+        ResidualArgs da{(const uint8_t *)L.w_down, d->act, d->h, c.dim};
+        st = c.hidden == 9216 ? run_residual<9216>(da, d->r_down, s) : run_residual<2048>(da, d->r_down, s);
+    }
+    if (st)
+        return st;
+    LmHeadArgs la{d->tok_embd, c.vocab, d->h, d->out_norm, c.norm_eps, logits, d->ctl, tok_out};
+    return c.dim == 3072 ? run_lmhead<3072>(la, d->r_head, s) : run_lmhead<1024>(la, d->r_head, s);
+}
+
+static void drop_graphs(vox_decoder *d)
+{
+    for (auto &g : d->graphs) {
+        if (g)
+            hipGraphExecDestroy(g);
+        g = nullptr;
+    }
+}
+
+}  // namespace vox
+
+extern "C" int vox_decoder_workspace(const vox_decoder_config *c, size_t *kv_bytes, size_t *scratch_bytes)
+{
+    int st = check_config(c);
+    if (st)
+        return st;
+    if (!kv_bytes || !scratch_bytes)
+        return fail(VOX_E_INVAL, "vox_decoder_workspace: null output pointer");
+    *kv_bytes = kv_bytes_for(*c);
+    *scratch_bytes = scratch_layout(*c).total;
+    return ok();
+}
+
+extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder_weights *w, void *kv, size_t kv_bytes,
+                                  void *scratch, size_t scratch_bytes, void *stream, vox_decoder_t **out)
+{
+    if (!out)
+        return fail(VOX_E_INVAL, "vox_decoder_create: null output handle");
+    *out = nullptr;
+    int st = check_config(c);
+    if (st)
+        return st;
+    if (!w || !w->tok_embd || !w->out_norm || !w->layers || !kv || !scratch)
+        return fail(VOX_E_INVAL, "vox_decoder_create: null weight or buffer pointer");
+    for (int l = 0; l < c->n_layers; ++l) {
+        const vox_layer_weights &L = w->layers[l];
+        const void *ps[] = {L.attn_norm, L.ffn_norm, L.wq, L.wk, L.wv, L.wo, L.w_gate, L.w_up, L.w_down};
+        for (const void *p : ps) {
+            if (!p)
+                return fail(VOX_E_INVAL, "vox_decoder_create: layer %d has a null weight", l);
+            if (!aligned(p, 16))
+                return fail(VOX_E_UNSUPPORTED, "vox_decoder_create: layer %d weight not 16-byte aligned", l);
+        }
+    }
+    if (!aligned(w->tok_embd, 16) || !aligned(w->out_norm, 16) || !aligned(kv, 256) || !aligned(scratch, 256))
+        return fail(VOX_E_UNSUPPORTED, "vox_decoder_create: embedding/norm need 16-byte, buffers 256-byte alignment");
+    const Layout lay = scratch_layout(*c);
+    if (kv_bytes < kv_bytes_for(*c) || scratch_bytes < lay.total)
+        return fail(VOX_E_WORKSPACE, "vox_decoder_create: kv %zu (need %zu), scratch %zu (need %zu)", kv_bytes,
+                    kv_bytes_for(*c), scratch_bytes, lay.total);
+    if (overlaps(kv, kv_bytes_for(*c), scratch, lay.total))
+        return fail(VOX_E_INVAL, "vox_decoder_create: kv and scratch overlap");
+
+    vox_decoder *d = new (std::nothrow) vox_decoder();
+    if (!d)
+        return fail(VOX_E_INVAL, "vox_decoder_create: out of host memory");
+    d->c = *c;
+    d->layers.assign(w->layers, w->layers + c->n_layers);
+    d->tok_embd = (const uint8_t *)w->tok_embd;
+    d->out_norm = w->out_norm;
+    d->kv = (float *)kv;
+    d->scratch = (uint8_t *)scratch;
+    d->lay = lay;
+    d->ctl = (DecCtl *)(d->scratch + lay.ctl);
+    d->h = (float *)(d->scratch + lay.h);
+    d->q = (float *)(d->scratch + lay.q);
+    d->o = (float *)(d->scratch + lay.o);
+    d->act = (float *)(d->scratch + lay.act);
+    d->part = (float *)(d->scratch + lay.part);
+    d->group = c->n_heads / c->n_kv_heads;
+    d->s_cap = attn_split_cap(c->n_slots);
+    const int qd = c->n_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+    const int gmin_model = c->dim == 3072 ? 4 : 8;
+    d->r_qkv = pick_r(qd + 2 * kvd, 8);
+    d->r_o = pick_r(c->dim, qd == 4096 ? 4 : 8);
+    d->r_ffn = pick_r(2 * c->hidden, 8);
+    d->r_down = pick_r(c->dim, 4);
+    d->r_head = pick_r(c->vocab, gmin_model > 4 ? 8 : 8);
+    d->host_pos = 0;
+    d->use_graph = true;
+    d->cap_stream = nullptr;
+    for (auto &g : d->graphs)
+        g = nullptr;
+    st = check_hip(hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking), "vox_decoder_create: stream");
+    if (!st) {
+        hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl);
+        st = check_launch("vox_decoder_create: reset");
+    }
+    if (st) {
+        if (d->cap_stream)
+            hipStreamDestroy(d->cap_stream);
+        delete d;
+        return st;
+    }
+    *out = d;
+    return ok();
+}
+
+extern "C" int vox_decoder_reset(vox_decoder_t *d, void *stream)
+{
+    if (!d)
+        return fail(VOX_E_INVAL, "vox_decoder_reset: null handle");
+    hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl);
+    int st = check_launch("vox_decoder_reset");
+    if (st)
+        return st;
+    d->host_pos = 0;
+    return ok();
+}
+
+extern "C" int vox_decoder_step(vox_decoder_t *d, const int32_t *token_in, int32_t *token_out, float *logits,
+                                void *stream)
+{
+    if (!d || !token_in || !token_out)
+        return fail(VOX_E_INVAL, "vox_decoder_step: null pointer");
+    hipStream_t s = (hipStream_t)stream;
+    const int bucket = attn_bucket(d, d->host_pos);
+    int st;
+    if (!d->use_graph) {
+        st = enqueue_step(d, token_in, token_out, logits, bucket, s);
+    } else {
+        if (d->g_in != token_in || d->g_out != token_out || d->g_logits != logits) {
+            drop_graphs(d);
+            d->g_in = token_in;
+            d->g_out = token_out;
+            d->g_logits = logits;
+        }
+        if (!d->graphs[bucket]) {
+            st = check_hip(hipStreamBeginCapture(d->cap_stream, hipStreamCaptureModeThreadLocal), "begin capture");
+            if (st)
+                return st;
+            st = enqueue_step(d, token_in, token_out, logits, bucket, d->cap_stream);
+            hipGraph_t graph = nullptr;
+            const int st2 = check_hip(hipStreamEndCapture(d->cap_stream, &graph), "end capture");
+            if (!st)
+                st = st2;
+            if (!st)
+                st = check_hip(hipGraphInstantiate(&d->graphs[bucket], graph, nullptr, nullptr, 0), "instantiate");
+            if (graph)
+                hipGraphDestroy(graph);
+            if (st) {
+                d->graphs[bucket] = nullptr;
+                return st;
+            }
+        }
+        st = check_hip(hipGraphLaunch(d->graphs[bucket], s), "graph launch");
+    }
+    if (st)
+        return st;
+    d->host_pos += 1;
+    return ok();
+}
+
+extern "C" int vox_decoder_position(const vox_decoder_t *d, int64_t *pos)
+{
+    if (!d || !pos)
+        return fail(VOX_E_INVAL, "vox_decoder_position: null pointer");
+    *pos = d->host_pos;
+    return ok();
+}
+
+extern "C" int vox_decoder_set_graph(vox_decoder_t *d, int enable)
+{
+    if (!d)
+        return fail(VOX_E_INVAL, "vox_decoder_set_graph: null handle");
+    d->use_graph = enable != 0;
+    return ok();
+}
+
+extern "C" void vox_decoder_destroy(vox_decoder_t *d)
+{
+    if (!d)
+        return;
+    drop_graphs(d);
+    if (d->cap_stream)
+        hipStreamDestroy(d->cap_stream);
+    delete d;
+}

@@ -57,7 +57,8 @@ struct AttnArgs {
     float *part;             // [n_kv][s_cap][GROUP][ATTN_PART]
     uint32_t *ticket;        // [n_kv] arrival counters (fused merge only); left at zero
     const int64_t *pos;      // when set: n_valid = min(*pos + 1, n_slots)
-    int n_slots, n_valid, s_cap;
+    int n_slots, n_valid;
+    int s_cap;               // split cap (partials stride); the grid has >= plan.splits columns
     float scale;
 };
 
@@ -111,7 +112,7 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
         const int64_t p = *a.pos + 1;
         nv = p < a.n_slots ? (int)p : a.n_slots;
     }
-    const AttnPlan plan = attn_plan(nv, gridDim.x);
+    const AttnPlan plan = attn_plan(nv, a.s_cap);   // the host derives the same plan
     if (s >= plan.splits)
         return;
     const int t0 = s * plan.chunk;
@@ -187,8 +188,11 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
             }
         }
         __syncthreads();
-        // online softmax update: one wave per query head
-        for (int h = wave; h < GROUP; h += 4) {
+        // online softmax update: wave (h % 4) handles query head h
+#pragma unroll
+        for (int h = 0; h < GROUP; ++h) {
+            if ((h & 3) != wave)
+                continue;
             const float v = sc[h][lane];
             const float mx = wave_max(v);
             const float m_new = fmaxf(m_run[h], mx);
@@ -228,8 +232,9 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
         ored[wave][h][2 * lane] = acc[h].x;
         ored[wave][h][2 * lane + 1] = acc[h].y;
     }
-    for (int h = wave; h < GROUP; h += 4) {
-        if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        if ((h & 3) == wave && lane == 0) {
             ml[h][0] = m_run[h];
             ml[h][1] = l_run[h];
         }
