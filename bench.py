@@ -1,0 +1,226 @@
+"""Benchmark of the streaming Voxtral decoder-step hot path on one MI355X.
+
+Workload (one "step" = one decoder token): the full decoder shape - 26 layers, width 3072,
+GQA 32 query / 8 KV heads of 128, SwiGLU 9216, tied Q4_0 embedding / LM head of 131072 rows,
+8192-slot KV ring - with random-init Q4_0 weights from the seeded generator.  A 38-position
+prefix is teacher-forced (untimed), then K greedy steps run back to back with the token fed
+back on the device; each step replays the captured HIP graph of the step.
+
+Printed: one JSON line with decoder ms/token, the roofline of the dominant kernel (the Q4_0
+GEMV, timed with HIP events at the LM-head shape over rotating weight copies so that every
+launch streams from HBM), and the CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--gemv-launches", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--leg", choices=["all", "gemv"], default="all",
+                    help="gemv: only the GEMV roofline leg and a copy of known size (for counter runs)")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("gemv_core.h", "q4_gemv.hip", "vox_common.h"):
+        with open(os.path.join(ROOT, "streaming_speech_text_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(digest: str, launch_bytes: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    p = os.path.join(ROOT, "profiles", "q4_gemv_lmhead_counters.json")
+    try:
+        with open(p) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_digest") != digest:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def gemv_leg(args, torch, synth, vox, dev, stream):
+    """The Q4_0 GEMV at the LM-head shape (131072 x 3072), rotating over weight copies (more
+    than 1 GiB in total, so no launch is served from the 256 MB Infinity Cache), timed with
+    HIP events on the stream the launches go to."""
+    n, k = synth.VOXTRAL_DECODER.vocab, synth.VOXTRAL_DECODER.dim
+    gw, gx = synth.gemv_inputs(synth.SEED_GEMV, n, k)
+    copies = max(1, int(np.ceil(1.1 * 2 ** 30 / gw.nbytes)))
+    ws = [torch.from_numpy(gw).to(dev) for _ in range(copies)]
+    xd = torch.from_numpy(gx).to(dev)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    for i in range(copies):
+        vox.q4_gemv(ws[i], xd, y, stream=stream)
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(args.gemv_launches):
+        vox.q4_gemv(ws[i % copies], xd, y, stream=stream)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gemv_us = g0.elapsed_time(g1) * 1e3 / args.gemv_launches
+    launch_bytes = n * synth.q4_row_bytes(k) + 4 * (n + k)
+    achieved = launch_bytes / (gemv_us * 1e-6) / 1e9
+    print(f"[bench] q4 gemv {n}x{k}: {gemv_us:.2f} us/launch, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    del ws
+    torch.cuda.empty_cache()
+    return {"n": n, "k": k, "us": gemv_us, "bytes": launch_bytes, "gbs": achieved}
+
+
+def copy_calibration(torch, dev):
+    """A plain device copy of known size (256 MiB read + 256 MiB written), the reference the
+    HBM byte counters are scaled by."""
+    a = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
+              "described in DESIGN.md and not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from streaming_speech_text_amd import synth, vox
+
+    vox.lib()   # raises if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    if args.leg == "gemv":
+        copy_calibration(torch, dev)
+        g = gemv_leg(args, torch, synth, vox, dev, stream)
+        print(json.dumps({"leg": "gemv", **g}), flush=True)
+        return
+    s = synth.VOXTRAL_DECODER
+    print(f"[bench] generating weights ({s.n_layers} layers, vocab {s.vocab})", file=sys.stderr, flush=True)
+    w = synth.decoder_weights(synth.SEED_DECODER, s)
+    wd = {"tok_embd": torch.from_numpy(w["tok_embd"]).to(dev), "out_norm": torch.from_numpy(w["out_norm"]).to(dev),
+          "layers": [{k: torch.from_numpy(v).to(dev) for k, v in L.items()} for L in w["layers"]]}
+    cfg = vox.DecoderConfig(s.n_layers, s.dim, s.n_heads, s.n_kv_heads, s.head_dim, s.hidden, s.vocab, s.n_slots,
+                            s.norm_eps, s.rope_theta)
+    dec = vox.Decoder(cfg, wd)
+    prefix, start = synth.decoder_tokens(synth.SEED_DECODER, s.vocab)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run_prefix():
+        dec.reset()
+        for t in prefix:
+            tok.fill_(int(t))
+            dec.step(tok, tok)
+        tok.fill_(start)
+
+    # warmup: captures the graphs of every attention bucket the timed positions use
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    run_prefix()
+    for _ in range(max(args.warmup, args.steps)):
+        dec.step(tok, tok)
+    torch.cuda.synchronize()
+
+    run_prefix()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        dec.step(tok, tok)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_token = wall * 1e3 / args.steps
+    dev_ms = ev0.elapsed_time(ev1) / args.steps
+    last_token = int(tok.item())
+    step_weight_bytes = (s.n_layers * sum(o * synth.q4_row_bytes(i) for o, i in synth.LAYER_LINEARS.values())
+                         + s.vocab * synth.q4_row_bytes(s.dim) + synth.q4_row_bytes(s.dim))
+    kv_bytes = sum(s.n_layers * 2 * s.n_kv_heads * s.head_dim * 4 * min(p + 1, s.n_slots)
+                   for p in range(len(prefix), len(prefix) + args.steps)) / args.steps
+    step_bytes = step_weight_bytes + kv_bytes
+    print(f"[bench] decoder {ms_per_token:.4f} ms/token (device {dev_ms:.4f}), "
+          f"{step_bytes / (ms_per_token * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+    dec.close()
+    del wd
+    torch.cuda.empty_cache()
+
+    gemv = gemv_leg(args, torch, synth, vox, dev, stream)
+    traffic = measured_traffic(kernel_source_digest(), gemv["bytes"])
+
+    # CPU baseline: the oracle on the host cores, bounded sample of the same decoder workload
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        od = oracle.Decoder(s, w)
+        times = []
+        t_start = time.perf_counter()
+        for t in list(prefix):
+            a = time.perf_counter()
+            od.step(int(t), want_logits=False)
+            times.append(time.perf_counter() - a)
+            if time.perf_counter() - t_start > args.cpu_seconds and len(times) >= 3:
+                break
+        od.close()
+        cpu = {"value": round(1e3 * float(np.mean(times)), 3), "unit": "ms/token", "cores": threads,
+               "kind": "oracle",
+               "sample": f"first {len(times)} teacher-forced steps of the 38-token prefix at the full decoder "
+                         f"shape (fp64 oracle, OpenMP over output rows)"}
+
+    out = {
+        "metric": "decoder ms/token + Q4_0 GEMV achieved HBM GB/s (% of peak), 1 MI355X",
+        "value": round(ms_per_token, 4),
+        "unit": "ms/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_token, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_0 weights x fp32 activations, fp32 accumulate",
+        "data": "synthetic (seeded random-init Q4_0 weights, seeded token ids)",
+        "config": {"workload": "Voxtral decoder step: 26 layers, dim 3072, GQA 32/8 x 128, SwiGLU 9216, "
+                               "tied Q4_0 head 131072, 8192-slot KV ring, 38-token prefix then greedy steps",
+                   "tokens_timed": args.steps, "kv_positions": [len(prefix), len(prefix) + args.steps]},
+        "roofline": {"bound": "hbm", "achieved": round(gemv["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gemv["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": f"q4_gemv {gemv['n']}x{gemv['k']} (LM-head shape)", "bytes_per_launch": gemv["bytes"],
+                     "us_per_launch": round(gemv["us"], 3)},
+        "decoder_device_ms_per_token": round(dev_ms, 4),
+        "decoder_hbm_gbs": round(step_bytes / (ms_per_token * 1e-3) / 1e9, 1),
+        "decoder_bytes_per_token": int(step_bytes),
+        "last_token": last_token,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

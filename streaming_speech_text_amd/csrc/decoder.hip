@@ -24,6 +24,7 @@
 #include <stdlib.h>
 
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "gemv_core.h"
@@ -45,7 +46,8 @@ struct DecCtl {
 // ---------------------------------------------------------------------------------------
 
 struct QkvArgs {
-    const uint8_t *wq, *wk, *wv;
+    const uint8_t *wq;
+    int64_t dk, dv;              // byte offsets from wq to the K and V weights
     int qrows, kvrows;
     const float *h;              // residual stream (layers >= 1)
     float *h_out;                // layer 0: receives the embedding row
@@ -56,44 +58,112 @@ struct QkvArgs {
     float eps;
     float *q_out, *kc, *vc;      // q [qrows]; this layer's K, V rings [n_kv][n_slots][128]
     const DecCtl *ctl;
+    const double *rope_freq;     // [64]: theta^(-2i/128) / pi
     int n_slots;
-    float rope_theta;
+};
+
+// xs = RMSNorm(row) * gain for the token's row of the Q4_0 embedding table; the workgroup that
+// passes h_out also stores the raw row there (it is the first residual stream).
+template <int NT, int K>
+struct EmbedRmsNormX {
+    static constexpr int PAIRS = K / 64;
+    static constexpr int PER = (PAIRS + NT - 1) / NT;
+    static constexpr int GPER = (K / 4) / NT;
+    static_assert((K / 4) % NT == 0, "the workgroup must cover the vector evenly");
+    uint32_t raw[PER][9];
+    f32x4 gv[GPER];
+
+    __device__ __forceinline__ void issue(const uint8_t *__restrict__ row, const float *__restrict__ gain)
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = min((int)threadIdx.x + j * NT, PAIRS - 1);   // unconditional load
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(row + 36 * c);
+#pragma unroll
+            for (int i = 0; i < 9; ++i)
+                raw[j][i] = p[i];
+        }
+        const f32x4 *g4 = reinterpret_cast<const f32x4 *>(gain);
+#pragma unroll
+        for (int j = 0; j < GPER; ++j)
+            gv[j] = g4[threadIdx.x + j * NT];
+    }
+    __device__ __forceinline__ void stage(float *xs, float eps, float *wsum, float *h_out)
+    {
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c = threadIdx.x + j * NT;
+            if (c < PAIRS) {
+                float v[64];
+                dequant_pair_words(raw[j], v);
+                float4 *d4 = reinterpret_cast<float4 *>(xs + 64 * c);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float4 q = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+                    d4[i] = q;
+                    if (h_out)
+                        reinterpret_cast<float4 *>(h_out + 64 * c)[i] = q;
+                }
+#pragma unroll
+                for (int i = 0; i < 64; ++i)
+                    ss = fmaf(v[i], v[i], ss);
+            }
+        }
+        const float tot = block_sum_fixed<NT>(ss, wsum);   // its barriers also publish xs
+        const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+        f32x4 *x4 = reinterpret_cast<f32x4 *>(xs);
+#pragma unroll
+        for (int j = 0; j < GPER; ++j)
+            x4[threadIdx.x + j * NT] = x4[threadIdx.x + j * NT] * inv * gv[j];
+        __syncthreads();
+    }
 };
 
 template <class Gm, bool EMBED>
 struct QkvPolicy {
     QkvArgs a;
+    int64_t pos;
+    double freq;   // RoPE frequency of this thread's row pair in the next tile
 
     __host__ __device__ static int tiles(const QkvArgs &a) { return (a.qrows + 2 * a.kvrows) / Gm::R; }
 
-    __device__ void load_x(int c, PairX &px, float *lds)
+    typedef std::conditional_t<EMBED, EmbedRmsNormX<Gm::NT, Gm::K>, RmsNormX<Gm::NT, Gm::K>> XRegs;
+    __device__ void x_issue(XRegs &x)
     {
-        if (EMBED) {
+        if constexpr (EMBED) {
             int t = *a.tok;
             t = t < 0 ? 0 : (t >= a.vocab ? a.vocab - 1 : t);
-            dequant_pair_global(a.emb + (size_t)t * Gm::RB, c, px.x);
-            if (blockIdx.x == 0 && threadIdx.x < Gm::TR) {
-                float4 *o = reinterpret_cast<float4 *>(a.h_out + 64 * c);
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    o[i] = make_float4(px.x[4 * i], px.x[4 * i + 1], px.x[4 * i + 2], px.x[4 * i + 3]);
-            }
+            x.issue(a.emb + (size_t)t * Gm::RB, a.gain);
         } else {
-            load_x_plain(a.h, c, px);
+            x.issue(a.h, a.gain);
         }
-        rmsnorm_x<Gm::NT, Gm::TR>(px, a.gain, c, a.eps, lds);
+    }
+    __device__ void x_stage(XRegs &x, float *xs, float *wsum)
+    {
+        if constexpr (EMBED)
+            x.stage(xs, a.eps, wsum, blockIdx.x == 0 ? a.h_out : nullptr);
+        else
+            x.stage(xs, a.eps, wsum);
+    }
+    __device__ void pre(int t)
+    {
+        pos = a.ctl->pos;
+        const int r0 = t * Gm::R + 2 * min((int)threadIdx.x, Gm::R / 2 - 1);
+        freq = a.rope_freq[(r0 % ATTN_HD) / 2];   // unconditional load (v rows ignore it)
     }
     __device__ int num_tiles() const { return tiles(a); }
     __device__ const uint8_t *slice(int t, int, int &rows_valid) const
     {
+        // integer selects (a choice among pointer fields would be lowered to an indexed load
+        // from a stack copy of the arguments)
         rows_valid = Gm::R;
-        int r0 = t * Gm::R;
-        if (r0 < a.qrows)
-            return a.wq + (size_t)r0 * Gm::RB;
-        r0 -= a.qrows;
-        if (r0 < a.kvrows)
-            return a.wk + (size_t)r0 * Gm::RB;
-        return a.wv + (size_t)(r0 - a.kvrows) * Gm::RB;
+        const int r0 = t * Gm::R;
+        const bool is_q = r0 < a.qrows, is_k = !is_q && r0 < a.qrows + a.kvrows;
+        const int64_t off = is_q ? (int64_t)r0 * Gm::RB
+                                 : (is_k ? a.dk + (int64_t)(r0 - a.qrows) * Gm::RB
+                                         : a.dv + (int64_t)(r0 - a.qrows - a.kvrows) * Gm::RB);
+        return a.wq + off;
     }
     __device__ void epilogue(int t, const float *rs)
     {
@@ -102,14 +172,13 @@ struct QkvPolicy {
             return;
         const int r0 = t * Gm::R + 2 * tid;
         float y0 = rs[2 * tid], y1 = rs[2 * tid + 1];
-        const int64_t pos = a.ctl->pos;
         const int region = r0 < a.qrows ? 0 : (r0 < a.qrows + a.kvrows ? 1 : 2);
         if (region < 2) {
-            // rotary position: pair i of the head turns by pos * theta^(-2i/128) (angle in fp64)
-            const int i = (r0 % ATTN_HD) / 2;
-            const double ang = (double)pos * pow((double)a.rope_theta, -2.0 * (double)i / (double)ATTN_HD);
+            // rotary position: pair i of the head turns by pos * theta^(-2i/128) radians; the
+            // angle is formed in fp64 in units of pi so that its reduction is exact
+            const double ang_pi = (double)pos * freq;
             double sn, cs;
-            sincos(ang, &sn, &cs);
+            sincospi(ang_pi, &sn, &cs);
             const float c = (float)cs, s = (float)sn;
             const float u = y0 * c - y1 * s;
             const float v = y0 * s + y1 * c;
@@ -142,9 +211,16 @@ struct ResidualArgs {
 template <class Gm>
 struct ResidualPolicy {
     ResidualArgs a;
+    float hv;   // residual value of this thread's row, loaded with the tile
 
     __host__ __device__ static int tiles(const ResidualArgs &a) { return a.n / Gm::R; }
-    __device__ void load_x(int c, PairX &px, float *) { load_x_plain(a.x, c, px); }
+    typedef PlainX<Gm::NT, Gm::K> XRegs;
+    __device__ void x_issue(XRegs &r) { r.issue(a.x); }
+    __device__ void x_stage(XRegs &r, float *xs, float *) { r.stage(xs); }
+    __device__ void pre(int t)
+    {
+        hv = a.h[t * Gm::R + min((int)threadIdx.x, Gm::R - 1)];   // unconditional load
+    }
     __device__ int num_tiles() const { return tiles(a); }
     __device__ const uint8_t *slice(int t, int, int &rows_valid) const
     {
@@ -155,7 +231,7 @@ struct ResidualPolicy {
     {
         const int tid = threadIdx.x;
         if (tid < Gm::R)
-            a.h[t * Gm::R + tid] += rs[tid];
+            a.h[t * Gm::R + tid] = hv + rs[tid];
     }
     __device__ void finish(float *) {}
 };
@@ -175,11 +251,10 @@ struct GateUpPolicy {
     GateUpArgs a;
 
     __host__ __device__ static int tiles(const GateUpArgs &a) { return a.n / (Gm::R / 2); }
-    __device__ void load_x(int c, PairX &px, float *lds)
-    {
-        load_x_plain(a.h, c, px);
-        rmsnorm_x<Gm::NT, Gm::TR>(px, a.gain, c, a.eps, lds);
-    }
+    typedef RmsNormX<Gm::NT, Gm::K> XRegs;
+    __device__ void x_issue(XRegs &r) { r.issue(a.h, a.gain); }
+    __device__ void x_stage(XRegs &r, float *xs, float *wsum) { r.stage(xs, a.eps, wsum); }
+    __device__ void pre(int) {}
     __device__ int num_tiles() const { return tiles(a); }
     __device__ const uint8_t *slice(int t, int part, int &rows_valid) const
     {
@@ -211,12 +286,14 @@ struct LmHeadPolicy {
     unsigned long long best;
 
     __host__ __device__ static int tiles(const LmHeadArgs &a) { return (a.vocab + Gm::R - 1) / Gm::R; }
-    __device__ void load_x(int c, PairX &px, float *lds)
+    typedef RmsNormX<Gm::NT, Gm::K> XRegs;
+    __device__ void x_issue(XRegs &r)
     {
         best = 0ull;
-        load_x_plain(a.h, c, px);
-        rmsnorm_x<Gm::NT, Gm::TR>(px, a.gain, c, a.eps, lds);
+        r.issue(a.h, a.gain);
     }
+    __device__ void x_stage(XRegs &r, float *xs, float *wsum) { r.stage(xs, a.eps, wsum); }
+    __device__ void pre(int) {}
     __device__ int num_tiles() const { return tiles(a); }
     __device__ const uint8_t *slice(int t, int, int &rows_valid) const
     {
@@ -274,9 +351,17 @@ __global__ __launch_bounds__(Gm::NT) void dec_gemv_kernel(Policy P)
 }
 
 template <int GROUP>
-__global__ __launch_bounds__(256) void dec_attn_kernel(AttnArgs a)
+__global__ __launch_bounds__(ATTN_THREADS) void dec_attn_kernel(AttnArgs a)
 {
     attn_chunk<GROUP, true>(a);
+}
+
+// RoPE frequencies theta^(-2i/head_dim) / pi, i < head_dim/2, in fp64 (once per decoder).
+__global__ void dec_rope_table_kernel(double *freq, float theta)
+{
+    const int i = threadIdx.x;
+    if (i < ATTN_HD / 2)
+        freq[i] = pow((double)theta, -2.0 * (double)i / (double)ATTN_HD) / 3.14159265358979323846;
 }
 
 __global__ void dec_reset_kernel(DecCtl *ctl)
@@ -384,7 +469,7 @@ static int pick_r(int64_t rows, int min_r)
 }
 
 struct Layout {
-    size_t ctl, h, q, o, act, part, total;
+    size_t ctl, rope, h, q, o, act, part, total;
 };
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -400,6 +485,7 @@ static Layout scratch_layout(const vox_decoder_config &c)
     };
     const int group = c.n_heads / c.n_kv_heads;
     L.ctl = take(sizeof(DecCtl));
+    L.rope = take(sizeof(double) * ATTN_HD / 2);
     L.h = take((size_t)c.dim * 4);
     L.q = take((size_t)c.n_heads * c.head_dim * 4);
     L.o = take((size_t)c.n_heads * c.head_dim * 4);
@@ -450,6 +536,7 @@ struct vox_decoder {
     uint8_t *scratch;
     Layout lay;
     DecCtl *ctl;
+    double *rope;
     float *h, *q, *o, *act, *part;
     int group, s_cap;
     int r_qkv, r_o, r_ffn, r_down, r_head;
@@ -477,7 +564,7 @@ static int attn_bucket(const vox_decoder *d, int64_t pos)
 template <int GROUP>
 static int launch_attn(const AttnArgs &a, int width, int n_kv, hipStream_t s)
 {
-    hipLaunchKernelGGL(dec_attn_kernel<GROUP>, dim3(width, n_kv), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(dec_attn_kernel<GROUP>, dim3(width, n_kv), dim3(ATTN_THREADS), 0, s, a);
     return check_launch("decoder attention");
 }
 
@@ -498,8 +585,8 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
 
         QkvArgs qa{};
         qa.wq = (const uint8_t *)L.wq;
-        qa.wk = (const uint8_t *)L.wk;
-        qa.wv = (const uint8_t *)L.wv;
+        qa.dk = (int64_t)((uintptr_t)L.wk - (uintptr_t)L.wq);
+        qa.dv = (int64_t)((uintptr_t)L.wv - (uintptr_t)L.wq);
         qa.qrows = qd;
         qa.kvrows = kvd;
         qa.h = d->h;
@@ -513,8 +600,8 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
         qa.kc = kc;
         qa.vc = vc;
         qa.ctl = d->ctl;
+        qa.rope_freq = d->rope;
         qa.n_slots = c.n_slots;
-        qa.rope_theta = c.rope_theta;
         if (c.dim == 3072)
             st = l == 0 ? run_qkv<3072, true>(qa, d->r_qkv, s) : run_qkv<3072, false>(qa, d->r_qkv, s);
         else
@@ -627,6 +714,7 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     d->scratch = (uint8_t *)scratch;
     d->lay = lay;
     d->ctl = (DecCtl *)(d->scratch + lay.ctl);
+    d->rope = (double *)(d->scratch + lay.rope);
     d->h = (float *)(d->scratch + lay.h);
     d->q = (float *)(d->scratch + lay.q);
     d->o = (float *)(d->scratch + lay.o);
@@ -648,8 +736,9 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
         g = nullptr;
     st = check_hip(hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking), "vox_decoder_create: stream");
     if (!st) {
+        hipLaunchKernelGGL(dec_rope_table_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->rope, c->rope_theta);
         hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl);
-        st = check_launch("vox_decoder_create: reset");
+        st = check_launch("vox_decoder_create: init");
     }
     if (st) {
         if (d->cap_stream)

@@ -31,6 +31,7 @@ namespace vox {
 // Native 16-byte vector (HIP's uint4 is a union-based struct that keeps arrays of it out of
 // registers).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int K_, int NT_, int R_, int NPART_ = 1>
 struct GemvGeom {
@@ -118,21 +119,26 @@ struct PairX {
     }
 };
 
-// Workgroup-wide sum of one float per thread, taken in a fixed order (thread 0 first).
-// `buf` holds at least NT floats of LDS.  All threads return the same value.
+// Workgroup-wide sum of one float per thread in a fixed order: a butterfly within each wave,
+// then the wave totals in wave order.  `buf` holds at least NT/64 floats of LDS.  All threads
+// return the same value.
 template <int NT>
-__device__ __forceinline__ float block_sum_ordered(float v, float *buf, int count)
+__device__ __forceinline__ float block_sum_fixed(float v, float *buf)
 {
-    buf[threadIdx.x] = v;
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0)
+        buf[threadIdx.x >> 6] = v;
     __syncthreads();
     float s = 0.0f;
-    for (int i = 0; i < count; ++i)
-        s += buf[i];
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w)
+        s += buf[w];
     __syncthreads();
     return s;
 }
-
-// Issues the 16-byte loads of tile t into the thread's prefetch registers.
+// Issues the 16-byte loads of tile t into the thread's prefetch registers.  The loads are
+// unconditional (chunks past the end of a short tile re-read the tile's first chunk), so no
+// branch separates them and the compiler's wait counts stay exact.
 template <class Gm, class Policy>
 __device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT])
 {
@@ -144,54 +150,84 @@ __device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT
         base[p] = P.slice(t, p, rows_valid);
         valid_chunks[p] = rows_valid * (Gm::RB / 16);
     }
+    // one base pointer plus integer offsets: a choice between pointers would turn the loads
+    // into flat loads, which also count against the LDS wait counter
+    const int64_t delta = Gm::NPART == 1 ? 0 : (int64_t)((uintptr_t)base[Gm::NPART - 1] - (uintptr_t)base[0]);
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < Gm::CPT; ++i) {
         const int ch = tid + i * Gm::NT;
         const int p = Gm::NPART == 1 ? 0 : (ch < Gm::PC ? 0 : 1);
-        const int off = ch - p * Gm::PC;
-        if (ch < Gm::TC && off < valid_chunks[p])
-            pf[i] = *reinterpret_cast<const u32x4 *>(base[p] + (size_t)off * 16);
+        int off = ch - p * Gm::PC;
+        off = (ch < Gm::TC && off < valid_chunks[p]) ? off : 0;
+        pf[i] = *reinterpret_cast<const u32x4 *>(base[0] + (p ? delta : (int64_t)0) + (int64_t)off * 16);
     }
 }
 
 // The tile pipeline shared by every Q4_0 GEMV flavour.  Policy supplies:
-//   load_x(c, PairX&, float* lds_scratch)  prologue (may synchronise the workgroup)
+//   XRegs, x_issue(XRegs&)                 issue the activation loads into registers
+//   x_stage(XRegs&, float* xs, float* wsum) fill xs[K] with the activations (all threads call
+//                                          it; it ends with a workgroup barrier)
 //   num_tiles()                            tiles of R rows
+//   pre(tile)                              early loads the epilogue of `tile` will need
 //   slice(tile, part, &rows_valid)         base pointer of slice `part` of the tile
 //   epilogue(tile, const float* rowsum)    consume the R row sums (all threads call it)
 //   finish(float* lds_scratch)             after the last tile (all threads call it)
 template <class Gm, class Policy>
 __device__ __forceinline__ void gemv_tiles(Policy &P)
 {
-    __shared__ u32x4 tile[Gm::TC];
-    __shared__ float red[Gm::R * Gm::TR > Gm::NT ? Gm::R * Gm::TR : Gm::NT];
+    __shared__ u32x4 tile[Gm::CPT * Gm::NT];   // padded: every thread stores all its chunks
+    __shared__ float red[Gm::R * Gm::TR];
     __shared__ float rowsum[Gm::R];
+    __shared__ __attribute__((aligned(16))) float xs[Gm::K];   // the activation vector of the product
+    __shared__ float wsum[Gm::NT / 64];
 
     const int tid = threadIdx.x;
     const int c = tid % Gm::TR;
     const int g = tid / Gm::TR;
-
-    PairX px;
-    P.load_x(c, px, red);
-    px.finish();
-
     const int ntiles = P.num_tiles();
     u32x4 pf[Gm::CPT];
 
+    // Memory requests in issue order: the activations (needed first), then the first tile of
+    // weights, then whatever the epilogue needs.  Loads retire in order, so waiting for the
+    // activations leaves the weight tile in flight while the prologue runs.
+    typename Policy::XRegs xr;
+    P.x_issue(xr);
     int t = blockIdx.x;
-    if (t < ntiles)
-        gemv_fetch<Gm>(P, t, pf);
+    {
+        // unconditional (no branch around the loads); the grid never exceeds the tile count
+        const int t0 = t < ntiles ? t : ntiles - 1;
+        gemv_fetch<Gm>(P, t0, pf);
+        P.pre(t0);
+    }
+    // keeps the compiler from sinking the weight loads below the prologue
+    asm volatile("" ::: "memory");
+    // The workgroup stages the activation vector once in LDS (normalisation applied there);
+    // each thread then keeps the 64 values of its pair column in registers.
+    P.x_stage(xr, xs, wsum);
+    PairX px;
+    {
+        const float4 *x4 = reinterpret_cast<const float4 *>(xs + 64 * c);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float4 v = x4[i];
+            px.x[4 * i + 0] = v.x;
+            px.x[4 * i + 1] = v.y;
+            px.x[4 * i + 2] = v.z;
+            px.x[4 * i + 3] = v.w;
+        }
+    }
+    px.finish();
+
     for (; t < ntiles; t += gridDim.x) {
 #pragma unroll
-        for (int i = 0; i < Gm::CPT; ++i) {
-            const int ch = tid + i * Gm::NT;
-            if (ch < Gm::TC)
-                tile[ch] = pf[i];
-        }
+        for (int i = 0; i < Gm::CPT; ++i)
+            tile[tid + i * Gm::NT] = pf[i];
         __syncthreads();
-        if (t + (int)gridDim.x < ntiles)
+        if (t + (int)gridDim.x < ntiles) {
             gemv_fetch<Gm>(P, t + gridDim.x, pf);   // next tile's loads stay in flight during the compute
+        }
+        asm volatile("" ::: "memory");
 
         const uint32_t *lds32 = reinterpret_cast<const uint32_t *>(tile);
 #pragma unroll
@@ -220,59 +256,87 @@ __device__ __forceinline__ void gemv_tiles(Policy &P)
         }
         __syncthreads();
         P.epilogue(t, rowsum);
+        if (t + (int)gridDim.x < ntiles)
+            P.pre(t + gridDim.x);
     }
     P.finish(red);
 }
 
 // ---------------------------------------------------------------------------------------
-// Prologues
+// Prologues: stage the activation vector in LDS
 // ---------------------------------------------------------------------------------------
 
-// x read from a global fp32 vector.
-__device__ __forceinline__ void load_x_plain(const float *__restrict__ xg, int c, PairX &px)
-{
-    const float4 *x4 = reinterpret_cast<const float4 *>(xg + 64 * c);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float4 v = x4[i];
-        px.x[4 * i + 0] = v.x;
-        px.x[4 * i + 1] = v.y;
-        px.x[4 * i + 2] = v.z;
-        px.x[4 * i + 3] = v.w;
-    }
-}
+// Activation staging in two halves: *_issue loads this thread's share of the vector into
+// registers (fully unrolled, so every load is in flight at once), *_stage finishes the
+// arithmetic and writes xs[K] in LDS.
 
-// RMSNorm of the residual stream h (dim = 64 * TR) with gain g, eps inside the root:
-// x = h / sqrt(mean(h^2) + eps) * g.  The sum of squares is taken in a fixed order.
-template <int NT, int TR>
-__device__ __forceinline__ void rmsnorm_x(PairX &px, const float *__restrict__ gain, int c, float eps,
-                                          float *lds)
-{
-    float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 64; ++j)
-        ss = fmaf(px.x[j], px.x[j], ss);
-    const float tot = block_sum_ordered<NT>(ss, lds, TR);
-    const float inv = 1.0f / sqrtf(tot / (float)(64 * TR) + eps);
-    const float4 *g4 = reinterpret_cast<const float4 *>(gain + 64 * c);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float4 gv = g4[i];
-        px.x[4 * i + 0] = px.x[4 * i + 0] * inv * gv.x;
-        px.x[4 * i + 1] = px.x[4 * i + 1] * inv * gv.y;
-        px.x[4 * i + 2] = px.x[4 * i + 2] * inv * gv.z;
-        px.x[4 * i + 3] = px.x[4 * i + 3] * inv * gv.w;
-    }
-}
+// xs = x (a global fp32 vector of K values).
+template <int NT, int K>
+struct PlainX {
+    static constexpr int PER = (K / 4 + NT - 1) / NT;
+    f32x4 v[PER];
 
-// Dequantise block pair c of one Q4_0 row (global memory) into 64 floats: (code - 8) * d.
-__device__ __forceinline__ void dequant_pair_global(const uint8_t *__restrict__ row, int c, float (&out)[64])
-{
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(row + 36 * c);
-    uint32_t D[9];
+    static_assert((K / 4) % NT == 0, "the workgroup must cover the vector evenly");
+
+    __device__ __forceinline__ void issue(const float *__restrict__ xg)
+    {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(xg);
 #pragma unroll
-    for (int i = 0; i < 9; ++i)
-        D[i] = p[i];
+        for (int j = 0; j < PER; ++j)
+            v[j] = src[threadIdx.x + j * NT];
+    }
+    __device__ __forceinline__ void stage(float *xs)
+    {
+        f32x4 *dst = reinterpret_cast<f32x4 *>(xs);
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            dst[threadIdx.x + j * NT] = v[j];
+        __syncthreads();
+    }
+};
+
+// xs = RMSNorm(h) * gain: h / sqrt(mean(h^2) + eps) * gain, eps inside the root; the sum of
+// squares is taken in a fixed order.
+template <int NT, int K>
+struct RmsNormX {
+    static constexpr int PER = (K / 4 + NT - 1) / NT;
+    f32x4 hv[PER], gv[PER];
+
+    static_assert((K / 4) % NT == 0, "the workgroup must cover the vector evenly");
+
+    __device__ __forceinline__ void issue(const float *__restrict__ h, const float *__restrict__ gain)
+    {
+        const f32x4 *h4 = reinterpret_cast<const f32x4 *>(h);
+        const f32x4 *g4 = reinterpret_cast<const f32x4 *>(gain);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            hv[j] = h4[threadIdx.x + j * NT];
+            gv[j] = g4[threadIdx.x + j * NT];
+        }
+    }
+    __device__ __forceinline__ void stage(float *xs, float eps, float *wsum)
+    {
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            ss = fmaf(hv[j].x, hv[j].x, ss);
+            ss = fmaf(hv[j].y, hv[j].y, ss);
+            ss = fmaf(hv[j].z, hv[j].z, ss);
+            ss = fmaf(hv[j].w, hv[j].w, ss);
+        }
+        const float tot = block_sum_fixed<NT>(ss, wsum);
+        const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(xs);
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            dst[threadIdx.x + j * NT] = hv[j] * inv * gv[j];
+        __syncthreads();
+    }
+};
+
+// Dequantise one block pair given as its 9 dwords into 64 floats: (code - 8) * d (exact).
+__device__ __forceinline__ void dequant_pair_words(const uint32_t (&D)[9], float (&out)[64])
+{
     const uint32_t q0[4] = {(D[0] >> 16) | (D[1] << 16), (D[1] >> 16) | (D[2] << 16),
                             (D[2] >> 16) | (D[3] << 16), (D[3] >> 16) | (D[4] << 16)};
     const float d0 = half_bits_to_float(D[0]);

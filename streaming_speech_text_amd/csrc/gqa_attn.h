@@ -8,12 +8,13 @@
 // For query head h of group g = h / GROUP:  s_t = scale * <q_h, K[g][t]>,
 // p = softmax(s) over the live slots, out_h = sum_t p_t V[g][t].
 //
-// MI355X mapping: eight KV heads cannot fill 256 compute units, so the live window is split
-// into S chunks (grid = S x n_kv_heads).  A workgroup streams its chunk of K and V for one
-// KV head once and serves all GROUP query heads of that head from the same loads.  Inside
-// the chunk it walks 64-position sub-chunks with an online softmax (running max and sum);
-// it writes a partial (max, sum, unnormalised output) and the partials are merged in a
-// fixed order, either by a second kernel or by the last workgroup of the head to finish.
+// MI355X mapping: eight KV heads cannot fill 256 compute units, so a long live window is
+// split into S chunks of at least 128 positions (grid = S x n_kv_heads).  A workgroup of 8
+// waves streams its chunk of K and V for one KV head once and serves all GROUP query heads
+// of that head from the same loads.  Inside the chunk it walks 128-position sub-chunks with
+// an online softmax (running max and sum).  With one chunk the workgroup writes the output
+// directly; otherwise it writes a partial (max, sum, unnormalised output) and the partials are
+// merged in a fixed order, either by a second kernel or by the last workgroup of the head.
 #pragma once
 
 #include "vox_common.h"
@@ -21,8 +22,10 @@
 namespace vox {
 
 constexpr int ATTN_HD = 128;          // head size handled by the kernels
-constexpr int ATTN_SUB = 64;          // positions per online-softmax sub-chunk
-constexpr int ATTN_MIN_CHUNK = 32;    // do not split below this many positions
+constexpr int ATTN_WAVES = 8;         // waves per workgroup
+constexpr int ATTN_THREADS = 64 * ATTN_WAVES;
+constexpr int ATTN_SUB = 128;         // positions per online-softmax sub-chunk
+constexpr int ATTN_MIN_CHUNK = 128;   // do not split below this many positions
 constexpr int ATTN_PART = 132;        // floats per partial: m, l, 2 pad, o[128]
 
 __host__ __device__ inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
@@ -46,7 +49,7 @@ __host__ __device__ inline AttnPlan attn_plan(int n_valid, int s_max)
 // Most chunks a ring of n_slots may be split into.
 __host__ __device__ inline int attn_split_cap(int n_slots)
 {
-    int c = ceil_div_i(n_slots, 64);
+    int c = ceil_div_i(n_slots, ATTN_MIN_CHUNK);
     return c < 1 ? 1 : (c > 128 ? 128 : c);
 }
 
@@ -99,9 +102,9 @@ __device__ __forceinline__ void attn_merge(const AttnArgs &a, int g, int nsplit,
 template <int GROUP, bool FUSED_MERGE>
 __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
 {
-    __shared__ float sc[GROUP][ATTN_SUB];            // scores, then weights, of a sub-chunk
-    __shared__ float alpha_s[GROUP];                 // rescale of the running sums
-    __shared__ float ored[4][GROUP][ATTN_HD];        // per-wave partial outputs
+    __shared__ float sc[GROUP][ATTN_SUB];                 // scores, then weights, of a sub-chunk
+    __shared__ float alpha_s[GROUP];                      // rescale of the running sums
+    __shared__ float ored[ATTN_WAVES][GROUP][ATTN_HD];    // per-wave partial outputs
     __shared__ float ml[GROUP][2];
     __shared__ int last_flag;
 
@@ -127,15 +130,6 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
     const float *kbase = a.kc + (size_t)g * a.n_slots * ATTN_HD;
     const float *vbase = a.vc + (size_t)g * a.n_slots * ATTN_HD;
 
-    float qv[GROUP][8];
-#pragma unroll
-    for (int h = 0; h < GROUP; ++h) {
-        const float4 *q4 = reinterpret_cast<const float4 *>(a.q + ((size_t)g * GROUP + h) * ATTN_HD + 8 * seg);
-        const float4 u = q4[0], v = q4[1];
-        qv[h][0] = u.x; qv[h][1] = u.y; qv[h][2] = u.z; qv[h][3] = u.w;
-        qv[h][4] = v.x; qv[h][5] = v.y; qv[h][6] = v.z; qv[h][7] = v.w;
-    }
-
     float m_run[GROUP], l_run[GROUP];
     float2 acc[GROUP];
 #pragma unroll
@@ -144,14 +138,17 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
         l_run[h] = 0.0f;
         acc[h] = make_float2(0.0f, 0.0f);
     }
+    float qv[GROUP][8];
+    bool q_loaded = false;
 
     for (int base = t0; base < t1; base += ATTN_SUB) {
-        // issue the K and V loads of the whole sub-chunk first
+        // issue the K and V loads of the whole sub-chunk first (the first time, the query
+        // loads follow them so the two latencies overlap)
         float4 kr[4][2];
         float2 vr[16];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int t = base + it * 16 + wave * 4 + pslot;
+            const int t = base + it * 32 + wave * 4 + pslot;
             if (t < t1) {
                 const float4 *k4 = reinterpret_cast<const float4 *>(kbase + (size_t)t * ATTN_HD + 8 * seg);
                 kr[it][0] = k4[0];
@@ -163,14 +160,25 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int t = base + wave + 4 * i;
+            const int t = base + wave + ATTN_WAVES * i;
             vr[i] = t < t1 ? *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane)
                            : make_float2(0.0f, 0.0f);
+        }
+        if (!q_loaded) {
+#pragma unroll
+            for (int h = 0; h < GROUP; ++h) {
+                const float4 *q4 =
+                    reinterpret_cast<const float4 *>(a.q + ((size_t)g * GROUP + h) * ATTN_HD + 8 * seg);
+                const float4 u = q4[0], v = q4[1];
+                qv[h][0] = u.x; qv[h][1] = u.y; qv[h][2] = u.z; qv[h][3] = u.w;
+                qv[h][4] = v.x; qv[h][5] = v.y; qv[h][6] = v.z; qv[h][7] = v.w;
+            }
+            q_loaded = true;
         }
         // scores
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int p = it * 16 + wave * 4 + pslot;
+            const int p = it * 32 + wave * 4 + pslot;
             const float kk[8] = {kr[it][0].x, kr[it][0].y, kr[it][0].z, kr[it][0].w,
                                  kr[it][1].x, kr[it][1].y, kr[it][1].z, kr[it][1].w};
 #pragma unroll
@@ -188,17 +196,20 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
             }
         }
         __syncthreads();
-        // online softmax update: wave (h % 4) handles query head h
+        // online softmax update: wave (h % 8) handles query head h, two positions per lane
 #pragma unroll
         for (int h = 0; h < GROUP; ++h) {
-            if ((h & 3) != wave)
+            if ((h % ATTN_WAVES) != wave)
                 continue;
-            const float v = sc[h][lane];
-            const float mx = wave_max(v);
+            const float v0 = sc[h][lane];
+            const float v1 = sc[h][lane + 64];
+            const float mx = wave_max(fmaxf(v0, v1));
             const float m_new = fmaxf(m_run[h], mx);
-            const float e = (v == -INFINITY) ? 0.0f : __expf(v - m_new);
-            const float sum = wave_sum(e);
-            sc[h][lane] = e;
+            const float e0 = (v0 == -INFINITY) ? 0.0f : __expf(v0 - m_new);
+            const float e1 = (v1 == -INFINITY) ? 0.0f : __expf(v1 - m_new);
+            const float sum = wave_sum(e0 + e1);
+            sc[h][lane] = e0;
+            sc[h][lane + 64] = e1;
             const float al = (m_run[h] == -INFINITY) ? 0.0f : __expf(m_run[h] - m_new);
             if (lane == 0)
                 alpha_s[h] = al;
@@ -206,7 +217,7 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
             m_run[h] = m_new;
         }
         __syncthreads();
-        // weighted values: wave w takes positions w, w+4, ...; lane owns dims 2*lane, 2*lane+1
+        // weighted values: wave w takes positions w, w+8, ...; lane owns dims 2*lane, 2*lane+1
 #pragma unroll
         for (int h = 0; h < GROUP; ++h) {
             const float al = alpha_s[h];
@@ -215,7 +226,7 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int p = wave + 4 * i;
+            const int p = wave + ATTN_WAVES * i;
 #pragma unroll
             for (int h = 0; h < GROUP; ++h) {
                 const float w = sc[h][p];
@@ -226,7 +237,7 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
         __syncthreads();
     }
 
-    // combine the four waves' partial outputs
+    // combine the waves' partial outputs
 #pragma unroll
     for (int h = 0; h < GROUP; ++h) {
         ored[wave][h][2 * lane] = acc[h].x;
@@ -234,26 +245,32 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
     }
 #pragma unroll
     for (int h = 0; h < GROUP; ++h) {
-        if ((h & 3) == wave && lane == 0) {
+        if ((h % ATTN_WAVES) == wave && lane == 0) {
             ml[h][0] = m_run[h];
             ml[h][1] = l_run[h];
         }
     }
     __syncthreads();
 
+    auto wave_total = [&](int h, int d) {
+        float o = ored[0][h][d];
+#pragma unroll
+        for (int w = 1; w < ATTN_WAVES; ++w)
+            o += ored[w][h][d];
+        return o;
+    };
     if (plan.splits == 1) {
-        for (int i = tid; i < GROUP * ATTN_HD; i += 256) {
+        for (int i = tid; i < GROUP * ATTN_HD; i += ATTN_THREADS) {
             const int h = i / ATTN_HD, d = i % ATTN_HD;
-            const float o = ((ored[0][h][d] + ored[1][h][d]) + ored[2][h][d]) + ored[3][h][d];
-            a.out[((size_t)g * GROUP + h) * ATTN_HD + d] = o / ml[h][1];
+            a.out[((size_t)g * GROUP + h) * ATTN_HD + d] = wave_total(h, d) / ml[h][1];
         }
         return;
     }
 
     float *mypart = a.part + ((size_t)g * a.s_cap + s) * GROUP * ATTN_PART;
-    for (int i = tid; i < GROUP * ATTN_HD; i += 256) {
+    for (int i = tid; i < GROUP * ATTN_HD; i += ATTN_THREADS) {
         const int h = i / ATTN_HD, d = i % ATTN_HD;
-        mypart[h * ATTN_PART + 4 + d] = ((ored[0][h][d] + ored[1][h][d]) + ored[2][h][d]) + ored[3][h][d];
+        mypart[h * ATTN_PART + 4 + d] = wave_total(h, d);
     }
     if (tid < GROUP) {
         mypart[tid * ATTN_PART + 0] = ml[tid][0];

@@ -6,7 +6,7 @@
 namespace vox {
 
 template <int GROUP, bool FUSED>
-__global__ __launch_bounds__(256) void gqa_attn_kernel(AttnArgs a)
+__global__ __launch_bounds__(ATTN_THREADS) void gqa_attn_kernel(AttnArgs a)
 {
     attn_chunk<GROUP, FUSED>(a);
 }
@@ -22,7 +22,7 @@ template <int GROUP>
 static int launch_attn(const AttnArgs &a, int n_kv, hipStream_t s)
 {
     const AttnPlan plan = attn_plan(a.n_valid, a.s_cap);
-    hipLaunchKernelGGL((gqa_attn_kernel<GROUP, false>), dim3(plan.splits, n_kv), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gqa_attn_kernel<GROUP, false>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
     int st = check_launch("gqa attention launch");
     if (st || plan.splits == 1)
         return st;
