@@ -9,16 +9,17 @@
 // section 아키텍처 - GGUF Q4_0 linears with dequantisation fused into the product; section 브라우저
 // 실행을 위한 기술적 해결 - the embedding stays on the GPU as Q4 and one row is used per token.
 //
-// One step = 4 kernels per layer + 1:
+// One step = 5 kernels per layer (6 with a split window) + 2:
 //   qkv    RMSNorm prologue (layer 0: from the token's embedding row), Q/K/V Q4_0 GEMV over one
 //          concatenated row space, RoPE on q and k, k and v written to ring slot pos % n_slots
-//   attn   split-K grouped attention over min(pos+1, n_slots) slots; the last workgroup of a
-//          KV head merges the partials
+//   attn   grouped attention over min(pos+1, n_slots) slots (split over the window when it is
+//          long, with a merge kernel after it)
 //   o      Q4_0 GEMV of the attention output, added into the residual stream
 //   ffn    RMSNorm prologue, gate and up rows in the same tile, silu(gate) * up
 //   down   Q4_0 GEMV, added into the residual stream
-//   head   final RMSNorm, tied Q4_0 table as LM head, logits (optional) and a device-wide
-//          argmax; the last workgroup writes the token, clears the argmax state and advances pos
+//   head   final RMSNorm, tied Q4_0 table as LM head, logits (optional) and each workgroup's
+//          best (logit, index) key
+//   final  one workgroup reduces the keys, writes the token and advances pos
 // The sequence is captured once into a HIP graph and replayed per token.
 #include <math.h>
 #include <stdlib.h>
@@ -35,11 +36,9 @@ namespace vox {
 
 struct DecCtl {
     int64_t pos;                  // absolute position of the next token
-    unsigned long long argmax;    // packed (logit, index) key of the running argmax
-    uint32_t lm_ticket;           // LM-head workgroups finished
-    uint32_t pad;
-    uint32_t attn_ticket[64];     // per KV head: attention workgroups finished
 };
+
+constexpr int MAX_HEAD_WGS = 4096;   // most LM-head workgroups (one argmax key each)
 
 // ---------------------------------------------------------------------------------------
 // policies for the shared Q4_0 tile pipeline (gemv_core.h)
@@ -97,7 +96,7 @@ struct EmbedRmsNormX {
             if (c < PAIRS) {
                 float v[64];
                 dequant_pair_words(raw[j], v);
-                float4 *d4 = reinterpret_cast<float4 *>(xs + 64 * c);
+                float4 *d4 = reinterpret_cast<float4 *>(xs + XS_ROW * c);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float4 q = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -112,10 +111,11 @@ struct EmbedRmsNormX {
         }
         const float tot = block_sum_fixed<NT>(ss, wsum);   // its barriers also publish xs
         const float inv = 1.0f / sqrtf(tot / (float)K + eps);
-        f32x4 *x4 = reinterpret_cast<f32x4 *>(xs);
 #pragma unroll
-        for (int j = 0; j < GPER; ++j)
-            x4[threadIdx.x + j * NT] = x4[threadIdx.x + j * NT] * inv * gv[j];
+        for (int j = 0; j < GPER; ++j) {
+            f32x4 *p = reinterpret_cast<f32x4 *>(xs + xs_index(4 * (threadIdx.x + j * NT)));
+            *p = *p * inv * gv[j];
+        }
         __syncthreads();
     }
 };
@@ -275,9 +275,8 @@ struct LmHeadArgs {
     int vocab;
     const float *h, *gain;
     float eps;
-    float *logits;          // may be null
-    DecCtl *ctl;
-    int32_t *tok_out;
+    float *logits;                 // may be null
+    unsigned long long *keys;      // [gridDim.x] best (logit, index) key of each workgroup
 };
 
 template <class Gm>
@@ -313,10 +312,9 @@ struct LmHeadPolicy {
             best = k > best ? k : best;
         }
     }
-    __device__ void finish(float *lds)
+    __device__ void finish(float *)
     {
         __shared__ unsigned long long keys[Gm::R];
-        __shared__ int last;
         const int tid = threadIdx.x;
         if (tid < Gm::R)
             keys[tid] = best;
@@ -325,24 +323,34 @@ struct LmHeadPolicy {
             unsigned long long m = 0ull;
             for (int i = 0; i < Gm::R; ++i)
                 m = keys[i] > m ? keys[i] : m;
-            atomicMax(&a.ctl->argmax, m);
-            __threadfence();
-            const uint32_t prev = atomicAdd(&a.ctl->lm_ticket, 1u);
-            last = prev == gridDim.x - 1;
-        }
-        __syncthreads();
-        if (tid == 0 && last) {
-            // every workgroup's atomicMax happened before its ticket: the key is final
-            __threadfence();
-            const unsigned long long key = atomicMax(&a.ctl->argmax, 0ull);
-            a.tok_out[0] = (int32_t)argmax_key_index(key);
-            a.ctl->argmax = 0ull;
-            a.ctl->lm_ticket = 0u;
-            a.ctl->pos = a.ctl->pos + 1;
-            __threadfence();
+            a.keys[blockIdx.x] = m;
         }
     }
 };
+
+// Greedy choice: the largest of the LM-head workgroups' keys (value first, then the lowest
+// index); writes the token and advances the position.  One workgroup of 256 threads.
+__global__ __launch_bounds__(256) void dec_finalize_kernel(DecCtl *ctl, const unsigned long long *keys, int nkeys,
+                                                           int32_t *tok_out)
+{
+    __shared__ unsigned long long part[256];
+    unsigned long long m = 0ull;
+    for (int i = threadIdx.x; i < nkeys; i += 256)
+        m = keys[i] > m ? keys[i] : m;
+    part[threadIdx.x] = m;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            const unsigned long long o = part[threadIdx.x + w];
+            part[threadIdx.x] = o > part[threadIdx.x] ? o : part[threadIdx.x];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        tok_out[0] = (int32_t)argmax_key_index(part[0]);
+        ctl->pos = ctl->pos + 1;
+    }
+}
 
 template <class Gm, class Policy>
 __global__ __launch_bounds__(Gm::NT) void dec_gemv_kernel(Policy P)
@@ -353,7 +361,19 @@ __global__ __launch_bounds__(Gm::NT) void dec_gemv_kernel(Policy P)
 template <int GROUP>
 __global__ __launch_bounds__(ATTN_THREADS) void dec_attn_kernel(AttnArgs a)
 {
-    attn_chunk<GROUP, true>(a);
+    attn_chunk<GROUP, false>(a);
+}
+
+// Merges the split partials of one KV head (only launched when the window may be split).
+template <int GROUP>
+__global__ __launch_bounds__(256) void dec_attn_merge_kernel(AttnArgs a)
+{
+    __shared__ float lds[2 * 128 + 8];
+    const int64_t p = *a.pos + 1;
+    const int nv = p < a.n_slots ? (int)p : a.n_slots;
+    const AttnPlan plan = attn_plan(nv, a.s_cap);
+    if (plan.splits > 1)
+        attn_merge<GROUP>(a, blockIdx.x, plan.splits, lds);
 }
 
 // RoPE frequencies theta^(-2i/head_dim) / pi, i < head_dim/2, in fp64 (once per decoder).
@@ -366,15 +386,8 @@ __global__ void dec_rope_table_kernel(double *freq, float theta)
 
 __global__ void dec_reset_kernel(DecCtl *ctl)
 {
-    const int tid = threadIdx.x;
-    if (tid == 0) {
+    if (threadIdx.x == 0)
         ctl->pos = 0;
-        ctl->argmax = 0ull;
-        ctl->lm_ticket = 0u;
-        ctl->pad = 0u;
-    }
-    if (tid < 64)
-        ctl->attn_ticket[tid] = 0u;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -391,7 +404,7 @@ template <int K, int R, int NPART = 1>
 using DGeom = GemvGeom<K, nt_for<K>(), R, NPART>;
 
 template <class Gm, class Policy, class Args>
-static int launch_gemv(const Args &args, hipStream_t s, const char *what)
+static int launch_gemv(const Args &args, hipStream_t s, const char *what, int *grid_out = nullptr)
 {
     static int occ = 0;
     if (occ <= 0) {
@@ -403,7 +416,11 @@ static int launch_gemv(const Args &args, hipStream_t s, const char *what)
     }
     const int ntiles = Policy::tiles(args);
     const int cap = occ * cu_count();
-    const int grid = ntiles < cap ? ntiles : cap;
+    int grid = ntiles < cap ? ntiles : cap;
+    if (grid > MAX_HEAD_WGS)
+        grid = MAX_HEAD_WGS;
+    if (grid_out)
+        *grid_out = grid;
     Policy P{args};
     hipLaunchKernelGGL((dec_gemv_kernel<Gm, Policy>), dim3(grid > 0 ? grid : 1), dim3(Gm::NT), 0, s, P);
     return check_launch(what);
@@ -445,11 +462,11 @@ static int run_gateup(const GateUpArgs &a, int R, hipStream_t s)
 }
 
 template <int K>
-static int run_lmhead(const LmHeadArgs &a, int R, hipStream_t s)
+static int run_lmhead(const LmHeadArgs &a, int R, hipStream_t s, int *grid)
 {
     if (R == 16)
-        return launch_gemv<DGeom<K, 16>, LmHeadPolicy<DGeom<K, 16>>>(a, s, "decoder lm head");
-    return launch_gemv<DGeom<K, 8>, LmHeadPolicy<DGeom<K, 8>>>(a, s, "decoder lm head");
+        return launch_gemv<DGeom<K, 16>, LmHeadPolicy<DGeom<K, 16>>>(a, s, "decoder lm head", grid);
+    return launch_gemv<DGeom<K, 8>, LmHeadPolicy<DGeom<K, 8>>>(a, s, "decoder lm head", grid);
 }
 
 static bool model_width(int k) { return k == 1024 || k == 3072; }
@@ -469,7 +486,7 @@ static int pick_r(int64_t rows, int min_r)
 }
 
 struct Layout {
-    size_t ctl, rope, h, q, o, act, part, total;
+    size_t ctl, keys, rope, h, q, o, act, part, total;
 };
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -485,6 +502,7 @@ static Layout scratch_layout(const vox_decoder_config &c)
     };
     const int group = c.n_heads / c.n_kv_heads;
     L.ctl = take(sizeof(DecCtl));
+    L.keys = take(sizeof(unsigned long long) * MAX_HEAD_WGS);
     L.rope = take(sizeof(double) * ATTN_HD / 2);
     L.h = take((size_t)c.dim * 4);
     L.q = take((size_t)c.n_heads * c.head_dim * 4);
@@ -536,6 +554,7 @@ struct vox_decoder {
     uint8_t *scratch;
     Layout lay;
     DecCtl *ctl;
+    unsigned long long *keys;
     double *rope;
     float *h, *q, *o, *act, *part;
     int group, s_cap;
@@ -565,7 +584,11 @@ template <int GROUP>
 static int launch_attn(const AttnArgs &a, int width, int n_kv, hipStream_t s)
 {
     hipLaunchKernelGGL(dec_attn_kernel<GROUP>, dim3(width, n_kv), dim3(ATTN_THREADS), 0, s, a);
-    return check_launch("decoder attention");
+    int st = check_launch("decoder attention");
+    if (st || width == 1)
+        return st;
+    hipLaunchKernelGGL(dec_attn_merge_kernel<GROUP>, dim3(n_kv), dim3(256), 0, s, a);
+    return check_launch("decoder attention merge");
 }
 
 static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out, float *logits, int bucket,
@@ -615,7 +638,7 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
         aa.vc = vc;
         aa.out = d->o;
         aa.part = d->part;
-        aa.ticket = d->ctl->attn_ticket;
+        aa.ticket = nullptr;
         aa.pos = &d->ctl->pos;
         aa.n_slots = c.n_slots;
         aa.n_valid = 0;
@@ -646,8 +669,14 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
     }
     if (st)
         return st;
-    LmHeadArgs la{d->tok_embd, c.vocab, d->h, d->out_norm, c.norm_eps, logits, d->ctl, tok_out};
-    return c.dim == 3072 ? run_lmhead<3072>(la, d->r_head, s) : run_lmhead<1024>(la, d->r_head, s);
+    LmHeadArgs la{d->tok_embd, c.vocab, d->h, d->out_norm, c.norm_eps, logits, d->keys};
+    int grid = 0;
+    int st2 = c.dim == 3072 ? run_lmhead<3072>(la, d->r_head, s, &grid) : run_lmhead<1024>(la, d->r_head, s, &grid);
+    if (st2)
+        return st2;
+    hipLaunchKernelGGL(dec_finalize_kernel, dim3(1), dim3(256), 0, s, d->ctl, (const unsigned long long *)d->keys, grid,
+                       tok_out);
+    return check_launch("decoder finalize");
 }
 
 static void drop_graphs(vox_decoder *d)
@@ -714,6 +743,7 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     d->scratch = (uint8_t *)scratch;
     d->lay = lay;
     d->ctl = (DecCtl *)(d->scratch + lay.ctl);
+    d->keys = (unsigned long long *)(d->scratch + lay.keys);
     d->rope = (double *)(d->scratch + lay.rope);
     d->h = (float *)(d->scratch + lay.h);
     d->q = (float *)(d->scratch + lay.q);

@@ -66,6 +66,12 @@ __device__ __forceinline__ float ubyte_f(uint32_t v, int j)
     return r;
 }
 
+// The activation vector is staged in LDS as rows of 64 floats (one block pair each) padded to
+// XS_ROW floats: thread c reads row c, and with a 256-byte row pitch every lane of a wave
+// would start on the same bank; the 16-byte pad spreads consecutive rows over the banks.
+constexpr int XS_ROW = 68;
+__device__ __forceinline__ int xs_index(int i) { return (i >> 6) * XS_ROW + (i & 63); }
+
 // Sum over one block of (code - 8) * x, without the scale.  qs: the 16 code bytes;
 // x: the block's 32 activations; neg8sum = -8 * sum(x).
 __device__ __forceinline__ float q4_block_dot(const uint32_t (&qs)[4], const float *x, float neg8sum)
@@ -166,8 +172,9 @@ __device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT
 
 // The tile pipeline shared by every Q4_0 GEMV flavour.  Policy supplies:
 //   XRegs, x_issue(XRegs&)                 issue the activation loads into registers
-//   x_stage(XRegs&, float* xs, float* wsum) fill xs[K] with the activations (all threads call
-//                                          it; it ends with a workgroup barrier)
+//   x_stage(XRegs&, float* xs, float* wsum) fill xs with the activations, element i at
+//                                          xs[xs_index(i)] (all threads call it; it ends with a
+//                                          workgroup barrier)
 //   num_tiles()                            tiles of R rows
 //   pre(tile)                              early loads the epilogue of `tile` will need
 //   slice(tile, part, &rows_valid)         base pointer of slice `part` of the tile
@@ -179,7 +186,7 @@ __device__ __forceinline__ void gemv_tiles(Policy &P)
     __shared__ u32x4 tile[Gm::CPT * Gm::NT];   // padded: every thread stores all its chunks
     __shared__ float red[Gm::R * Gm::TR];
     __shared__ float rowsum[Gm::R];
-    __shared__ __attribute__((aligned(16))) float xs[Gm::K];   // the activation vector of the product
+    __shared__ __attribute__((aligned(16))) float xs[Gm::K / 64 * XS_ROW];   // the activation vector (padded rows)
     __shared__ float wsum[Gm::NT / 64];
 
     const int tid = threadIdx.x;
@@ -207,7 +214,7 @@ __device__ __forceinline__ void gemv_tiles(Policy &P)
     P.x_stage(xr, xs, wsum);
     PairX px;
     {
-        const float4 *x4 = reinterpret_cast<const float4 *>(xs + 64 * c);
+        const float4 *x4 = reinterpret_cast<const float4 *>(xs + XS_ROW * c);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float4 v = x4[i];
@@ -287,10 +294,9 @@ struct PlainX {
     }
     __device__ __forceinline__ void stage(float *xs)
     {
-        f32x4 *dst = reinterpret_cast<f32x4 *>(xs);
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            dst[threadIdx.x + j * NT] = v[j];
+            *reinterpret_cast<f32x4 *>(xs + xs_index(4 * (threadIdx.x + j * NT))) = v[j];
         __syncthreads();
     }
 };
@@ -326,10 +332,9 @@ struct RmsNormX {
         }
         const float tot = block_sum_fixed<NT>(ss, wsum);
         const float inv = 1.0f / sqrtf(tot / (float)K + eps);
-        f32x4 *dst = reinterpret_cast<f32x4 *>(xs);
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            dst[threadIdx.x + j * NT] = hv[j] * inv * gv[j];
+            *reinterpret_cast<f32x4 *>(xs + xs_index(4 * (threadIdx.x + j * NT))) = hv[j] * inv * gv[j];
         __syncthreads();
     }
 };

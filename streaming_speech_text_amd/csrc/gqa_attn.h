@@ -187,10 +187,7 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     d = fmaf(qv[h][i], kk[i], d);
-                d += __shfl_xor(d, 8, 64);
-                d += __shfl_xor(d, 4, 64);
-                d += __shfl_xor(d, 2, 64);
-                d += __shfl_xor(d, 1, 64);
+                d = row16_sum(d);   // the 16 lanes of a row hold one position
                 if (seg == 0)
                     sc[h][p] = (base + p < t1) ? d * a.scale : -INFINITY;
             }

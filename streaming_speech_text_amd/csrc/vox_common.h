@@ -21,21 +21,53 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits)
     return __builtin_bit_cast(float, bits << 16);
 }
 
-// Sum over the 64 lanes of a wavefront; every lane gets the total.
+// Cross-lane data movement with DPP (one VALU op each, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_ROR4 = 0x124;   // rotate right by 4 within a row of 16 lanes
+constexpr int DPP_ROW_ROR8 = 0x128;   // rotate right by 8 within a row of 16 lanes
+
+// Sum over each row of 16 lanes; every lane of the row gets the row's total.  The order of the
+// additions is fixed (deterministic).
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_f<DPP_QUAD_XOR1>(v);
+    v += dpp_f<DPP_QUAD_XOR2>(v);
+    v += dpp_f<DPP_ROW_ROR4>(v);
+    v += dpp_f<DPP_ROW_ROR8>(v);
+    return v;
+}
+
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_ROW_ROR4>(v));
+    v = fmaxf(v, dpp_f<DPP_ROW_ROR8>(v));
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes of a wavefront, in a fixed order; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    v = row16_sum(v);
+    return ((lane_value(v, 0) + lane_value(v, 16)) + lane_value(v, 32)) + lane_value(v, 48);
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = row16_max(v);
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 // Order-preserving map of a non-NaN float to an unsigned key (larger float -> larger key).

@@ -72,6 +72,16 @@ def test_decoder_small_window_wraps(vx, orc):
     say(f"worst err/limit {worst:.3f}, near-tie token differences {ties}")
 
 
+def test_decoder_split_window_wraps(vx, orc):
+    # a 320-slot window: past 128 live positions the attention splits over the window and a
+    # merge kernel combines the splits; 340 steps also wrap the ring
+    shape = synth.DecoderShape(**{**SMALL.__dict__, "n_slots": 320})
+    tokens = synth.generator(75, 3).integers(0, shape.vocab, size=340).tolist()
+    say("decoder small config, 340 teacher-forced steps over a 320-slot window (split attention)")
+    worst, ties, _ = run_teacher_forced(vx, orc, shape, 75, tokens, check_every=7)
+    say(f"worst err/limit {worst:.3f}, near-tie token differences {ties}")
+
+
 def test_decoder_graph_matches_eager(vx, orc):
     tokens = synth.generator(72, 3).integers(0, SMALL.vocab, size=70).tolist()
     _, _, a = run_teacher_forced(vx, orc, SMALL, 72, tokens, graph=True)
