@@ -1,0 +1,74 @@
+"""GPU parity of the encoder-chunk Q4_0 dequant-GEMM (matrix cores) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from streaming_speech_text_amd import synth
+from tests.gpu_util import assert_close, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vx():
+    from streaming_speech_text_amd import vox
+    vox.lib()
+    return vox
+
+
+def _gemm(vx, w, xb, m, n, k):
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    vx.q4_gemm(dev(w), dev(xb), y, m=m, n=n, k=k)
+    return host(y)
+
+
+@pytest.mark.parametrize("m", synth.ENCODER_M)
+def test_gemm_encoder_chunk(vx, orc, m):
+    for name, n, k in synth.ENCODER_LINEARS:
+        say(f"gemm {name}: m={m} n={n} k={k}")
+        w, xb = synth.gemm_inputs(synth.SEED_GEMM, m, n, k)
+        assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm {name} m={m}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1280, 1280), (17, 100, 96), (63, 65, 32), (65, 1000, 5120), (130, 64, 2080),
+                                   (3, 5, 64)])
+def test_gemm_ragged(vx, orc, m, n, k):
+    w, xb = synth.gemm_inputs(600 + m, m, n, k)
+    say(f"gemm ragged m={m} n={n} k={k}")
+    assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm ragged {m}x{n}x{k}")
+
+
+def test_gemm_exact_dyadic(vx, orc):
+    # small-integer activations and power-of-two scales: every product and partial sum is exact,
+    # so the matrix-core result must equal the oracle bit for bit
+    m, n, k = 70, 96, 1280
+    g = synth.generator(610)
+    w = synth.q4_matrix(g, n, k).reshape(n, k // 32, 18)
+    e = g.integers(-3, 1, size=(n, k // 32)).astype(np.float64)
+    w[:, :, 0:2] = (2.0 ** e).astype("<f2").view(np.uint8).reshape(n, k // 32, 2)
+    w = w.reshape(n, -1)
+    xi = g.integers(-4, 5, size=(m, k)).astype(np.float32)
+    xb = synth.bf16_bits(xi)
+    got = _gemm(vx, w, xb, m, n, k)
+    assert np.array_equal(got.astype(np.float64), orc.q4_gemm(w, xb))
+
+
+def test_gemm_row_matches_gemv(vx):
+    # one GEMM row equals the GEMV of that row's (bf16-valued) activations
+    m, n, k = 5, 3072, 3072
+    w, xb = synth.gemm_inputs(611, m, n, k)
+    y = _gemm(vx, w, xb, m, n, k)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    yv = torch.empty(n, dtype=torch.float32, device="cuda")
+    vx.q4_gemv(dev(w), dev(np.ascontiguousarray(xf[2])), yv)
+    assert_close(y[2], host(yv), "gemm row vs gemv", rtol=1e-5, atol=1e-5)
+
+
+def test_gemm_errors(vx):
+    w = torch.zeros(18 * 64, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(4, 64, dtype=torch.uint16, device="cuda")
+    y = torch.zeros(4, 32, dtype=torch.float32, device="cuda")
+    with pytest.raises(vx.VoxError) as e:
+        vx.q4_gemm(w, x, y, m=4, n=32, k=48)
+    assert e.value.status == vx.VOX_E_INVAL
+    vx.q4_gemm(w, x, y, m=0, n=32, k=64)
