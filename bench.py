@@ -35,8 +35,9 @@ def parse():
     ap.add_argument("--gemv-launches", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--leg", choices=["all", "gemv"], default="all",
-                    help="gemv: only the GEMV roofline leg and a copy of known size (for counter runs)")
+    ap.add_argument("--leg", choices=["all", "gemv", "kernels"], default="all",
+                    help="gemv: only the GEMV roofline leg and a copy of known size (for counter runs); "
+                         "kernels: per-kernel timings of the other workloads, one JSON line each")
     return ap.parse_args()
 
 
@@ -64,25 +65,16 @@ def measured_traffic(digest: str, launch_bytes: int):
 
 def gemv_leg(args, torch, synth, vox, dev, stream):
     """The Q4_0 GEMV at the LM-head shape (131072 x 3072), rotating over weight copies (more
-    than 1 GiB in total, so no launch is served from the 256 MB Infinity Cache), timed with
-    HIP events on the stream the launches go to."""
+    than 1 GiB in total, so no launch is served from the 256 MB Infinity Cache).  The launches
+    are captured in a HIP graph and its replay is timed with HIP events on the stream it runs
+    on, so the per-launch time is the kernel's own duration plus the graph's launch gap."""
     n, k = synth.VOXTRAL_DECODER.vocab, synth.VOXTRAL_DECODER.dim
     gw, gx = synth.gemv_inputs(synth.SEED_GEMV, n, k)
     copies = max(1, int(np.ceil(1.1 * 2 ** 30 / gw.nbytes)))
     ws = [torch.from_numpy(gw).to(dev) for _ in range(copies)]
     xd = torch.from_numpy(gx).to(dev)
     y = torch.empty(n, dtype=torch.float32, device=dev)
-    for i in range(copies):
-        vox.q4_gemv(ws[i], xd, y, stream=stream)
-    torch.cuda.synchronize()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for i in range(args.gemv_launches):
-        vox.q4_gemv(ws[i % copies], xd, y, stream=stream)
-    g1.record(stream)
-    torch.cuda.synchronize()
-    gemv_us = g0.elapsed_time(g1) * 1e3 / args.gemv_launches
+    gemv_us = timed(torch, stream, lambda i: vox.q4_gemv(ws[i], xd, y), copies, args.gemv_launches)
     launch_bytes = n * synth.q4_row_bytes(k) + 4 * (n + k)
     achieved = launch_bytes / (gemv_us * 1e-6) / 1e9
     print(f"[bench] q4 gemv {n}x{k}: {gemv_us:.2f} us/launch, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
@@ -99,6 +91,104 @@ def copy_calibration(torch, dev):
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
+
+
+def timed(torch, stream, launch, copies, reps):
+    """Average device time (us) of `launch(i)` (which enqueues on the current stream) over `reps`
+    launches rotating over `copies`, captured once in a HIP graph and replayed, so host launch
+    cost is not measured."""
+    for i in range(min(copies, 4)):
+        launch(i % copies)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(reps):
+                launch(i % copies)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def kernels_leg(torch, synth, vox, dev, stream):
+    """Per-kernel device times of the workloads beside the decoder step: the single 3072x3072
+    GEMV, one decoder layer's linears, GQA attention at three ring fills, the encoder-chunk
+    GEMM set.  Every measurement rotates over more than 1 GiB of distinct copies."""
+    GiB = 2 ** 30
+    out = []
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+        out.append(d)
+
+    def gemv_case(name, n, k, seed):
+        w, x = synth.gemv_inputs(seed, n, k)
+        copies = max(2, int(np.ceil(1.1 * GiB / w.nbytes)))
+        ws = [torch.from_numpy(w).to(dev) for _ in range(copies)]
+        xd = torch.from_numpy(x).to(dev)
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        us = timed(torch, stream, lambda i: vox.q4_gemv(ws[i], xd, y), copies, 200)
+        b = n * synth.q4_row_bytes(k) + 4 * (n + k)
+        emit({"kernel": "q4_gemv", "case": name, "n": n, "k": k, "us": round(us, 3), "bytes": b,
+              "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del ws
+
+    gemv_case("single 3072x3072", 3072, 3072, synth.SEED_GEMV)
+    for i, (name, (n, k)) in enumerate(synth.LAYER_LINEARS.items()):
+        gemv_case(f"layer {name}", n, k, 100 * synth.SEED_LAYER + i)
+    torch.cuda.empty_cache()
+
+    # attention over an 8192-slot ring
+    nq, nkv, hd, slots = 32, 8, 128, 8192
+    q, kc, vc = synth.attention_inputs(synth.SEED_ATTN, nq, nkv, hd, slots)
+    copies = max(2, int(np.ceil(1.1 * GiB / (kc.nbytes + vc.nbytes))))
+    ks = [torch.from_numpy(kc).to(dev) for _ in range(copies)]
+    vs = [torch.from_numpy(vc).to(dev) for _ in range(copies)]
+    qd = torch.from_numpy(q).to(dev)
+    o = torch.empty(nq, hd, dtype=torch.float32, device=dev)
+    wsb = vox.gqa_decode_attn_workspace(nq, nkv, hd, slots)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    for L in (1024, 4096, 8192):
+        us = timed(torch, stream, lambda i: vox.gqa_decode_attn(qd, ks[i], vs[i], o, nq, nkv, hd, slots, L,
+                                                                 1 / np.sqrt(hd), ws), copies, 100)
+        b = 8192 * L + 2 * nq * hd * 4
+        emit({"kernel": "gqa_decode_attn", "case": f"n_valid {L}", "us": round(us, 3), "bytes": b,
+              "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+    del ks, vs
+    torch.cuda.empty_cache()
+
+    # encoder-chunk GEMM set: the six linears of one layer, each M
+    for m in synth.ENCODER_M:
+        sets = []
+        for name, n, k in synth.ENCODER_LINEARS:
+            w, xb = synth.gemm_inputs(synth.SEED_GEMM, m, n, k)
+            sets.append((name, n, k, w, torch.from_numpy(xb.view(np.int16)).to(dev)))
+        wbytes = sum(s_[3].nbytes for s_ in sets)
+        copies = max(2, int(np.ceil(1.1 * GiB / wbytes)))
+        wdev = [[torch.from_numpy(s_[3]).to(dev) for s_ in sets] for _ in range(copies)]
+        ys = [torch.empty(m, s_[1], dtype=torch.float32, device=dev) for s_ in sets]
+
+        def launch(i):
+            for j, (name, n, k, _, xd) in enumerate(sets):
+                vox.lib().vox_q4_gemm(vox._ptr(wdev[i][j]), vox._ptr(xd), vox._ptr(ys[j]), m, n, k,
+                                      vox._stream(None))
+        us = timed(torch, stream, launch, copies, 50)
+        flops = 2 * m * sum(n * k for _, n, k in synth.ENCODER_LINEARS)
+        b = wbytes + sum(m * k * 2 + m * n * 4 for _, n, k in synth.ENCODER_LINEARS)
+        emit({"kernel": "q4_gemm", "case": f"encoder linears set, M={m}", "us": round(us, 3), "flops": flops,
+              "tflops": round(flops / us / 1e6, 2), "frac_mfma_bf16": round(flops / us / 1e6 / 2500.0, 4),
+              "bytes": b, "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del wdev
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -119,6 +209,9 @@ def main():
         copy_calibration(torch, dev)
         g = gemv_leg(args, torch, synth, vox, dev, stream)
         print(json.dumps({"leg": "gemv", **g}), flush=True)
+        return
+    if args.leg == "kernels":
+        kernels_leg(torch, synth, vox, dev, stream)
         return
     s = synth.VOXTRAL_DECODER
     print(f"[bench] generating weights ({s.n_layers} layers, vocab {s.vocab})", file=sys.stderr, flush=True)

@@ -119,8 +119,10 @@ typedef struct {
 int vox_decoder_workspace(const vox_decoder_config *c, size_t *kv_bytes, size_t *scratch_bytes);
 
 /* Creates a decoder over caller-owned weights and buffers (which must outlive it and stay
- * unchanged while work is in flight).  Supported shapes: dim, hidden and n_heads*head_dim
- * multiples of 256 and at most 16384, head_dim 128, n_heads/n_kv_heads in {1,2,4,8}.
+ * unchanged while work is in flight).  Supported shapes: head_dim 128, n_heads/n_kv_heads in
+ * {1,2,4,8}, n_kv_heads <= 64, and the width triple (dim, n_heads*head_dim, hidden) drawn from
+ * dim in {3072, 1024}, n_heads*head_dim in {4096, 1024}, hidden in {9216, 2048} (the Voxtral
+ * decoder and a small test shape); anything else returns VOX_E_UNSUPPORTED.
  * Enqueues the clearing of the scratch counters on `stream`. */
 int vox_decoder_create(const vox_decoder_config *c, const vox_decoder_weights *w, void *kv,
                        size_t kv_bytes, void *scratch, size_t scratch_bytes, void *stream,

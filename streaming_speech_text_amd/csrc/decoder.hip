@@ -361,14 +361,14 @@ __global__ __launch_bounds__(Gm::NT) void dec_gemv_kernel(Policy P)
 template <int GROUP>
 __global__ __launch_bounds__(ATTN_THREADS) void dec_attn_kernel(AttnArgs a)
 {
-    attn_chunk<GROUP, false>(a);
+    attn_chunk<GROUP>(a);
 }
 
 // Merges the split partials of one KV head (only launched when the window may be split).
 template <int GROUP>
 __global__ __launch_bounds__(256) void dec_attn_merge_kernel(AttnArgs a)
 {
-    __shared__ float lds[2 * 128 + 8];
+    __shared__ float lds[2 * ATTN_MAX_SPLITS + 8];
     const int64_t p = *a.pos + 1;
     const int nv = p < a.n_slots ? (int)p : a.n_slots;
     const AttnPlan plan = attn_plan(nv, a.s_cap);
@@ -638,7 +638,6 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
         aa.vc = vc;
         aa.out = d->o;
         aa.part = d->part;
-        aa.ticket = nullptr;
         aa.pos = &d->ctl->pos;
         aa.n_slots = c.n_slots;
         aa.n_valid = 0;

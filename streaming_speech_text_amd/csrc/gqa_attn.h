@@ -50,7 +50,7 @@ __host__ __device__ inline AttnPlan attn_plan(int n_valid, int s_max)
 __host__ __device__ inline int attn_split_cap(int n_slots)
 {
     int c = ceil_div_i(n_slots, ATTN_MIN_CHUNK);
-    return c < 1 ? 1 : (c > 128 ? 128 : c);
+    return c < 1 ? 1 : (c > 128 ? 128 : c);   // at most ATTN_MAX_SPLITS
 }
 
 struct AttnArgs {
@@ -58,55 +58,73 @@ struct AttnArgs {
     const float *kc, *vc;    // [n_kv][n_slots][128]
     float *out;              // [n_q][128]
     float *part;             // [n_kv][s_cap][GROUP][ATTN_PART]
-    uint32_t *ticket;        // [n_kv] arrival counters (fused merge only); left at zero
     const int64_t *pos;      // when set: n_valid = min(*pos + 1, n_slots)
     int n_slots, n_valid;
     int s_cap;               // split cap (partials stride); the grid has >= plan.splits columns
     float scale;
 };
 
+// Merges the nsplit partials (m_s, l_s, o_s) of KV head g in a fixed order:
+//   M = max_s m_s,  out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+// Threads split over the splits for the weights and over the 128 dims for the outputs; every
+// sum is taken in split order.  lds: at least 2 * ATTN_MAX_SPLITS + 8 floats.
+constexpr int ATTN_MAX_SPLITS = 128;
 template <int GROUP>
 __device__ __forceinline__ void attn_merge(const AttnArgs &a, int g, int nsplit, float *lds)
 {
-    // lds: at least 2 * nsplit + 8 floats
-    float *wts = lds;             // exp(m_s - M)
-    float *red = lds + nsplit;    // scratch
+    float *wts = lds;                        // e^(m_s - M), per split
+    float *ls = lds + ATTN_MAX_SPLITS;       // l_s, per split
+    float *red = lds + 2 * ATTN_MAX_SPLITS;  // 1 / L
     const int tid = threadIdx.x;
+    const size_t sstride = (size_t)GROUP * ATTN_PART;
     for (int h = 0; h < GROUP; ++h) {
         const float *p0 = a.part + ((size_t)g * a.s_cap * GROUP + h) * ATTN_PART;
-        const size_t sstride = (size_t)GROUP * ATTN_PART;
-        // max of the partial maxima (fixed order: one thread walks the splits)
+        if (tid < nsplit) {
+            wts[tid] = p0[tid * sstride];
+            ls[tid] = p0[tid * sstride + 1];
+        }
+        __syncthreads();
         if (tid == 0) {
             float M = -INFINITY;
             for (int s = 0; s < nsplit; ++s)
-                M = fmaxf(M, p0[s * sstride]);
+                M = fmaxf(M, wts[s]);
             float L = 0.0f;
             for (int s = 0; s < nsplit; ++s) {
-                const float w = __expf(p0[s * sstride] - M);
+                const float w = __expf(wts[s] - M);
                 wts[s] = w;
-                L = fmaf(w, p0[s * sstride + 1], L);
+                L = fmaf(w, ls[s], L);
             }
             red[0] = 1.0f / L;
         }
         __syncthreads();
         if (tid < ATTN_HD) {
             float o = 0.0f;
-            for (int s = 0; s < nsplit; ++s)
-                o = fmaf(wts[s], p0[s * sstride + 4 + tid], o);
+            int s = 0;
+            for (; s + 4 <= nsplit; s += 4) {   // four independent loads in flight
+                const float o0 = p0[(size_t)s * sstride + 4 + tid];
+                const float o1 = p0[(size_t)(s + 1) * sstride + 4 + tid];
+                const float o2 = p0[(size_t)(s + 2) * sstride + 4 + tid];
+                const float o3 = p0[(size_t)(s + 3) * sstride + 4 + tid];
+                o = fmaf(wts[s], o0, o);
+                o = fmaf(wts[s + 1], o1, o);
+                o = fmaf(wts[s + 2], o2, o);
+                o = fmaf(wts[s + 3], o3, o);
+            }
+            for (; s < nsplit; ++s)
+                o = fmaf(wts[s], p0[(size_t)s * sstride + 4 + tid], o);
             a.out[((size_t)g * GROUP + h) * ATTN_HD + tid] = o * red[0];
         }
         __syncthreads();
     }
 }
 
-template <int GROUP, bool FUSED_MERGE>
+template <int GROUP>
 __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
 {
     __shared__ float sc[GROUP][ATTN_SUB];                 // scores, then weights, of a sub-chunk
     __shared__ float alpha_s[GROUP];                      // rescale of the running sums
     __shared__ float ored[ATTN_WAVES][GROUP][ATTN_HD];    // per-wave partial outputs
     __shared__ float ml[GROUP][2];
-    __shared__ int last_flag;
 
     const int g = blockIdx.y;
     const int s = blockIdx.x;
@@ -273,23 +291,6 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
         mypart[tid * ATTN_PART + 0] = ml[tid][0];
         mypart[tid * ATTN_PART + 1] = ml[tid][1];
     }
-    if (!FUSED_MERGE)
-        return;
-
-    // last workgroup of this KV head merges the partials
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&a.ticket[g], 1u);
-        last_flag = (prev == (uint32_t)plan.splits - 1);
-    }
-    __syncthreads();
-    if (!last_flag)
-        return;
-    __threadfence();
-    attn_merge<GROUP>(a, g, plan.splits, &ored[0][0][0]);
-    if (tid == 0)
-        a.ticket[g] = 0u;   // ready for the next launch
 }
 
 }  // namespace vox

@@ -5,16 +5,16 @@
 
 namespace vox {
 
-template <int GROUP, bool FUSED>
+template <int GROUP>
 __global__ __launch_bounds__(ATTN_THREADS) void gqa_attn_kernel(AttnArgs a)
 {
-    attn_chunk<GROUP, FUSED>(a);
+    attn_chunk<GROUP>(a);
 }
 
 template <int GROUP>
 __global__ __launch_bounds__(256) void gqa_attn_merge_kernel(AttnArgs a, int nsplit)
 {
-    __shared__ float lds[2 * 128 + 8];
+    __shared__ float lds[2 * ATTN_MAX_SPLITS + 8];
     attn_merge<GROUP>(a, blockIdx.x, nsplit, lds);
 }
 
@@ -22,7 +22,7 @@ template <int GROUP>
 static int launch_attn(const AttnArgs &a, int n_kv, hipStream_t s)
 {
     const AttnPlan plan = attn_plan(a.n_valid, a.s_cap);
-    hipLaunchKernelGGL((gqa_attn_kernel<GROUP, false>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
+    hipLaunchKernelGGL((gqa_attn_kernel<GROUP>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
     int st = check_launch("gqa attention launch");
     if (st || plan.splits == 1)
         return st;
@@ -80,7 +80,6 @@ extern "C" int vox_gqa_decode_attn(const float *q, const float *k_cache, const f
     a.vc = v_cache;
     a.out = out;
     a.part = (float *)workspace;
-    a.ticket = nullptr;
     a.pos = nullptr;
     a.n_slots = n_slots;
     a.n_valid = n_valid;
