@@ -364,16 +364,16 @@ __global__ __launch_bounds__(ATTN_THREADS) void dec_attn_kernel(AttnArgs a)
     attn_chunk<GROUP>(a);
 }
 
-// Merges the split partials of one KV head (only launched when the window may be split).
+// Merges the split partials of one query head (only launched when the window may be split).
 template <int GROUP>
-__global__ __launch_bounds__(256) void dec_attn_merge_kernel(AttnArgs a)
+__global__ __launch_bounds__(ATTN_MERGE_THREADS) void dec_attn_merge_kernel(AttnArgs a)
 {
-    __shared__ float lds[2 * ATTN_MAX_SPLITS + 8];
+    __shared__ AttnMergeLds lds;
     const int64_t p = *a.pos + 1;
     const int nv = p < a.n_slots ? (int)p : a.n_slots;
     const AttnPlan plan = attn_plan(nv, a.s_cap);
     if (plan.splits > 1)
-        attn_merge<GROUP>(a, blockIdx.x, plan.splits, lds);
+        attn_merge<GROUP>(a, blockIdx.x / GROUP, blockIdx.x % GROUP, plan.splits, lds);
 }
 
 // RoPE frequencies theta^(-2i/head_dim) / pi, i < head_dim/2, in fp64 (once per decoder).
@@ -446,6 +446,10 @@ static int run_residual(const ResidualArgs &a, int R, hipStream_t s)
 {
     if (R == 16)
         return launch_gemv<DGeom<K, 16>, ResidualPolicy<DGeom<K, 16>>>(a, s, "decoder residual gemv");
+    if constexpr (12 % min_rows<K>() == 0) {
+        if (R == 12)
+            return launch_gemv<DGeom<K, 12>, ResidualPolicy<DGeom<K, 12>>>(a, s, "decoder residual gemv");
+    }
     if (R == 8 || min_rows<K>() > 4)
         return launch_gemv<DGeom<K, 8>, ResidualPolicy<DGeom<K, 8>>>(a, s, "decoder residual gemv");
     if constexpr (min_rows<K>() <= 4)
@@ -587,7 +591,7 @@ static int launch_attn(const AttnArgs &a, int width, int n_kv, hipStream_t s)
     int st = check_launch("decoder attention");
     if (st || width == 1)
         return st;
-    hipLaunchKernelGGL(dec_attn_merge_kernel<GROUP>, dim3(n_kv), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(dec_attn_merge_kernel<GROUP>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, a);
     return check_launch("decoder attention merge");
 }
 
@@ -758,6 +762,16 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     d->r_ffn = pick_r(2 * c->hidden, 8);
     d->r_down = pick_r(c->dim, 4);
     d->r_head = pick_r(c->vocab, gmin_model > 4 ? 8 : 8);
+    if (c->dim == 3072 && qd == 4096 && c->hidden == 9216) {
+        // measured on MI355X at this shape (decoder ms/token over tile heights per kernel):
+        // one 12-row tile per workgroup for the down projection puts its whole 16 MB in flight
+        // at once; 8-row gate/up tiles (4 + 4) avoid a second round of tiles on a few workgroups
+        d->r_qkv = 8;
+        d->r_o = 4;
+        d->r_ffn = 8;
+        d->r_down = 12;
+        d->r_head = 16;
+    }
     d->host_pos = 0;
     d->use_graph = true;
     d->cap_stream = nullptr;

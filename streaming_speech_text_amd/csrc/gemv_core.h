@@ -183,10 +183,15 @@ __device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT
 template <class Gm, class Policy>
 __device__ __forceinline__ void gemv_tiles(Policy &P)
 {
-    __shared__ u32x4 tile[Gm::CPT * Gm::NT];   // padded: every thread stores all its chunks
+    // The staged activation vector is dead once every thread holds its 64 values in registers,
+    // so the weight tile reuses its LDS (a barrier separates the two uses).
+    constexpr int TILE_VEC = Gm::CPT * Gm::NT;                 // padded: every thread stores all its chunks
+    constexpr int XS_VEC = (Gm::K / 64 * XS_ROW + 3) / 4;      // the activation vector (padded rows)
+    __shared__ u32x4 lds_main[TILE_VEC > XS_VEC ? TILE_VEC : XS_VEC];
+    u32x4 *const tile = lds_main;
+    float *const xs = reinterpret_cast<float *>(lds_main);
     __shared__ float red[Gm::R * Gm::TR];
     __shared__ float rowsum[Gm::R];
-    __shared__ __attribute__((aligned(16))) float xs[Gm::K / 64 * XS_ROW];   // the activation vector (padded rows)
     __shared__ float wsum[Gm::NT / 64];
 
     const int tid = threadIdx.x;
@@ -225,6 +230,7 @@ __device__ __forceinline__ void gemv_tiles(Policy &P)
         }
     }
     px.finish();
+    __syncthreads();   // xs is read by every thread before the first tile overwrites it
 
     for (; t < ntiles; t += gridDim.x) {
 #pragma unroll

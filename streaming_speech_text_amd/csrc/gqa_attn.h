@@ -13,8 +13,8 @@
 // waves streams its chunk of K and V for one KV head once and serves all GROUP query heads
 // of that head from the same loads.  Inside the chunk it walks 128-position sub-chunks with
 // an online softmax (running max and sum).  With one chunk the workgroup writes the output
-// directly; otherwise it writes a partial (max, sum, unnormalised output) and the partials are
-// merged in a fixed order, either by a second kernel or by the last workgroup of the head.
+// directly; otherwise it writes a partial (max, sum, unnormalised output) and a second kernel
+// merges the partials in a fixed order.
 #pragma once
 
 #include "vox_common.h"
@@ -64,57 +64,74 @@ struct AttnArgs {
     float scale;
 };
 
-// Merges the nsplit partials (m_s, l_s, o_s) of KV head g in a fixed order:
-//   M = max_s m_s,  out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
-// Threads split over the splits for the weights and over the 128 dims for the outputs; every
-// sum is taken in split order.  lds: at least 2 * ATTN_MAX_SPLITS + 8 floats.
+// Merges the nsplit partials (m_s, l_s, o_s) of query head h of KV head g in a fixed order:
+//   M = max_s m_s,  w_s = e^(m_s - M),  out = (sum_s w_s o_s) / (sum_s w_s l_s).
+// One workgroup of ATTN_MERGE_THREADS per query head.  Every load is issued before the first
+// use (the partials were written by another kernel, so each load is a full memory round trip;
+// issuing them all at once keeps the merge at about one round trip).  Thread (j, d) sums the
+// splits s = j, j + 4, ... of output dim d; the four part sums and the weight sums are added
+// in a fixed order, so the result does not depend on timing.
 constexpr int ATTN_MAX_SPLITS = 128;
+constexpr int ATTN_MERGE_THREADS = 512;
+constexpr int ATTN_MERGE_J = ATTN_MERGE_THREADS / ATTN_HD;          // 4 split phases
+constexpr int ATTN_MERGE_PER = ATTN_MAX_SPLITS / ATTN_MERGE_J;      // 32 splits per thread
+struct AttnMergeLds {
+    float w[ATTN_MAX_SPLITS];                 // e^(m_s - M)
+    float wred[ATTN_MERGE_THREADS / 64][2];   // per-wave max, then per-wave sum of w_s l_s
+    float osum[ATTN_MERGE_J][ATTN_HD];
+};
 template <int GROUP>
-__device__ __forceinline__ void attn_merge(const AttnArgs &a, int g, int nsplit, float *lds)
+__device__ __forceinline__ void attn_merge(const AttnArgs &a, int g, int h, int nsplit, AttnMergeLds &L)
 {
-    float *wts = lds;                        // e^(m_s - M), per split
-    float *ls = lds + ATTN_MAX_SPLITS;       // l_s, per split
-    float *red = lds + 2 * ATTN_MAX_SPLITS;  // 1 / L
     const int tid = threadIdx.x;
+    const int wave = tid >> 6;
     const size_t sstride = (size_t)GROUP * ATTN_PART;
-    for (int h = 0; h < GROUP; ++h) {
-        const float *p0 = a.part + ((size_t)g * a.s_cap * GROUP + h) * ATTN_PART;
-        if (tid < nsplit) {
-            wts[tid] = p0[tid * sstride];
-            ls[tid] = p0[tid * sstride + 1];
-        }
-        __syncthreads();
-        if (tid == 0) {
-            float M = -INFINITY;
-            for (int s = 0; s < nsplit; ++s)
-                M = fmaxf(M, wts[s]);
-            float L = 0.0f;
-            for (int s = 0; s < nsplit; ++s) {
-                const float w = __expf(wts[s] - M);
-                wts[s] = w;
-                L = fmaf(w, ls[s], L);
-            }
-            red[0] = 1.0f / L;
-        }
-        __syncthreads();
-        if (tid < ATTN_HD) {
-            float o = 0.0f;
-            int s = 0;
-            for (; s + 4 <= nsplit; s += 4) {   // four independent loads in flight
-                const float o0 = p0[(size_t)s * sstride + 4 + tid];
-                const float o1 = p0[(size_t)(s + 1) * sstride + 4 + tid];
-                const float o2 = p0[(size_t)(s + 2) * sstride + 4 + tid];
-                const float o3 = p0[(size_t)(s + 3) * sstride + 4 + tid];
-                o = fmaf(wts[s], o0, o);
-                o = fmaf(wts[s + 1], o1, o);
-                o = fmaf(wts[s + 2], o2, o);
-                o = fmaf(wts[s + 3], o3, o);
-            }
-            for (; s < nsplit; ++s)
-                o = fmaf(wts[s], p0[(size_t)s * sstride + 4 + tid], o);
-            a.out[((size_t)g * GROUP + h) * ATTN_HD + tid] = o * red[0];
-        }
-        __syncthreads();
+    const float *p0 = a.part + ((size_t)g * a.s_cap * GROUP + h) * ATTN_PART;
+    // (m_s, l_s) for s = tid, then o_s[d] for this thread's splits; indices are clamped so that
+    // every load is unconditional, and out-of-range splits get weight 0 below
+    const int sm = tid < nsplit ? tid : 0;
+    const float m_s = p0[(size_t)sm * sstride];
+    const float l_s = p0[(size_t)sm * sstride + 1];
+    const int j = tid / ATTN_HD, d = tid % ATTN_HD;
+    float ov[ATTN_MERGE_PER];
+#pragma unroll
+    for (int i = 0; i < ATTN_MERGE_PER; ++i) {
+        const int sp = j + ATTN_MERGE_J * i;
+        ov[i] = p0[(size_t)(sp < nsplit ? sp : 0) * sstride + 4 + d];
+    }
+    // M over the splits (max is exact in any order)
+    const float mv = tid < nsplit ? m_s : -INFINITY;
+    const float wm = wave_max(mv);
+    if ((tid & 63) == 0)
+        L.wred[wave][0] = wm;
+    __syncthreads();
+    float M = L.wred[0][0];
+#pragma unroll
+    for (int w = 1; w < ATTN_MERGE_THREADS / 64; ++w)
+        M = fmaxf(M, L.wred[w][0]);
+    const float w_s = tid < nsplit ? __expf(m_s - M) : 0.0f;
+    if (tid < ATTN_MAX_SPLITS)
+        L.w[tid] = w_s;
+    const float ws = wave_sum(w_s * l_s);
+    if ((tid & 63) == 0)
+        L.wred[wave][1] = ws;
+    __syncthreads();
+    float o = 0.0f;
+#pragma unroll
+    for (int i = 0; i < ATTN_MERGE_PER; ++i)
+        o = fmaf(L.w[j + ATTN_MERGE_J * i], ov[i], o);
+    L.osum[j][d] = o;
+    __syncthreads();
+    if (tid < ATTN_HD) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int w = 0; w < ATTN_MAX_SPLITS / 64; ++w)   // the waves that hold splits
+            tot += L.wred[w][1];
+        float os = L.osum[0][tid];
+#pragma unroll
+        for (int jj = 1; jj < ATTN_MERGE_J; ++jj)
+            os += L.osum[jj][tid];
+        a.out[((size_t)g * GROUP + h) * ATTN_HD + tid] = os / tot;
     }
 }
 
@@ -162,25 +179,43 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
     for (int base = t0; base < t1; base += ATTN_SUB) {
         // issue the K and V loads of the whole sub-chunk first (the first time, the query
         // loads follow them so the two latencies overlap)
+        // A full sub-chunk loads unconditionally (no branches between the loads, so the wait
+        // before the scores leaves the V loads in flight).  A partial one skips the positions
+        // past the chunk end; their scores are -inf below, so their weights are exactly 0.
         float4 kr[4][2];
         float2 vr[16];
+        if (base + ATTN_SUB <= t1) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int t = base + it * 32 + wave * 4 + pslot;
-            if (t < t1) {
+            for (int it = 0; it < 4; ++it) {
+                const int t = base + it * 32 + wave * 4 + pslot;
                 const float4 *k4 = reinterpret_cast<const float4 *>(kbase + (size_t)t * ATTN_HD + 8 * seg);
                 kr[it][0] = k4[0];
                 kr[it][1] = k4[1];
-            } else {
-                kr[it][0] = make_float4(0.f, 0.f, 0.f, 0.f);
-                kr[it][1] = kr[it][0];
             }
-        }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = base + wave + ATTN_WAVES * i;
-            vr[i] = t < t1 ? *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane)
-                           : make_float2(0.0f, 0.0f);
+            for (int i = 0; i < 16; ++i) {
+                const int t = base + wave + ATTN_WAVES * i;
+                vr[i] = *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int t = base + it * 32 + wave * 4 + pslot;
+                if (t < t1) {
+                    const float4 *k4 = reinterpret_cast<const float4 *>(kbase + (size_t)t * ATTN_HD + 8 * seg);
+                    kr[it][0] = k4[0];
+                    kr[it][1] = k4[1];
+                } else {
+                    kr[it][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    kr[it][1] = kr[it][0];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int t = base + wave + ATTN_WAVES * i;
+                vr[i] = t < t1 ? *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane)
+                               : make_float2(0.0f, 0.0f);
+            }
         }
         if (!q_loaded) {
 #pragma unroll

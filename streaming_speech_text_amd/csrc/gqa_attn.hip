@@ -5,17 +5,19 @@
 
 namespace vox {
 
+// Two resident workgroups per compute unit (at most 128 registers per lane).
 template <int GROUP>
 __global__ __launch_bounds__(ATTN_THREADS) void gqa_attn_kernel(AttnArgs a)
 {
     attn_chunk<GROUP>(a);
 }
 
+// grid: n_kv_heads * GROUP, one query head per workgroup
 template <int GROUP>
-__global__ __launch_bounds__(256) void gqa_attn_merge_kernel(AttnArgs a, int nsplit)
+__global__ __launch_bounds__(ATTN_MERGE_THREADS) void gqa_attn_merge_kernel(AttnArgs a, int nsplit)
 {
-    __shared__ float lds[2 * ATTN_MAX_SPLITS + 8];
-    attn_merge<GROUP>(a, blockIdx.x, nsplit, lds);
+    __shared__ AttnMergeLds lds;
+    attn_merge<GROUP>(a, blockIdx.x / GROUP, blockIdx.x % GROUP, nsplit, lds);
 }
 
 template <int GROUP>
@@ -26,7 +28,7 @@ static int launch_attn(const AttnArgs &a, int n_kv, hipStream_t s)
     int st = check_launch("gqa attention launch");
     if (st || plan.splits == 1)
         return st;
-    hipLaunchKernelGGL(gqa_attn_merge_kernel<GROUP>, dim3(n_kv), dim3(256), 0, s, a, plan.splits);
+    hipLaunchKernelGGL(gqa_attn_merge_kernel<GROUP>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, a, plan.splits);
     return check_launch("gqa attention merge launch");
 }
 

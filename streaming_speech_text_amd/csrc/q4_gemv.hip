@@ -94,8 +94,9 @@ struct PlainGemvPolicy {
     __device__ void finish(float *) {}
 };
 
+// Three waves per SIMD: with 3-wave workgroups that is four resident workgroups per compute unit.
 template <class Gm>
-__global__ __launch_bounds__(Gm::NT) void q4_gemv_tiled_kernel(PlainGemvPolicy<Gm> P)
+__global__ __launch_bounds__(Gm::NT) __attribute__((amdgpu_waves_per_eu(3))) void q4_gemv_tiled_kernel(PlainGemvPolicy<Gm> P)
 {
     gemv_tiles<Gm>(P);
 }
