@@ -65,7 +65,8 @@ int vox_q4_gemv(const void *w_q4, const float *x, float *y, int64_t n, int64_t k
  * [RS] 아키텍처: Q4_0 linears), on the matrix cores.  x_bf16: m rows by k, bf16 bit patterns,
  * row major; w_q4: n rows by k; y: m by n fp32, row major, must not overlap the inputs.
  * Products of the exact Q4 codes with bf16 activations, fp32 accumulation.
- * m == 0 or n == 0 is a no-op.  k % 32 != 0 -> VOX_E_INVAL. */
+ * m == 0 or n == 0 is a no-op.  k % 32 != 0 -> VOX_E_INVAL; m > 1048560 or n, k > 2^24 ->
+ * VOX_E_UNSUPPORTED.  x_bf16 must be 8-byte and w_q4 2-byte aligned (VOX_E_UNSUPPORTED). */
 int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, int64_t m, int64_t n, int64_t k,
                 void *stream);
 

@@ -7,21 +7,21 @@
 //
 // Exactness: a dequantised weight (code - 8) * d needs up to 15 significant bits, more than
 // bf16 holds, so the matrix cores never see it.  Each 32-input Q4_0 block is one
-// v_mfma_f32_16x16x32_bf16 whose B operand holds the exact integers (code - 8) in bf16 and
-// whose A operand holds the bf16 activations; the fp32 result is multiplied by the block's
-// scale d and accumulated in fp32 on the vector units.
+// v_mfma_f32_16x16x32_bf16 per 16 x 16 output block whose B operand holds exact small integers
+// in bf16 and whose A operand holds the bf16 activations; the fp32 result is multiplied by the
+// block's scale d and accumulated in fp32 on the vector units.
 //
-// Work split: a workgroup of 8 waves owns a (16*MI) x (16*NJ) tile of Y.  The eight waves split
-// the K blocks into eight contiguous ranges; each wave loads its MFMA operands straight from
-// memory (no LDS staging, no barrier per block) with GEMV_PF blocks in flight in registers, and
-// at the end the eight partial tiles are added in LDS in wave order (deterministic).  Chunks of
-// a few frames (small M) are weight-streaming problems; splitting K over the waves is what
-// puts enough requests in flight.
-//
-// Order of k inside a block: the MFMA sums over its 32 k slots; which hardware slot holds
-// which input does not matter as long as A and B agree.  Lane group g (= lane / 16) takes
-// code bytes 4g..4g+3, i.e. inputs {4g..4g+3} (low nibbles) then {16+4g..16+4g+3} (high
-// nibbles), and reads the activations of the same inputs.
+// Two kernels:
+//  * small outputs: a workgroup of 8 waves owns a (16*MI) x (16*NJ) tile; the waves
+//    split the K blocks into eight contiguous ranges, load their operands straight from memory
+//    with GM_PF blocks in flight, and the eight partial tiles are added in LDS in wave order.
+//    These are weight-streaming problems; splitting K over the waves puts requests in flight.
+//    B holds (code - 8).  Lane group g (= lane / 16) takes code bytes 4g..4g+3, i.e. inputs
+//    {4g..4g+3} (low nibbles) then {16+4g..16+4g+3} (high nibbles), and the activations of
+//    the same inputs (the MFMA's k slots may hold the inputs in any order A and B agree on).
+//  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS).
+#include <type_traits>
+
 #include "vox_common.h"
 #include "vox_host.h"
 
@@ -39,7 +39,8 @@ constexpr int GM_PF = 4;           // K blocks in flight per wave
 // bf16 bits of two small integers given as exact fp32 values: the upper halves.
 __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi)
 {
-    return (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
+    // bytes 2, 3 of lo then bytes 2, 3 of hi (one v_perm_b32)
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
 }
 
 // (code - 8) as bf16 for the 8 codes of one lane (4 code bytes): low nibbles then high nibbles.
@@ -176,6 +177,258 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Tiled kernel for longer chunks (K of 1280 or 5120).  A workgroup of 8 waves owns a 64 x 64
+// tile of Y and walks K in stages of 8 Q4_0 blocks; in every stage wave w takes block w, so
+// each wave computes the whole tile over one eighth of K and no operand is shared:
+//  * the wave loads its A operands straight from memory one stage ahead: lane L's 16 bytes
+//    of a 16-row block are row L % 16, inputs 8(L/16) .. 8(L/16)+7 of the Q4_0 block;
+//  * the workgroup copies the stage's weight bytes (8 blocks = 144 contiguous, 16-byte aligned
+//    bytes per row) to LDS with 16-byte loads; each wave then reads the bytes of its block
+//    with aligned dword reads and unpacks the codes in registers to exact bf16: lane group g
+//    of a column takes inputs 8g .. 8g+7, i.e. the low (g < 2) or high (g >= 2) nibbles of
+//    code bytes 8(g%2) .. 8(g%2)+7;
+//  * per block the wave runs 4 x 4 matrix-core products of A with the codes, each seeded (as
+//    accumulator input) with A times a constant -8 operand, so each product is exactly the
+//    block's sum of a * (code - 8) up to fp32 rounding; scale * product goes into fp32.
+// The eight waves' partial tiles are added through LDS in a fixed tree order at the end.
+// ---------------------------------------------------------------------------------------
+constexpr int GT_BM = 64, GT_BN = 64, GT_KC = 8, GT_THREADS = 512;
+constexpr int GT_RAW = GT_KC * 18;                          // weight bytes of one row per stage
+constexpr int GT_W_CHUNKS = GT_BN * GT_RAW / 16;            // 16-byte weight pieces per stage
+static_assert(GT_W_CHUNKS <= 2 * GT_THREADS, "two rounds of weight loads cover a stage");
+static_assert(GT_KC == GT_THREADS / 64, "one block per wave per stage");
+
+// Byte j of v as a float (one v_cvt_f32_ubyte{j}).
+__device__ __forceinline__ float ubyte_to_f(uint32_t v, int j)
+{
+    float r;
+    switch (j) {
+    case 0: asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v)); break;
+    case 1: asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v)); break;
+    case 2: asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v)); break;
+    default: asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v)); break;
+    }
+    return r;
+}
+
+// The codes themselves (0 .. 15, exact in bf16) for 8 codes taken from one nibble of 8 bytes
+// (lo: bytes 0-3, hi: 4-7).  The - 8 is added by the matrix core through its accumulator input.
+__device__ __forceinline__ u32x4v nibbles_to_bf16(uint32_t lo, uint32_t hi, bool high_nibble)
+{
+    const uint32_t a = (high_nibble ? lo >> 4 : lo) & 0x0F0F0F0Fu;
+    const uint32_t b = (high_nibble ? hi >> 4 : hi) & 0x0F0F0F0Fu;
+    u32x4v p;
+    p.x = pack_bf16_pair(ubyte_to_f(a, 0), ubyte_to_f(a, 1));
+    p.y = pack_bf16_pair(ubyte_to_f(a, 2), ubyte_to_f(a, 3));
+    p.z = pack_bf16_pair(ubyte_to_f(b, 0), ubyte_to_f(b, 1));
+    p.w = pack_bf16_pair(ubyte_to_f(b, 2), ubyte_to_f(b, 3));
+    return p;
+}
+
+// Reads the bytes of block `blk` (0..7 of the stage) of the four 16-column blocks from the raw
+// stage copy (144 bytes per row) with aligned dword reads and unpacks this lane's operand
+// (column 16j + l16, inputs 8*grp .. 8*grp+7) and scale.  ODD: blk is odd, so the block starts
+// at 2 mod 4 and its code bytes are 4-aligned; otherwise the block is 4-aligned and the code
+// bytes are 2 mod 4.
+template <bool ODD>
+__device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, int grp, bf16x8 (&bf)[4],
+                                         float (&d)[4])
+{
+    uint32_t dw[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t *p = raw + (((16 * j + l16) * GT_RAW + 18 * blk) >> 2);
+        if constexpr (ODD) {
+            const uint32_t *q = p + 1 + 2 * (grp & 1);
+            dw[j][0] = p[0];
+            dw[j][1] = q[0];
+            dw[j][2] = q[1];
+        } else {
+            const uint32_t *q = p + 2 * (grp & 1);
+            dw[j][0] = p[0];
+            dw[j][1] = q[0];
+            dw[j][2] = q[1];
+            dw[j][3] = q[2];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t d16, lo, hi;
+        if constexpr (ODD) {
+            d16 = dw[j][0] >> 16;
+            lo = dw[j][1];
+            hi = dw[j][2];
+        } else {
+            d16 = dw[j][0] & 0xFFFFu;
+            lo = __builtin_amdgcn_alignbyte(dw[j][2], dw[j][1], 2);
+            hi = __builtin_amdgcn_alignbyte(dw[j][3], dw[j][2], 2);
+        }
+        bf[j] = __builtin_bit_cast(bf16x8, nibbles_to_bf16(lo, hi, grp >= 2));
+        d[j] = half_bits_to_float(d16);
+    }
+}
+
+// NST: stages (K / 256), fixed at compile time.
+template <int NST>
+__global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t *__restrict__ w,
+                                                                   const uint16_t *__restrict__ x,
+                                                                   float *__restrict__ y, int m, int n, int k)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t braw[2][GT_BN * GT_RAW / 4];
+    __shared__ f32x4v red[4][16][64];   // tree reduction of the waves' tiles
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int m0 = blockIdx.y * GT_BM;
+    const int n0 = blockIdx.x * GT_BN;
+    const uint32_t row_bytes = (uint32_t)(k / 32) * 18;
+
+    // A operands of this lane: rows m0 + 16i + l16 (clamped), inputs 8*grp .. of block `wave`
+    uint32_t aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        aoff[i] = (uint32_t)min(m0 + 16 * i + l16, m - 1) * (uint32_t)k + (uint32_t)(32 * wave + 8 * grp);
+    // weight pieces: chunk c -> row c / 9 of the tile, piece c % 9; the second round is clamped
+    // to the last chunk (a duplicate load and an identical LDS store)
+    uint32_t woff[2];
+    int wlds[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int c = min(tid + GT_THREADS * r, GT_W_CHUNKS - 1);
+        const int col = min(n0 + c / (GT_RAW / 16), n - 1);
+        woff[r] = (uint32_t)col * row_bytes + (uint32_t)(16 * (c % (GT_RAW / 16)));
+        wlds[r] = 4 * c;
+    }
+
+    // two stages of loads in flight: register slots 0 and 1 (compile-time indices)
+    u32x4v ar[2][4], wr[2][2];
+    auto load_stage = [&](int st, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        st = min(st, NST - 1);   // past the end: a harmless reload of the last stage
+        const uint16_t *xs = x + (size_t)st * (GT_KC * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ar[S][i] = *reinterpret_cast<const u32x4v *>(xs + aoff[i]);
+        const uint8_t *ws = w + (size_t)st * GT_RAW;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            wr[S][r] = *reinterpret_cast<const u32x4v *>(ws + woff[r]);
+    };
+
+    f32x4v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = 0.0f;
+
+    auto stage = [&](int st, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        const int b = st & 1;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            *reinterpret_cast<u32x4v *>(&braw[b][wlds[r]]) = wr[S][r];
+        bf16x8 af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            af[i] = __builtin_bit_cast(bf16x8, ar[S][i]);
+        __syncthreads();   // braw[b] complete; braw[b] is next written two stages later
+        // B operands of block `wave` for the four 16-column blocks.  The block of column c
+        // starts at byte o = c*144 + 18*wave: 4-aligned for even waves, 2 mod 4 for odd ones
+        // (the parity is uniform over a wave, so each wave runs one straight-line path).
+        bf16x8 bf[4];
+        float d[4];
+        if ((wave & 1) == 0)
+            unpack_b<false>(&braw[b][0], wave, l16, grp, bf, d);
+        else
+            unpack_b<true>(&braw[b][0], wave, l16, grp, bf, d);
+        // products in two rounds of 8 with independent result registers, then the scaled sums.
+        // B holds the codes c; sum_k a_k (c_k - 8) = sum_k a_k c_k + sum_k a_k (-8), and the
+        // second term (one product per row block) enters as the accumulator input.
+        const bf16x8 neg8 = __builtin_bit_cast(bf16x8, (u32x4v)0xC100C100u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4v t[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const f32x4v c8 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[2 * h + i], neg8, (f32x4v)0.0f, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    t[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[2 * h + i], bf[j], c8, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[2 * h + i][j] += d[j] * t[i][j];
+        }
+        load_stage(st + 2, slot);   // after the products, so the slot's registers are free
+    };
+    typedef std::integral_constant<int, 0> S0;
+    typedef std::integral_constant<int, 1> S1;
+    load_stage(0, S0());
+    load_stage(1, S1());
+    int st = 0;
+    for (; st + 1 < NST; st += 2) {
+        stage(st, S0());
+        stage(st + 1, S1());
+    }
+    if constexpr (NST % 2)
+        stage(NST - 1, S0());
+
+    // tree: (w + 4) -> w, then (w + 2) -> w, then 1 -> 0; fixed order
+#pragma unroll
+    for (int half = 4; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    red[wave - half][i * 4 + j][lane] = acc[i][j];
+        }
+        __syncthreads();
+        if (wave < half) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] += red[wave][i * 4 + j][lane];
+        }
+        __syncthreads();
+    }
+    if (wave == 0) {
+        // D layout of a 16x16 block: lane holds rows 4*(lane/16) .. +3 of column lane%16
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + 16 * j + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + 16 * i + 4 * grp + r;
+                    if (row < m && col < n)
+                        y[(size_t)row * n + col] = acc[i][j][r];
+                }
+            }
+    }
+}
+
+// K values with a compiled stage sequence (the encoder's widths)
+static bool tiled_k(int64_t k) { return k == 1280 || k == 5120; }
+
+static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
+{
+    const dim3 grid((unsigned)((n + GT_BN - 1) / GT_BN), (unsigned)((m + GT_BM - 1) / GT_BM));
+    if (k == 1280)
+        hipLaunchKernelGGL(q4_gemm_tiled_kernel<5>, grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y, m, n, k);
+    else
+        hipLaunchKernelGGL(q4_gemm_tiled_kernel<20>, grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y, m, n, k);
+    return check_launch("vox_q4_gemm tiled");
+}
+
 template <int MI, int NJ>
 static int launch_gemm(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
 {
@@ -198,8 +451,8 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
         return ok();
     if (!w_q4 || !x_bf16 || !y)
         return fail(VOX_E_INVAL, "vox_q4_gemm: null pointer");
-    if (m > (1 << 24) || n > (1 << 24) || k > (1 << 24))
-        return fail(VOX_E_UNSUPPORTED, "vox_q4_gemm: dimension too large");
+    if (m > 65535 * 16 || n > (1 << 24) || k > (1 << 24))   // grid rows: m / 16 <= 65535
+        return fail(VOX_E_UNSUPPORTED, "vox_q4_gemm: dimension too large (m <= 1048560, n, k <= 2^24)");
     if (!aligned(x_bf16, 8) || !aligned(w_q4, 2))
         return fail(VOX_E_UNSUPPORTED, "vox_q4_gemm: x must be 8-byte and w 2-byte aligned");
     const size_t wbytes = (size_t)n * (size_t)(k / 32) * 18, xbytes = (size_t)m * k * 2, ybytes = (size_t)m * n * 4;
@@ -207,11 +460,14 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
         return fail(VOX_E_INVAL, "vox_q4_gemm: y overlaps an input");
     hipStream_t s = (hipStream_t)stream;
     int st;
-    if (m <= 16)
-        st = launch_gemm<1, 1>(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
-    else if (m <= 32)
-        st = launch_gemm<2, 2>(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
+    // the tiled kernel: 16-byte aligned operands, a compiled K, and offsets that fit 32 bits
+    const bool tiled_ok = aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_k(k) &&
+                          (uint64_t)m * (uint64_t)k < (1ull << 31) && wbytes < (1ull << 31);
+    // measured on MI355X at the encoder's shapes: the split-K kernel is the faster one while the
+    // output is small (up to about 48 x 1280 values), the tiled kernel beyond that
+    if (tiled_ok && m * n > 48 * 1280)
+        st = launch_gemm_tiled(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
     else
-        st = launch_gemm<4, 2>(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
+        st = launch_gemm<1, 1>(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
     return st ? st : ok();
 }

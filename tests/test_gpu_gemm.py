@@ -31,7 +31,7 @@ def test_gemm_encoder_chunk(vx, orc, m):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1280, 1280), (17, 100, 96), (63, 65, 32), (65, 1000, 5120), (130, 64, 2080),
-                                   (3, 5, 64)])
+                                   (3, 5, 64), (97, 77, 1280), (751, 130, 5120), (40, 1280, 5120)])
 def test_gemm_ragged(vx, orc, m, n, k):
     w, xb = synth.gemm_inputs(600 + m, m, n, k)
     say(f"gemm ragged m={m} n={n} k={k}")
