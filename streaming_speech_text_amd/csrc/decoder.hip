@@ -352,8 +352,9 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(DecCtl *ctl, const un
     }
 }
 
+// At least three waves per SIMD: four resident 3-wave workgroups per compute unit.
 template <class Gm, class Policy>
-__global__ __launch_bounds__(Gm::NT) void dec_gemv_kernel(Policy P)
+__global__ __launch_bounds__(Gm::NT) __attribute__((amdgpu_waves_per_eu(3))) void dec_gemv_kernel(Policy P)
 {
     gemv_tiles<Gm>(P);
 }
@@ -434,10 +435,8 @@ constexpr int min_rows()
 }
 
 template <int K, bool EMBED>
-static int run_qkv(const QkvArgs &a, int R, hipStream_t s)
+static int run_qkv(const QkvArgs &a, int, hipStream_t s)
 {
-    if (R == 16)
-        return launch_gemv<DGeom<K, 16>, QkvPolicy<DGeom<K, 16>, EMBED>>(a, s, "decoder qkv");
     return launch_gemv<DGeom<K, 8>, QkvPolicy<DGeom<K, 8>, EMBED>>(a, s, "decoder qkv");
 }
 
@@ -757,7 +756,7 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     d->s_cap = attn_split_cap(c->n_slots);
     const int qd = c->n_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
     const int gmin_model = c->dim == 3072 ? 4 : 8;
-    d->r_qkv = pick_r(qd + 2 * kvd, 8);
+    d->r_qkv = 8;   // 8-row tiles stay inside one of the q, k, v row ranges for every width
     d->r_o = pick_r(c->dim, qd == 4096 ? 4 : 8);
     d->r_ffn = pick_r(2 * c->hidden, 8);
     d->r_down = pick_r(c->dim, 4);
