@@ -359,10 +359,11 @@ __global__ __launch_bounds__(Gm::NT) __attribute__((amdgpu_waves_per_eu(3))) voi
     gemv_tiles<Gm>(P);
 }
 
-template <int GROUP>
-__global__ __launch_bounds__(ATTN_THREADS) void dec_attn_kernel(AttnArgs a)
+// LATE_V for the split-window buckets: two resident workgroups per compute unit.
+template <int GROUP, bool LATE_V>
+__global__ __launch_bounds__(ATTN_THREADS) __attribute__((amdgpu_waves_per_eu(LATE_V && GROUP <= 4 ? 4 : 1))) void dec_attn_kernel(AttnArgs a)
 {
-    attn_chunk<GROUP>(a);
+    attn_chunk<GROUP, LATE_V>(a);
 }
 
 // Merges the split partials of one query head (only launched when the window may be split).
@@ -586,7 +587,10 @@ static int attn_bucket(const vox_decoder *d, int64_t pos)
 template <int GROUP>
 static int launch_attn(const AttnArgs &a, int width, int n_kv, hipStream_t s)
 {
-    hipLaunchKernelGGL(dec_attn_kernel<GROUP>, dim3(width, n_kv), dim3(ATTN_THREADS), 0, s, a);
+    if (width > 1)
+        hipLaunchKernelGGL((dec_attn_kernel<GROUP, true>), dim3(width, n_kv), dim3(ATTN_THREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL((dec_attn_kernel<GROUP, false>), dim3(width, n_kv), dim3(ATTN_THREADS), 0, s, a);
     int st = check_launch("decoder attention");
     if (st || width == 1)
         return st;

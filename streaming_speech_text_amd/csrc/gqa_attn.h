@@ -135,7 +135,10 @@ __device__ __forceinline__ void attn_merge(const AttnArgs &a, int g, int h, int 
     }
 }
 
-template <int GROUP>
+// LATE_V: issue the V loads after the scores instead of with the K loads.  K and V then never
+// hold registers at the same time (two workgroups fit a compute unit), and the V latency overlaps
+// the softmax; used when the window is split, where many workgroups share the chip.
+template <int GROUP, bool LATE_V>
 __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
 {
     __shared__ float sc[GROUP][ATTN_SUB];                 // scores, then weights, of a sub-chunk
@@ -184,18 +187,30 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
         // past the chunk end; their scores are -inf below, so their weights are exactly 0.
         float4 kr[4][2];
         float2 vr[16];
-        if (base + ATTN_SUB <= t1) {
+        const bool full = base + ATTN_SUB <= t1;
+        auto load_v = [&]() {
+            if (full) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = base + wave + ATTN_WAVES * i;
+                    vr[i] = *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = base + wave + ATTN_WAVES * i;
+                    vr[i] = t < t1 ? *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane)
+                                   : make_float2(0.0f, 0.0f);
+                }
+            }
+        };
+        if (full) {
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int t = base + it * 32 + wave * 4 + pslot;
                 const float4 *k4 = reinterpret_cast<const float4 *>(kbase + (size_t)t * ATTN_HD + 8 * seg);
                 kr[it][0] = k4[0];
                 kr[it][1] = k4[1];
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = base + wave + ATTN_WAVES * i;
-                vr[i] = *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane);
             }
         } else {
 #pragma unroll
@@ -210,13 +225,9 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
                     kr[it][1] = kr[it][0];
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = base + wave + ATTN_WAVES * i;
-                vr[i] = t < t1 ? *reinterpret_cast<const float2 *>(vbase + (size_t)t * ATTN_HD + 2 * lane)
-                               : make_float2(0.0f, 0.0f);
-            }
         }
+        if constexpr (!LATE_V)
+            load_v();
         if (!q_loaded) {
 #pragma unroll
             for (int h = 0; h < GROUP; ++h) {
@@ -245,6 +256,8 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
                     sc[h][p] = (base + p < t1) ? d * a.scale : -INFINITY;
             }
         }
+        if constexpr (LATE_V)
+            load_v();
         __syncthreads();
         // online softmax update: wave (h % 8) handles query head h, two positions per lane
 #pragma unroll

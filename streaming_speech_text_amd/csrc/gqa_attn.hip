@@ -6,10 +6,12 @@
 namespace vox {
 
 // Two resident workgroups per compute unit (at most 128 registers per lane).
-template <int GROUP>
-__global__ __launch_bounds__(ATTN_THREADS) void gqa_attn_kernel(AttnArgs a)
+// LATE_V (split windows), groups up to 4: at least four waves per SIMD, i.e. two resident workgroups per
+// compute unit.
+template <int GROUP, bool LATE_V>
+__global__ __launch_bounds__(ATTN_THREADS) __attribute__((amdgpu_waves_per_eu(LATE_V && GROUP <= 4 ? 4 : 1))) void gqa_attn_kernel(AttnArgs a)
 {
-    attn_chunk<GROUP>(a);
+    attn_chunk<GROUP, LATE_V>(a);
 }
 
 // grid: n_kv_heads * GROUP, one query head per workgroup
@@ -24,7 +26,10 @@ template <int GROUP>
 static int launch_attn(const AttnArgs &a, int n_kv, hipStream_t s)
 {
     const AttnPlan plan = attn_plan(a.n_valid, a.s_cap);
-    hipLaunchKernelGGL((gqa_attn_kernel<GROUP>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
+    if (plan.splits > 1)
+        hipLaunchKernelGGL((gqa_attn_kernel<GROUP, true>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL((gqa_attn_kernel<GROUP, false>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
     int st = check_launch("gqa attention launch");
     if (st || plan.splits == 1)
         return st;
