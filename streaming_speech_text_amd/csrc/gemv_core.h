@@ -170,6 +170,68 @@ __device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT
     }
 }
 
+// Row sums of the tile in LDS: each thread takes the block pair `c` of rows g, g+G, ...; the
+// partial dots go through `red` and are added per row in a fixed order into rowsum[R].
+// Ends with a workgroup barrier, after which the tile buffer may be overwritten.
+template <class Gm>
+__device__ __forceinline__ void gemv_tile_rows(const u32x4 *tile, float *red, float *rowsum, const PairX &px)
+{
+    const int tid = threadIdx.x;
+    const int c = tid % Gm::TR;
+    const int g = tid / Gm::TR;
+    const uint32_t *lds32 = reinterpret_cast<const uint32_t *>(tile);
+#pragma unroll
+    for (int j = 0; j < Gm::R / Gm::G; ++j) {
+        const int rr = g + j * Gm::G;
+        const uint32_t *p = lds32 + rr * (Gm::RB / 4) + 9 * c;
+        uint32_t D[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i)
+            D[i] = p[i];
+        red[rr * Gm::TR + c] = q4_pair_dot(D, px.x, px.n8a, px.n8b);
+    }
+    __syncthreads();
+    // Each row's TR partials are added by a row of 16 lanes (TR/16 each, then a DPP tree), in
+    // a fixed order; rows beyond NT/16 take a second pass.
+    static_assert(Gm::TR % 16 == 0, "row partials split over 16 lanes");
+    constexpr int ROWS_PER_PASS = Gm::NT / 16;
+#pragma unroll
+    for (int r0 = 0; r0 < Gm::R; r0 += ROWS_PER_PASS) {
+        const int row = r0 + tid / 16;
+        if (row < Gm::R) {   // uniform over each 16-lane row
+            const int j = tid % 16;
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < Gm::TR / 16; ++i)
+                s += red[row * Gm::TR + i * 16 + j];
+            s = row16_sum(s);
+            if (j == 0)
+                rowsum[row] = s;
+        }
+    }
+    __syncthreads();
+}
+
+// The workgroup stages the activation vector once in LDS (normalisation applied there); each
+// thread then keeps the 64 values of its pair column in registers.  Ends with a barrier, after
+// which the LDS of xs may be reused.
+template <class Gm, class Policy>
+__device__ __forceinline__ void gemv_load_x(Policy &P, typename Policy::XRegs &xr, float *xs, float *wsum, PairX &px)
+{
+    P.x_stage(xr, xs, wsum);
+    const float4 *x4 = reinterpret_cast<const float4 *>(xs + XS_ROW * (threadIdx.x % Gm::TR));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float4 v = x4[i];
+        px.x[4 * i + 0] = v.x;
+        px.x[4 * i + 1] = v.y;
+        px.x[4 * i + 2] = v.z;
+        px.x[4 * i + 3] = v.w;
+    }
+    px.finish();
+    __syncthreads();
+}
+
 // The tile pipeline shared by every Q4_0 GEMV flavour.  Policy supplies:
 //   XRegs, x_issue(XRegs&)                 issue the activation loads into registers
 //   x_stage(XRegs&, float* xs, float* wsum) fill xs with the activations, element i at
@@ -180,6 +242,8 @@ __device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT
 //   slice(tile, part, &rows_valid)         base pointer of slice `part` of the tile
 //   epilogue(tile, const float* rowsum)    consume the R row sums (all threads call it)
 //   finish(float* lds_scratch)             after the last tile (all threads call it)
+// A workgroup walks tiles blockIdx.x, +gridDim.x, ... with the next tile's loads in flight
+// while it computes the current one.
 template <class Gm, class Policy>
 __device__ __forceinline__ void gemv_tiles(Policy &P)
 {
@@ -195,8 +259,6 @@ __device__ __forceinline__ void gemv_tiles(Policy &P)
     __shared__ float wsum[Gm::NT / 64];
 
     const int tid = threadIdx.x;
-    const int c = tid % Gm::TR;
-    const int g = tid / Gm::TR;
     const int ntiles = P.num_tiles();
     u32x4 pf[Gm::CPT];
 
@@ -214,23 +276,8 @@ __device__ __forceinline__ void gemv_tiles(Policy &P)
     }
     // keeps the compiler from sinking the weight loads below the prologue
     asm volatile("" ::: "memory");
-    // The workgroup stages the activation vector once in LDS (normalisation applied there);
-    // each thread then keeps the 64 values of its pair column in registers.
-    P.x_stage(xr, xs, wsum);
     PairX px;
-    {
-        const float4 *x4 = reinterpret_cast<const float4 *>(xs + XS_ROW * c);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float4 v = x4[i];
-            px.x[4 * i + 0] = v.x;
-            px.x[4 * i + 1] = v.y;
-            px.x[4 * i + 2] = v.z;
-            px.x[4 * i + 3] = v.w;
-        }
-    }
-    px.finish();
-    __syncthreads();   // xs is read by every thread before the first tile overwrites it
+    gemv_load_x<Gm>(P, xr, xs, wsum, px);
 
     for (; t < ntiles; t += gridDim.x) {
 #pragma unroll
@@ -241,33 +288,7 @@ __device__ __forceinline__ void gemv_tiles(Policy &P)
             gemv_fetch<Gm>(P, t + gridDim.x, pf);   // next tile's loads stay in flight during the compute
         }
         asm volatile("" ::: "memory");
-
-        const uint32_t *lds32 = reinterpret_cast<const uint32_t *>(tile);
-#pragma unroll
-        for (int j = 0; j < Gm::R / Gm::G; ++j) {
-            const int rr = g + j * Gm::G;
-            const uint32_t *p = lds32 + rr * (Gm::RB / 4) + 9 * c;
-            uint32_t D[9];
-#pragma unroll
-            for (int i = 0; i < 9; ++i)
-                D[i] = p[i];
-            red[rr * Gm::TR + c] = q4_pair_dot(D, px.x, px.n8a, px.n8b);
-        }
-        __syncthreads();
-        if (tid < Gm::R) {
-            const float4 *r4 = reinterpret_cast<const float4 *>(red + tid * Gm::TR);
-            float s = 0.0f;
-#pragma unroll 4
-            for (int i = 0; i < Gm::TR / 4; ++i) {
-                const float4 v = r4[i];
-                s += v.x;
-                s += v.y;
-                s += v.z;
-                s += v.w;
-            }
-            rowsum[tid] = s;
-        }
-        __syncthreads();
+        gemv_tile_rows<Gm>(tile, red, rowsum, px);
         P.epilogue(t, rowsum);
         if (t + (int)gridDim.x < ntiles)
             P.pre(t + gridDim.x);
