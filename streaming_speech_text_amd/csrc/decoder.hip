@@ -36,7 +36,21 @@ namespace vox {
 
 struct DecCtl {
     int64_t pos;                  // absolute position of the next token
+    float rope_cs[ATTN_HD];       // (cos, sin) of pos * theta^(-2i/128) for pair i, i < 64
 };
+
+// Rotation table of position p for the pair of thread i < 64: the angle is formed in fp64 in
+// units of pi (freq_pi[i] = theta^(-2i/128) / pi), so that its range reduction is exact.
+__device__ __forceinline__ void rope_fill(DecCtl *ctl, const double *freq_pi, int64_t p)
+{
+    const int i = threadIdx.x;
+    if (i < ATTN_HD / 2) {
+        double sn, cs;
+        sincospi((double)p * freq_pi[i], &sn, &cs);
+        ctl->rope_cs[2 * i] = (float)cs;
+        ctl->rope_cs[2 * i + 1] = (float)sn;
+    }
+}
 
 constexpr int MAX_HEAD_WGS = 4096;   // most LM-head workgroups (one argmax key each)
 
@@ -56,8 +70,7 @@ struct QkvArgs {
     const float *gain;
     float eps;
     float *q_out, *kc, *vc;      // q [qrows]; this layer's K, V rings [n_kv][n_slots][128]
-    const DecCtl *ctl;
-    const double *rope_freq;     // [64]: theta^(-2i/128) / pi
+    const DecCtl *ctl;           // position and its rotation table
     int n_slots;
 };
 
@@ -87,7 +100,7 @@ struct EmbedRmsNormX {
         for (int j = 0; j < GPER; ++j)
             gv[j] = g4[threadIdx.x + j * NT];
     }
-    __device__ __forceinline__ void stage(float *xs, float eps, float *wsum, float *h_out)
+    __device__ __forceinline__ float stage(float *xs, float eps, float *wsum, float *h_out)
     {
         float ss = 0.0f;
 #pragma unroll
@@ -117,6 +130,7 @@ struct EmbedRmsNormX {
             *p = *p * inv * gv[j];
         }
         __syncthreads();
+        return 1.0f;
     }
 };
 
@@ -124,7 +138,7 @@ template <class Gm, bool EMBED>
 struct QkvPolicy {
     QkvArgs a;
     int64_t pos;
-    double freq;   // RoPE frequency of this thread's row pair in the next tile
+    float rot_c, rot_s;   // cos and sin of this thread's row pair in the next tile
 
     __host__ __device__ static int tiles(const QkvArgs &a) { return (a.qrows + 2 * a.kvrows) / Gm::R; }
 
@@ -139,18 +153,19 @@ struct QkvPolicy {
             x.issue(a.h, a.gain);
         }
     }
-    __device__ void x_stage(XRegs &x, float *xs, float *wsum)
+    __device__ float x_stage(XRegs &x, float *xs, float *wsum)
     {
         if constexpr (EMBED)
-            x.stage(xs, a.eps, wsum, blockIdx.x == 0 ? a.h_out : nullptr);
+            return x.stage(xs, a.eps, wsum, blockIdx.x == 0 ? a.h_out : nullptr);
         else
-            x.stage(xs, a.eps, wsum);
+            return x.stage(xs, a.eps, wsum);
     }
     __device__ void pre(int t)
     {
         pos = a.ctl->pos;
         const int r0 = t * Gm::R + 2 * min((int)threadIdx.x, Gm::R / 2 - 1);
-        freq = a.rope_freq[(r0 % ATTN_HD) / 2];   // unconditional load (v rows ignore it)
+        rot_c = a.ctl->rope_cs[r0 % ATTN_HD];       // unconditional loads (v rows ignore them)
+        rot_s = a.ctl->rope_cs[r0 % ATTN_HD + 1];
     }
     __device__ int num_tiles() const { return tiles(a); }
     __device__ const uint8_t *slice(int t, int, int &rows_valid) const
@@ -174,14 +189,9 @@ struct QkvPolicy {
         float y0 = rs[2 * tid], y1 = rs[2 * tid + 1];
         const int region = r0 < a.qrows ? 0 : (r0 < a.qrows + a.kvrows ? 1 : 2);
         if (region < 2) {
-            // rotary position: pair i of the head turns by pos * theta^(-2i/128) radians; the
-            // angle is formed in fp64 in units of pi so that its reduction is exact
-            const double ang_pi = (double)pos * freq;
-            double sn, cs;
-            sincospi(ang_pi, &sn, &cs);
-            const float c = (float)cs, s = (float)sn;
-            const float u = y0 * c - y1 * s;
-            const float v = y0 * s + y1 * c;
+            // rotary position: pair i of the head turns by pos * theta^(-2i/128) radians
+            const float u = y0 * rot_c - y1 * rot_s;
+            const float v = y0 * rot_s + y1 * rot_c;
             y0 = u;
             y1 = v;
         }
@@ -216,7 +226,7 @@ struct ResidualPolicy {
     __host__ __device__ static int tiles(const ResidualArgs &a) { return a.n / Gm::R; }
     typedef PlainX<Gm::NT, Gm::K> XRegs;
     __device__ void x_issue(XRegs &r) { r.issue(a.x); }
-    __device__ void x_stage(XRegs &r, float *xs, float *) { r.stage(xs); }
+    __device__ float x_stage(XRegs &r, float *xs, float *) { return r.stage(xs); }
     __device__ void pre(int t)
     {
         hv = a.h[t * Gm::R + min((int)threadIdx.x, Gm::R - 1)];   // unconditional load
@@ -253,7 +263,7 @@ struct GateUpPolicy {
     __host__ __device__ static int tiles(const GateUpArgs &a) { return a.n / (Gm::R / 2); }
     typedef RmsNormX<Gm::NT, Gm::K> XRegs;
     __device__ void x_issue(XRegs &r) { r.issue(a.h, a.gain); }
-    __device__ void x_stage(XRegs &r, float *xs, float *wsum) { r.stage(xs, a.eps, wsum); }
+    __device__ float x_stage(XRegs &r, float *xs, float *wsum) { return r.stage(xs, a.eps, wsum); }
     __device__ void pre(int) {}
     __device__ int num_tiles() const { return tiles(a); }
     __device__ const uint8_t *slice(int t, int part, int &rows_valid) const
@@ -291,7 +301,7 @@ struct LmHeadPolicy {
         best = 0ull;
         r.issue(a.h, a.gain);
     }
-    __device__ void x_stage(XRegs &r, float *xs, float *wsum) { r.stage(xs, a.eps, wsum); }
+    __device__ float x_stage(XRegs &r, float *xs, float *wsum) { return r.stage(xs, a.eps, wsum); }
     __device__ void pre(int) {}
     __device__ int num_tiles() const { return tiles(a); }
     __device__ const uint8_t *slice(int t, int, int &rows_valid) const
@@ -331,9 +341,11 @@ struct LmHeadPolicy {
 // Greedy choice: the largest of the LM-head workgroups' keys (value first, then the lowest
 // index); writes the token and advances the position.  One workgroup of 256 threads.
 __global__ __launch_bounds__(256) void dec_finalize_kernel(DecCtl *ctl, const unsigned long long *keys, int nkeys,
-                                                           int32_t *tok_out)
+                                                           int32_t *tok_out, const double *freq_pi)
 {
     __shared__ unsigned long long part[256];
+    const int64_t next = ctl->pos + 1;
+    rope_fill(ctl, freq_pi, next);   // the next step's rotation table
     unsigned long long m = 0ull;
     for (int i = threadIdx.x; i < nkeys; i += 256)
         m = keys[i] > m ? keys[i] : m;
@@ -348,7 +360,7 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(DecCtl *ctl, const un
     }
     if (threadIdx.x == 0) {
         tok_out[0] = (int32_t)argmax_key_index(part[0]);
-        ctl->pos = ctl->pos + 1;
+        ctl->pos = next;
     }
 }
 
@@ -386,8 +398,9 @@ __global__ void dec_rope_table_kernel(double *freq, float theta)
         freq[i] = pow((double)theta, -2.0 * (double)i / (double)ATTN_HD) / 3.14159265358979323846;
 }
 
-__global__ void dec_reset_kernel(DecCtl *ctl)
+__global__ void dec_reset_kernel(DecCtl *ctl, const double *freq_pi)
 {
+    rope_fill(ctl, freq_pi, 0);
     if (threadIdx.x == 0)
         ctl->pos = 0;
 }
@@ -630,7 +643,6 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
         qa.kc = kc;
         qa.vc = vc;
         qa.ctl = d->ctl;
-        qa.rope_freq = d->rope;
         qa.n_slots = c.n_slots;
         if (c.dim == 3072)
             st = l == 0 ? run_qkv<3072, true>(qa, d->r_qkv, s) : run_qkv<3072, false>(qa, d->r_qkv, s);
@@ -681,7 +693,7 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
     if (st2)
         return st2;
     hipLaunchKernelGGL(dec_finalize_kernel, dim3(1), dim3(256), 0, s, d->ctl, (const unsigned long long *)d->keys, grid,
-                       tok_out);
+                       tok_out, (const double *)d->rope);
     return check_launch("decoder finalize");
 }
 
@@ -783,7 +795,7 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     st = check_hip(hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking), "vox_decoder_create: stream");
     if (!st) {
         hipLaunchKernelGGL(dec_rope_table_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->rope, c->rope_theta);
-        hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl);
+        hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl, (const double *)d->rope);
         st = check_launch("vox_decoder_create: init");
     }
     if (st) {
@@ -800,7 +812,7 @@ extern "C" int vox_decoder_reset(vox_decoder_t *d, void *stream)
 {
     if (!d)
         return fail(VOX_E_INVAL, "vox_decoder_reset: null handle");
-    hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl);
+    hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl, (const double *)d->rope);
     int st = check_launch("vox_decoder_reset");
     if (st)
         return st;

@@ -111,6 +111,7 @@ __device__ __forceinline__ float q4_pair_dot(const uint32_t (&D)[9], const float
 struct PairX {
     float x[64];
     float n8a, n8b;
+    float scale;   // applied to every row sum (1 unless the prologue normalises afterwards)
 
     __device__ __forceinline__ void finish()
     {
@@ -206,7 +207,7 @@ __device__ __forceinline__ void gemv_tile_rows(const u32x4 *tile, float *red, fl
                 s += red[row * Gm::TR + i * 16 + j];
             s = row16_sum(s);
             if (j == 0)
-                rowsum[row] = s;
+                rowsum[row] = s * px.scale;
         }
     }
     __syncthreads();
@@ -218,7 +219,7 @@ __device__ __forceinline__ void gemv_tile_rows(const u32x4 *tile, float *red, fl
 template <class Gm, class Policy>
 __device__ __forceinline__ void gemv_load_x(Policy &P, typename Policy::XRegs &xr, float *xs, float *wsum, PairX &px)
 {
-    P.x_stage(xr, xs, wsum);
+    px.scale = P.x_stage(xr, xs, wsum);
     const float4 *x4 = reinterpret_cast<const float4 *>(xs + XS_ROW * (threadIdx.x % Gm::TR));
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -236,7 +237,8 @@ __device__ __forceinline__ void gemv_load_x(Policy &P, typename Policy::XRegs &x
 //   XRegs, x_issue(XRegs&)                 issue the activation loads into registers
 //   x_stage(XRegs&, float* xs, float* wsum) fill xs with the activations, element i at
 //                                          xs[xs_index(i)] (all threads call it; it ends with a
-//                                          workgroup barrier)
+//                                          workgroup barrier); returns a factor applied to the
+//                                          row sums
 //   num_tiles()                            tiles of R rows
 //   pre(tile)                              early loads the epilogue of `tile` will need
 //   slice(tile, part, &rows_valid)         base pointer of slice `part` of the tile
@@ -319,12 +321,13 @@ struct PlainX {
         for (int j = 0; j < PER; ++j)
             v[j] = src[threadIdx.x + j * NT];
     }
-    __device__ __forceinline__ void stage(float *xs)
+    __device__ __forceinline__ float stage(float *xs)
     {
 #pragma unroll
         for (int j = 0; j < PER; ++j)
             *reinterpret_cast<f32x4 *>(xs + xs_index(4 * (threadIdx.x + j * NT))) = v[j];
         __syncthreads();
+        return 1.0f;
     }
 };
 
@@ -347,7 +350,9 @@ struct RmsNormX {
             gv[j] = g4[threadIdx.x + j * NT];
         }
     }
-    __device__ __forceinline__ void stage(float *xs, float eps, float *wsum)
+    // Stages h * gain; the normalisation 1/rms(h) is returned and applied to the row sums (the
+    // product is linear in x), so one barrier publishes both the vector and the wave sums.
+    __device__ __forceinline__ float stage(float *xs, float eps, float *wsum)
     {
         float ss = 0.0f;
 #pragma unroll
@@ -357,12 +362,18 @@ struct RmsNormX {
             ss = fmaf(hv[j].z, hv[j].z, ss);
             ss = fmaf(hv[j].w, hv[j].w, ss);
         }
-        const float tot = block_sum_fixed<NT>(ss, wsum);
-        const float inv = 1.0f / sqrtf(tot / (float)K + eps);
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            *reinterpret_cast<f32x4 *>(xs + xs_index(4 * (threadIdx.x + j * NT))) = hv[j] * inv * gv[j];
+            *reinterpret_cast<f32x4 *>(xs + xs_index(4 * (threadIdx.x + j * NT))) = hv[j] * gv[j];
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0)
+            wsum[threadIdx.x >> 6] = ss;
         __syncthreads();
+        float tot = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w)
+            tot += wsum[w];
+        return 1.0f / sqrtf(tot / (float)K + eps);
     }
 };
 

@@ -74,7 +74,7 @@ struct PlainGemvPolicy {
 
     typedef PlainX<Gm::NT, Gm::K> XRegs;
     __device__ void x_issue(XRegs &r) { r.issue(x); }
-    __device__ void x_stage(XRegs &r, float *xs, float *) { r.stage(xs); }
+    __device__ float x_stage(XRegs &r, float *xs, float *) { return r.stage(xs); }
     __device__ void pre(int) {}
     __device__ int num_tiles() const { return (int)((n + Gm::R - 1) / Gm::R); }
     __device__ const uint8_t *slice(int t, int, int &rows_valid) const
