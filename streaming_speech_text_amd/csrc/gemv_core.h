@@ -17,9 +17,9 @@
 //    of that column in registers for the whole kernel, reads its 9 dwords per row from LDS,
 //    unpacks the nibbles in registers and accumulates in fp32.
 //  * Per block: sum_j (code_j - 8) x_j = sum_j code_j x_j - 8 sum_j x_j; the second term is
-//    computed once per kernel.  High nibbles are masked in place (code*16) and the factor
-//    1/16 is folded into the block sum, so a nibble costs one mask share, one
-//    byte-to-float conversion and one FMA.
+//    computed once per kernel.  Nibbles masked in place inside 16-bit halves are exact fp16
+//    subnormals and feed mixed-precision FMAs directly, so a weight costs one FMA plus a
+//    share of the masks (no separate integer-to-float conversion).
 //  * The K/64 partial sums of a row are combined through LDS in a fixed order (the result is
 //    deterministic run to run).
 #pragma once
@@ -52,43 +52,52 @@ struct GemvGeom {
     static_assert(R % G == 0 && R % NPART == 0, "tile rows must split over the row groups");
 };
 
-// Byte j of v as a float: one v_cvt_f32_ubyte{j}.  Written as inline asm so that the
-// compiler cannot fold the nibble masks below into per-element bit-field extracts.
-__device__ __forceinline__ float ubyte_f(uint32_t v, int j)
-{
-    float r;
-    switch (j) {
-    case 0: asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v)); break;
-    case 1: asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v)); break;
-    case 2: asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v)); break;
-    default: asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v)); break;
-    }
-    return r;
-}
-
 // The activation vector is staged in LDS as rows of 64 floats (one block pair each) padded to
 // XS_ROW floats: thread c reads row c, and with a 256-byte row pitch every lane of a wave
 // would start on the same bank; the 16-byte pad spreads consecutive rows over the banks.
 constexpr int XS_ROW = 68;
 __device__ __forceinline__ int xs_index(int i) { return (i >> 6) * XS_ROW + (i & 63); }
 
+// acc + h * x with h the fp16 value in the low (HI = false) or high half of h2, x and acc fp32
+// (one v_fma_mix_f32: the fp16 operand is widened exactly and the FMA rounds once, in fp32).
+template <bool HI>
+__device__ __forceinline__ float fma_f16h(uint32_t h2, float x, float acc)
+{
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(h2), "v"(x));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(h2), "v"(x));
+    return acc;
+}
+
 // Sum over one block of (code - 8) * x, without the scale.  qs: the 16 code bytes;
 // x: the block's 32 activations; neg8sum = -8 * sum(x).
+// A nibble masked in place inside a 16-bit half is an fp16 subnormal: bits 0-3 read as
+// code * 2^-24, bits 4-7 as code * 2^-20, both exact.  So each weight costs one v_fma_mix_f32
+// plus a share of five masks per four code bytes, and every product carries the factor 2^-24
+// (the high nibbles 16 * 2^-24, removed with the 1/16 below), undone exactly at the end.
 __device__ __forceinline__ float q4_block_dot(const uint32_t (&qs)[4], const float *x, float neg8sum)
 {
-    float lo_acc = neg8sum;
+    float lo_acc = neg8sum * 0x1p-24f;
     float hi_acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = qs[i] & 0x0F0F0F0Fu;   // codes of weights 4i .. 4i+3
-        const uint32_t hi = qs[i] & 0xF0F0F0F0u;   // 16 * codes of weights 16+4i .. 16+4i+3
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            lo_acc = fmaf(ubyte_f(lo, j), x[4 * i + j], lo_acc);
-            hi_acc = fmaf(ubyte_f(hi, j), x[16 + 4 * i + j], hi_acc);
-        }
+        // code bytes 4i .. 4i+3: bytes 0 and 2 sit at the bottom of the two halves of q,
+        // bytes 1 and 3 at the bottom of the halves of q >> 8
+        const uint32_t q = qs[i], t = q >> 8;
+        const uint32_t lo02 = q & 0x000F000Fu, hi02 = q & 0x00F000F0u;
+        const uint32_t lo13 = t & 0x000F000Fu, hi13 = t & 0x00F000F0u;
+        const float *xl = x + 4 * i, *xh = x + 16 + 4 * i;
+        lo_acc = fma_f16h<false>(lo02, xl[0], lo_acc);
+        hi_acc = fma_f16h<false>(hi02, xh[0], hi_acc);
+        lo_acc = fma_f16h<false>(lo13, xl[1], lo_acc);
+        hi_acc = fma_f16h<false>(hi13, xh[1], hi_acc);
+        lo_acc = fma_f16h<true>(lo02, xl[2], lo_acc);
+        hi_acc = fma_f16h<true>(hi02, xh[2], hi_acc);
+        lo_acc = fma_f16h<true>(lo13, xl[3], lo_acc);
+        hi_acc = fma_f16h<true>(hi13, xh[3], hi_acc);
     }
-    return fmaf(hi_acc, 0.0625f, lo_acc);
+    return fmaf(hi_acc, 0.0625f, lo_acc) * 0x1p24f;
 }
 
 // Dot product of one block pair (9 dwords as stored) with its 64 activations.
