@@ -94,9 +94,11 @@ struct PlainGemvPolicy {
     __device__ void finish(float *) {}
 };
 
-// Three waves per SIMD: with 3-wave workgroups that is four resident workgroups per compute unit.
+// Four waves per SIMD (at most 128 VGPRs): with 3-wave workgroups, five resident workgroups per
+// compute unit.  Measured at the LM-head shape: 8-row tiles with four waves per SIMD beat
+// 16-row tiles with three (16-row tiles do not fit 128 VGPRs).
 template <class Gm>
-__global__ __launch_bounds__(Gm::NT) __attribute__((amdgpu_waves_per_eu(3))) void q4_gemv_tiled_kernel(PlainGemvPolicy<Gm> P)
+__global__ __launch_bounds__(Gm::NT) __attribute__((amdgpu_waves_per_eu(4))) void q4_gemv_tiled_kernel(PlainGemvPolicy<Gm> P)
 {
     gemv_tiles<Gm>(P);
 }
@@ -119,41 +121,26 @@ static int launch_tiled(const void *w, const float *x, float *y, int64_t n, hipS
     return check_launch("q4_gemv tiled launch");
 }
 
-// Picks the tile height: tall tiles for long matrices, short ones so that a few thousand
-// rows still spread over every compute unit.
-static int pick_rows(int64_t n, int max_r)
+// Picks the tile height: 8-row tiles for long matrices, 4-row ones so that a few thousand rows
+// still spread over every compute unit.
+static int pick_rows(int64_t n)
 {
-    const int64_t cu = cu_count();
-    if (max_r >= 16 && n >= 16 * 4 * cu)
-        return 16;
-    if (max_r >= 8 && n >= 8 * 2 * cu)
-        return 8;
-    return 4;
+    return n >= 8 * 2 * (int64_t)cu_count() ? 8 : 4;
 }
 
 int q4_gemv_launch(const void *w, const float *x, float *y, int64_t n, int64_t k, hipStream_t s)
 {
     const bool fast_layout = aligned(w, 16) && aligned(x, 16);
-    if (fast_layout && k == 3072) {
-        switch (pick_rows(n, 16)) {
-        case 16: return launch_tiled<GemvGeom<3072, 192, 16>>(w, x, y, n, s);
-        case 8: return launch_tiled<GemvGeom<3072, 192, 8>>(w, x, y, n, s);
-        default: return launch_tiled<GemvGeom<3072, 192, 4>>(w, x, y, n, s);
-        }
-    }
-    if (fast_layout && k == 4096) {
-        switch (pick_rows(n, 16)) {
-        case 16: return launch_tiled<GemvGeom<4096, 256, 16>>(w, x, y, n, s);
-        case 8: return launch_tiled<GemvGeom<4096, 256, 8>>(w, x, y, n, s);
-        default: return launch_tiled<GemvGeom<4096, 256, 4>>(w, x, y, n, s);
-        }
-    }
-    if (fast_layout && k == 9216) {
-        switch (pick_rows(n, 8)) {
-        case 8: return launch_tiled<GemvGeom<9216, 576, 8>>(w, x, y, n, s);
-        default: return launch_tiled<GemvGeom<9216, 576, 4>>(w, x, y, n, s);
-        }
-    }
+    const bool tall = pick_rows(n) == 8;
+    if (fast_layout && k == 3072)
+        return tall ? launch_tiled<GemvGeom<3072, 192, 8>>(w, x, y, n, s)
+                    : launch_tiled<GemvGeom<3072, 192, 4>>(w, x, y, n, s);
+    if (fast_layout && k == 4096)
+        return tall ? launch_tiled<GemvGeom<4096, 256, 8>>(w, x, y, n, s)
+                    : launch_tiled<GemvGeom<4096, 256, 4>>(w, x, y, n, s);
+    if (fast_layout && k == 9216)
+        return tall ? launch_tiled<GemvGeom<9216, 576, 8>>(w, x, y, n, s)
+                    : launch_tiled<GemvGeom<9216, 576, 4>>(w, x, y, n, s);
     const int64_t grid = (n + 3) / 4;
     hipLaunchKernelGGL(q4_gemv_generic_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)w, x, y, n,
                        k);
