@@ -66,8 +66,9 @@ def measured_traffic(digest: str, launch_bytes: int):
 def gemv_leg(args, torch, synth, vox, dev, stream):
     """The Q4_0 GEMV at the LM-head shape (131072 x 3072), rotating over weight copies (more
     than 1 GiB in total, so no launch is served from the 256 MB Infinity Cache).  The launches
-    are captured in a HIP graph and its replay is timed with HIP events on the stream it runs
-    on, so the per-launch time is the kernel's own duration plus the graph's launch gap."""
+    are captured in a HIP graph whose replays are timed with HIP events on the stream it runs on
+    (median of five), so the per-launch time is the kernel's own duration plus the graph's launch
+    gap."""
     n, k = synth.VOXTRAL_DECODER.vocab, synth.VOXTRAL_DECODER.dim
     gw, gx = synth.gemv_inputs(synth.SEED_GEMV, n, k)
     copies = max(1, int(np.ceil(1.1 * 2 ** 30 / gw.nbytes)))
@@ -93,10 +94,11 @@ def copy_calibration(torch, dev):
     torch.cuda.synchronize()
 
 
-def timed(torch, stream, launch, copies, reps):
-    """Average device time (us) of `launch(i)` (which enqueues on the current stream) over `reps`
-    launches rotating over `copies`, captured once in a HIP graph and replayed, so host launch
-    cost is not measured."""
+def timed(torch, stream, launch, copies, reps, replays=5):
+    """Device time (us) of `launch(i)` (which enqueues on the current stream), averaged over `reps`
+    launches rotating over `copies`.  The launches are captured once in a HIP graph, so host
+    launch cost is not measured; after two warm replays, `replays` replays are timed one by one
+    with HIP events on the stream the graph runs on, and the median is returned."""
     for i in range(min(copies, 4)):
         launch(i % copies)
     torch.cuda.synchronize()
@@ -107,15 +109,19 @@ def timed(torch, stream, launch, copies, reps):
             for i in range(reps):
                 launch(i % copies)
     torch.cuda.synchronize()
-    g.replay()
+    for _ in range(2):
+        g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+    per = []
+    for _ in range(replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return float(np.median(per))
 
 
 def kernels_leg(torch, synth, vox, dev, stream):
