@@ -181,11 +181,14 @@ def kernels_leg(torch, synth, vox, dev, stream):
         copies = max(2, int(np.ceil(1.1 * GiB / wbytes)))
         wdev = [[torch.from_numpy(s_[3]).to(dev) for s_ in sets] for _ in range(copies)]
         ys = [torch.empty(m, s_[1], dtype=torch.float32, device=dev) for s_ in sets]
+        # one workspace serves the set (the launches run one after another on the stream)
+        wsb = max(vox.q4_gemm_workspace(m, n, k) for _, n, k in synth.ENCODER_LINEARS)
+        gws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
         def launch(i):
             for j, (name, n, k, _, xd) in enumerate(sets):
-                vox.lib().vox_q4_gemm(vox._ptr(wdev[i][j]), vox._ptr(xd), vox._ptr(ys[j]), m, n, k,
-                                      vox._stream(None))
+                vox._check(vox.lib().vox_q4_gemm(vox._ptr(wdev[i][j]), vox._ptr(xd), vox._ptr(ys[j]), m, n, k,
+                                                 vox._ptr(gws) if wsb else None, wsb, vox._stream(None)))
         us = timed(torch, stream, launch, copies, 50)
         flops = 2 * m * sum(n * k for _, n, k in synth.ENCODER_LINEARS)
         b = wbytes + sum(m * k * 2 + m * n * 4 for _, n, k in synth.ENCODER_LINEARS)

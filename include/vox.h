@@ -65,10 +65,16 @@ int vox_q4_gemv(const void *w_q4, const float *x, float *y, int64_t n, int64_t k
  * [RS] 아키텍처: Q4_0 linears), on the matrix cores.  x_bf16: m rows by k, bf16 bit patterns,
  * row major; w_q4: n rows by k; y: m by n fp32, row major, must not overlap the inputs.
  * Products of the exact Q4 codes with bf16 activations, fp32 accumulation.
+ * workspace: NULL with workspace_bytes 0, or device memory of at least
+ * vox_q4_gemm_workspace(m, n, k) bytes, 16-byte aligned, apart from x, y and w, contents
+ * irrelevant (the call may then split K over more workgroups and add the slices' partial
+ * results in a fixed order; results do not depend on the split beyond fp32 rounding order, and
+ * exact sums stay exact).  A non-null workspace below the size -> VOX_E_WORKSPACE.
  * m == 0 or n == 0 is a no-op.  k % 32 != 0 -> VOX_E_INVAL; m > 1048560 or n, k > 2^24 ->
  * VOX_E_UNSUPPORTED.  x_bf16 must be 8-byte and w_q4 2-byte aligned (VOX_E_UNSUPPORTED). */
+size_t vox_q4_gemm_workspace(int64_t m, int64_t n, int64_t k);
 int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, int64_t m, int64_t n, int64_t k,
-                void *stream);
+                void *workspace, size_t workspace_bytes, void *stream);
 
 /* Grouped-query decode attention of one token over a KV ring ([RS] 아키텍처 and [VC] 모델
  * 아키텍처: query head h reads KV head h / (n_q_heads / n_kv_heads); [VC] 주요 기능: rolling

@@ -269,11 +269,14 @@ __device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, 
     }
 }
 
-// NST: stages (K / 256), fixed at compile time.
-template <int NST>
+// NS: stages (of 256 inputs) per workgroup, fixed at compile time.  Workgroup z of the grid's
+// third dimension takes stages z*NS .. z*NS+NS-1; with one slice it writes y, otherwise its fp32
+// partial tile goes to part[z][m][n] and q4_gemm_reduce_kernel adds the slices.
+template <int NS>
 __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t *__restrict__ w,
                                                                    const uint16_t *__restrict__ x,
-                                                                   float *__restrict__ y, int m, int n, int k)
+                                                                   float *__restrict__ y, float *__restrict__ part,
+                                                                   int m, int n, int k)
 {
     __shared__ __attribute__((aligned(16))) uint32_t braw[2][GT_BN * GT_RAW / 4];
     __shared__ f32x4v red[4][16][64];   // tree reduction of the waves' tiles
@@ -284,6 +287,7 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
     const int l16 = lane & 15, grp = lane >> 4;
     const int m0 = blockIdx.y * GT_BM;
     const int n0 = blockIdx.x * GT_BN;
+    const int st0 = blockIdx.z * NS, st_end = st0 + NS;
     const uint32_t row_bytes = (uint32_t)(k / 32) * 18;
 
     // A operands of this lane: rows m0 + 16i + l16 (clamped), inputs 8*grp .. of block `wave`
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
     u32x4v ar[2][4], wr[2][2];
     auto load_stage = [&](int st, auto slot) {
         constexpr int S = decltype(slot)::value;
-        st = min(st, NST - 1);   // past the end: a harmless reload of the last stage
+        st = min(st, st_end - 1);   // past the slice: a harmless reload of its last stage
         const uint16_t *xs = x + (size_t)st * (GT_KC * 32);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -369,15 +373,14 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
     };
     typedef std::integral_constant<int, 0> S0;
     typedef std::integral_constant<int, 1> S1;
-    load_stage(0, S0());
-    load_stage(1, S1());
-    int st = 0;
-    for (; st + 1 < NST; st += 2) {
-        stage(st, S0());
-        stage(st + 1, S1());
+    load_stage(st0, S0());
+    load_stage(st0 + 1, S1());
+    for (int r = 0; r + 1 < NS; r += 2) {
+        stage(st0 + r, S0());
+        stage(st0 + r + 1, S1());
     }
-    if constexpr (NST % 2)
-        stage(NST - 1, S0());
+    if constexpr (NS % 2)
+        stage(st_end - 1, S0());
 
     // tree: (w + 4) -> w, then (w + 2) -> w, then 1 -> 0; fixed order
 #pragma unroll
@@ -400,6 +403,7 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
         __syncthreads();
     }
     if (wave == 0) {
+        float *const dst = part ? part + (size_t)blockIdx.z * m * n : y;
         // D layout of a 16x16 block: lane holds rows 4*(lane/16) .. +3 of column lane%16
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -410,23 +414,105 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
                 for (int r = 0; r < 4; ++r) {
                     const int row = m0 + 16 * i + 4 * grp + r;
                     if (row < m && col < n)
-                        y[(size_t)row * n + col] = acc[i][j][r];
+                        dst[(size_t)row * n + col] = acc[i][j][r];
                 }
             }
+    }
+}
+
+// y = sum over z of part[z] (count values per slice), slices added in order z = 0, 1, ...
+__global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__restrict__ part, float *__restrict__ y,
+                                                             int64_t count, int slices, bool vec4)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (vec4) {
+        const int64_t i = 4 * t;
+        if (i >= count)
+            return;
+        f32x4v a = *reinterpret_cast<const f32x4v *>(part + i);
+        for (int z = 1; z < slices; ++z)
+            a += *reinterpret_cast<const f32x4v *>(part + (size_t)z * count + i);
+        *reinterpret_cast<f32x4v *>(y + i) = a;
+    } else {
+        if (t >= count)
+            return;
+        float a = part[t];
+        for (int z = 1; z < slices; ++z)
+            a += part[(size_t)z * count + t];
+        y[t] = a;
     }
 }
 
 // K values with a compiled stage sequence (the encoder's widths)
 static bool tiled_k(int64_t k) { return k == 1280 || k == 5120; }
 
-static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
+// Whether the tiled kernel runs (given 16-byte aligned operands): a compiled K, offsets that fit
+// 32 bits, and either a long K or an output past about 48 x 1280 values - measured on MI355X at
+// the encoder's shapes, the split-K-over-waves kernel is the faster one below that for K = 1280.
+static bool tiled_shape(int64_t m, int64_t n, int64_t k)
 {
-    const dim3 grid((unsigned)((n + GT_BN - 1) / GT_BN), (unsigned)((m + GT_BM - 1) / GT_BM));
-    if (k == 1280)
-        hipLaunchKernelGGL(q4_gemm_tiled_kernel<5>, grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y, m, n, k);
-    else
-        hipLaunchKernelGGL(q4_gemm_tiled_kernel<20>, grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y, m, n, k);
-    return check_launch("vox_q4_gemm tiled");
+    const size_t wbytes = (size_t)n * (size_t)(k / 32) * 18;
+    return tiled_k(k) && (uint64_t)m * (uint64_t)k < (1ull << 31) && wbytes < (1ull << 31) &&
+           (k >= 5120 || m * n > 48 * 1280);
+}
+
+// K slices for the tiled kernel (measured on MI355X at the encoder's shapes): none once the
+// output tiles alone give 160 workgroups; for 20 stages, the fewest slices that reach 160
+// workgroups (at least two stages each); for 5 stages, one stage per workgroup when there are at
+// most 40 tiles, else none.  The slices' partial tiles are added by q4_gemm_reduce_kernel.
+static int tiled_slices(int64_t m, int64_t n, int64_t k)
+{
+    const int64_t tiles = ((n + GT_BN - 1) / GT_BN) * ((m + GT_BM - 1) / GT_BM);
+    const int nst = (int)(k / 256);
+    if (tiles >= 160)
+        return 1;
+    if (nst >= 20) {
+        for (int ks : {2, 4, 5, 10})
+            if (nst % ks == 0 && tiles * ks >= 160)
+                return ks;
+        return 10;
+    }
+    return tiles <= 40 ? nst : 1;
+}
+
+static size_t tiled_workspace(int64_t m, int64_t n, int slices)
+{
+    return slices > 1 ? (size_t)slices * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
+template <int S>
+static void launch_tiled_slices(const void *w, const uint16_t *x, float *y, float *part, int m, int n, int k,
+                                int slices, hipStream_t s)
+{
+    const dim3 grid((unsigned)((n + GT_BN - 1) / GT_BN), (unsigned)((m + GT_BM - 1) / GT_BM), (unsigned)slices);
+    hipLaunchKernelGGL(q4_gemm_tiled_kernel<S>, grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y, part, m, n,
+                       k);
+}
+
+// part: slices x m x n floats when slices > 1, else null (the kernel then writes y)
+static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, float *part, int m, int n, int k,
+                             int slices, hipStream_t s)
+{
+    if ((slices > 1) != (part != nullptr))
+        return fail(VOX_E_INVAL, "vox_q4_gemm: partial-tile buffer must be set exactly when K is split");
+    switch ((k / 256) / slices) {   // stages per workgroup
+    case 20: launch_tiled_slices<20>(w, x, y, part, m, n, k, slices, s); break;
+    case 10: launch_tiled_slices<10>(w, x, y, part, m, n, k, slices, s); break;
+    case 5: launch_tiled_slices<5>(w, x, y, part, m, n, k, slices, s); break;
+    case 4: launch_tiled_slices<4>(w, x, y, part, m, n, k, slices, s); break;
+    case 2: launch_tiled_slices<2>(w, x, y, part, m, n, k, slices, s); break;
+    case 1: launch_tiled_slices<1>(w, x, y, part, m, n, k, slices, s); break;
+    default: return fail(VOX_E_UNSUPPORTED, "vox_q4_gemm: no compiled stage count for k=%d in %d slices", k, slices);
+    }
+    int st = check_launch("vox_q4_gemm tiled");
+    if (st || slices == 1)
+        return st;
+    const int64_t count = (int64_t)m * n;
+    const bool vec4 = count % 4 == 0 && aligned(y, 16);
+    const int64_t threads = vec4 ? count / 4 : count;
+    hipLaunchKernelGGL(q4_gemm_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, y,
+                       count, slices, vec4);
+    return check_launch("vox_q4_gemm reduce");
 }
 
 template <int MI, int NJ>
@@ -441,8 +527,16 @@ static int launch_gemm(const void *w, const uint16_t *x, float *y, int m, int n,
 
 using namespace vox;
 
+extern "C" size_t vox_q4_gemm_workspace(int64_t m, int64_t n, int64_t k)
+{
+    if (m <= 0 || n <= 0 || k <= 0 || k % 32 || m > 65535 * 16 || n > (1 << 24) || k > (1 << 24) ||
+        !tiled_shape(m, n, k))
+        return 0;
+    return tiled_workspace(m, n, tiled_slices(m, n, k));
+}
+
 extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, int64_t m, int64_t n, int64_t k,
-                           void *stream)
+                           void *workspace, size_t workspace_bytes, void *stream)
 {
     if (m < 0 || n < 0 || k <= 0 || k % 32)
         return fail(VOX_E_INVAL, "vox_q4_gemm: need m, n >= 0 and k a positive multiple of 32 (m=%lld n=%lld k=%lld)",
@@ -458,16 +552,23 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
     const size_t wbytes = (size_t)n * (size_t)(k / 32) * 18, xbytes = (size_t)m * k * 2, ybytes = (size_t)m * n * 4;
     if (overlaps(y, ybytes, x_bf16, xbytes) || overlaps(y, ybytes, w_q4, wbytes))
         return fail(VOX_E_INVAL, "vox_q4_gemm: y overlaps an input");
+    if (!workspace != !workspace_bytes)
+        return fail(VOX_E_INVAL, "vox_q4_gemm: workspace and workspace_bytes must be both set or both zero");
     hipStream_t s = (hipStream_t)stream;
     int st;
-    // the tiled kernel: 16-byte aligned operands, a compiled K, and offsets that fit 32 bits
-    const bool tiled_ok = aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_k(k) &&
-                          (uint64_t)m * (uint64_t)k < (1ull << 31) && wbytes < (1ull << 31);
-    // measured on MI355X at the encoder's shapes: the split-K kernel is the faster one while the
-    // output is small (up to about 48 x 1280 values), the tiled kernel beyond that
-    if (tiled_ok && m * n > 48 * 1280)
-        st = launch_gemm_tiled(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
-    else
+    if (aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_shape(m, n, k)) {
+        int slices = workspace ? tiled_slices(m, n, k) : 1;
+        const size_t need = tiled_workspace(m, n, slices);
+        if (need > workspace_bytes)
+            return fail(VOX_E_WORKSPACE, "vox_q4_gemm: workspace of %zu bytes, need %zu", workspace_bytes, need);
+        if (need && (!aligned(workspace, 16) || overlaps(workspace, need, y, ybytes) ||
+                     overlaps(workspace, need, x_bf16, xbytes) || overlaps(workspace, need, w_q4, wbytes)))
+            return fail(VOX_E_INVAL, "vox_q4_gemm: workspace must be 16-byte aligned and apart from x, y and w");
+        // the partial tiles go to the workspace only when K is split; one slice writes y
+        st = launch_gemm_tiled(w_q4, x_bf16, y, slices > 1 ? (float *)workspace : nullptr, (int)m, (int)n, (int)k,
+                               slices, s);
+    } else {
         st = launch_gemm<1, 1>(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
+    }
     return st ? st : ok();
 }

@@ -51,7 +51,8 @@ _SIGS = {
     "vox_last_error": (C.c_char_p, []),
     "vox_q4_dequant": (_int, [_vp, _i64, _vp, _vp]),
     "vox_q4_gemv": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
-    "vox_q4_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "vox_q4_gemm_workspace": (_sz, [_i64, _i64, _i64]),
+    "vox_q4_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "vox_gqa_decode_attn_workspace": (_sz, [_int, _int, _int, _int]),
     "vox_gqa_decode_attn": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _f32, _vp, _sz, _vp]),
     "vox_decoder_workspace": (_int, [C.POINTER(DecoderConfig), C.POINTER(_sz), C.POINTER(_sz)]),
@@ -131,13 +132,21 @@ def q4_gemv(w_q4, x, y, n=None, k=None, stream=None):
                              _ptr(y, torch.float32, "y"), n, k, _stream(stream)))
 
 
-def q4_gemm(w_q4, x_bf16, y, m=None, n=None, k=None, stream=None):
+def q4_gemm_workspace(m, n, k) -> int:
+    return int(lib().vox_q4_gemm_workspace(m, n, k))
+
+
+def q4_gemm(w_q4, x_bf16, y, m=None, n=None, k=None, workspace=None, stream=None):
+    """workspace: None (K is never split) or a device buffer of at least q4_gemm_workspace(m, n, k)
+    bytes (a zero-size request needs none)."""
     if m is None or k is None:
         m, k = x_bf16.shape
     n = y.shape[-1] if n is None else n
     xdt = torch.uint16 if x_bf16.dtype == torch.uint16 else torch.bfloat16
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().vox_q4_gemm(_ptr(w_q4, torch.uint8, "w_q4"), _ptr(x_bf16, xdt, "x_bf16"),
-                             _ptr(y, torch.float32, "y"), m, n, k, _stream(stream)))
+                             _ptr(y, torch.float32, "y"), m, n, k,
+                             _ptr(workspace, None, "workspace") if wsb else None, wsb, _stream(stream)))
 
 
 def gqa_decode_attn_workspace(n_q_heads, n_kv_heads, head_dim, n_slots) -> int:

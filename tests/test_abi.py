@@ -24,7 +24,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     fns = header_functions()
-    for name in ("vox_q4_dequant", "vox_q4_gemv", "vox_q4_gemm", "vox_gqa_decode_attn", "vox_gqa_decode_attn_workspace",
+    for name in ("vox_q4_dequant", "vox_q4_gemv", "vox_q4_gemm", "vox_q4_gemm_workspace", "vox_gqa_decode_attn", "vox_gqa_decode_attn_workspace",
                  "vox_decoder_step", "vox_decoder_create", "vox_decoder_workspace", "vox_strerror", "vox_last_error"):
         assert name in fns
 
@@ -61,8 +61,13 @@ def test_validation_before_device_work(lib):
     assert "multiple of 32" in vox.last_error() or vox.last_error() == ""
     assert lib.vox_q4_dequant(p, -1, p, None) == vox.VOX_E_INVAL
     assert lib.vox_q4_dequant(p, 0, p, None) == vox.VOX_OK
-    assert lib.vox_q4_gemm(p, p, p, 4, 4, 48, None) == vox.VOX_E_INVAL
-    assert lib.vox_q4_gemm(p, p, p, 0, 4, 64, None) == vox.VOX_OK
+    assert lib.vox_q4_gemm(p, p, p, 4, 4, 48, None, 0, None) == vox.VOX_E_INVAL
+    assert lib.vox_q4_gemm(p, p, p, 0, 4, 64, None, 0, None) == vox.VOX_OK
+    assert lib.vox_q4_gemm(p, p, C.c_void_p(0x800000), 4, 4, 64, p, 0, None) == vox.VOX_E_INVAL   # ws without size
+    # the workspace is sized only where K is split: long K on few output tiles
+    assert lib.vox_q4_gemm_workspace(64, 1280, 5120) > 0
+    assert lib.vox_q4_gemm_workspace(750, 5120, 1280) == 0
+    assert lib.vox_q4_gemm_workspace(4, 4, 48) == 0
     ws = lib.vox_gqa_decode_attn_workspace(32, 8, 128, 8192)
     assert ws > 0 and lib.vox_gqa_decode_attn_workspace(32, 8, 64, 8192) == 0
     args = (p, C.c_void_p(0x200000), C.c_void_p(0x400000), C.c_void_p(0x800000))

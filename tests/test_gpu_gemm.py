@@ -16,9 +16,12 @@ def vx():
     return vox
 
 
-def _gemm(vx, w, xb, m, n, k):
+def _gemm(vx, w, xb, m, n, k, split=True):
+    """split: pass the workspace the call asks for (K may be split over workgroups)."""
     y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
-    vx.q4_gemm(dev(w), dev(xb), y, m=m, n=n, k=k)
+    need = vx.q4_gemm_workspace(m, n, k) if split else 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda") if need else None
+    vx.q4_gemm(dev(w), dev(xb), y, m=m, n=n, k=k, workspace=ws)
     return host(y)
 
 
@@ -27,21 +30,63 @@ def test_gemm_encoder_chunk(vx, orc, m):
     for name, n, k in synth.ENCODER_LINEARS:
         say(f"gemm {name}: m={m} n={n} k={k}")
         w, xb = synth.gemm_inputs(synth.SEED_GEMM, m, n, k)
-        assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm {name} m={m}")
+        ref = orc.q4_gemm(w, xb)
+        assert_close(_gemm(vx, w, xb, m, n, k), ref, f"gemm {name} m={m}")
+        if vx.q4_gemm_workspace(m, n, k):
+            assert_close(_gemm(vx, w, xb, m, n, k, split=False), ref, f"gemm {name} m={m} unsplit")
+
+
+def test_gemm_split_repeatable(vx):
+    # the sliced path adds the partial tiles in a fixed order: two calls agree bit for bit, and a
+    # call with a dirty, larger workspace agrees too
+    m, n, k = 64, 1280, 5120
+    assert vx.q4_gemm_workspace(m, n, k) > 0
+    w, xb = synth.gemm_inputs(612, m, n, k)
+    a = _gemm(vx, w, xb, m, n, k)
+    b = _gemm(vx, w, xb, m, n, k)
+    assert np.array_equal(a, b)
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    big = torch.full((vx.q4_gemm_workspace(m, n, k) + 4096,), 0x7F, dtype=torch.uint8, device="cuda")
+    vx.q4_gemm(dev(w), dev(xb), y, m=m, n=n, k=k, workspace=big)
+    assert np.array_equal(host(y), a)
+
+
+@pytest.mark.parametrize("m,n,k", [(200, 5120, 1280), (750, 1280, 5120), (16, 1280, 1280)])
+def test_gemm_workspace_on_unsplit_shape(vx, orc, m, n, k):
+    # a workspace handed to a call that does not split K must leave y as the result (regression:
+    # the single-slice tiled launch once wrote its tile into the workspace)
+    assert vx.q4_gemm_workspace(m, n, k) == 0
+    w, xb = synth.gemm_inputs(614, m, n, k)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.zeros((4 * m * n + 4096,), dtype=torch.uint8, device="cuda")
+    vx.q4_gemm(dev(w), dev(xb), y, m=m, n=n, k=k, workspace=ws)
+    assert_close(host(y), orc.q4_gemm(w, xb), f"gemm {m}x{n}x{k} with an unused workspace")
+
+
+def test_gemm_small_workspace(vx):
+    m, n, k = 64, 1280, 5120
+    need = vx.q4_gemm_workspace(m, n, k)
+    w, xb = synth.gemm_inputs(613, m, n, k)
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty((need - 16,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(vx.VoxError) as e:
+        vx.q4_gemm(dev(w), dev(xb), y, m=m, n=n, k=k, workspace=ws)
+    assert e.value.status == vx.VOX_E_WORKSPACE
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1280, 1280), (17, 100, 96), (63, 65, 32), (65, 1000, 5120), (130, 64, 2080),
-                                   (3, 5, 64), (97, 77, 1280), (751, 130, 5120), (40, 1280, 5120)])
+                                   (3, 5, 64), (97, 77, 1280), (751, 130, 5120), (40, 1280, 5120), (49, 1283, 5120),
+                                   (129, 1283, 1280)])
 def test_gemm_ragged(vx, orc, m, n, k):
     w, xb = synth.gemm_inputs(600 + m, m, n, k)
     say(f"gemm ragged m={m} n={n} k={k}")
     assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm ragged {m}x{n}x{k}")
 
 
-def test_gemm_exact_dyadic(vx, orc):
+@pytest.mark.parametrize("m,n,k", [(70, 96, 1280), (64, 1280, 5120)])
+def test_gemm_exact_dyadic(vx, orc, m, n, k):
     # small-integer activations and power-of-two scales: every product and partial sum is exact,
-    # so the matrix-core result must equal the oracle bit for bit
-    m, n, k = 70, 96, 1280
+    # so the matrix-core result must equal the oracle bit for bit (also when K is split)
     g = synth.generator(610)
     w = synth.q4_matrix(g, n, k).reshape(n, k // 32, 18)
     e = g.integers(-3, 1, size=(n, k // 32)).astype(np.float64)
