@@ -19,7 +19,9 @@
 //    B holds (code - 8).  Lane group g (= lane / 16) takes code bytes 4g..4g+3, i.e. inputs
 //    {4g..4g+3} (low nibbles) then {16+4g..16+4g+3} (high nibbles), and the activations of
 //    the same inputs (the MFMA's k slots may hold the inputs in any order A and B agree on).
-//  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS).
+//  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS),
+//    optionally with K split over workgroups (partial tiles in the caller's workspace, added in
+//    a fixed order by a second kernel).
 #include <type_traits>
 
 #include "vox_common.h"
