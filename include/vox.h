@@ -130,14 +130,15 @@ int vox_decoder_workspace(const vox_decoder_config *c, size_t *kv_bytes, size_t 
  * {1,2,4,8}, n_kv_heads <= 64, and the width triple (dim, n_heads*head_dim, hidden) drawn from
  * dim in {3072, 1024}, n_heads*head_dim in {4096, 1024}, hidden in {9216, 2048} (the Voxtral
  * decoder and a small test shape); anything else returns VOX_E_UNSUPPORTED.
- * Enqueues the clearing of the scratch counters on `stream`. */
+ * Enqueues the initialisation of the scratch (position 0, RoPE tables) on `stream`. */
 int vox_decoder_create(const vox_decoder_config *c, const vox_decoder_weights *w, void *kv,
                        size_t kv_bytes, void *scratch, size_t scratch_bytes, void *stream,
                        vox_decoder_t **out);
-/* Position back to 0 (the KV window is logically emptied). */
+/* Position back to 0 (the KV window is logically emptied); enqueued on `stream`. */
 int vox_decoder_reset(vox_decoder_t *d, void *stream);
-/* One token: reads token_in[0] (device int32 in [0, vocab)), writes token_out[0] (device
- * int32) and, when logits is not NULL, logits[vocab] fp32.  token_out may equal token_in. */
+/* One token: reads token_in[0] (device int32 in [0, vocab); an id outside is clamped to the
+ * range), writes token_out[0] (device int32) and, when logits is not NULL, logits[vocab] fp32.
+ * token_out may equal token_in. */
 int vox_decoder_step(vox_decoder_t *d, const int32_t *token_in, int32_t *token_out, float *logits,
                      void *stream);
 /* Number of steps taken since create/reset (the absolute position of the next token). */

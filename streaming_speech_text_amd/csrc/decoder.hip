@@ -19,7 +19,8 @@
 //   down   Q4_0 GEMV, added into the residual stream
 //   head   final RMSNorm, tied Q4_0 table as LM head, logits (optional) and each workgroup's
 //          best (logit, index) key
-//   final  one workgroup reduces the keys, writes the token and advances pos
+//   final  one workgroup reduces the keys, writes the token, advances pos and fills the
+//          (cos, sin) table of the new position for the next step's RoPE
 // The sequence is captured once into a HIP graph and replayed per token.
 #include <math.h>
 #include <stdlib.h>
