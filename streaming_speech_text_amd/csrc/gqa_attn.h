@@ -62,6 +62,7 @@ struct AttnArgs {
     int n_slots, n_valid;
     int s_cap;               // split cap (partials stride); the grid has >= plan.splits columns
     float scale;
+    int kv_shift;            // with GROUP = 1 per workgroup: KV head = blockIdx.y >> kv_shift
 };
 
 // Merges the nsplit partials (m_s, l_s, o_s) of query head h of KV head g in a fixed order:
@@ -165,8 +166,9 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
     const int pslot = lane >> 4;     // score phase: 4 positions per wave, 16 lanes each
     const int seg = lane & 15;       // 8 dims per lane
 
-    const float *kbase = a.kc + (size_t)g * a.n_slots * ATTN_HD;
-    const float *vbase = a.vc + (size_t)g * a.n_slots * ATTN_HD;
+    const int kvh = g >> a.kv_shift;   // one workgroup per query head when GROUP = 1 serves a group
+    const float *kbase = a.kc + (size_t)kvh * a.n_slots * ATTN_HD;
+    const float *vbase = a.vc + (size_t)kvh * a.n_slots * ATTN_HD;
 
     float m_run[GROUP], l_run[GROUP];
     float2 acc[GROUP];
