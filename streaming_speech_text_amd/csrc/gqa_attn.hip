@@ -22,16 +22,22 @@ __global__ __launch_bounds__(ATTN_MERGE_THREADS) void gqa_attn_merge_kernel(Attn
     attn_merge<GROUP>(a, blockIdx.x / GROUP, blockIdx.x % GROUP, nsplit, lds);
 }
 
+// One chunk: one workgroup per query head (the group's heads read their KV head's chunk through
+// the cache).  Several chunks: one workgroup per (KV head, chunk) serving the group's query
+// heads from one load of K and V, then the merge.
 template <int GROUP>
 static int launch_attn(const AttnArgs &a, int n_kv, hipStream_t s)
 {
     const AttnPlan plan = attn_plan(a.n_valid, a.s_cap);
-    if (plan.splits > 1)
-        hipLaunchKernelGGL((gqa_attn_kernel<GROUP, true>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
-    else
-        hipLaunchKernelGGL((gqa_attn_kernel<GROUP, false>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
+    if (plan.splits == 1) {
+        AttnArgs b = a;
+        b.kv_shift = GROUP == 8 ? 3 : GROUP == 4 ? 2 : GROUP == 2 ? 1 : 0;
+        hipLaunchKernelGGL((gqa_attn_kernel<1, false>), dim3(1, n_kv * GROUP), dim3(ATTN_THREADS), 0, s, b);
+        return check_launch("gqa attention launch");
+    }
+    hipLaunchKernelGGL((gqa_attn_kernel<GROUP, true>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
     int st = check_launch("gqa attention launch");
-    if (st || plan.splits == 1)
+    if (st)
         return st;
     hipLaunchKernelGGL(gqa_attn_merge_kernel<GROUP>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, a, plan.splits);
     return check_launch("gqa attention merge launch");
