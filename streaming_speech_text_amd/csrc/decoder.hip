@@ -779,21 +779,20 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     d->group = c->n_heads / c->n_kv_heads;
     d->s_cap = attn_split_cap(c->n_slots);
     const int qd = c->n_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
-    const int gmin_model = c->dim == 3072 ? 4 : 8;
     d->r_qkv = 8;   // 8-row tiles stay inside one of the q, k, v row ranges for every width
     d->r_o = pick_r(c->dim, qd == 4096 ? 4 : 8);
     d->r_ffn = pick_r(2 * c->hidden, 8);
     d->r_down = pick_r(c->dim, 4);
-    d->r_head = pick_r(c->vocab, gmin_model > 4 ? 8 : 8);
+    d->r_head = pick_r(c->vocab, 8);
     if (c->dim == 3072 && qd == 4096 && c->hidden == 9216) {
-        // measured on MI355X at this shape (decoder ms/token over tile heights per kernel):
-        // one 12-row tile per workgroup for the down projection puts its whole 16 MB in flight
-        // at once; 8-row gate/up tiles (4 + 4) avoid a second round of tiles on a few workgroups
+        // measured on MI355X at this shape (decoder ms/token over tile heights per kernel, with
+        // the rest of the step as it is): 4-row tiles for the O and down projections (768
+        // workgroups of one tile), 8-row gate/up tiles (4 + 4) and LM-head tiles
         d->r_qkv = 8;
         d->r_o = 4;
         d->r_ffn = 8;
-        d->r_down = 12;
-        d->r_head = 16;
+        d->r_down = 4;
+        d->r_head = 8;
     }
     d->host_pos = 0;
     d->use_graph = true;
