@@ -598,24 +598,32 @@ static int attn_bucket(const vox_decoder *d, int64_t pos)
     return b;   // grid width 1 << b, capped at s_cap at launch
 }
 
-// A window that fits one chunk: one workgroup per query head (each reads its KV head's chunk;
-// the group's heads share it through the cache), so the scores and the weighted sum of a head
-// run on a compute unit of their own.  Longer windows: one workgroup per (KV head, chunk) serves
-// the group's query heads from one load of K and V, then the merge.
+// Up to eight chunks: one workgroup per (query head, chunk), each reading its KV head's chunk
+// (the group's heads share it through the cache), so the scores and the weighted sums of the
+// heads run on compute units of their own.  More chunks: one workgroup per (KV head, chunk)
+// serving the group's query heads from one load of K and V (measured on MI355X: past eight
+// chunks the extra reads of the shared chunks cost more than the spread).  A split window ends
+// with the merge.
 template <int GROUP>
 static int launch_attn(const AttnArgs &a, int width, int n_kv, hipStream_t s)
 {
-    if (width == 1) {
-        AttnArgs b = a;
+    const bool per_head = width <= 8;
+    AttnArgs b = a;
+    if (per_head)
         b.kv_shift = GROUP == 8 ? 3 : GROUP == 4 ? 2 : GROUP == 2 ? 1 : 0;
+    if (width == 1)
         hipLaunchKernelGGL((dec_attn_kernel<1, false>), dim3(1, n_kv * GROUP), dim3(ATTN_THREADS), 0, s, b);
-        return check_launch("decoder attention");
-    }
-    hipLaunchKernelGGL((dec_attn_kernel<GROUP, true>), dim3(width, n_kv), dim3(ATTN_THREADS), 0, s, a);
+    else if (per_head)
+        hipLaunchKernelGGL((dec_attn_kernel<1, true>), dim3(width, n_kv * GROUP), dim3(ATTN_THREADS), 0, s, b);
+    else
+        hipLaunchKernelGGL((dec_attn_kernel<GROUP, true>), dim3(width, n_kv), dim3(ATTN_THREADS), 0, s, b);
     int st = check_launch("decoder attention");
-    if (st)
+    if (st || width == 1)
         return st;
-    hipLaunchKernelGGL(dec_attn_merge_kernel<GROUP>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, a);
+    if (per_head)
+        hipLaunchKernelGGL(dec_attn_merge_kernel<1>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, b);
+    else
+        hipLaunchKernelGGL(dec_attn_merge_kernel<GROUP>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, b);
     return check_launch("decoder attention merge");
 }
 

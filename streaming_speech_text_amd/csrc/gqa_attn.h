@@ -14,10 +14,10 @@
 // of that head from the same loads.  Inside the chunk it walks 128-position sub-chunks with
 // an online softmax (running max and sum).  With one chunk the workgroup writes the output
 // directly; otherwise it writes a partial (max, sum, unnormalised output) and a second kernel
-// merges the partials in a fixed order.  A window of one chunk is instead run with GROUP = 1
-// and one workgroup per query head (kv_shift maps it to its KV head): the same K and V are read
-// once per query head, mostly from the cache, and the arithmetic spreads over GROUP times as
-// many compute units.
+// merges the partials in a fixed order.  A window of up to eight chunks is instead run with
+// GROUP = 1 and one workgroup per (query head, chunk) (kv_shift maps it to its KV head): the same
+// K and V are read once per query head, mostly from the cache, and the arithmetic spreads over
+// GROUP times as many compute units.
 #pragma once
 
 #include "vox_common.h"

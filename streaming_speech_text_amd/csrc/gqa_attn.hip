@@ -22,24 +22,33 @@ __global__ __launch_bounds__(ATTN_MERGE_THREADS) void gqa_attn_merge_kernel(Attn
     attn_merge<GROUP>(a, blockIdx.x / GROUP, blockIdx.x % GROUP, nsplit, lds);
 }
 
-// One chunk: one workgroup per query head (the group's heads read their KV head's chunk through
-// the cache).  Several chunks: one workgroup per (KV head, chunk) serving the group's query
-// heads from one load of K and V, then the merge.
+// Up to eight chunks: one workgroup per (query head, chunk), each reading its KV head's chunk
+// (the group's heads share it through the cache).  More chunks: one workgroup per (KV head,
+// chunk) serving the group's query heads from one load of K and V (measured on MI355X: past
+// eight chunks the extra reads of the shared chunks cost more than the spread).  A split window
+// ends with the merge.
 template <int GROUP>
 static int launch_attn(const AttnArgs &a, int n_kv, hipStream_t s)
 {
     const AttnPlan plan = attn_plan(a.n_valid, a.s_cap);
-    if (plan.splits == 1) {
-        AttnArgs b = a;
+    const bool per_head = plan.splits <= 8;
+    AttnArgs b = a;
+    if (per_head)
         b.kv_shift = GROUP == 8 ? 3 : GROUP == 4 ? 2 : GROUP == 2 ? 1 : 0;
+    if (plan.splits == 1)
         hipLaunchKernelGGL((gqa_attn_kernel<1, false>), dim3(1, n_kv * GROUP), dim3(ATTN_THREADS), 0, s, b);
-        return check_launch("gqa attention launch");
-    }
-    hipLaunchKernelGGL((gqa_attn_kernel<GROUP, true>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, a);
+    else if (per_head)
+        hipLaunchKernelGGL((gqa_attn_kernel<1, true>), dim3(plan.splits, n_kv * GROUP), dim3(ATTN_THREADS), 0, s, b);
+    else
+        hipLaunchKernelGGL((gqa_attn_kernel<GROUP, true>), dim3(plan.splits, n_kv), dim3(ATTN_THREADS), 0, s, b);
     int st = check_launch("gqa attention launch");
-    if (st)
+    if (st || plan.splits == 1)
         return st;
-    hipLaunchKernelGGL(gqa_attn_merge_kernel<GROUP>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, a, plan.splits);
+    if (per_head)
+        hipLaunchKernelGGL(gqa_attn_merge_kernel<1>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, b, plan.splits);
+    else
+        hipLaunchKernelGGL(gqa_attn_merge_kernel<GROUP>, dim3(n_kv * GROUP), dim3(ATTN_MERGE_THREADS), 0, s, b,
+                           plan.splits);
     return check_launch("gqa attention merge launch");
 }
 
