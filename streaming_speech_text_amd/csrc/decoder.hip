@@ -422,14 +422,8 @@ using DGeom = GemvGeom<K, nt_for<K>(), R, NPART>;
 template <class Gm, class Policy, class Args>
 static int launch_gemv(const Args &args, hipStream_t s, const char *what, int *grid_out = nullptr)
 {
-    static int occ = 0;
-    if (occ <= 0) {
-        int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, dec_gemv_kernel<Gm, Policy>, Gm::NT, 0) != hipSuccess ||
-            v < 1)
-            v = 1;
-        occ = v;
-    }
+    static std::atomic<int> occ_cache{0};
+    const int occ = resident_per_cu(occ_cache, dec_gemv_kernel<Gm, Policy>, Gm::NT);
     const int ntiles = Policy::tiles(args);
     const int cap = occ * cu_count();
     int grid = ntiles < cap ? ntiles : cap;
@@ -717,7 +711,7 @@ static void drop_graphs(vox_decoder *d)
 {
     for (auto &g : d->graphs) {
         if (g)
-            hipGraphExecDestroy(g);
+            (void)hipGraphExecDestroy(g);   // teardown: nothing to report
         g = nullptr;
     }
 }
@@ -786,7 +780,7 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     d->part = (float *)(d->scratch + lay.part);
     d->group = c->n_heads / c->n_kv_heads;
     d->s_cap = attn_split_cap(c->n_slots);
-    const int qd = c->n_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+    const int qd = c->n_heads * c->head_dim;
     d->r_qkv = 8;   // 8-row tiles stay inside one of the q, k, v row ranges for every width
     d->r_o = pick_r(c->dim, qd == 4096 ? 4 : 8);
     d->r_ffn = pick_r(2 * c->hidden, 8);
@@ -815,7 +809,7 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     }
     if (st) {
         if (d->cap_stream)
-            hipStreamDestroy(d->cap_stream);
+            (void)hipStreamDestroy(d->cap_stream);
         delete d;
         return st;
     }
@@ -864,7 +858,7 @@ extern "C" int vox_decoder_step(vox_decoder_t *d, const int32_t *token_in, int32
             if (!st)
                 st = check_hip(hipGraphInstantiate(&d->graphs[bucket], graph, nullptr, nullptr, 0), "instantiate");
             if (graph)
-                hipGraphDestroy(graph);
+                (void)hipGraphDestroy(graph);
             if (st) {
                 d->graphs[bucket] = nullptr;
                 return st;
@@ -900,6 +894,6 @@ extern "C" void vox_decoder_destroy(vox_decoder_t *d)
         return;
     drop_graphs(d);
     if (d->cap_stream)
-        hipStreamDestroy(d->cap_stream);
+        (void)hipStreamDestroy(d->cap_stream);
     delete d;
 }

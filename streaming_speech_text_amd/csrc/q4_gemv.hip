@@ -106,13 +106,8 @@ __global__ __launch_bounds__(Gm::NT) __attribute__((amdgpu_waves_per_eu(4))) voi
 template <class Gm>
 static int launch_tiled(const void *w, const float *x, float *y, int64_t n, hipStream_t s)
 {
-    static int occ = 0;
-    if (occ <= 0) {
-        int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, q4_gemv_tiled_kernel<Gm>, Gm::NT, 0) != hipSuccess || v < 1)
-            v = 1;
-        occ = v;
-    }
+    static std::atomic<int> occ_cache{0};
+    const int occ = resident_per_cu(occ_cache, q4_gemv_tiled_kernel<Gm>, Gm::NT);
     const int64_t ntiles = (n + Gm::R - 1) / Gm::R;
     const int64_t cap = (int64_t)occ * cu_count();
     const int grid = (int)(ntiles < cap ? ntiles : cap);

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/vox.h"
 
 namespace vox {
@@ -19,6 +21,20 @@ int check_hip(hipError_t e, const char *what);
 
 // Number of compute units of the current device (cached per device).
 int cu_count();
+
+// Resident workgroups of `threads` threads per compute unit for `kernel`, computed on first use
+// and kept in `cache` (at least 1).  Safe to call from several threads.
+template <class K>
+int resident_per_cu(std::atomic<int> &cache, K kernel, int threads)
+{
+    int v = cache.load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, 0) != hipSuccess || v < 1)
+            v = 1;
+        cache.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
 
 inline bool overlaps(const void *a, size_t an, const void *b, size_t bn)
 {
