@@ -30,6 +30,14 @@ void orc_q4_gemv_rows(const uint8_t *w, const float *x, const int64_t *rows, int
                       double *y, int64_t k);
 void orc_q4_gemm(const uint8_t *w, const uint16_t *x_bf16, double *y, int64_t m, int64_t n, int64_t k);
 
+/* Adapter: linear, GELU, linear */
+double orc_gelu(double x);
+void orc_gelu_array(const double *x, int64_t n, double *out);
+uint16_t orc_f32_to_bf16(float f);
+void orc_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out);
+void orc_adapter(const uint8_t *w1, const uint8_t *w2, const uint16_t *x_bf16, double *y, int64_t m,
+                 int64_t k, int64_t n_mid, int64_t n_out);
+
 /* Decoder pieces */
 void orc_rmsnorm(const double *x, const float *g, int64_t dim, double eps, double *out);
 void orc_rope(double *x, int64_t n_heads, int64_t head_dim, int64_t pos, double theta);

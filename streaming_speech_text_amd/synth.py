@@ -109,9 +109,14 @@ LAYER_LINEARS = {
 ENCODER_LINEARS = [("q", 1280, 1280), ("k", 1280, 1280), ("v", 1280, 1280), ("o", 1280, 1280),
                    ("ffn_up", 5120, 1280), ("ffn_down", 1280, 5120)]
 ENCODER_M = (16, 64, 200, 750)
+# Adapter (in, mid, out): a linear 5120 -> 3072, GELU, a linear 3072 -> 3072 (voxtral.c page,
+# section 모델 아키텍처).  It reads the encoder output four frames to a row (4 x 1280 = 5120), so an
+# encoder chunk of M frames gives M / 4 adapter rows.
+ADAPTER = (5120, 3072, 3072)
+ADAPTER_M = tuple(m // 4 for m in ENCODER_M)
 
 # Seeds: one per workload.
-SEED_GEMV, SEED_LAYER, SEED_ATTN, SEED_DECODER, SEED_GEMM = 1, 2, 3, 4, 5
+SEED_GEMV, SEED_LAYER, SEED_ATTN, SEED_DECODER, SEED_GEMM, SEED_ADAPTER = 1, 2, 3, 4, 5, 6
 
 
 def gemv_inputs(seed: int, n: int, k: int):
@@ -122,6 +127,12 @@ def gemv_inputs(seed: int, n: int, k: int):
 def gemm_inputs(seed: int, m: int, n: int, k: int):
     """(W q4 [n, k/32*18], X bf16 bits [m, k])."""
     return q4_matrix(generator(seed, 0, n, k), n, k), bf16_normal(generator(seed, 1, m, k), (m, k))
+
+
+def adapter_inputs(seed: int, m: int, k: int, n_mid: int, n_out: int):
+    """(W1 q4 [n_mid, k/32*18], W2 q4 [n_out, n_mid/32*18], X bf16 bits [m, k])."""
+    return (q4_matrix(generator(seed, 0, n_mid, k), n_mid, k), q4_matrix(generator(seed, 1, n_out, n_mid), n_out, n_mid),
+            bf16_normal(generator(seed, 2, m, k), (m, k)))
 
 
 def attention_inputs(seed: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_slots: int):

@@ -484,3 +484,125 @@ def test_page_figures_pin_shapes():
     total = s.n_layers * per_layer + s.vocab * synth.q4_row_bytes(s.dim)
     assert total < fig["q4_model_bytes"]["approx_bytes"]
     assert synth.ENCODER_LINEARS[0][1] == fig["encoder"]["dim"]
+
+
+# ---------------------------------------------------------------------------------------
+# adapter: linear, GELU, linear
+# ---------------------------------------------------------------------------------------
+
+def test_gelu_library_and_closed_forms(orc):
+    from scipy.special import ndtr
+    x = np.concatenate([np.linspace(-12, 12, 4801), synth.generator(30).standard_normal(2000) * 3])
+    got = orc.gelu(x)
+    # x * Phi(x) with the library's normal distribution function
+    assert np.allclose(got, x * ndtr(x), rtol=1e-13, atol=1e-300)   # a few ulps in the far tail
+    # torch's exact GELU in double (its 1 + erf form flushes the far negative tail to zero, so an
+    # absolute floor of 1e-15 covers that tail)
+    assert np.allclose(got, F.gelu(torch.from_numpy(x), approximate="none").numpy(), rtol=1e-14, atol=1e-15)
+    # GELU(x) - GELU(-x) = x, since Phi(x) + Phi(-x) = 1
+    assert np.allclose(got - orc.gelu(-x), x, rtol=0, atol=1e-13)
+    assert orc.gelu([0.0])[0] == 0.0
+    # Phi(1) = 0.841344746068543 (standard normal table); GELU(1) = Phi(1), GELU(-1) = -(1 - Phi(1))
+    assert abs(orc.gelu([1.0])[0] - 0.841344746068543) < 1e-15
+    assert abs(orc.gelu([-1.0])[0] + 0.158655253931457) < 1e-15
+    # the tanh approximation is a different function: they differ by more than rounding here
+    tanh_form = 0.5 * x * (1 + np.tanh(math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3)))
+    assert np.abs(got - tanh_form).max() > 1e-4
+
+
+def _bf16_nearest_bruteforce(f: np.ndarray) -> np.ndarray:
+    """Nearest bf16 by comparing the two neighbouring patterns' values in double (ties: even)."""
+    u = f.view(np.uint32)
+    t = (u >> 16).astype(np.uint32)                  # truncation toward zero
+    a = (t + 1).astype(np.uint32)                    # next pattern away from zero
+    vt = (t << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    va = (a << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    fv = f.astype(np.float64)
+    dt, da = np.abs(fv - vt), np.abs(va - fv)
+    with np.errstate(invalid="ignore"):
+        pick_a = (da < dt) | ((da == dt) & (t % 2 == 1))
+    return np.where(pick_a, a, t).astype(np.uint16)
+
+
+def test_f32_to_bf16_rounding(orc):
+    g = synth.generator(31)
+    bits = g.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    finite = np.isfinite(f) & (np.abs(f) < np.float32(3.38e38))
+    f = f[finite]
+    # halfway cases and their neighbours, both signs
+    hw = (g.integers(0, 0x7F7F, size=5000).astype(np.uint32) << 16) | 0x8000   # finite patterns
+    f = np.concatenate([f, hw.view(np.float32), (hw + 1).view(np.float32), (hw - 1).view(np.float32),
+                        -hw.view(np.float32), np.float32([0.0, -0.0, 1.0, 1e-45, -1e-45])])
+    got = orc.f32_to_bf16(f)
+    assert np.array_equal(got, _bf16_nearest_bruteforce(f))
+    # the library's conversion rounds the same way
+    assert np.array_equal(got, torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    # special values: the largest finite fp32 rounds to infinity; infinities pass; NaN stays NaN
+    sp = orc.f32_to_bf16(np.float32([np.finfo(np.float32).max, np.inf, -np.inf, np.nan]))
+    assert list(sp[:3]) == [0x7F80, 0x7F80, 0xFF80]
+    assert (sp[3] & 0x7F80) == 0x7F80 and (sp[3] & 0x7F) != 0
+
+
+def test_adapter_identity_second_linear(orc):
+    # W2 = identity (code 9 on the diagonal, 8 elsewhere, scale 1): Y = bf16(GELU(X W1^T))
+    g = synth.generator(32)
+    m, k, n_mid = 6, 128, 64
+    w1 = synth.q4_matrix(g, n_mid, k)
+    xb = synth.bf16_normal(g, (m, k))
+    eye = np.zeros((n_mid, n_mid // 32, 18), np.uint8)
+    eye[:, :, 0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    codes = np.full((n_mid, n_mid), 8, np.uint8)
+    codes[np.arange(n_mid), np.arange(n_mid)] = 9
+    for b in range(n_mid // 32):
+        c = codes[:, 32 * b:32 * b + 32]
+        eye[:, b, 2:] = c[:, :16] | (c[:, 16:] << 4)
+    y = orc.adapter(w1, eye.reshape(n_mid, -1), xb)
+    h = orc.q4_gemm(w1, xb)
+    gel = F.gelu(torch.from_numpy(h), approximate="none").to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    assert np.array_equal(y, gel.numpy())
+    # GELU really sits between the linears: negative pre-activations shrink toward zero
+    assert (h < -1).any() and np.all(y[h < -1] > h[h < -1])
+
+
+def test_adapter_bruteforce_tiny(orc):
+    # pure-Python loops over the definition; non-square shapes catch a transposed operand
+    g = synth.generator(33)
+    m, k, n_mid, n_out = 3, 64, 96, 5
+    w1 = synth.q4_matrix(g, n_mid, k)
+    w2 = synth.q4_matrix(g, n_out, n_mid)
+    xb = synth.bf16_normal(g, (m, k))
+
+    def deq(w, n, kk):
+        out = []
+        for r in range(n):
+            row = []
+            for b in range(kk // 32):
+                blk = w[r, 18 * b:18 * b + 18]
+                d = float(blk[0:2].view(np.float16)[0])
+                lo = [(int(q) & 15) - 8 for q in blk[2:]]
+                hi = [(int(q) >> 4) - 8 for q in blk[2:]]
+                row += [c * d for c in lo + hi]
+            out.append(row)
+        return out
+
+    W1, W2 = deq(w1, n_mid, k), deq(w2, n_out, n_mid)
+    X = [[float((np.uint32(v) << np.uint32(16)).view(np.float32)) for v in row] for row in xb]
+    ref = []
+    for r in range(m):
+        hrow = []
+        for c in range(n_mid):
+            s = sum(X[r][i] * W1[c][i] for i in range(k))
+            ge = 0.5 * s * (1 + math.erf(s / math.sqrt(2)))
+            hrow.append(float(torch.tensor(ge, dtype=torch.float32).to(torch.bfloat16).item()))
+        ref.append([sum(hrow[i] * W2[c][i] for i in range(n_mid)) for c in range(n_out)])
+    got = orc.adapter(w1, w2, xb)
+    assert got.shape == (m, n_out)
+    assert np.allclose(got, np.array(ref), rtol=1e-12, atol=1e-12)
+
+
+def test_page_figures_pin_adapter_shape():
+    fig = json.load(open(os.path.join(GOLDEN, "page_figures.json")))["adapter"]
+    assert synth.ADAPTER == (fig["in"], fig["mid"], fig["out"])
+    # four encoder frames of width 1280 make one adapter row
+    assert fig["in"] == 4 * json.load(open(os.path.join(GOLDEN, "page_figures.json")))["encoder"]["dim"]
