@@ -142,14 +142,10 @@ void orc_q4_gemv_rows(const uint8_t *w, const float *x, const int64_t *rows, int
     free(xd);
 }
 
-/* Encoder-chunk linear: Y[m][n] = sum over k ascending of bf16(X[m][k]) * W[n][k]
- * ([VC] section 모델 아키텍처: encoder width 1280; [RS] section 아키텍처: Q4_0 linears). */
-void orc_q4_gemm(const uint8_t *w, const uint16_t *x_bf16, double *y, int64_t m, int64_t n, int64_t k)
+/* Y[m][n] = sum over k ascending of X[m][k] * W[n][k], X in double. */
+static void q4_gemm_f64(const uint8_t *w, const double *xd, double *y, int64_t m, int64_t n, int64_t k)
 {
     const int64_t row_bytes = (k / 32) * 18;
-    double *xd = (double *)malloc(sizeof(double) * (size_t)(m * k));
-    for (int64_t i = 0; i < m * k; i++)
-        xd[i] = orc_bf16_to_double(x_bf16[i]);
 #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < n; c++) {
         double *wrow = (double *)malloc(sizeof(double) * (size_t)k);
@@ -163,6 +159,16 @@ void orc_q4_gemm(const uint8_t *w, const uint16_t *x_bf16, double *y, int64_t m,
         }
         free(wrow);
     }
+}
+
+/* Encoder-chunk linear: Y[m][n] = sum over k ascending of bf16(X[m][k]) * W[n][k]
+ * ([VC] section 모델 아키텍처: encoder width 1280; [RS] section 아키텍처: Q4_0 linears). */
+void orc_q4_gemm(const uint8_t *w, const uint16_t *x_bf16, double *y, int64_t m, int64_t n, int64_t k)
+{
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(m * k));
+    for (int64_t i = 0; i < m * k; i++)
+        xd[i] = orc_bf16_to_double(x_bf16[i]);
+    q4_gemm_f64(w, xd, y, m, n, k);
     free(xd);
 }
 
@@ -171,8 +177,7 @@ void orc_q4_gemm(const uint8_t *w, const uint16_t *x_bf16, double *y, int64_t m,
  * 3072 inputs, GELU, a linear from 3072 to 3072).  READINGS: no biases (the pages name none,
  * and the Q4_0 linears of the quantised path carry none); GELU is the exact form
  * x * Phi(x) with Phi the standard normal distribution function, not the tanh approximation;
- * the GELU output enters the second linear in bf16 (its fp32 value rounded to nearest, ties to
- * even), the activation format of the matrix-core linears.
+ * the GELU output enters the second linear unrounded (here in double).
  * ---------------------------------------------------------------------------------- */
 
 /* GELU(x) = x * Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2 = erfc(-x / sqrt 2) / 2 (the erfc form
@@ -188,44 +193,16 @@ void orc_gelu_array(const double *x, int64_t n, double *out)
         out[i] = orc_gelu(x[i]);
 }
 
-/* fp32 -> bf16, round to nearest, ties to even.  A finite value lies between its truncation
- * toward zero (the upper 16 bits) and the next bf16 away from zero (those bits + 1, which for a
- * sign-magnitude pattern is one unit further out; past the largest finite value that is the
- * infinity of the same sign, as rounding requires).  The dropped 16 bits say which is nearer:
- * above half a unit -> away, below -> toward zero, exactly half -> the even pattern.
- * Infinities pass; a NaN stays a (quiet) NaN. */
-uint16_t orc_f32_to_bf16(float f)
-{
-    uint32_t u;
-    memcpy(&u, &f, sizeof u);
-    uint16_t hi = (uint16_t)(u >> 16);
-    uint32_t rest = u & 0xFFFFu;
-    if ((u & 0x7F800000u) == 0x7F800000u)
-        return (u & 0x007FFFFFu) ? (uint16_t)(hi | 0x0040u) : hi;
-    if (rest > 0x8000u || (rest == 0x8000u && (hi & 1u)))
-        hi++;
-    return hi;
-}
-
-void orc_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out)
-{
-    for (int64_t i = 0; i < n; i++)
-        out[i] = orc_f32_to_bf16(x[i]);
-}
-
-/* Y[m][n_out] = bf16(GELU(X W1^T)) W2^T: X bf16 [m][k], W1 Q4_0 [n_mid][k], W2 Q4_0
- * [n_out][n_mid].  The first product and GELU in double, the GELU output rounded to fp32 and
- * then to bf16 (the step the matrix-core path takes), the second product in double. */
+/* Y[m][n_out] = GELU(X W1^T) W2^T: X bf16 [m][k], W1 Q4_0 [n_mid][k], W2 Q4_0 [n_out][n_mid];
+ * both products, GELU and the intermediate in double. */
 void orc_adapter(const uint8_t *w1, const uint8_t *w2, const uint16_t *x_bf16, double *y, int64_t m,
                  int64_t k, int64_t n_mid, int64_t n_out)
 {
     double *h = (double *)malloc(sizeof(double) * (size_t)(m * n_mid));
-    uint16_t *hb = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(m * n_mid));
     orc_q4_gemm(w1, x_bf16, h, m, n_mid, k);
     for (int64_t i = 0; i < m * n_mid; i++)
-        hb[i] = orc_f32_to_bf16((float)orc_gelu(h[i]));
-    orc_q4_gemm(w2, hb, y, m, n_out, n_mid);
-    free(hb);
+        h[i] = orc_gelu(h[i]);
+    q4_gemm_f64(w2, h, y, m, n_out, n_mid);
     free(h);
 }
 

@@ -33,8 +33,6 @@ void orc_q4_gemm(const uint8_t *w, const uint16_t *x_bf16, double *y, int64_t m,
 /* Adapter: linear, GELU, linear */
 double orc_gelu(double x);
 void orc_gelu_array(const double *x, int64_t n, double *out);
-uint16_t orc_f32_to_bf16(float f);
-void orc_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out);
 void orc_adapter(const uint8_t *w1, const uint8_t *w2, const uint16_t *x_bf16, double *y, int64_t m,
                  int64_t k, int64_t n_mid, int64_t n_out);
 

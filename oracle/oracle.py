@@ -55,7 +55,6 @@ def lib():
             "orc_gqa_attn": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _dbl, _vp],
             "orc_swiglu": [_vp, _vp, _i64, _vp],
             "orc_gelu_array": [_vp, _i64, _vp],
-            "orc_f32_to_bf16_array": [_vp, _i64, _vp],
             "orc_adapter": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64],
             "orc_decoder_destroy": [_vp],
             "orc_decoder_reset": [_vp],
@@ -202,17 +201,9 @@ def gelu(x) -> np.ndarray:
     return out
 
 
-def f32_to_bf16(x) -> np.ndarray:
-    """fp32 values -> bf16 bit patterns (uint16), nearest-even."""
-    x = _c(x, np.float32)
-    out = np.empty(x.shape, np.uint16)
-    lib().orc_f32_to_bf16_array(_p(x), x.size, _p(out))
-    return out
-
-
 def adapter(w1, w2, x_bf16) -> np.ndarray:
     """w1: uint8 [n_mid, k/32*18]; w2: uint8 [n_out, n_mid/32*18]; x_bf16: uint16 [m, k]
-    -> float64 [m, n_out] = bf16(GELU(X W1^T)) W2^T."""
+    -> float64 [m, n_out] = GELU(X W1^T) W2^T."""
     w1 = _c(w1, np.uint8)
     w2 = _c(w2, np.uint8)
     x = _c(x_bf16, np.uint16)

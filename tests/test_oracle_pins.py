@@ -510,42 +510,8 @@ def test_gelu_library_and_closed_forms(orc):
     assert np.abs(got - tanh_form).max() > 1e-4
 
 
-def _bf16_nearest_bruteforce(f: np.ndarray) -> np.ndarray:
-    """Nearest bf16 by comparing the two neighbouring patterns' values in double (ties: even)."""
-    u = f.view(np.uint32)
-    t = (u >> 16).astype(np.uint32)                  # truncation toward zero
-    a = (t + 1).astype(np.uint32)                    # next pattern away from zero
-    vt = (t << 16).astype(np.uint32).view(np.float32).astype(np.float64)
-    va = (a << 16).astype(np.uint32).view(np.float32).astype(np.float64)
-    fv = f.astype(np.float64)
-    dt, da = np.abs(fv - vt), np.abs(va - fv)
-    with np.errstate(invalid="ignore"):
-        pick_a = (da < dt) | ((da == dt) & (t % 2 == 1))
-    return np.where(pick_a, a, t).astype(np.uint16)
-
-
-def test_f32_to_bf16_rounding(orc):
-    g = synth.generator(31)
-    bits = g.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
-    f = bits.view(np.float32)
-    finite = np.isfinite(f) & (np.abs(f) < np.float32(3.38e38))
-    f = f[finite]
-    # halfway cases and their neighbours, both signs
-    hw = (g.integers(0, 0x7F7F, size=5000).astype(np.uint32) << 16) | 0x8000   # finite patterns
-    f = np.concatenate([f, hw.view(np.float32), (hw + 1).view(np.float32), (hw - 1).view(np.float32),
-                        -hw.view(np.float32), np.float32([0.0, -0.0, 1.0, 1e-45, -1e-45])])
-    got = orc.f32_to_bf16(f)
-    assert np.array_equal(got, _bf16_nearest_bruteforce(f))
-    # the library's conversion rounds the same way
-    assert np.array_equal(got, torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
-    # special values: the largest finite fp32 rounds to infinity; infinities pass; NaN stays NaN
-    sp = orc.f32_to_bf16(np.float32([np.finfo(np.float32).max, np.inf, -np.inf, np.nan]))
-    assert list(sp[:3]) == [0x7F80, 0x7F80, 0xFF80]
-    assert (sp[3] & 0x7F80) == 0x7F80 and (sp[3] & 0x7F) != 0
-
-
 def test_adapter_identity_second_linear(orc):
-    # W2 = identity (code 9 on the diagonal, 8 elsewhere, scale 1): Y = bf16(GELU(X W1^T))
+    # W2 = identity (code 9 on the diagonal, 8 elsewhere, scale 1): Y = GELU(X W1^T)
     g = synth.generator(32)
     m, k, n_mid = 6, 128, 64
     w1 = synth.q4_matrix(g, n_mid, k)
@@ -559,8 +525,8 @@ def test_adapter_identity_second_linear(orc):
         eye[:, b, 2:] = c[:, :16] | (c[:, 16:] << 4)
     y = orc.adapter(w1, eye.reshape(n_mid, -1), xb)
     h = orc.q4_gemm(w1, xb)
-    gel = F.gelu(torch.from_numpy(h), approximate="none").to(torch.float32).to(torch.bfloat16).to(torch.float64)
-    assert np.array_equal(y, gel.numpy())
+    from scipy.special import ndtr
+    assert np.allclose(y, h * ndtr(h), rtol=1e-13, atol=1e-300)
     # GELU really sits between the linears: negative pre-activations shrink toward zero
     assert (h < -1).any() and np.all(y[h < -1] > h[h < -1])
 
@@ -593,8 +559,7 @@ def test_adapter_bruteforce_tiny(orc):
         hrow = []
         for c in range(n_mid):
             s = sum(X[r][i] * W1[c][i] for i in range(k))
-            ge = 0.5 * s * (1 + math.erf(s / math.sqrt(2)))
-            hrow.append(float(torch.tensor(ge, dtype=torch.float32).to(torch.bfloat16).item()))
+            hrow.append(0.5 * s * (1 + math.erf(s / math.sqrt(2))))
         ref.append([sum(hrow[i] * W2[c][i] for i in range(n_mid)) for c in range(n_out)])
     got = orc.adapter(w1, w2, xb)
     assert got.shape == (m, n_out)
