@@ -127,7 +127,7 @@ def timed(torch, stream, launch, copies, reps, replays=5):
 def kernels_leg(torch, synth, vox, dev, stream):
     """Per-kernel device times of the workloads beside the decoder step: the single 3072x3072
     GEMV, one decoder layer's linears, GQA attention at three ring fills, the encoder-chunk
-    GEMM set.  Every measurement rotates over more than 1 GiB of distinct copies."""
+    GEMM set, the adapter.  Every measurement rotates over more than 1 GiB of distinct copies."""
     GiB = 2 ** 30
     out = []
 
@@ -196,6 +196,31 @@ def kernels_leg(torch, synth, vox, dev, stream):
               "tflops": round(flops / us / 1e6, 2), "frac_mfma_bf16": round(flops / us / 1e6 / 2500.0, 4),
               "bytes": b, "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
         del wdev
+        torch.cuda.empty_cache()
+
+    # adapter (linear 5120 -> 3072, GELU, linear 3072 -> 3072) over the rows of one encoder chunk
+    k, n_mid, n_out = synth.ADAPTER
+    for m in synth.ADAPTER_M:
+        w1, w2, xb = synth.adapter_inputs(synth.SEED_ADAPTER, m, k, n_mid, n_out)
+        wbytes = w1.nbytes + w2.nbytes
+        copies = max(2, int(np.ceil(1.1 * GiB / wbytes)))
+        w1s = [torch.from_numpy(w1).to(dev) for _ in range(copies)]
+        w2s = [torch.from_numpy(w2).to(dev) for _ in range(copies)]
+        xd = torch.from_numpy(xb.view(np.int16)).to(dev)
+        y = torch.empty(m, n_out, dtype=torch.float32, device=dev)
+        wsb = vox.adapter_workspace(m, k, n_mid, n_out)
+        aws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def launch(i):
+            vox._check(vox.lib().vox_adapter(vox._ptr(w1s[i]), vox._ptr(w2s[i]), vox._ptr(xd), vox._ptr(y), m, k, n_mid,
+                                             n_out, vox._ptr(aws), wsb, vox._stream(None)))
+        us = timed(torch, stream, launch, copies, 50)
+        flops = 2 * m * (n_mid * k + n_out * n_mid)   # the two products as defined
+        b = wbytes + m * k * 2 + m * n_out * 4
+        emit({"kernel": "adapter", "case": f"{k}->{n_mid}->{n_out}, M={m} rows", "us": round(us, 3), "flops": flops,
+              "tflops": round(flops / us / 1e6, 2), "bytes": b, "gbs": round(b / us / 1e3, 1),
+              "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del w1s, w2s
         torch.cuda.empty_cache()
     return out
 

@@ -76,6 +76,25 @@ size_t vox_q4_gemm_workspace(int64_t m, int64_t n, int64_t k);
 int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, int64_t m, int64_t n, int64_t k,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Adapter from the audio encoder to the decoder ([VC] 모델 아키텍처: a linear from 5120 to 3072
+ * inputs, GELU, a linear from 3072 to 3072; [RS] 아키텍처: Q4_0 linears):
+ *   Y = GELU(X * W1^T) * W2^T,
+ * GELU(v) = v * Phi(v) with Phi the standard normal distribution function (the exact form), no
+ * biases.  x_bf16: m rows by k, bf16 bit patterns, row major; w1_q4: n_mid rows by k; w2_q4:
+ * n_out rows by n_mid; y: m by n_out fp32, row major, must not overlap the inputs.  Products of
+ * the exact Q4 codes with bf16 activations on the matrix cores, fp32 accumulation; the GELU
+ * output is computed in fp32 and enters the second product as a pair of bf16 values whose sum
+ * is within 2^-18 of it (relative).  workspace: at least vox_adapter_workspace(m, k, n_mid, n_out)
+ * bytes of device memory, 16-byte aligned, apart from the other buffers, contents irrelevant.
+ * The call is deterministic: the order of every sum is fixed.
+ * m == 0 or n_out == 0 is a no-op.  k or n_mid not a positive multiple of 32 -> VOX_E_INVAL;
+ * k outside {1280, 3072, 5120}, n_mid outside {1280, 3072}, or m * k, 2 * m * n_mid >= 2^31 ->
+ * VOX_E_UNSUPPORTED (the workspace query then returns 0); x_bf16, w1_q4, w2_q4 not 16-byte
+ * aligned -> VOX_E_UNSUPPORTED; a null or smaller workspace -> VOX_E_INVAL / VOX_E_WORKSPACE. */
+size_t vox_adapter_workspace(int64_t m, int64_t k, int64_t n_mid, int64_t n_out);
+int vox_adapter(const void *w1_q4, const void *w2_q4, const uint16_t *x_bf16, float *y, int64_t m, int64_t k,
+                int64_t n_mid, int64_t n_out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Grouped-query decode attention of one token over a KV ring ([RS] 아키텍처 and [VC] 모델
  * 아키텍처: query head h reads KV head h / (n_q_heads / n_kv_heads); [VC] 주요 기능: rolling
  * window).  q: [n_q_heads][head_dim]; k_cache, v_cache: [n_kv_heads][n_slots][head_dim];

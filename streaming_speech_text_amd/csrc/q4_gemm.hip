@@ -22,6 +22,12 @@
 //  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS),
 //    optionally with K split over workgroups (partial tiles in the caller's workspace, added in
 //    a fixed order by a second kernel).
+//
+// The adapter between encoder and decoder (voxtral.c page, section 모델 아키텍처: a linear from
+// 5120 to 3072 inputs, GELU, a linear from 3072 to 3072) is two tiled products.  The first one's
+// epilogue applies GELU (the exact x * Phi(x) form) in fp32 and stores each value as a pair of
+// bf16 values (hi + lo, within 2^-18 of it); the second product reads the pairs as activations
+// over a doubled K, every weight stage serving the hi and then the lo half.
 #include <type_traits>
 
 #include "vox_common.h"
@@ -62,6 +68,20 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t q)
     p.z = pack_bf16_pair(f[4], f[5]);
     p.w = pack_bf16_pair(f[6], f[7]);
     return __builtin_bit_cast(bf16x8, p);
+}
+
+// GELU(v) = v * Phi(v) = v * erfc(-v / sqrt 2) / 2 in fp32, stored as hi = GELU(v) rounded to
+// bf16 and lo = the (exact fp32) remainder rounded to bf16, so hi + lo is within 2^-18 |GELU(v)|.
+// Layout: row `row` of hl is 2n values; column c of stage s = c / 256 puts hi at 512 s + c % 256
+// and lo 256 further, i.e. the stages of K alternate hi and lo halves.
+__device__ __forceinline__ void store_gelu_pair(uint16_t *hl, int n, int64_t row, int col, float v)
+{
+    const float g = 0.5f * v * erfcf(-0.70710678118654752f * v);
+    const __bf16 hi = (__bf16)g;
+    const __bf16 lo = (__bf16)(g - (float)hi);
+    uint16_t *p = hl + row * 2 * n + 2 * (col & ~255) + (col & 255);
+    p[0] = __builtin_bit_cast(uint16_t, hi);
+    p[256] = __builtin_bit_cast(uint16_t, lo);
 }
 
 template <int MI, int NJ>
@@ -190,9 +210,8 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
 //    with aligned dword reads and unpacks the codes in registers to exact bf16: lane group g
 //    of a column takes inputs 8g .. 8g+7, i.e. the low (g < 2) or high (g >= 2) nibbles of
 //    code bytes 8(g%2) .. 8(g%2)+7;
-//  * per block the wave runs 4 x 4 matrix-core products of A with the codes, each seeded (as
-//    accumulator input) with A times a constant -8 operand, so each product is exactly the
-//    block's sum of a * (code - 8) up to fp32 rounding; scale * product goes into fp32.
+//  * per block the wave runs 4 x 4 matrix-core products of A with the exact (code - 8) values,
+//    each the block's sum of a * (code - 8) up to fp32 rounding; scale * product goes into fp32.
 // The eight waves' partial tiles are added through LDS in a fixed tree order at the end.
 // ---------------------------------------------------------------------------------------
 constexpr int GT_BM = 64, GT_BN = 64, GT_KC = 8, GT_THREADS = 512;
@@ -214,17 +233,19 @@ __device__ __forceinline__ float ubyte_to_f(uint32_t v, int j)
     return r;
 }
 
-// The codes themselves (0 .. 15, exact in bf16) for 8 codes taken from one nibble of 8 bytes
-// (lo: bytes 0-3, hi: 4-7).  The - 8 is added by the matrix core through its accumulator input.
+// (code - 8) for 8 codes taken from one nibble of 8 bytes (lo: bytes 0-3, hi: 4-7), exact in bf16.
+// (Feeding the raw codes and adding -8 times the activations' block sum through the accumulator
+// saves the subtractions but cancels two sums of size 8 sum|a|: measured on MI355X, no faster,
+// and its rounding shows where the weights are sparse.)
 __device__ __forceinline__ u32x4v nibbles_to_bf16(uint32_t lo, uint32_t hi, bool high_nibble)
 {
     const uint32_t a = (high_nibble ? lo >> 4 : lo) & 0x0F0F0F0Fu;
     const uint32_t b = (high_nibble ? hi >> 4 : hi) & 0x0F0F0F0Fu;
     u32x4v p;
-    p.x = pack_bf16_pair(ubyte_to_f(a, 0), ubyte_to_f(a, 1));
-    p.y = pack_bf16_pair(ubyte_to_f(a, 2), ubyte_to_f(a, 3));
-    p.z = pack_bf16_pair(ubyte_to_f(b, 0), ubyte_to_f(b, 1));
-    p.w = pack_bf16_pair(ubyte_to_f(b, 2), ubyte_to_f(b, 3));
+    p.x = pack_bf16_pair(ubyte_to_f(a, 0) - 8.0f, ubyte_to_f(a, 1) - 8.0f);
+    p.y = pack_bf16_pair(ubyte_to_f(a, 2) - 8.0f, ubyte_to_f(a, 3) - 8.0f);
+    p.z = pack_bf16_pair(ubyte_to_f(b, 0) - 8.0f, ubyte_to_f(b, 1) - 8.0f);
+    p.w = pack_bf16_pair(ubyte_to_f(b, 2) - 8.0f, ubyte_to_f(b, 3) - 8.0f);
     return p;
 }
 
@@ -271,14 +292,22 @@ __device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, 
     }
 }
 
+// Modes of the tiled kernel (compile-time, so the plain product carries no code of the others):
+//  T_PLAIN      fp32 output y;
+//  T_GELU_OUT   the unsplit output goes through GELU into hl as store_gelu_pair lays it out;
+//  T_PAIR_IN    the activations are GELU pairs (row length k = 2 x the weights' K): stage st
+//               reads weight stage st / 2, so each weight stage serves its hi and lo halves.
+enum { T_PLAIN = 0, T_GELU_OUT = 1, T_PAIR_IN = 2 };
+
 // NS: stages (of 256 inputs) per workgroup, fixed at compile time.  Workgroup z of the grid's
-// third dimension takes stages z*NS .. z*NS+NS-1; with one slice it writes y, otherwise its fp32
-// partial tile goes to part[z][m][n] and q4_gemm_reduce_kernel adds the slices.
-template <int NS>
+// third dimension takes stages z*NS .. z*NS+NS-1; with one slice it writes the output itself,
+// otherwise its fp32 partial tile goes to part[z][m][n] and q4_gemm_reduce_kernel adds the
+// slices.  k is the activations' row length.
+template <int NS, int MODE>
 __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t *__restrict__ w,
                                                                    const uint16_t *__restrict__ x,
-                                                                   float *__restrict__ y, float *__restrict__ part,
-                                                                   int m, int n, int k)
+                                                                   float *__restrict__ y, uint16_t *__restrict__ hl,
+                                                                   float *__restrict__ part, int m, int n, int k)
 {
     __shared__ __attribute__((aligned(16))) uint32_t braw[2][GT_BN * GT_RAW / 4];
     __shared__ f32x4v red[4][16][64];   // tree reduction of the waves' tiles
@@ -290,7 +319,8 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
     const int m0 = blockIdx.y * GT_BM;
     const int n0 = blockIdx.x * GT_BN;
     const int st0 = blockIdx.z * NS, st_end = st0 + NS;
-    const uint32_t row_bytes = (uint32_t)(k / 32) * 18;
+    constexpr int KWS = MODE == T_PAIR_IN ? 1 : 0;   // weight stage = activation stage >> KWS
+    const uint32_t row_bytes = (uint32_t)((k >> KWS) / 32) * 18;
 
     // A operands of this lane: rows m0 + 16i + l16 (clamped), inputs 8*grp .. of block `wave`
     uint32_t aoff[4];
@@ -318,7 +348,7 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             ar[S][i] = *reinterpret_cast<const u32x4v *>(xs + aoff[i]);
-        const uint8_t *ws = w + (size_t)st * GT_RAW;
+        const uint8_t *ws = w + (size_t)(st >> KWS) * GT_RAW;
 #pragma unroll
         for (int r = 0; r < 2; ++r)
             wr[S][r] = *reinterpret_cast<const u32x4v *>(ws + woff[r]);
@@ -351,19 +381,15 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
             unpack_b<false>(&braw[b][0], wave, l16, grp, bf, d);
         else
             unpack_b<true>(&braw[b][0], wave, l16, grp, bf, d);
-        // products in two rounds of 8 with independent result registers, then the scaled sums.
-        // B holds the codes c; sum_k a_k (c_k - 8) = sum_k a_k c_k + sum_k a_k (-8), and the
-        // second term (one product per row block) enters as the accumulator input.
-        const bf16x8 neg8 = __builtin_bit_cast(bf16x8, (u32x4v)0xC100C100u);
+        // products in two rounds of 8 with independent result registers, then the scaled sums
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f32x4v t[2][4];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const f32x4v c8 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[2 * h + i], neg8, (f32x4v)0.0f, 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    t[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[2 * h + i], bf[j], c8, 0, 0, 0);
+                    t[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[2 * h + i], bf[j], (f32x4v)0.0f, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -405,6 +431,7 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
         __syncthreads();
     }
     if (wave == 0) {
+        const bool gelu = MODE == T_GELU_OUT && !part;   // uniform over the workgroup
         float *const dst = part ? part + (size_t)blockIdx.z * m * n : y;
         // D layout of a 16x16 block: lane holds rows 4*(lane/16) .. +3 of column lane%16
 #pragma unroll
@@ -415,16 +442,23 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = m0 + 16 * i + 4 * grp + r;
-                    if (row < m && col < n)
-                        dst[(size_t)row * n + col] = acc[i][j][r];
+                    if (row < m && col < n) {
+                        if (gelu)
+                            store_gelu_pair(hl, n, row, col, acc[i][j][r]);
+                        else
+                            dst[(size_t)row * n + col] = acc[i][j][r];
+                    }
                 }
             }
     }
 }
 
-// y = sum over z of part[z] (count values per slice), slices added in order z = 0, 1, ...
+// y = sum over z of part[z] (count values per slice, rows of n), slices added in order z = 0, 1,
+// ...; GELU: GELU pairs of the sums go to hl instead (store_gelu_pair).
+template <bool GELU>
 __global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__restrict__ part, float *__restrict__ y,
-                                                             int64_t count, int slices, bool vec4)
+                                                             uint16_t *__restrict__ hl, int64_t count, int n,
+                                                             int slices, bool vec4)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (vec4) {
@@ -434,19 +468,30 @@ __global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__rest
         f32x4v a = *reinterpret_cast<const f32x4v *>(part + i);
         for (int z = 1; z < slices; ++z)
             a += *reinterpret_cast<const f32x4v *>(part + (size_t)z * count + i);
-        *reinterpret_cast<f32x4v *>(y + i) = a;
+        if constexpr (GELU) {
+            const int64_t row = i / n;
+            const int col = (int)(i - row * n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                store_gelu_pair(hl, n, row, col + e, a[e]);
+        } else {
+            *reinterpret_cast<f32x4v *>(y + i) = a;
+        }
     } else {
         if (t >= count)
             return;
         float a = part[t];
         for (int z = 1; z < slices; ++z)
             a += part[(size_t)z * count + t];
-        y[t] = a;
+        if constexpr (GELU)
+            store_gelu_pair(hl, n, t / n, (int)(t % n), a);
+        else
+            y[t] = a;
     }
 }
 
-// K values with a compiled stage sequence (the encoder's widths)
-static bool tiled_k(int64_t k) { return k == 1280 || k == 5120; }
+// K values with a compiled stage sequence (the encoder's widths and the decoder's)
+static bool tiled_k(int64_t k) { return k == 1280 || k == 3072 || k == 5120; }
 
 // Whether the tiled kernel runs (given 16-byte aligned operands): a compiled K, offsets that fit
 // 32 bits, and either a long K or an output past about 48 x 1280 values - measured on MI355X at
@@ -459,20 +504,25 @@ static bool tiled_shape(int64_t m, int64_t n, int64_t k)
 }
 
 // K slices for the tiled kernel (measured on MI355X at the encoder's shapes): none once the
-// output tiles alone give 160 workgroups; for 20 stages, the fewest slices that reach 160
-// workgroups (at least two stages each); for 5 stages, one stage per workgroup when there are at
-// most 40 tiles, else none.  The slices' partial tiles are added by q4_gemm_reduce_kernel.
+// output tiles alone give 160 workgroups; for 12 or 20 stages, the fewest slices (dividing the
+// stages, at least two stages each) that reach 160 workgroups, else the most; for 5 stages, one
+// stage per workgroup when there are at most 40 tiles, else none.  The slices' partial tiles are
+// added by q4_gemm_reduce_kernel.
 static int tiled_slices(int64_t m, int64_t n, int64_t k)
 {
     const int64_t tiles = ((n + GT_BN - 1) / GT_BN) * ((m + GT_BM - 1) / GT_BM);
     const int nst = (int)(k / 256);
     if (tiles >= 160)
         return 1;
-    if (nst >= 20) {
-        for (int ks : {2, 4, 5, 10})
-            if (nst % ks == 0 && tiles * ks >= 160)
-                return ks;
-        return 10;
+    if (nst >= 10) {
+        int most = 1;
+        for (int ks = 2; 2 * ks <= nst; ++ks)
+            if (nst % ks == 0) {
+                if (tiles * ks >= 160)
+                    return ks;
+                most = ks;
+            }
+        return most;
     }
     return tiles <= 40 ? nst : 1;
 }
@@ -482,39 +532,48 @@ static size_t tiled_workspace(int64_t m, int64_t n, int slices)
     return slices > 1 ? (size_t)slices * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
-template <int S>
-static void launch_tiled_slices(const void *w, const uint16_t *x, float *y, float *part, int m, int n, int k,
-                                int slices, hipStream_t s)
+template <int S, int MODE>
+static void launch_tiled_slices(const void *w, const uint16_t *x, float *y, uint16_t *hl, float *part, int m, int n,
+                                int k, int slices, hipStream_t s)
 {
     const dim3 grid((unsigned)((n + GT_BN - 1) / GT_BN), (unsigned)((m + GT_BM - 1) / GT_BM), (unsigned)slices);
-    hipLaunchKernelGGL(q4_gemm_tiled_kernel<S>, grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y, part, m, n,
-                       k);
+    hipLaunchKernelGGL((q4_gemm_tiled_kernel<S, MODE>), grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y, hl,
+                       part, m, n, k);
 }
 
-// part: slices x m x n floats when slices > 1, else null (the kernel then writes y)
-static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, float *part, int m, int n, int k,
-                             int slices, hipStream_t s)
+// Output: y (fp32), or for T_GELU_OUT GELU pairs in hl (n a multiple of 256).  part: slices x m x n
+// floats when slices > 1, else null (the kernel then writes the output itself).  k: the
+// activations' row length.
+template <int MODE>
+static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_t *hl, float *part, int m, int n,
+                             int k, int slices, hipStream_t s)
 {
-    if ((slices > 1) != (part != nullptr))
-        return fail(VOX_E_INVAL, "vox_q4_gemm: partial-tile buffer must be set exactly when K is split");
+    constexpr bool gelu = MODE == T_GELU_OUT;
+    if ((slices > 1) != (part != nullptr) || (gelu ? (hl == nullptr || n % 256) : y == nullptr))
+        return fail(VOX_E_INVAL, "q4 tiled product: one output, and a partial-tile buffer exactly when K is split");
     switch ((k / 256) / slices) {   // stages per workgroup
-    case 20: launch_tiled_slices<20>(w, x, y, part, m, n, k, slices, s); break;
-    case 10: launch_tiled_slices<10>(w, x, y, part, m, n, k, slices, s); break;
-    case 5: launch_tiled_slices<5>(w, x, y, part, m, n, k, slices, s); break;
-    case 4: launch_tiled_slices<4>(w, x, y, part, m, n, k, slices, s); break;
-    case 2: launch_tiled_slices<2>(w, x, y, part, m, n, k, slices, s); break;
-    case 1: launch_tiled_slices<1>(w, x, y, part, m, n, k, slices, s); break;
-    default: return fail(VOX_E_UNSUPPORTED, "vox_q4_gemm: no compiled stage count for k=%d in %d slices", k, slices);
+    case 24: launch_tiled_slices<24, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 20: launch_tiled_slices<20, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 12: launch_tiled_slices<12, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 10: launch_tiled_slices<10, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 8: launch_tiled_slices<8, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 6: launch_tiled_slices<6, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 5: launch_tiled_slices<5, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 4: launch_tiled_slices<4, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 3: launch_tiled_slices<3, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 2: launch_tiled_slices<2, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 1: launch_tiled_slices<1, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    default: return fail(VOX_E_UNSUPPORTED, "q4 tiled product: no compiled stage count for k=%d in %d slices", k, slices);
     }
-    int st = check_launch("vox_q4_gemm tiled");
+    int st = check_launch("q4 tiled product");
     if (st || slices == 1)
         return st;
     const int64_t count = (int64_t)m * n;
-    const bool vec4 = count % 4 == 0 && aligned(y, 16);
+    const bool vec4 = count % 4 == 0 && (gelu ? n % 4 == 0 : aligned(y, 16));
     const int64_t threads = vec4 ? count / 4 : count;
-    hipLaunchKernelGGL(q4_gemm_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, y,
-                       count, slices, vec4);
-    return check_launch("vox_q4_gemm reduce");
+    hipLaunchKernelGGL(q4_gemm_reduce_kernel<gelu>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part,
+                       y, hl, count, n, slices, vec4);
+    return check_launch("q4 tiled product: slice sum");
 }
 
 template <int MI, int NJ>
@@ -567,10 +626,90 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
                      overlaps(workspace, need, x_bf16, xbytes) || overlaps(workspace, need, w_q4, wbytes)))
             return fail(VOX_E_INVAL, "vox_q4_gemm: workspace must be 16-byte aligned and apart from x, y and w");
         // the partial tiles go to the workspace only when K is split; one slice writes y
-        st = launch_gemm_tiled(w_q4, x_bf16, y, slices > 1 ? (float *)workspace : nullptr, (int)m, (int)n, (int)k,
-                               slices, s);
+        st = launch_gemm_tiled<T_PLAIN>(w_q4, x_bf16, y, nullptr, slices > 1 ? (float *)workspace : nullptr, (int)m,
+                                        (int)n, (int)k, slices, s);
     } else {
         st = launch_gemm<1, 1>(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
     }
+    return st ? st : ok();
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Adapter: Y = GELU(X W1^T) W2^T.  Workspace: the GELU pairs H [m][2 n_mid] bf16 (rounded up to
+// 256 bytes), then the partial tiles of whichever product splits K (the two products run one
+// after the other on the stream, so they share that region).
+// ---------------------------------------------------------------------------------------
+namespace vox {
+
+static size_t adapter_h_bytes(int64_t m, int64_t n_mid)
+{
+    return ((size_t)m * (size_t)n_mid * 4 + 255) & ~(size_t)255;
+}
+
+static size_t adapter_part_bytes(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
+{
+    const size_t a = tiled_workspace(m, n_mid, tiled_slices(m, n_mid, k));
+    const size_t b = tiled_workspace(m, n_out, tiled_slices(m, n_out, 2 * n_mid));
+    return a > b ? a : b;
+}
+
+// shapes the adapter runs: compiled stage sequences for K = k and 2 n_mid, 32-bit operand
+// offsets, grid rows
+static bool adapter_shape(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
+{
+    return tiled_k(k) && (n_mid == 1280 || n_mid == 3072) && m <= 65535LL * GT_BM && n_out <= (1 << 24) &&
+           (uint64_t)m * (uint64_t)k < (1ull << 31) && (uint64_t)m * (uint64_t)(2 * n_mid) < (1ull << 31) &&
+           (uint64_t)n_out * (uint64_t)(n_mid / 32) * 18 < (1ull << 31);
+}
+
+}  // namespace vox
+
+extern "C" size_t vox_adapter_workspace(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
+{
+    if (m <= 0 || n_out <= 0 || !adapter_shape(m, k, n_mid, n_out))
+        return 0;
+    return adapter_h_bytes(m, n_mid) + adapter_part_bytes(m, k, n_mid, n_out);
+}
+
+extern "C" int vox_adapter(const void *w1_q4, const void *w2_q4, const uint16_t *x_bf16, float *y, int64_t m,
+                           int64_t k, int64_t n_mid, int64_t n_out, void *workspace, size_t workspace_bytes,
+                           void *stream)
+{
+    if (m < 0 || n_out < 0 || k <= 0 || k % 32 || n_mid <= 0 || n_mid % 32)
+        return fail(VOX_E_INVAL,
+                    "vox_adapter: need m, n_out >= 0 and k, n_mid positive multiples of 32 (m=%lld k=%lld n_mid=%lld "
+                    "n_out=%lld)",
+                    (long long)m, (long long)k, (long long)n_mid, (long long)n_out);
+    if (m == 0 || n_out == 0)
+        return ok();
+    if (!adapter_shape(m, k, n_mid, n_out))
+        return fail(VOX_E_UNSUPPORTED,
+                    "vox_adapter: k must be 1280, 3072 or 5120, n_mid 1280 or 3072, and the operands within 2^31 "
+                    "elements (k=%lld n_mid=%lld m=%lld)",
+                    (long long)k, (long long)n_mid, (long long)m);
+    if (!w1_q4 || !w2_q4 || !x_bf16 || !y || !workspace)
+        return fail(VOX_E_INVAL, "vox_adapter: null pointer");
+    if (!aligned(x_bf16, 16) || !aligned(w1_q4, 16) || !aligned(w2_q4, 16))
+        return fail(VOX_E_UNSUPPORTED, "vox_adapter: x, w1 and w2 must be 16-byte aligned");
+    const size_t need = vox_adapter_workspace(m, k, n_mid, n_out);
+    if (workspace_bytes < need)
+        return fail(VOX_E_WORKSPACE, "vox_adapter: workspace of %zu bytes, need %zu", workspace_bytes, need);
+    const size_t xbytes = (size_t)m * k * 2, ybytes = (size_t)m * n_out * 4;
+    const size_t w1bytes = (size_t)n_mid * (k / 32) * 18, w2bytes = (size_t)n_out * (n_mid / 32) * 18;
+    if (!aligned(workspace, 16) || overlaps(workspace, need, x_bf16, xbytes) || overlaps(workspace, need, y, ybytes) ||
+        overlaps(workspace, need, w1_q4, w1bytes) || overlaps(workspace, need, w2_q4, w2bytes))
+        return fail(VOX_E_INVAL, "vox_adapter: workspace must be 16-byte aligned and apart from x, y and the weights");
+    if (overlaps(y, ybytes, x_bf16, xbytes) || overlaps(y, ybytes, w1_q4, w1bytes) || overlaps(y, ybytes, w2_q4, w2bytes))
+        return fail(VOX_E_INVAL, "vox_adapter: y overlaps an input");
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t *h = (uint16_t *)workspace;
+    float *part = (float *)((char *)workspace + adapter_h_bytes(m, n_mid));
+    const int s1 = tiled_slices(m, n_mid, k), s2 = tiled_slices(m, n_out, 2 * n_mid);
+    int st = launch_gemm_tiled<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, s1 > 1 ? part : nullptr, (int)m, (int)n_mid,
+                                           (int)k, s1, s);
+    if (!st)
+        st = launch_gemm_tiled<T_PAIR_IN>(w2_q4, h, y, nullptr, s2 > 1 ? part : nullptr, (int)m, (int)n_out,
+                                          (int)(2 * n_mid), s2, s);
     return st ? st : ok();
 }

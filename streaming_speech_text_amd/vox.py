@@ -53,6 +53,8 @@ _SIGS = {
     "vox_q4_gemv": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "vox_q4_gemm_workspace": (_sz, [_i64, _i64, _i64]),
     "vox_q4_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "vox_adapter_workspace": (_sz, [_i64, _i64, _i64, _i64]),
+    "vox_adapter": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     "vox_gqa_decode_attn_workspace": (_sz, [_int, _int, _int, _int]),
     "vox_gqa_decode_attn": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _f32, _vp, _sz, _vp]),
     "vox_decoder_workspace": (_int, [C.POINTER(DecoderConfig), C.POINTER(_sz), C.POINTER(_sz)]),
@@ -147,6 +149,25 @@ def q4_gemm(w_q4, x_bf16, y, m=None, n=None, k=None, workspace=None, stream=None
     _check(lib().vox_q4_gemm(_ptr(w_q4, torch.uint8, "w_q4"), _ptr(x_bf16, xdt, "x_bf16"),
                              _ptr(y, torch.float32, "y"), m, n, k,
                              _ptr(workspace, None, "workspace") if wsb else None, wsb, _stream(stream)))
+
+
+def adapter_workspace(m, k, n_mid, n_out) -> int:
+    return int(lib().vox_adapter_workspace(m, k, n_mid, n_out))
+
+
+def adapter(w1_q4, w2_q4, x_bf16, y, workspace, m=None, k=None, n_mid=None, n_out=None, stream=None):
+    """Y = GELU(X W1^T) W2^T; workspace: a device buffer of at least adapter_workspace(m, k, n_mid, n_out)
+    bytes."""
+    if m is None or k is None:
+        m, k = x_bf16.shape
+    n_out = y.shape[-1] if n_out is None else n_out
+    if n_mid is None:
+        n_mid = w1_q4.numel() // ((k // 32) * 18)
+    xdt = torch.uint16 if x_bf16.dtype == torch.uint16 else torch.bfloat16
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().vox_adapter(_ptr(w1_q4, torch.uint8, "w1_q4"), _ptr(w2_q4, torch.uint8, "w2_q4"),
+                             _ptr(x_bf16, xdt, "x_bf16"), _ptr(y, torch.float32, "y"), m, k, n_mid, n_out,
+                             _ptr(workspace, None, "workspace"), wsb, _stream(stream)))
 
 
 def gqa_decode_attn_workspace(n_q_heads, n_kv_heads, head_dim, n_slots) -> int:

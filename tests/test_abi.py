@@ -24,8 +24,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     fns = header_functions()
-    for name in ("vox_q4_dequant", "vox_q4_gemv", "vox_q4_gemm", "vox_q4_gemm_workspace", "vox_gqa_decode_attn", "vox_gqa_decode_attn_workspace",
-                 "vox_decoder_step", "vox_decoder_create", "vox_decoder_workspace", "vox_strerror", "vox_last_error"):
+    for name in ("vox_q4_dequant", "vox_q4_gemv", "vox_q4_gemm", "vox_q4_gemm_workspace", "vox_gqa_decode_attn",
+                 "vox_gqa_decode_attn_workspace", "vox_adapter", "vox_adapter_workspace", "vox_decoder_step",
+                 "vox_decoder_create", "vox_decoder_workspace", "vox_strerror", "vox_last_error"):
         assert name in fns
 
 
@@ -68,6 +69,22 @@ def test_validation_before_device_work(lib):
     assert lib.vox_q4_gemm_workspace(64, 1280, 5120) > 0
     assert lib.vox_q4_gemm_workspace(750, 5120, 1280) == 0
     assert lib.vox_q4_gemm_workspace(4, 4, 48) == 0
+    # adapter: workspace holds the GELU pairs (2 x bf16 per value) plus the larger product's partials
+    assert lib.vox_adapter_workspace(16, 5120, 3072, 3072) >= 16 * 3072 * 4
+    assert lib.vox_adapter_workspace(16, 5120, 3072, 3072) % 16 == 0
+    assert lib.vox_adapter_workspace(16, 4096, 3072, 3072) == 0       # k without compiled stages
+    assert lib.vox_adapter_workspace(16, 5120, 5120, 3072) == 0       # n_mid without compiled stages
+    assert lib.vox_adapter_workspace(0, 5120, 3072, 3072) == 0
+    big = C.c_void_p(0x10000000)
+    aw = lib.vox_adapter_workspace(4, 1280, 1280, 64)
+    assert lib.vox_adapter(p, p, p, p, 4, 48, 1280, 64, big, aw, None) == vox.VOX_E_INVAL          # k % 32
+    assert lib.vox_adapter(p, p, p, p, 4, 1280, 1280, 0, big, aw, None) == vox.VOX_OK              # empty
+    assert lib.vox_adapter(p, p, p, p, 4, 1024, 1280, 64, big, aw, None) == vox.VOX_E_UNSUPPORTED  # k
+    assert lib.vox_adapter(p, p, p, p, 4, 1280, 1280, 64, None, 0, None) == vox.VOX_E_INVAL        # no workspace
+    assert lib.vox_adapter(C.c_void_p(0x1008), p, p, big, 4, 1280, 1280, 64, big, aw, None) == \
+        vox.VOX_E_UNSUPPORTED                                                                       # alignment
+    assert lib.vox_adapter(p, C.c_void_p(0x200000), C.c_void_p(0x400000), C.c_void_p(0x800000), 4, 1280, 1280, 64,
+                           big, aw - 16, None) == vox.VOX_E_WORKSPACE
     ws = lib.vox_gqa_decode_attn_workspace(32, 8, 128, 8192)
     assert ws > 0 and lib.vox_gqa_decode_attn_workspace(32, 8, 64, 8192) == 0
     args = (p, C.c_void_p(0x200000), C.c_void_p(0x400000), C.c_void_p(0x800000))

@@ -76,7 +76,8 @@ def test_gemm_small_workspace(vx):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1280, 1280), (17, 100, 96), (63, 65, 32), (65, 1000, 5120), (130, 64, 2080),
                                    (3, 5, 64), (97, 77, 1280), (751, 130, 5120), (40, 1280, 5120), (49, 1283, 5120),
-                                   (129, 1283, 1280)])
+                                   (129, 1283, 1280), (200, 3072, 3072), (64, 1280, 3072), (100, 3072, 3072),
+                                   (70, 1100, 3072)])
 def test_gemm_ragged(vx, orc, m, n, k):
     w, xb = synth.gemm_inputs(600 + m, m, n, k)
     say(f"gemm ragged m={m} n={n} k={k}")
