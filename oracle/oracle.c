@@ -207,6 +207,40 @@ void orc_adapter(const uint8_t *w1, const uint8_t *w2, const uint16_t *x_bf16, d
 }
 
 /* ------------------------------------------------------------------------------------
+ * Encoder self-attention over a chunk ([VC] section 모델 아키텍처: the audio encoder is a causal
+ * transformer, 1280 wide, 32 heads, window 750; section 주요 기능: the encoder runs over chunks of
+ * the audio).  READINGS: the window counts the query's own position (a query at position p sees
+ * keys p - window + 1 .. p); scores are scaled by 1/sqrt(head_dim); positions are already in q and
+ * k when they arrive (nothing positional inside the operation); keys before the chunk come from the
+ * previous chunks' K/V.
+ * Layout: q [m][n_heads*head_dim] holds the chunk's queries; k, v [n_ctx + m][n_heads*head_dim]
+ * hold n_ctx earlier positions followed by the chunk's own, so query i is at row n_ctx + i of k.
+ * out [m][n_heads*head_dim].
+ * ---------------------------------------------------------------------------------- */
+void orc_enc_attn(const double *q, const double *k, const double *v, int64_t m, int64_t n_ctx,
+                  int64_t n_heads, int64_t head_dim, int64_t window, double scale, double *out)
+{
+    const int64_t width = n_heads * head_dim;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int64_t i = 0; i < m; i++)
+        for (int64_t h = 0; h < n_heads; h++) {
+            const int64_t last = n_ctx + i;                          /* the query's own row */
+            const int64_t first = last - window + 1 > 0 ? last - window + 1 : 0;
+            const int64_t len = last - first + 1;
+            double *p = (double *)malloc(sizeof(double) * (size_t)len);
+            orc_attn_probs(q + i * width + h * head_dim, k + first * width + h * head_dim, len, head_dim,
+                           width, scale, p);
+            for (int64_t d = 0; d < head_dim; d++) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < len; t++)
+                    acc += p[t] * v[(first + t) * width + h * head_dim + d];
+                out[i * width + h * head_dim + d] = acc;
+            }
+            free(p);
+        }
+}
+
+/* ------------------------------------------------------------------------------------
  * Decoder pieces.  [VC] section 모델 아키텍처: the LLM decoder is a 26-layer transformer
  * "based on Ministral-3" with GQA (32 heads / 8 KV heads).  READING: a Llama-style
  * pre-norm block - RMSNorm, attention with rotary positions, residual add, RMSNorm,

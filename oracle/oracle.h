@@ -36,6 +36,10 @@ void orc_gelu_array(const double *x, int64_t n, double *out);
 void orc_adapter(const uint8_t *w1, const uint8_t *w2, const uint16_t *x_bf16, double *y, int64_t m,
                  int64_t k, int64_t n_mid, int64_t n_out);
 
+/* Encoder self-attention over a chunk (causal, sliding window) */
+void orc_enc_attn(const double *q, const double *k, const double *v, int64_t m, int64_t n_ctx,
+                  int64_t n_heads, int64_t head_dim, int64_t window, double scale, double *out);
+
 /* Decoder pieces */
 void orc_rmsnorm(const double *x, const float *g, int64_t dim, double eps, double *out);
 void orc_rope(double *x, int64_t n_heads, int64_t head_dim, int64_t pos, double theta);

@@ -56,6 +56,7 @@ def lib():
             "orc_swiglu": [_vp, _vp, _i64, _vp],
             "orc_gelu_array": [_vp, _i64, _vp],
             "orc_adapter": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64],
+            "orc_enc_attn": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _dbl, _vp],
             "orc_decoder_destroy": [_vp],
             "orc_decoder_reset": [_vp],
         }.items():
@@ -213,6 +214,22 @@ def adapter(w1, w2, x_bf16) -> np.ndarray:
     y = np.empty((m, n_out), np.float64)
     lib().orc_adapter(_p(w1), _p(w2), _p(x), _p(y), m, k, n_mid, n_out)
     return y
+
+
+def enc_attn(q, k, v, n_heads, window, scale=None) -> np.ndarray:
+    """q: [m, n_heads*hd]; k, v: [n_ctx + m, n_heads*hd] (query i at row n_ctx + i)
+    -> out [m, n_heads*hd] (float64).  scale defaults to 1/sqrt(hd)."""
+    q = _c(q, np.float64)
+    k = _c(k, np.float64)
+    v = _c(v, np.float64)
+    m, width = q.shape
+    n_ctx = k.shape[0] - m
+    hd = width // n_heads
+    if scale is None:
+        scale = 1.0 / np.sqrt(hd)
+    out = np.empty((m, width), np.float64)
+    lib().orc_enc_attn(_p(q), _p(k), _p(v), m, n_ctx, n_heads, hd, window, float(scale), _p(out))
+    return out
 
 
 def argmax_f32(v) -> int:

@@ -109,6 +109,11 @@ LAYER_LINEARS = {
 ENCODER_LINEARS = [("q", 1280, 1280), ("k", 1280, 1280), ("v", 1280, 1280), ("o", 1280, 1280),
                    ("ffn_up", 5120, 1280), ("ffn_down", 1280, 5120)]
 ENCODER_M = (16, 64, 200, 750)
+# Encoder self-attention: 32 heads over the 1280 width (head size 40), causal with a window of 750
+# positions (voxtral.c page, section 모델 아키텍처).  A chunk of M frames attends over its own rows
+# and the window's worth of earlier rows, 749 of them once the stream is past its start.
+ENC_HEADS, ENC_WINDOW = 32, 750
+ENC_HEAD_DIM = ENCODER_LINEARS[0][1] // ENC_HEADS
 # Adapter (in, mid, out): a linear 5120 -> 3072, GELU, a linear 3072 -> 3072 (voxtral.c page,
 # section 모델 아키텍처).  It reads the encoder output four frames to a row (4 x 1280 = 5120), so an
 # encoder chunk of M frames gives M / 4 adapter rows.
@@ -116,7 +121,7 @@ ADAPTER = (5120, 3072, 3072)
 ADAPTER_M = tuple(m // 4 for m in ENCODER_M)
 
 # Seeds: one per workload.
-SEED_GEMV, SEED_LAYER, SEED_ATTN, SEED_DECODER, SEED_GEMM, SEED_ADAPTER = 1, 2, 3, 4, 5, 6
+SEED_GEMV, SEED_LAYER, SEED_ATTN, SEED_DECODER, SEED_GEMM, SEED_ADAPTER, SEED_ENC_ATTN = 1, 2, 3, 4, 5, 6, 7
 
 
 def gemv_inputs(seed: int, n: int, k: int):
@@ -133,6 +138,13 @@ def adapter_inputs(seed: int, m: int, k: int, n_mid: int, n_out: int):
     """(W1 q4 [n_mid, k/32*18], W2 q4 [n_out, n_mid/32*18], X bf16 bits [m, k])."""
     return (q4_matrix(generator(seed, 0, n_mid, k), n_mid, k), q4_matrix(generator(seed, 1, n_out, n_mid), n_out, n_mid),
             bf16_normal(generator(seed, 2, m, k), (m, k)))
+
+
+def enc_attention_inputs(seed: int, m: int, n_ctx: int, width: int = 1280):
+    """(q [m, width], k [n_ctx + m, width], v [n_ctx + m, width]) fp32 N(0, 1); row n_ctx + i of k
+    and v belongs to query i."""
+    return (normal_f32(generator(seed, 0, m, n_ctx), (m, width)), normal_f32(generator(seed, 1, m, n_ctx), (n_ctx + m, width)),
+            normal_f32(generator(seed, 2, m, n_ctx), (n_ctx + m, width)))
 
 
 def attention_inputs(seed: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_slots: int):

@@ -571,3 +571,99 @@ def test_page_figures_pin_adapter_shape():
     assert synth.ADAPTER == (fig["in"], fig["mid"], fig["out"])
     # four encoder frames of width 1280 make one adapter row
     assert fig["in"] == 4 * json.load(open(os.path.join(GOLDEN, "page_figures.json")))["encoder"]["dim"]
+
+
+# ---------------------------------------------------------------------------------------
+# encoder self-attention over a chunk: causal, sliding window
+# ---------------------------------------------------------------------------------------
+
+def _sdpa_masked(q, k, v, n_heads, n_ctx, window):
+    """torch float64 SDPA with an explicit boolean mask built from positions."""
+    m, width = q.shape
+    hd = width // n_heads
+    T = k.shape[0]
+    qh = torch.from_numpy(q).reshape(m, n_heads, hd).transpose(0, 1)
+    kh = torch.from_numpy(k).reshape(T, n_heads, hd).transpose(0, 1)
+    vh = torch.from_numpy(v).reshape(T, n_heads, hd).transpose(0, 1)
+    qpos = n_ctx + np.arange(m)[:, None]
+    kpos = np.arange(T)[None, :]
+    mask = torch.from_numpy((kpos <= qpos) & (kpos > qpos - window))
+    o = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask)
+    return o.transpose(0, 1).reshape(m, width).numpy()
+
+
+def test_enc_attn_causal_matches_sdpa(orc):
+    # no earlier rows and a window past the chunk: plain causal attention
+    g = synth.generator(40)
+    m, H, hd = 37, 4, 40
+    q, k, v = (g.standard_normal((m, H * hd)) for _ in range(3))
+    got = orc.enc_attn(q, k, v, H, window=1000)
+    qh = torch.from_numpy(q).reshape(m, H, hd).transpose(0, 1)
+    kh = torch.from_numpy(k).reshape(m, H, hd).transpose(0, 1)
+    vh = torch.from_numpy(v).reshape(m, H, hd).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(qh, kh, vh, is_causal=True).transpose(0, 1).reshape(m, H * hd).numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_enc_attn_sliding_window_matches_masked_sdpa(orc):
+    g = synth.generator(41)
+    for m, n_ctx, window in [(20, 9, 10), (5, 30, 7), (16, 0, 4), (33, 12, 13)]:
+        H, hd = 3, 40
+        q = g.standard_normal((m, H * hd))
+        k, v = (g.standard_normal((n_ctx + m, H * hd)) for _ in range(2))
+        got = orc.enc_attn(q, k, v, H, window)
+        assert np.allclose(got, _sdpa_masked(q, k, v, H, n_ctx, window), rtol=1e-12, atol=1e-12)
+
+
+def test_enc_attn_special_cases(orc):
+    g = synth.generator(42)
+    m, n_ctx, H, hd = 9, 6, 2, 40
+    q = g.standard_normal((m, H * hd))
+    k, v = (g.standard_normal((n_ctx + m, H * hd)) for _ in range(2))
+    # a window of one position: each query returns its own value row
+    assert np.allclose(orc.enc_attn(q, k, v, H, 1), v[n_ctx:], rtol=0, atol=1e-15)
+    # equal keys: the mean of the values in the window (first = max(0, n_ctx + i - window + 1))
+    w = 4
+    kc = np.tile(k[:1], (n_ctx + m, 1))
+    got = orc.enc_attn(q, kc, v, H, w)
+    ref = np.stack([v[max(0, n_ctx + i - w + 1):n_ctx + i + 1].mean(axis=0) for i in range(m)])
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+    # values of ones give ones (weights sum to one)
+    assert np.allclose(orc.enc_attn(q, k, np.ones_like(v), H, 5), 1.0, rtol=0, atol=1e-14)
+    # the window edge matters: widening it by one changes every query that had a full window
+    a, b = orc.enc_attn(q, k, v, H, 5), orc.enc_attn(q, k, v, H, 6)
+    full = [i for i in range(m) if n_ctx + i >= 5]
+    assert all(not np.allclose(a[i], b[i]) for i in full)
+    # heads are independent: changing head 1's keys leaves head 0's output alone
+    k2 = k.copy()
+    k2[:, hd:] += g.standard_normal((n_ctx + m, hd))
+    c = orc.enc_attn(q, k2, v, H, 5)
+    assert np.array_equal(c[:, :hd], a[:, :hd]) and not np.allclose(c[:, hd:], a[:, hd:])
+    # adding the same vector to every key of a head shifts each query's scores by a constant: no change
+    k3 = k.copy()
+    k3[:, hd:] += g.standard_normal(hd)
+    assert np.allclose(orc.enc_attn(q, k3, v, H, 5), a, rtol=1e-12, atol=1e-12)
+
+
+def test_enc_attn_bruteforce_tiny(orc):
+    g = synth.generator(43)
+    m, n_ctx, H, hd, w = 4, 3, 2, 40, 5
+    q = g.standard_normal((m, H * hd))
+    k, v = (g.standard_normal((n_ctx + m, H * hd)) for _ in range(2))
+    ref = np.zeros((m, H * hd))
+    for i in range(m):
+        for h in range(H):
+            rows = [j for j in range(n_ctx + m) if n_ctx + i - w < j <= n_ctx + i]
+            s = [sum(q[i, h * hd + d] * k[j, h * hd + d] for d in range(hd)) / math.sqrt(hd) for j in rows]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            for d in range(hd):
+                ref[i, h * hd + d] = sum(e[t] / z * v[j, h * hd + d] for t, j in enumerate(rows))
+    assert np.allclose(orc.enc_attn(q, k, v, H, w), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_page_figures_pin_encoder_attention():
+    enc = json.load(open(os.path.join(GOLDEN, "page_figures.json")))["encoder"]
+    assert (synth.ENC_HEADS, synth.ENC_WINDOW) == (enc["n_heads"], enc["window"])
+    assert synth.ENC_HEADS * synth.ENC_HEAD_DIM == enc["dim"]
