@@ -127,7 +127,8 @@ def timed(torch, stream, launch, copies, reps, replays=5):
 def kernels_leg(torch, synth, vox, dev, stream):
     """Per-kernel device times of the workloads beside the decoder step: the single 3072x3072
     GEMV, one decoder layer's linears, GQA attention at three ring fills, the encoder-chunk
-    GEMM set, the adapter.  Every measurement rotates over more than 1 GiB of distinct copies."""
+    GEMM set, the encoder's chunk attention, the adapter.  Every measurement rotates over more than
+    1 GiB of distinct copies."""
     GiB = 2 ** 30
     out = []
 
@@ -196,6 +197,33 @@ def kernels_leg(torch, synth, vox, dev, stream):
               "tflops": round(flops / us / 1e6, 2), "frac_mfma_bf16": round(flops / us / 1e6 / 2500.0, 4),
               "bytes": b, "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
         del wdev
+        torch.cuda.empty_cache()
+
+    # encoder self-attention over a chunk (32 heads x 40, window 750, a full window of earlier rows)
+    H, W = synth.ENC_HEADS, synth.ENC_WINDOW
+    hd, n_ctx = synth.ENC_HEAD_DIM, synth.ENC_WINDOW - 1
+    for m in synth.ENCODER_M:
+        q, k, v = synth.enc_attention_inputs(synth.SEED_ENC_ATTN, m, n_ctx)
+        per = q.nbytes + k.nbytes + v.nbytes
+        copies = max(2, int(np.ceil(1.1 * GiB / per)))
+        qs = [torch.from_numpy(q).to(dev) for _ in range(copies)]
+        kvs = [(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)) for _ in range(copies)]
+        o = torch.empty(m, H * hd, dtype=torch.float32, device=dev)
+        wsb = vox.enc_attn_workspace(m, n_ctx, H, hd, W)
+        ews = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+        def launch(i):
+            vox._check(vox.lib().vox_enc_attn(vox._ptr(qs[i]), vox._ptr(kvs[i][0]), vox._ptr(kvs[i][1]), vox._ptr(o), m,
+                                              n_ctx, H, hd, W, hd ** -0.5, vox._ptr(ews) if wsb else None, wsb,
+                                              vox._stream(None)))
+        us = timed(torch, stream, launch, copies, 50)
+        keys = sum(min(n_ctx + i + 1, W) for i in range(m))
+        flops = 4 * keys * hd * H          # scores and weighted sums, as defined
+        b = per + o.numel() * 4
+        emit({"kernel": "enc_attn", "case": f"M={m}, {n_ctx} earlier rows", "us": round(us, 3), "flops": flops,
+              "tflops": round(flops / us / 1e6, 2), "frac_mfma_fp32": round(flops / us / 1e6 / 157.3, 4),
+              "bytes": b, "gbs": round(b / us / 1e3, 1)})
+        del qs, kvs
         torch.cuda.empty_cache()
 
     # adapter (linear 5120 -> 3072, GELU, linear 3072 -> 3072) over the rows of one encoder chunk

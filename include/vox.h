@@ -95,6 +95,22 @@ size_t vox_adapter_workspace(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
 int vox_adapter(const void *w1_q4, const void *w2_q4, const uint16_t *x_bf16, float *y, int64_t m, int64_t k,
                 int64_t n_mid, int64_t n_out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Self-attention of the audio encoder over one chunk of frames ([VC] 모델 아키텍처: causal
+ * transformer, 32 heads over width 1280, window 750; [VC] 주요 기능: the encoder runs over chunks).
+ * q: m rows of n_heads * head_dim fp32 (the chunk's queries, heads side by side as a linear writes
+ * them); k, v: n_ctx + m rows of the same width, the n_ctx positions before the chunk followed by
+ * the chunk's own, so query i sits at row n_ctx + i; out: m rows like q.  Per head h and query i:
+ *   s_j = scale * <q_i, k_j> for n_ctx + i - window + 1 <= j <= n_ctx + i (and j >= 0),
+ *   out_i = sum_j softmax(s)_j v_j.
+ * fp32 throughout (fp32 matrix cores).  workspace: vox_enc_attn_workspace(...) bytes of device
+ * memory, 16-byte aligned, apart from the other buffers (0 bytes -> may be NULL), contents
+ * irrelevant.  m == 0 is a no-op.  head_dim not a multiple of 4 or above 48 ->
+ * VOX_E_UNSUPPORTED; q, k not 16-byte aligned -> VOX_E_UNSUPPORTED; out overlapping an input ->
+ * VOX_E_INVAL; a smaller workspace -> VOX_E_WORKSPACE. */
+size_t vox_enc_attn_workspace(int64_t m, int64_t n_ctx, int n_heads, int head_dim, int window);
+int vox_enc_attn(const float *q, const float *k, const float *v, float *out, int64_t m, int64_t n_ctx, int n_heads,
+                 int head_dim, int window, float scale, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Grouped-query decode attention of one token over a KV ring ([RS] 아키텍처 and [VC] 모델
  * 아키텍처: query head h reads KV head h / (n_q_heads / n_kv_heads); [VC] 주요 기능: rolling
  * window).  q: [n_q_heads][head_dim]; k_cache, v_cache: [n_kv_heads][n_slots][head_dim];

@@ -1,0 +1,355 @@
+// enc_attn.hip - self-attention of the audio encoder over one chunk of frames: causal, with a
+// sliding window, on the fp32 matrix cores.
+//
+// Pages: the audio encoder is a causal transformer of width 1280 with 32 heads and a window of
+// 750 (voxtral.c page "Mistral Voxtral Realtime 4B 음성 인식 모델의 순수 C 기반 CPU 전용 추론 구현",
+// GeekNews 26608, section 모델 아키텍처), run over chunks of the audio (section 주요 기능).
+//
+// Operation (per head h, query i of the chunk at row n_ctx + i of K and V):
+//   s_j = scale * <q_i, k_j> for j in [n_ctx + i - window + 1, n_ctx + i] (and j >= 0),
+//   out_i = sum_j softmax(s)_j v_j.
+//
+// One wave per (head, 16 queries, key range).  With 16 keys per step the wave computes
+// S^T = K Q^T (16 keys x 16 queries) with v_mfma_f32_16x16x4_f32 over the head size (inputs in
+// any order A and B agree on: lane group g supplies dims 16s + 4g + r in product 4s + r), so each
+// lane ends up holding four keys (4g .. 4g+3) of one query (lane % 16).  That is exactly the
+// layout of the B operand of O^T += V^T P^T, whose k slots are the same keys (product t takes key
+// 4g + t from lane group g), so the probabilities never leave the registers.  Online softmax in
+// base 2 (q pre-scaled by scale * log2 e); the row max is shared by the four lane groups of a
+// query through two lane swaps, the row sums stay per lane until the end.  Keys are read through
+// the cache, the next step's K and V loaded before the current step's products.
+//
+// Short chunks split each wave's key range over the grid's third dimension; partial (max, sum,
+// unnormalised output) go to the workspace and enc_attn_merge_kernel combines them in split order.
+#include <cmath>
+
+#include "vox_common.h"
+#include "vox_host.h"
+
+namespace vox {
+
+typedef float f32x4e __attribute__((ext_vector_type(4)));
+
+constexpr int EA_MAX_HD = 48;                 // head sizes up to 48 (three 16-wide blocks)
+
+struct EncAttnArgs {
+    const float *q, *k, *v;
+    float *out;          // [m][width] when unsplit
+    float *part;         // split: [splits][n_heads][m][hd] unnormalised outputs
+    float *pm, *pl;      // split: [splits][n_heads][m] running max (base 2) and sum
+    int m, n_ctx, n_heads, hd, width, window;
+    int steps_per_split; // 16-key steps per split
+    float qscale;        // scale * log2(e)
+};
+
+__device__ __forceinline__ float xor_max(float v, int mask)
+{
+    return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+// Head size HD (a multiple of 4 up to 48) at compile time.  Score products: the full 16-dim blocks
+// take dims 16s + 4g + r in product (s, r) (a float4 per lane); the last block's HD % 16 dims take
+// dims 16s + 4r + g in product r (one float per lane and product), so no product runs on padding.
+template <int HD>
+__global__ __launch_bounds__(64) void enc_attn_kernel(EncAttnArgs a)
+{
+    constexpr int FULL = HD / 16;             // full 16-dim blocks
+    constexpr int TAILP = (HD % 16) / 4;      // products of the last, partial block
+    constexpr int NDB = (HD + 15) / 16;       // 16-dim output blocks
+    const int h = blockIdx.x;           // head in the fast grid dimension: a head's waves share an XCD
+    const int i0 = blockIdx.y * 16;     // first query of the wave
+    const int z = blockIdx.z;           // key split
+    const int lane = threadIdx.x;
+    const int qi = lane & 15, g = lane >> 4;
+    const int width = a.width;
+    const int iq = min(i0 + qi, a.m - 1);          // this lane's query (clamped; stores are masked)
+    const float *qrow = a.q + (uint32_t)(iq * width + h * HD);
+
+    // B operand of S^T
+    f32x4e qv[FULL > 0 ? FULL : 1];
+    float qt[TAILP > 0 ? TAILP : 1];
+#pragma unroll
+    for (int s = 0; s < FULL; ++s)
+        qv[s] = *reinterpret_cast<const f32x4e *>(qrow + 16 * s + 4 * g) * a.qscale;
+#pragma unroll
+    for (int r = 0; r < TAILP; ++r)
+        qt[r] = qrow[16 * FULL + 4 * r + g] * a.qscale;
+
+    // key range of the wave: union over its queries, then this split's share of 16-key steps
+    const int last_q = min(i0 + 15, a.m - 1);
+    const int jlo = max(0, a.n_ctx + i0 - a.window + 1);
+    const int jhi = a.n_ctx + last_q;                              // inclusive
+    const int steps = (jhi - jlo + 16) / 16;
+    const int st0 = z * a.steps_per_split;
+    const int st1 = min(steps, st0 + a.steps_per_split);
+    // this lane's own query bounds (keys outside them get no weight)
+    const int my_hi = a.n_ctx + i0 + qi, my_lo = my_hi - a.window + 1;
+    const int T = a.n_ctx + a.m;
+    // V operand: dims 16 db + qi (past the head size: read dim 0, weight 0)
+    bool vok[NDB];
+    int voff[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        vok[db] = 16 * db + qi < HD;
+        voff[db] = h * HD + (vok[db] ? 16 * db + qi : 0);
+    }
+
+    f32x4e o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        o[db] = (f32x4e)0.0f;
+    float mrun = -INFINITY, lpart = 0.0f;
+
+    // operand loads of one step: K row kb + qi, V rows kb + 4g + t
+    f32x4e kv[FULL > 0 ? FULL : 1];
+    float kt[TAILP > 0 ? TAILP : 1];
+    float vv[NDB][4];
+    auto load = [&](int st) {
+        const int kb = jlo + 16 * st;
+        const float *krow = a.k + (uint32_t)(min(kb + qi, T - 1) * width + h * HD);
+#pragma unroll
+        for (int s = 0; s < FULL; ++s)
+            kv[s] = *reinterpret_cast<const f32x4e *>(krow + 16 * s + 4 * g);
+#pragma unroll
+        for (int r = 0; r < TAILP; ++r)
+            kt[r] = krow[16 * FULL + 4 * r + g];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float *vrow = a.v + (uint32_t)(min(kb + 4 * g + t, T - 1) * width);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                vv[db][t] = vrow[voff[db]];
+        }
+    };
+
+    if (st0 < st1)
+        load(st0);
+    for (int st = st0; st < st1; ++st) {
+        const int kb = jlo + 16 * st;
+        f32x4e kc[FULL > 0 ? FULL : 1];
+        float ktc[TAILP > 0 ? TAILP : 1];
+        float vc[NDB][4];
+#pragma unroll
+        for (int s = 0; s < FULL; ++s)
+            kc[s] = kv[s];
+#pragma unroll
+        for (int r = 0; r < TAILP; ++r)
+            ktc[r] = kt[r];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                vc[db][t] = vok[db] ? vv[db][t] : 0.0f;
+        if (st + 1 < st1)
+            load(st + 1);
+
+        // S^T block: lane holds keys kb + 4g + r (r = 0..3) of query i0 + qi
+        f32x4e sc = (f32x4e)0.0f;
+#pragma unroll
+        for (int s = 0; s < FULL; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[s][r], qv[s][r], sc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < TAILP; ++r)
+            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(ktc[r], qt[r], sc, 0, 0, 0);
+        // masked scores, block max over the query's four lane groups
+        float sm[4];
+        const int j0 = kb + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sm[r] = (j0 + r >= my_lo && j0 + r <= my_hi) ? sc[r] : -INFINITY;
+        float bmax = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+        bmax = xor_max(bmax, 16);
+        bmax = xor_max(bmax, 32);
+        const float mnew = fmaxf(mrun, bmax);
+        const float ms = mnew == -INFINITY ? 0.0f : mnew;   // nothing live yet: weights stay 0
+        const float c = __builtin_amdgcn_exp2f(mrun - ms);
+        mrun = mnew;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            p[r] = __builtin_amdgcn_exp2f(sm[r] - ms);
+        lpart = lpart * c + (p[0] + p[1]) + (p[2] + p[3]);
+        // O^T += V^T P^T: product t takes key kb + 4g + t from lane group g
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            o[db] *= c;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vc[db][t], p[t], o[db], 0, 0, 0);
+        }
+    }
+
+    // this query's sum over the four lane groups (all share mrun)
+    float l = lpart + __shfl_xor(lpart, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int i = i0 + qi;
+    if (i >= a.m)
+        return;
+    // O^T layout: lane holds dims 16 db + 4g + r of query i0 + qi
+    if (a.part == nullptr) {
+        const float inv = 1.0f / l;
+        float *orow = a.out + (size_t)i * width + (size_t)h * HD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * db + 4 * g + r;
+                if (d < HD)
+                    orow[d] = o[db][r] * inv;
+            }
+    } else {
+        const size_t row = ((size_t)z * a.n_heads + h) * a.m + i;
+        float *prow = a.part + row * HD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * db + 4 * g + r;
+                if (d < HD)
+                    prow[d] = o[db][r];
+            }
+        if (g == 0) {
+            a.pm[row] = mrun;
+            a.pl[row] = l;
+        }
+    }
+}
+
+// out[i][h*hd + d] = sum_z 2^(m_z - M) O_z[d] / sum_z 2^(m_z - M) l_z, splits in order z = 0, 1, ...
+// One thread per output value.
+__global__ __launch_bounds__(256) void enc_attn_merge_kernel(EncAttnArgs a, int splits)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)a.m * a.n_heads * a.hd;
+    if (t >= total)
+        return;
+    const int d = (int)(t % a.hd);
+    const int64_t hi = t / a.hd;           // (i * n_heads + h)
+    const int h = (int)(hi % a.n_heads);
+    const int i = (int)(hi / a.n_heads);
+    float mx = -INFINITY;
+    for (int z = 0; z < splits; ++z)
+        mx = fmaxf(mx, a.pm[((size_t)z * a.n_heads + h) * a.m + i]);
+    float l = 0.0f, o = 0.0f;
+    for (int z = 0; z < splits; ++z) {
+        const size_t row = ((size_t)z * a.n_heads + h) * a.m + i;
+        const float w = __builtin_amdgcn_exp2f(a.pm[row] - mx);   // an empty split (max -inf) weighs 0
+        l += w * a.pl[row];
+        o += w * a.part[row * a.hd + d];
+    }
+    a.out[(size_t)i * a.width + (size_t)h * a.hd + d] = o / l;
+}
+
+struct EncAttnPlan {
+    int qblocks, steps, splits, per;
+};
+
+// Splits: enough waves for about two per SIMD (measured over the chunk sizes 16 .. 750), at
+// least four 16-key steps per split.
+static EncAttnPlan enc_attn_plan(int64_t m, int64_t n_ctx, int n_heads, int window)
+{
+    EncAttnPlan p;
+    p.qblocks = (int)((m + 15) / 16);
+    // the longest key range of a wave: window - 1 earlier keys plus its 16 queries
+    const int64_t span = std::min<int64_t>(n_ctx + m, (int64_t)window + 15);
+    p.steps = (int)((span + 15) / 16);
+    const int64_t waves = (int64_t)p.qblocks * n_heads;
+    int splits = (int)std::min<int64_t>((2048 + waves - 1) / waves, std::max(1, p.steps / 4));
+    splits = std::max(splits, 1);
+    p.per = (p.steps + splits - 1) / splits;
+    p.splits = (p.steps + p.per - 1) / p.per;
+    return p;
+}
+
+static size_t enc_attn_ws(const EncAttnPlan &p, int64_t m, int n_heads, int hd)
+{
+    if (p.splits <= 1)
+        return 0;
+    const size_t rows = (size_t)p.splits * n_heads * m;
+    return (rows * hd + 2 * rows) * sizeof(float);
+}
+
+}  // namespace vox
+
+using namespace vox;
+
+extern "C" size_t vox_enc_attn_workspace(int64_t m, int64_t n_ctx, int n_heads, int head_dim, int window)
+{
+    if (m <= 0 || n_ctx < 0 || n_heads <= 0 || head_dim <= 0 || head_dim > EA_MAX_HD || head_dim % 4 || window <= 0)
+        return 0;
+    return enc_attn_ws(enc_attn_plan(m, n_ctx, n_heads, window), m, n_heads, head_dim);
+}
+
+extern "C" int vox_enc_attn(const float *q, const float *k, const float *v, float *out, int64_t m, int64_t n_ctx,
+                            int n_heads, int head_dim, int window, float scale, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    if (m < 0 || n_ctx < 0 || n_heads <= 0 || head_dim <= 0 || window <= 0)
+        return fail(VOX_E_INVAL, "vox_enc_attn: need m, n_ctx >= 0 and n_heads, head_dim, window > 0");
+    if (m == 0)
+        return ok();
+    if (head_dim > EA_MAX_HD || head_dim % 4)
+        return fail(VOX_E_UNSUPPORTED, "vox_enc_attn: head_dim must be a multiple of 4 up to %d (got %d)", EA_MAX_HD,
+                    head_dim);
+    const int64_t width = (int64_t)n_heads * head_dim, T = n_ctx + m;
+    if (m > 65535LL * 16 || n_heads > 65535 || T * width >= (1LL << 31))
+        return fail(VOX_E_UNSUPPORTED, "vox_enc_attn: sizes beyond the grid or 32-bit element offsets");
+    if (!q || !k || !v || !out)
+        return fail(VOX_E_INVAL, "vox_enc_attn: null pointer");
+    if (!aligned(q, 16) || !aligned(k, 16))
+        return fail(VOX_E_UNSUPPORTED, "vox_enc_attn: q and k must be 16-byte aligned");
+    const size_t qbytes = (size_t)m * width * 4, kvbytes = (size_t)T * width * 4;
+    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) || overlaps(out, qbytes, v, kvbytes))
+        return fail(VOX_E_INVAL, "vox_enc_attn: out overlaps an input");
+    const EncAttnPlan p = enc_attn_plan(m, n_ctx, n_heads, window);
+    const size_t need = enc_attn_ws(p, m, n_heads, head_dim);
+    if (need > workspace_bytes || (need && !workspace))
+        return fail(VOX_E_WORKSPACE, "vox_enc_attn: workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (need && (!aligned(workspace, 16) || overlaps(workspace, need, out, qbytes) ||
+                 overlaps(workspace, need, q, qbytes) || overlaps(workspace, need, k, kvbytes) ||
+                 overlaps(workspace, need, v, kvbytes)))
+        return fail(VOX_E_INVAL, "vox_enc_attn: workspace must be 16-byte aligned and apart from the other buffers");
+
+    EncAttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    const size_t rows = (size_t)p.splits * n_heads * m;
+    a.part = p.splits > 1 ? (float *)workspace : nullptr;
+    a.pm = p.splits > 1 ? a.part + rows * head_dim : nullptr;
+    a.pl = p.splits > 1 ? a.pm + rows : nullptr;
+    a.m = (int)m;
+    a.n_ctx = (int)n_ctx;
+    a.n_heads = n_heads;
+    a.hd = head_dim;
+    a.width = (int)width;
+    a.window = window;
+    a.steps_per_split = p.per;
+    a.qscale = scale * 1.4426950408889634f;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((unsigned)n_heads, (unsigned)p.qblocks, (unsigned)p.splits);
+    switch (head_dim) {
+    case 4: hipLaunchKernelGGL(enc_attn_kernel<4>, grid, dim3(64), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(enc_attn_kernel<8>, grid, dim3(64), 0, s, a); break;
+    case 12: hipLaunchKernelGGL(enc_attn_kernel<12>, grid, dim3(64), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(enc_attn_kernel<16>, grid, dim3(64), 0, s, a); break;
+    case 20: hipLaunchKernelGGL(enc_attn_kernel<20>, grid, dim3(64), 0, s, a); break;
+    case 24: hipLaunchKernelGGL(enc_attn_kernel<24>, grid, dim3(64), 0, s, a); break;
+    case 28: hipLaunchKernelGGL(enc_attn_kernel<28>, grid, dim3(64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL(enc_attn_kernel<32>, grid, dim3(64), 0, s, a); break;
+    case 36: hipLaunchKernelGGL(enc_attn_kernel<36>, grid, dim3(64), 0, s, a); break;
+    case 40: hipLaunchKernelGGL(enc_attn_kernel<40>, grid, dim3(64), 0, s, a); break;
+    case 44: hipLaunchKernelGGL(enc_attn_kernel<44>, grid, dim3(64), 0, s, a); break;
+    default: hipLaunchKernelGGL(enc_attn_kernel<48>, grid, dim3(64), 0, s, a); break;
+    }
+    int st = check_launch("vox_enc_attn");
+    if (st || p.splits == 1)
+        return st ? st : ok();
+    const int64_t total = m * width;
+    hipLaunchKernelGGL(enc_attn_merge_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, p.splits);
+    st = check_launch("vox_enc_attn merge");
+    return st ? st : ok();
+}

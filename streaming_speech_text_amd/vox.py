@@ -55,6 +55,8 @@ _SIGS = {
     "vox_q4_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "vox_adapter_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "vox_adapter": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "vox_enc_attn_workspace": (_sz, [_i64, _i64, _int, _int, _int]),
+    "vox_enc_attn": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _f32, _vp, _sz, _vp]),
     "vox_gqa_decode_attn_workspace": (_sz, [_int, _int, _int, _int]),
     "vox_gqa_decode_attn": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _f32, _vp, _sz, _vp]),
     "vox_decoder_workspace": (_int, [C.POINTER(DecoderConfig), C.POINTER(_sz), C.POINTER(_sz)]),
@@ -168,6 +170,24 @@ def adapter(w1_q4, w2_q4, x_bf16, y, workspace, m=None, k=None, n_mid=None, n_ou
     _check(lib().vox_adapter(_ptr(w1_q4, torch.uint8, "w1_q4"), _ptr(w2_q4, torch.uint8, "w2_q4"),
                              _ptr(x_bf16, xdt, "x_bf16"), _ptr(y, torch.float32, "y"), m, k, n_mid, n_out,
                              _ptr(workspace, None, "workspace"), wsb, _stream(stream)))
+
+
+def enc_attn_workspace(m, n_ctx, n_heads, head_dim, window) -> int:
+    return int(lib().vox_enc_attn_workspace(m, n_ctx, n_heads, head_dim, window))
+
+
+def enc_attn(q, k, v, out, n_heads, window, scale=None, workspace=None, stream=None):
+    """Encoder self-attention over a chunk: q [m, width], k/v [n_ctx + m, width], out [m, width] (fp32);
+    workspace: None or a device buffer of at least enc_attn_workspace(...) bytes."""
+    m, width = q.shape
+    n_ctx = k.shape[0] - m
+    hd = width // n_heads
+    if scale is None:
+        scale = hd ** -0.5
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().vox_enc_attn(_ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+                              _ptr(out, torch.float32, "out"), m, n_ctx, n_heads, hd, window, scale,
+                              _ptr(workspace, None, "workspace") if wsb else None, wsb, _stream(stream)))
 
 
 def gqa_decode_attn_workspace(n_q_heads, n_kv_heads, head_dim, n_slots) -> int:

@@ -25,7 +25,8 @@ def lib():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("vox_q4_dequant", "vox_q4_gemv", "vox_q4_gemm", "vox_q4_gemm_workspace", "vox_gqa_decode_attn",
-                 "vox_gqa_decode_attn_workspace", "vox_adapter", "vox_adapter_workspace", "vox_decoder_step",
+                 "vox_gqa_decode_attn_workspace", "vox_adapter", "vox_adapter_workspace", "vox_enc_attn",
+                 "vox_enc_attn_workspace", "vox_decoder_step",
                  "vox_decoder_create", "vox_decoder_workspace", "vox_strerror", "vox_last_error"):
         assert name in fns
 
@@ -85,6 +86,16 @@ def test_validation_before_device_work(lib):
         vox.VOX_E_UNSUPPORTED                                                                       # alignment
     assert lib.vox_adapter(p, C.c_void_p(0x200000), C.c_void_p(0x400000), C.c_void_p(0x800000), 4, 1280, 1280, 64,
                            big, aw - 16, None) == vox.VOX_E_WORKSPACE
+    # encoder attention: short chunks split the key range (a workspace), long ones do not
+    assert lib.vox_enc_attn_workspace(16, 749, 32, 40, 750) > 0
+    assert lib.vox_enc_attn_workspace(16, 749, 32, 44, 750) > 0
+    assert lib.vox_enc_attn_workspace(16, 749, 32, 42, 750) == 0       # head size not a multiple of 4
+    assert lib.vox_enc_attn(p, p, p, C.c_void_p(0x800000), 0, 5, 32, 40, 750, 0.1, None, 0, None) == vox.VOX_OK
+    assert lib.vox_enc_attn(p, p, p, C.c_void_p(0x800000), 4, 5, 32, 64, 750, 0.1, None, 0, None) == \
+        vox.VOX_E_UNSUPPORTED
+    assert lib.vox_enc_attn(p, p, p, C.c_void_p(0x800000), 4, -1, 32, 40, 750, 0.1, None, 0, None) == vox.VOX_E_INVAL
+    assert lib.vox_enc_attn(p, C.c_void_p(0x200000), C.c_void_p(0x400000), C.c_void_p(0x800000), 16, 749, 32, 40,
+                            750, 0.1, None, 0, None) == vox.VOX_E_WORKSPACE
     ws = lib.vox_gqa_decode_attn_workspace(32, 8, 128, 8192)
     assert ws > 0 and lib.vox_gqa_decode_attn_workspace(32, 8, 64, 8192) == 0
     args = (p, C.c_void_p(0x200000), C.c_void_p(0x400000), C.c_void_p(0x800000))
