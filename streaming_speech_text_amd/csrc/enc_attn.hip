@@ -9,15 +9,15 @@
 //   s_j = scale * <q_i, k_j> for j in [n_ctx + i - window + 1, n_ctx + i] (and j >= 0),
 //   out_i = sum_j softmax(s)_j v_j.
 //
-// One wave per (head, 16 queries, key range).  With 16 keys per step the wave computes
+// A workgroup of four waves takes 64 queries of one head; K and V reach LDS in blocks of 64 keys
+// (one copy serves the four waves), and each wave owns 16 queries.  With 16 keys per step a wave computes
 // S^T = K Q^T (16 keys x 16 queries) with v_mfma_f32_16x16x4_f32 over the head size (inputs in
 // any order A and B agree on: lane group g supplies dims 16s + 4g + r in product 4s + r), so each
 // lane ends up holding four keys (4g .. 4g+3) of one query (lane % 16).  That is exactly the
 // layout of the B operand of O^T += V^T P^T, whose k slots are the same keys (product t takes key
 // 4g + t from lane group g), so the probabilities never leave the registers.  Online softmax in
 // base 2 (q pre-scaled by scale * log2 e); the row max is shared by the four lane groups of a
-// query through two lane swaps, the row sums stay per lane until the end.  Keys are read through
-// the cache, the next step's K and V loaded before the current step's products.
+// query through two lane swaps, the row sums stay per lane until the end.
 //
 // Short chunks split each wave's key range over the grid's third dimension; partial (max, sum,
 // unnormalised output) go to the workspace and enc_attn_merge_kernel combines them in split order.
@@ -47,22 +47,38 @@ __device__ __forceinline__ float xor_max(float v, int mask)
     return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
-// Head size HD (a multiple of 4 up to 48) at compile time.  Score products: the full 16-dim blocks
-// take dims 16s + 4g + r in product (s, r) (a float4 per lane); the last block's HD % 16 dims take
-// dims 16s + 4r + g in product r (one float per lane and product), so no product runs on padding.
+constexpr int EA_WAVES = 4;    // waves per workgroup, 16 queries each
+constexpr int EA_KB = 64;      // keys per LDS block
+
+// Head size HD (a multiple of 4 up to 48) at compile time.  A workgroup of four waves takes 64
+// consecutive queries of one head; per block of 64 keys the workgroup copies K and V rows to LDS
+// (rows padded to HD + 4 floats), and each wave runs the four 16-key steps that meet its queries'
+// windows with its operands read from LDS.  The next block's rows wait in registers while the
+// current block is computed.  Score products: the full 16-dim blocks take dims 16s + 4g + r in
+// product (s, r) (a float4 per lane); the last block's HD % 16 dims take dims 16s + 4r + g in
+// product r (one float per lane and product), so no product runs on padding.
 template <int HD>
-__global__ __launch_bounds__(64) void enc_attn_kernel(EncAttnArgs a)
+__global__ __launch_bounds__(64 * EA_WAVES) void enc_attn_kernel(EncAttnArgs a)
 {
     constexpr int FULL = HD / 16;             // full 16-dim blocks
     constexpr int TAILP = (HD % 16) / 4;      // products of the last, partial block
     constexpr int NDB = (HD + 15) / 16;       // 16-dim output blocks
+    constexpr int LD = HD + 4;                // LDS row stride (floats)
+    constexpr int ROW4 = HD / 4;              // float4 per row
+    constexpr int NCOPY = (2 * EA_KB * ROW4 + 64 * EA_WAVES - 1) / (64 * EA_WAVES);   // float4 per thread
+    __shared__ __attribute__((aligned(16))) float lk[EA_KB * LD];
+    __shared__ __attribute__((aligned(16))) float lv[EA_KB * LD];
+
     const int h = blockIdx.x;           // head in the fast grid dimension: a head's waves share an XCD
-    const int i0 = blockIdx.y * 16;     // first query of the wave
     const int z = blockIdx.z;           // key split
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int qi = lane & 15, g = lane >> 4;
     const int width = a.width;
-    const int iq = min(i0 + qi, a.m - 1);          // this lane's query (clamped; stores are masked)
+    const int q0 = blockIdx.y * (16 * EA_WAVES);     // first query of the workgroup
+    const int i0 = q0 + 16 * wave;                   // first query of the wave
+    const bool live = i0 < a.m;                      // wave has queries (uniform)
+    const int iq = min(i0 + qi, a.m - 1);            // this lane's query (clamped; stores are masked)
     const float *qrow = a.q + (uint32_t)(iq * width + h * HD);
 
     // B operand of S^T
@@ -75,23 +91,24 @@ __global__ __launch_bounds__(64) void enc_attn_kernel(EncAttnArgs a)
     for (int r = 0; r < TAILP; ++r)
         qt[r] = qrow[16 * FULL + 4 * r + g] * a.qscale;
 
-    // key range of the wave: union over its queries, then this split's share of 16-key steps
-    const int last_q = min(i0 + 15, a.m - 1);
-    const int jlo = max(0, a.n_ctx + i0 - a.window + 1);
-    const int jhi = a.n_ctx + last_q;                              // inclusive
-    const int steps = (jhi - jlo + 16) / 16;
-    const int st0 = z * a.steps_per_split;
-    const int st1 = min(steps, st0 + a.steps_per_split);
-    // this lane's own query bounds (keys outside them get no weight)
-    const int my_hi = a.n_ctx + i0 + qi, my_lo = my_hi - a.window + 1;
+    // key blocks of the workgroup (union over its queries), this split's share of them
     const int T = a.n_ctx + a.m;
-    // V operand: dims 16 db + qi (past the head size: read dim 0, weight 0)
+    const int jlo = max(0, a.n_ctx + q0 - a.window + 1);
+    const int jhi = a.n_ctx + min(q0 + 16 * EA_WAVES - 1, a.m - 1);   // inclusive
+    const int nblk = (jhi - jlo + EA_KB) / EA_KB;
+    const int b0 = z * a.steps_per_split;
+    const int b1 = min(nblk, b0 + a.steps_per_split);
+    // the wave's key range and this lane's own query bounds
+    const int w_lo = max(0, a.n_ctx + i0 - a.window + 1);
+    const int w_hi = a.n_ctx + min(i0 + 15, a.m - 1);
+    const int my_hi = a.n_ctx + i0 + qi, my_lo = my_hi - a.window + 1;
+    // V operand columns: dims 16 db + qi (past the head size: column 0, weight 0)
     bool vok[NDB];
-    int voff[NDB];
+    int vcol[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         vok[db] = 16 * db + qi < HD;
-        voff[db] = h * HD + (vok[db] ? 16 * db + qi : 0);
+        vcol[db] = vok[db] ? 16 * db + qi : 0;
     }
 
     f32x4e o[NDB];
@@ -100,84 +117,94 @@ __global__ __launch_bounds__(64) void enc_attn_kernel(EncAttnArgs a)
         o[db] = (f32x4e)0.0f;
     float mrun = -INFINITY, lpart = 0.0f;
 
-    // operand loads of one step: K row kb + qi, V rows kb + 4g + t
-    f32x4e kv[FULL > 0 ? FULL : 1];
-    float kt[TAILP > 0 ? TAILP : 1];
-    float vv[NDB][4];
-    auto load = [&](int st) {
-        const int kb = jlo + 16 * st;
-        const float *krow = a.k + (uint32_t)(min(kb + qi, T - 1) * width + h * HD);
+    // cooperative copy of one block: element e < 2 * 64 * ROW4 is (K or V, row, float4)
+    f32x4e stage[NCOPY];
+    auto fetch = [&](int b) {
+        const int kb = jlo + EA_KB * b;
 #pragma unroll
-        for (int s = 0; s < FULL; ++s)
-            kv[s] = *reinterpret_cast<const f32x4e *>(krow + 16 * s + 4 * g);
+        for (int c = 0; c < NCOPY; ++c) {
+            const int e = min(tid + 64 * EA_WAVES * c, 2 * EA_KB * ROW4 - 1);
+            const int which = e / (EA_KB * ROW4), rem = e % (EA_KB * ROW4);
+            const int row = rem / ROW4, c4 = rem % ROW4;
+            const float *src = (which ? a.v : a.k) + (uint32_t)(min(kb + row, T - 1) * width + h * HD + 4 * c4);
+            stage[c] = *reinterpret_cast<const f32x4e *>(src);
+        }
+    };
+    auto store = [&]() {
 #pragma unroll
-        for (int r = 0; r < TAILP; ++r)
-            kt[r] = krow[16 * FULL + 4 * r + g];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float *vrow = a.v + (uint32_t)(min(kb + 4 * g + t, T - 1) * width);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                vv[db][t] = vrow[voff[db]];
+        for (int c = 0; c < NCOPY; ++c) {
+            const int e = tid + 64 * EA_WAVES * c;
+            if (e < 2 * EA_KB * ROW4) {
+                const int which = e / (EA_KB * ROW4), rem = e % (EA_KB * ROW4);
+                const int row = rem / ROW4, c4 = rem % ROW4;
+                *reinterpret_cast<f32x4e *>((which ? lv : lk) + row * LD + 4 * c4) = stage[c];
+            }
         }
     };
 
-    if (st0 < st1)
-        load(st0);
-    for (int st = st0; st < st1; ++st) {
-        const int kb = jlo + 16 * st;
-        f32x4e kc[FULL > 0 ? FULL : 1];
-        float ktc[TAILP > 0 ? TAILP : 1];
-        float vc[NDB][4];
+    if (b0 < b1)
+        fetch(b0);
+    for (int b = b0; b < b1; ++b) {
+        __syncthreads();   // the previous block's LDS reads are done
+        store();
+        __syncthreads();
+        if (b + 1 < b1)
+            fetch(b + 1);
+        const int kb0 = jlo + EA_KB * b;
+        if (!live)
+            continue;
 #pragma unroll
-        for (int s = 0; s < FULL; ++s)
-            kc[s] = kv[s];
+        for (int u = 0; u < EA_KB / 16; ++u) {
+            const int kb = kb0 + 16 * u;
+            if (kb > w_hi || kb + 15 < w_lo)
+                continue;   // no key of this step is in the wave's windows (uniform)
+            // K operand: row 16u + qi; V operand: rows 16u + 4g + t
+            const float *kr = lk + (16 * u + qi) * LD;
+            f32x4e sc = (f32x4e)0.0f;
 #pragma unroll
-        for (int r = 0; r < TAILP; ++r)
-            ktc[r] = kt[r];
+            for (int s = 0; s < FULL; ++s) {
+                const f32x4e kc = *reinterpret_cast<const f32x4e *>(kr + 16 * s + 4 * g);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+                for (int r = 0; r < 4; ++r)
+                    sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[r], qv[s][r], sc, 0, 0, 0);
+            }
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                vc[db][t] = vok[db] ? vv[db][t] : 0.0f;
-        if (st + 1 < st1)
-            load(st + 1);
-
-        // S^T block: lane holds keys kb + 4g + r (r = 0..3) of query i0 + qi
-        f32x4e sc = (f32x4e)0.0f;
+            for (int r = 0; r < TAILP; ++r)
+                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[16 * FULL + 4 * r + g], qt[r], sc, 0, 0, 0);
+            float vc[NDB][4];
 #pragma unroll
-        for (int s = 0; s < FULL; ++s)
+            for (int t = 0; t < 4; ++t) {
+                const float *vr = lv + (16 * u + 4 * g + t) * LD;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    vc[db][t] = vok[db] ? vr[vcol[db]] : 0.0f;
+            }
+            // masked scores, block max over the query's four lane groups
+            float sm[4];
+            const int j0 = kb + 4 * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[s][r], qv[s][r], sc, 0, 0, 0);
+                sm[r] = (j0 + r >= my_lo && j0 + r <= my_hi) ? sc[r] : -INFINITY;
+            float bmax = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+            bmax = xor_max(bmax, 16);
+            bmax = xor_max(bmax, 32);
+            const float mnew = fmaxf(mrun, bmax);
+            const float ms = mnew == -INFINITY ? 0.0f : mnew;   // nothing live yet: weights stay 0
+            const float c = __builtin_amdgcn_exp2f(mrun - ms);
+            mrun = mnew;
+            float p[4];
 #pragma unroll
-        for (int r = 0; r < TAILP; ++r)
-            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(ktc[r], qt[r], sc, 0, 0, 0);
-        // masked scores, block max over the query's four lane groups
-        float sm[4];
-        const int j0 = kb + 4 * g;
+            for (int r = 0; r < 4; ++r)
+                p[r] = __builtin_amdgcn_exp2f(sm[r] - ms);
+            lpart = lpart * c + (p[0] + p[1]) + (p[2] + p[3]);
+            // O^T += V^T P^T: product t takes key kb + 4g + t from lane group g
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sm[r] = (j0 + r >= my_lo && j0 + r <= my_hi) ? sc[r] : -INFINITY;
-        float bmax = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-        bmax = xor_max(bmax, 16);
-        bmax = xor_max(bmax, 32);
-        const float mnew = fmaxf(mrun, bmax);
-        const float ms = mnew == -INFINITY ? 0.0f : mnew;   // nothing live yet: weights stay 0
-        const float c = __builtin_amdgcn_exp2f(mrun - ms);
-        mrun = mnew;
-        float p[4];
+            for (int db = 0; db < NDB; ++db) {
+                o[db] *= c;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            p[r] = __builtin_amdgcn_exp2f(sm[r] - ms);
-        lpart = lpart * c + (p[0] + p[1]) + (p[2] + p[3]);
-        // O^T += V^T P^T: product t takes key kb + 4g + t from lane group g
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            o[db] *= c;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vc[db][t], p[t], o[db], 0, 0, 0);
+                for (int t = 0; t < 4; ++t)
+                    o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vc[db][t], p[t], o[db], 0, 0, 0);
+            }
         }
     }
 
@@ -243,20 +270,21 @@ __global__ __launch_bounds__(256) void enc_attn_merge_kernel(EncAttnArgs a, int 
 }
 
 struct EncAttnPlan {
-    int qblocks, steps, splits, per;
+    int qblocks, steps, splits, per;   // steps: 64-key blocks of the longest workgroup range
 };
 
-// Splits: enough waves for about two per SIMD (measured over the chunk sizes 16 .. 750), at
-// least four 16-key steps per split.
+// Splits: enough waves for about two per SIMD, at least two 64-key blocks per split (measured on
+// MI355X over the chunk sizes 16 .. 750: one block per split, or a target of one or four waves per
+// SIMD, was slower somewhere and faster nowhere by more than a few percent).
 static EncAttnPlan enc_attn_plan(int64_t m, int64_t n_ctx, int n_heads, int window)
 {
     EncAttnPlan p;
-    p.qblocks = (int)((m + 15) / 16);
-    // the longest key range of a wave: window - 1 earlier keys plus its 16 queries
-    const int64_t span = std::min<int64_t>(n_ctx + m, (int64_t)window + 15);
-    p.steps = (int)((span + 15) / 16);
-    const int64_t waves = (int64_t)p.qblocks * n_heads;
-    int splits = (int)std::min<int64_t>((2048 + waves - 1) / waves, std::max(1, p.steps / 4));
+    p.qblocks = (int)((m + 16 * EA_WAVES - 1) / (16 * EA_WAVES));
+    // the longest key range of a workgroup: window - 1 earlier keys plus its 64 queries
+    const int64_t span = std::min<int64_t>(n_ctx + m, (int64_t)window + 16 * EA_WAVES - 1);
+    p.steps = (int)((span + EA_KB - 1) / EA_KB);
+    const int64_t waves = (int64_t)p.qblocks * n_heads * EA_WAVES;
+    int splits = (int)std::min<int64_t>((2048 + waves - 1) / waves, std::max(1, p.steps / 2));
     splits = std::max(splits, 1);
     p.per = (p.steps + splits - 1) / splits;
     p.splits = (p.steps + p.per - 1) / p.per;
@@ -332,18 +360,18 @@ extern "C" int vox_enc_attn(const float *q, const float *k, const float *v, floa
     hipStream_t s = (hipStream_t)stream;
     const dim3 grid((unsigned)n_heads, (unsigned)p.qblocks, (unsigned)p.splits);
     switch (head_dim) {
-    case 4: hipLaunchKernelGGL(enc_attn_kernel<4>, grid, dim3(64), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(enc_attn_kernel<8>, grid, dim3(64), 0, s, a); break;
-    case 12: hipLaunchKernelGGL(enc_attn_kernel<12>, grid, dim3(64), 0, s, a); break;
-    case 16: hipLaunchKernelGGL(enc_attn_kernel<16>, grid, dim3(64), 0, s, a); break;
-    case 20: hipLaunchKernelGGL(enc_attn_kernel<20>, grid, dim3(64), 0, s, a); break;
-    case 24: hipLaunchKernelGGL(enc_attn_kernel<24>, grid, dim3(64), 0, s, a); break;
-    case 28: hipLaunchKernelGGL(enc_attn_kernel<28>, grid, dim3(64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL(enc_attn_kernel<32>, grid, dim3(64), 0, s, a); break;
-    case 36: hipLaunchKernelGGL(enc_attn_kernel<36>, grid, dim3(64), 0, s, a); break;
-    case 40: hipLaunchKernelGGL(enc_attn_kernel<40>, grid, dim3(64), 0, s, a); break;
-    case 44: hipLaunchKernelGGL(enc_attn_kernel<44>, grid, dim3(64), 0, s, a); break;
-    default: hipLaunchKernelGGL(enc_attn_kernel<48>, grid, dim3(64), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(enc_attn_kernel<4>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(enc_attn_kernel<8>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 12: hipLaunchKernelGGL(enc_attn_kernel<12>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(enc_attn_kernel<16>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 20: hipLaunchKernelGGL(enc_attn_kernel<20>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 24: hipLaunchKernelGGL(enc_attn_kernel<24>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 28: hipLaunchKernelGGL(enc_attn_kernel<28>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 32: hipLaunchKernelGGL(enc_attn_kernel<32>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 36: hipLaunchKernelGGL(enc_attn_kernel<36>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 40: hipLaunchKernelGGL(enc_attn_kernel<40>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    case 44: hipLaunchKernelGGL(enc_attn_kernel<44>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
+    default: hipLaunchKernelGGL(enc_attn_kernel<48>, grid, dim3(64 * EA_WAVES), 0, s, a); break;
     }
     int st = check_launch("vox_enc_attn");
     if (st || p.splits == 1)
