@@ -17,7 +17,9 @@
 // layout of the B operand of O^T += V^T P^T, whose k slots are the same keys (product t takes key
 // 4g + t from lane group g), so the probabilities never leave the registers.  Online softmax in
 // base 2 (q pre-scaled by scale * log2 e); the row max is shared by the four lane groups of a
-// query through two lane swaps, the row sums stay per lane until the end.
+// query through two lane swaps, the row sums stay per lane until the end.  Per 64-key block a wave
+// computes all four score blocks first, updates the running max once, and rescales the output
+// only when some query's max grew.
 //
 // Short chunks split each wave's key range over the grid's third dimension; partial (max, sum,
 // unnormalised output) go to the workspace and enc_attn_merge_kernel combines them in split order.
@@ -42,9 +44,27 @@ struct EncAttnArgs {
     float qscale;        // scale * log2(e)
 };
 
-__device__ __forceinline__ float xor_max(float v, int mask)
+// Lane exchanges across rows of 16 lanes (v_permlane16_swap / v_permlane32_swap): each returns the
+// pair {own value, value of lane ^ 16 (or ^ 32)} in some order, so max and sum need no select.
+__device__ __forceinline__ float max_xor16(float v)
 {
-    return fmaxf(v, __shfl_xor(v, mask, 64));
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 constexpr int EA_WAVES = 4;    // waves per workgroup, 16 queries each
@@ -52,8 +72,8 @@ constexpr int EA_KB = 64;      // keys per LDS block
 
 // Head size HD (a multiple of 4 up to 48) at compile time.  A workgroup of four waves takes 64
 // consecutive queries of one head; per block of 64 keys the workgroup copies K and V rows to LDS
-// (rows padded to HD + 4 floats), and each wave runs the four 16-key steps that meet its queries'
-// windows with its operands read from LDS.  The next block's rows wait in registers while the
+// (rows padded to HD + 4 floats), and each wave whose queries' windows meet the block runs its four
+// 16-key steps with operands read from LDS.  The next block's rows wait in registers while the
 // current block is computed.  Score products: the full 16-dim blocks take dims 16s + 4g + r in
 // product (s, r) (a float4 per lane); the last block's HD % 16 dims take dims 16s + 4r + g in
 // product r (one float per lane and product), so no product runs on padding.
@@ -151,26 +171,62 @@ __global__ __launch_bounds__(64 * EA_WAVES) void enc_attn_kernel(EncAttnArgs a)
         if (b + 1 < b1)
             fetch(b + 1);
         const int kb0 = jlo + EA_KB * b;
-        if (!live)
-            continue;
+        if (!live || kb0 > w_hi || kb0 + EA_KB - 1 < w_lo)
+            continue;   // no key of this block is in the wave's windows (uniform)
+        // scores of the whole block first (independent products the scheduler can overlap with
+        // the softmax work), then one running-max update per block
+        f32x4e sc[EA_KB / 16];
 #pragma unroll
         for (int u = 0; u < EA_KB / 16; ++u) {
-            const int kb = kb0 + 16 * u;
-            if (kb > w_hi || kb + 15 < w_lo)
-                continue;   // no key of this step is in the wave's windows (uniform)
-            // K operand: row 16u + qi; V operand: rows 16u + 4g + t
+            // K operand: row 16u + qi
             const float *kr = lk + (16 * u + qi) * LD;
-            f32x4e sc = (f32x4e)0.0f;
+            sc[u] = (f32x4e)0.0f;
 #pragma unroll
             for (int s = 0; s < FULL; ++s) {
                 const f32x4e kc = *reinterpret_cast<const f32x4e *>(kr + 16 * s + 4 * g);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[r], qv[s][r], sc, 0, 0, 0);
+                    sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[r], qv[s][r], sc[u], 0, 0, 0);
             }
 #pragma unroll
             for (int r = 0; r < TAILP; ++r)
-                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[16 * FULL + 4 * r + g], qt[r], sc, 0, 0, 0);
+                sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[16 * FULL + 4 * r + g], qt[r], sc[u], 0, 0, 0);
+        }
+        // masked scores (lane holds keys kb0 + 16u + 4g + r of query i0 + qi), block max over the
+        // query's four lane groups
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < EA_KB / 16; ++u) {
+            const int j0 = kb0 + 16 * u + 4 * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sc[u][r] = (j0 + r >= my_lo && j0 + r <= my_hi) ? sc[u][r] : -INFINITY;
+                bmax = fmaxf(bmax, sc[u][r]);
+            }
+        }
+        bmax = max_xor32(max_xor16(bmax));
+        const float mnew = fmaxf(mrun, bmax);
+        const float ms = mnew == -INFINITY ? 0.0f : mnew;   // nothing live yet: weights stay 0
+        const float c = __builtin_amdgcn_exp2f(mrun - ms);
+        const bool grew = mnew > mrun;                      // c < 1 only where the max grew
+        mrun = mnew;
+        float psum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < EA_KB / 16; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sc[u][r] = __builtin_amdgcn_exp2f(sc[u][r] - ms);
+                psum += sc[u][r];
+            }
+        lpart = lpart * c + psum;
+        if (__any(grew)) {   // rescale only when some query's max grew (c = 1 elsewhere)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                o[db] *= c;
+        }
+        // O^T += V^T P^T: product (u, t) takes key kb0 + 16u + 4g + t from lane group g
+#pragma unroll
+        for (int u = 0; u < EA_KB / 16; ++u) {
             float vc[NDB][4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -179,38 +235,16 @@ __global__ __launch_bounds__(64 * EA_WAVES) void enc_attn_kernel(EncAttnArgs a)
                 for (int db = 0; db < NDB; ++db)
                     vc[db][t] = vok[db] ? vr[vcol[db]] : 0.0f;
             }
-            // masked scores, block max over the query's four lane groups
-            float sm[4];
-            const int j0 = kb + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sm[r] = (j0 + r >= my_lo && j0 + r <= my_hi) ? sc[r] : -INFINITY;
-            float bmax = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-            bmax = xor_max(bmax, 16);
-            bmax = xor_max(bmax, 32);
-            const float mnew = fmaxf(mrun, bmax);
-            const float ms = mnew == -INFINITY ? 0.0f : mnew;   // nothing live yet: weights stay 0
-            const float c = __builtin_amdgcn_exp2f(mrun - ms);
-            mrun = mnew;
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                p[r] = __builtin_amdgcn_exp2f(sm[r] - ms);
-            lpart = lpart * c + (p[0] + p[1]) + (p[2] + p[3]);
-            // O^T += V^T P^T: product t takes key kb + 4g + t from lane group g
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                o[db] *= c;
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vc[db][t], p[t], o[db], 0, 0, 0);
-            }
+                    o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vc[db][t], sc[u][t], o[db], 0, 0, 0);
         }
     }
 
     // this query's sum over the four lane groups (all share mrun)
-    float l = lpart + __shfl_xor(lpart, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = sum_xor32(sum_xor16(lpart));
     const int i = i0 + qi;
     if (i >= a.m)
         return;
