@@ -173,6 +173,24 @@ void orc_q4_gemm(const uint8_t *w, const uint16_t *x_bf16, double *y, int64_t m,
 }
 
 /* ------------------------------------------------------------------------------------
+ * 16-bit weights ([VC] section 모델 다운로드 및 구성: the weights ship as BF16; section 메모리
+ * 요구사항: the GPU cache holds them converted from BF16 to F16).  y[r] = sum over k ascending of
+ * W[r][k] * x[k], W row-major n x k of bf16 (fmt 0) or IEEE binary16 (fmt 1) bit patterns.
+ * ---------------------------------------------------------------------------------- */
+void orc_w16_gemv(const uint16_t *w, int64_t fmt, const float *x, double *y, int64_t n, int64_t k)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < k; i++) {
+            const uint16_t b = w[r * k + i];
+            acc += (fmt ? orc_fp16_to_double(b) : orc_bf16_to_double(b)) * (double)x[i];
+        }
+        y[r] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------------------
  * Adapter from the encoder to the decoder ([VC] section 모델 아키텍처: a linear from 5120 to
  * 3072 inputs, GELU, a linear from 3072 to 3072).  READINGS: no biases (the pages name none,
  * and the Q4_0 linears of the quantised path carry none); GELU is the exact form

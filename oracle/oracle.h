@@ -30,6 +30,9 @@ void orc_q4_gemv_rows(const uint8_t *w, const float *x, const int64_t *rows, int
                       double *y, int64_t k);
 void orc_q4_gemm(const uint8_t *w, const uint16_t *x_bf16, double *y, int64_t m, int64_t n, int64_t k);
 
+/* 16-bit weights (fmt 0: bf16, 1: fp16) */
+void orc_w16_gemv(const uint16_t *w, int64_t fmt, const float *x, double *y, int64_t n, int64_t k);
+
 /* Adapter: linear, GELU, linear */
 double orc_gelu(double x);
 void orc_gelu_array(const double *x, int64_t n, double *out);

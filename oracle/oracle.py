@@ -54,6 +54,7 @@ def lib():
             "orc_attn_probs": [_vp, _vp, _i64, _i64, _i64, _dbl, _vp],
             "orc_gqa_attn": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _dbl, _vp],
             "orc_swiglu": [_vp, _vp, _i64, _vp],
+            "orc_w16_gemv": [_vp, _i64, _vp, _vp, _i64, _i64],
             "orc_gelu_array": [_vp, _i64, _vp],
             "orc_adapter": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64],
             "orc_enc_attn": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _dbl, _vp],
@@ -193,6 +194,16 @@ def swiglu(gate, up) -> np.ndarray:
     out = np.empty_like(gate)
     lib().orc_swiglu(_p(gate), _p(up), gate.size, _p(out))
     return out
+
+
+def w16_gemv(w, x, fmt: str) -> np.ndarray:
+    """w: uint16 [n, k] bit patterns of bf16 (fmt 'bf16') or fp16 (fmt 'f16'); x: float32 [k] -> float64 [n]."""
+    w = _c(w, np.uint16)
+    x = _c(x, np.float32)
+    n, k = w.shape
+    y = np.empty(n, np.float64)
+    lib().orc_w16_gemv(_p(w), {"bf16": 0, "f16": 1}[fmt], _p(x), _p(y), n, k)
+    return y
 
 
 def gelu(x) -> np.ndarray:

@@ -121,7 +121,7 @@ ADAPTER = (5120, 3072, 3072)
 ADAPTER_M = tuple(m // 4 for m in ENCODER_M)
 
 # Seeds: one per workload.
-SEED_GEMV, SEED_LAYER, SEED_ATTN, SEED_DECODER, SEED_GEMM, SEED_ADAPTER, SEED_ENC_ATTN = 1, 2, 3, 4, 5, 6, 7
+SEED_GEMV, SEED_LAYER, SEED_ATTN, SEED_DECODER, SEED_GEMM, SEED_ADAPTER, SEED_ENC_ATTN, SEED_W16 = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def gemv_inputs(seed: int, n: int, k: int):
@@ -132,6 +132,22 @@ def gemv_inputs(seed: int, n: int, k: int):
 def gemm_inputs(seed: int, m: int, n: int, k: int):
     """(W q4 [n, k/32*18], X bf16 bits [m, k])."""
     return q4_matrix(generator(seed, 0, n, k), n, k), bf16_normal(generator(seed, 1, m, k), (m, k))
+
+
+def w16_matrix(g: np.random.Generator, n: int, k: int, fmt: str) -> np.ndarray:
+    """Random 16-bit weight matrix, uint16 [n, k]: values ~ N(0, 0.02^2) (the spread of a
+    trained linear's weights at this width) rounded to bf16 or fp16 (nearest even)."""
+    v = g.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    if fmt == "bf16":
+        return bf16_bits(v)
+    if fmt == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    raise ValueError(fmt)
+
+
+def w16_gemv_inputs(seed: int, n: int, k: int, fmt: str):
+    """(W uint16 [n, k], x fp32 [k])."""
+    return w16_matrix(generator(seed, 0, n, k), n, k, fmt), normal_f32(generator(seed, 1, k), (k,))
 
 
 def adapter_inputs(seed: int, m: int, k: int, n_mid: int, n_out: int):

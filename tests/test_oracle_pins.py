@@ -667,3 +667,33 @@ def test_page_figures_pin_encoder_attention():
     enc = json.load(open(os.path.join(GOLDEN, "page_figures.json")))["encoder"]
     assert (synth.ENC_HEADS, synth.ENC_WINDOW) == (enc["n_heads"], enc["window"])
     assert synth.ENC_HEADS * synth.ENC_HEAD_DIM == enc["dim"]
+
+
+# ---------------------------------------------------------------------------------------
+# 16-bit weights (bf16 and fp16)
+# ---------------------------------------------------------------------------------------
+
+def test_w16_gemv_exact_bruteforce(orc):
+    # dyadic weights (small integers times powers of two, exact in both formats) and small-integer
+    # activations: every product and sum is exact, so the result must equal the rational sum
+    g = synth.generator(50)
+    n, k = 7, 96
+    wi = g.integers(-8, 9, size=(n, k)).astype(np.float32) * np.float32(2.0) ** g.integers(-6, 2, size=(n, k))
+    x = g.integers(-5, 6, size=k).astype(np.float32)
+    for fmt, bits in (("bf16", synth.bf16_bits(wi)), ("f16", wi.astype(np.float16).view(np.uint16))):
+        y = orc.w16_gemv(bits, x, fmt)
+        ref = [sum(Fraction(float(wi[r, i])) * Fraction(float(x[i])) for i in range(k)) for r in range(n)]
+        assert all(Fraction(y[r]) == ref[r] for r in range(n)), fmt
+
+
+def test_w16_gemv_random_vs_numpy(orc):
+    g = synth.generator(51)
+    n, k = 300, 1000
+    for fmt in ("bf16", "f16"):
+        w, x = synth.w16_matrix(g, n, k, fmt), synth.normal_f32(g, (k,))
+        wd = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if fmt == "bf16" \
+            else w.view(np.float16).astype(np.float64)
+        assert np.allclose(orc.w16_gemv(w, x, fmt), wd @ x.astype(np.float64), rtol=1e-12, atol=1e-12)
+    # the two decodings differ: the same bits read as the other format give another result
+    w, x = synth.w16_matrix(g, 4, 64, "bf16"), synth.normal_f32(g, (64,))
+    assert not np.allclose(orc.w16_gemv(w, x, "bf16"), orc.w16_gemv(w, x, "f16"))
