@@ -127,8 +127,8 @@ def timed(torch, stream, launch, copies, reps, replays=5):
 def kernels_leg(torch, synth, vox, dev, stream):
     """Per-kernel device times of the workloads beside the decoder step: the single 3072x3072
     GEMV, one decoder layer's linears, GQA attention at three ring fills, the encoder-chunk
-    GEMM set, the encoder's chunk attention, the adapter.  Every measurement rotates over more than
-    1 GiB of distinct copies."""
+    GEMM set, the encoder's chunk attention, the GEMV over 16-bit weights, the adapter.  Every
+    measurement streams more than 1 GiB of distinct weights."""
     GiB = 2 ** 30
     out = []
 
@@ -224,6 +224,40 @@ def kernels_leg(torch, synth, vox, dev, stream):
               "tflops": round(flops / us / 1e6, 2), "frac_mfma_fp32": round(flops / us / 1e6 / 157.3, 4),
               "bytes": b, "gbs": round(b / us / 1e3, 1)})
         del qs, kvs
+        torch.cuda.empty_cache()
+
+    # GEMV over 16-bit weights: the LM-head shape, then every GEMV of a decoder step (26 layers of
+    # q, k, v, o, gate, up, down and the LM head, 4.2 GB of distinct weights) as one chain
+    s_ = synth.VOXTRAL_DECODER
+    for fmt in ("bf16", "f16"):
+        n, k = s_.vocab, s_.dim
+        w, x = synth.w16_gemv_inputs(synth.SEED_W16, n, k, fmt)
+        head = [torch.from_numpy(w).to(dev) for _ in range(2)]
+        del w
+        xd = torch.from_numpy(x).to(dev)
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        us = timed(torch, stream, lambda i: vox.w16_gemv(head[i], xd, y, fmt), 2, 50)
+        b = n * k * 2 + 4 * (n + k)
+        emit({"kernel": "w16_gemv", "case": f"{fmt} {n}x{k} (LM-head shape)", "us": round(us, 3), "bytes": b,
+              "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+        layer = []
+        for j, (name, (ln, lk)) in enumerate(synth.LAYER_LINEARS.items()):
+            lw, lx = synth.w16_gemv_inputs(synth.SEED_W16 + 1 + j, ln, lk, fmt)
+            layer.append((ln, lk, torch.from_numpy(lw).to(dev), torch.from_numpy(lx).to(dev),
+                          torch.empty(ln, dtype=torch.float32, device=dev)))
+        chain = [[(ln, lk, wt.clone(), xt, yt) for ln, lk, wt, xt, yt in layer] for _ in range(s_.n_layers)]
+        del layer
+
+        def step(i):
+            for lay in chain:
+                for ln, lk, wt, xt, yt in lay:
+                    vox.w16_gemv(wt, xt, yt, fmt)
+            vox.w16_gemv(head[0], xd, y, fmt)
+        us = timed(torch, stream, step, 1, 3)
+        b = s_.n_layers * sum(o * i * 2 for o, i in synth.LAYER_LINEARS.values()) + n * k * 2
+        emit({"kernel": "w16_gemv", "case": f"{fmt} decoder-step GEMV chain (26 layers + LM head)", "us": round(us, 3),
+              "bytes": b, "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del chain, head
         torch.cuda.empty_cache()
 
     # adapter (linear 5120 -> 3072, GELU, linear 3072 -> 3072) over the rows of one encoder chunk

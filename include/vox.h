@@ -61,6 +61,15 @@ int vox_q4_dequant(const void *w_q4, int64_t n_blocks, float *out, void *stream)
  * k % 32 != 0 or k <= 0 -> VOX_E_INVAL. */
 int vox_q4_gemv(const void *w_q4, const float *x, float *y, int64_t n, int64_t k, void *stream);
 
+/* Matrix-vector product over 16-bit weights ([VC] 모델 다운로드 및 구성: the weights ship as BF16;
+ * [VC] 메모리 요구사항: the GPU copy is F16): y[r] = sum_i W[r][i] * x[i], fp32 accumulation.
+ * w: n rows by k, row-major bit patterns of bf16 (fmt VOX_W16_BF16) or IEEE binary16
+ * (VOX_W16_F16); x: k floats; y: n floats, must not overlap x or w.  n == 0 is a no-op.
+ * k not a positive multiple of 8, or another fmt -> VOX_E_INVAL; w, x not 16-byte aligned ->
+ * VOX_E_UNSUPPORTED. */
+enum { VOX_W16_BF16 = 0, VOX_W16_F16 = 1 };
+int vox_w16_gemv(const void *w, int fmt, const float *x, float *y, int64_t n, int64_t k, void *stream);
+
 /* Encoder-chunk linear Y = X * W^T with Q4_0 weights ([VC] 모델 아키텍처: encoder width 1280;
  * [RS] 아키텍처: Q4_0 linears), on the matrix cores.  x_bf16: m rows by k, bf16 bit patterns,
  * row major; w_q4: n rows by k; y: m by n fp32, row major, must not overlap the inputs.

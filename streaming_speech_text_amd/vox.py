@@ -51,6 +51,7 @@ _SIGS = {
     "vox_last_error": (C.c_char_p, []),
     "vox_q4_dequant": (_int, [_vp, _i64, _vp, _vp]),
     "vox_q4_gemv": (_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
+    "vox_w16_gemv": (_int, [_vp, _int, _vp, _vp, _i64, _i64, _vp]),
     "vox_q4_gemm_workspace": (_sz, [_i64, _i64, _i64]),
     "vox_q4_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "vox_adapter_workspace": (_sz, [_i64, _i64, _i64, _i64]),
@@ -134,6 +135,18 @@ def q4_gemv(w_q4, x, y, n=None, k=None, stream=None):
     n = y.numel() if n is None else n
     _check(lib().vox_q4_gemv(_ptr(w_q4, torch.uint8, "w_q4"), _ptr(x, torch.float32, "x"),
                              _ptr(y, torch.float32, "y"), n, k, _stream(stream)))
+
+
+VOX_W16_BF16, VOX_W16_F16 = 0, 1
+
+
+def w16_gemv(w, x, y, fmt="bf16", n=None, k=None, stream=None):
+    """y = W x over 16-bit weights: w uint16 (or bfloat16 / float16) [n, k], x fp32 [k], y fp32 [n]."""
+    if n is None or k is None:
+        n, k = w.shape
+    code = {"bf16": VOX_W16_BF16, "f16": VOX_W16_F16}[fmt]
+    _check(lib().vox_w16_gemv(_ptr(w, None, "w"), code, _ptr(x, torch.float32, "x"), _ptr(y, torch.float32, "y"),
+                              n, k, _stream(stream)))
 
 
 def q4_gemm_workspace(m, n, k) -> int:

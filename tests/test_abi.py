@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("vox_q4_dequant", "vox_q4_gemv", "vox_q4_gemm", "vox_q4_gemm_workspace", "vox_gqa_decode_attn",
                  "vox_gqa_decode_attn_workspace", "vox_adapter", "vox_adapter_workspace", "vox_enc_attn",
-                 "vox_enc_attn_workspace", "vox_decoder_step",
+                 "vox_enc_attn_workspace", "vox_w16_gemv", "vox_decoder_step",
                  "vox_decoder_create", "vox_decoder_workspace", "vox_strerror", "vox_last_error"):
         assert name in fns
 
@@ -70,6 +70,10 @@ def test_validation_before_device_work(lib):
     assert lib.vox_q4_gemm_workspace(64, 1280, 5120) > 0
     assert lib.vox_q4_gemm_workspace(750, 5120, 1280) == 0
     assert lib.vox_q4_gemm_workspace(4, 4, 48) == 0
+    assert lib.vox_w16_gemv(p, 0, p, C.c_void_p(0x800000), 10, 12, None) == vox.VOX_E_INVAL    # k % 8
+    assert lib.vox_w16_gemv(p, 2, p, C.c_void_p(0x800000), 10, 16, None) == vox.VOX_E_INVAL    # fmt
+    assert lib.vox_w16_gemv(p, 1, p, C.c_void_p(0x800000), 0, 16, None) == vox.VOX_OK          # empty
+    assert lib.vox_w16_gemv(C.c_void_p(0x1008), 0, p, C.c_void_p(0x800000), 10, 16, None) == vox.VOX_E_UNSUPPORTED
     # adapter: workspace holds the GELU pairs (2 x bf16 per value) plus the larger product's partials
     assert lib.vox_adapter_workspace(16, 5120, 3072, 3072) >= 16 * 3072 * 4
     assert lib.vox_adapter_workspace(16, 5120, 3072, 3072) % 16 == 0
