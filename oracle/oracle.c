@@ -376,6 +376,53 @@ int64_t orc_argmax_f64(const double *v, int64_t n)
 }
 
 /* ------------------------------------------------------------------------------------
+ * Alternative tokens ([VC] section 사용 방법: --alt <cutoff> shows candidate tokens beside the
+ * chosen one, more of them for a higher cutoff; section C API 구조: the number of alternatives is
+ * set on the stream).  READING: with p = softmax(logits) and t the greedy token, a token i is a
+ * candidate when p_i >= (1 - cutoff) p_t, i.e. l_i >= l_t + ln(1 - cutoff); the comparison is made
+ * on the fp32 logits against tau = l_t + d in fp32 arithmetic, d = ln(1 - cutoff) rounded to fp32
+ * (cutoff >= 1: every token).  The candidates (the greedy token first) are listed by logit, higher
+ * first, ties to the lower index, at most max_out of them, each with its probability (double).
+ * Returns the count.
+ * ---------------------------------------------------------------------------------- */
+static int alt_before(const float *l, int64_t a, int64_t b)   /* a listed before b */
+{
+    return l[a] > l[b] || (l[a] == l[b] && a < b);
+}
+
+int64_t orc_alt_tokens(const float *logits, int64_t vocab, double cutoff, int64_t max_out, int64_t *ids,
+                       double *probs)
+{
+    const int64_t top = orc_argmax_f32(logits, vocab);
+    const float lt = logits[top];
+    const float d = cutoff >= 1.0 ? -INFINITY : (float)log(1.0 - cutoff);
+    const float tau = lt + d;
+    double z = 0.0;
+    for (int64_t i = 0; i < vocab; i++)
+        z += exp((double)logits[i] - (double)lt);
+    /* selection by insertion into the sorted output list */
+    int64_t count = 0;
+    for (int64_t i = 0; i < vocab; i++) {
+        if (!(logits[i] >= tau))
+            continue;
+        int64_t pos = count;
+        while (pos > 0 && alt_before(logits, i, ids[pos - 1]))
+            pos--;
+        if (pos >= max_out)
+            continue;
+        int64_t end = count < max_out ? count : max_out - 1;
+        for (int64_t j = end; j > pos; j--)
+            ids[j] = ids[j - 1];
+        ids[pos] = i;
+        if (count < max_out)
+            count++;
+    }
+    for (int64_t j = 0; j < count; j++)
+        probs[j] = exp((double)logits[ids[j]] - (double)lt) / z;
+    return count;
+}
+
+/* ------------------------------------------------------------------------------------
  * Whole decoder step.
  * ---------------------------------------------------------------------------------- */
 

@@ -54,6 +54,10 @@ void orc_swiglu(const double *gate, const double *up, int64_t n, double *out);
 int64_t orc_argmax_f32(const float *v, int64_t n);
 int64_t orc_argmax_f64(const double *v, int64_t n);
 
+/* Alternative tokens: candidates within ln(1 - cutoff) of the top logit, listed by logit */
+int64_t orc_alt_tokens(const float *logits, int64_t vocab, double cutoff, int64_t max_out, int64_t *ids,
+                       double *probs);
+
 /* Whole decoder step */
 typedef struct {
     int64_t n_layers, dim, n_heads, n_kv_heads, head_dim, hidden, vocab, n_slots;

@@ -64,6 +64,8 @@ def lib():
             f = getattr(L, name)
             f.restype = None
             f.argtypes = args
+        L.orc_alt_tokens.restype = _i64
+        L.orc_alt_tokens.argtypes = [_vp, _i64, _dbl, _i64, _vp, _vp]
         L.orc_argmax_f32.restype = _i64
         L.orc_argmax_f32.argtypes = [_vp, _i64]
         L.orc_argmax_f64.restype = _i64
@@ -241,6 +243,15 @@ def enc_attn(q, k, v, n_heads, window, scale=None) -> np.ndarray:
     out = np.empty((m, width), np.float64)
     lib().orc_enc_attn(_p(q), _p(k), _p(v), m, n_ctx, n_heads, hd, window, float(scale), _p(out))
     return out
+
+
+def alt_tokens(logits, cutoff, max_out):
+    """-> (ids int64 [count], probs float64 [count]): the greedy token and its alternatives."""
+    lg = _c(logits, np.float32)
+    ids = np.empty(max_out, np.int64)
+    probs = np.empty(max_out, np.float64)
+    n = int(lib().orc_alt_tokens(_p(lg), lg.size, float(cutoff), int(max_out), _p(ids), _p(probs)))
+    return ids[:n].copy(), probs[:n].copy()
 
 
 def argmax_f32(v) -> int:

@@ -697,3 +697,59 @@ def test_w16_gemv_random_vs_numpy(orc):
     # the two decodings differ: the same bits read as the other format give another result
     w, x = synth.w16_matrix(g, 4, 64, "bf16"), synth.normal_f32(g, (64,))
     assert not np.allclose(orc.w16_gemv(w, x, "bf16"), orc.w16_gemv(w, x, "f16"))
+
+
+# ---------------------------------------------------------------------------------------
+# alternative tokens
+# ---------------------------------------------------------------------------------------
+
+def _alt_numpy(l, cutoff, max_out):
+    """The same definition through numpy: fp32 threshold, lexicographic sort, scipy softmax."""
+    from scipy.special import softmax
+    t = int(np.argmax(l))
+    d = np.float32(-np.inf) if cutoff >= 1 else np.float32(np.log(1.0 - cutoff))
+    tau = np.float32(l[t]) + d
+    sel = np.nonzero(l >= tau)[0]
+    order = np.lexsort((sel, -l[sel].astype(np.float64)))
+    ids = sel[order][:max_out]
+    return ids, softmax(l.astype(np.float64))[ids]
+
+
+def test_alt_tokens_vs_numpy(orc):
+    g = synth.generator(60)
+    for vocab, cutoff, max_out in [(131072, 0.9, 8), (131072, 0.99, 32), (5000, 0.5, 5), (1000, 1.0, 7),
+                                   (64, 0.0, 4), (300, 0.999, 300)]:
+        l = (g.standard_normal(vocab) * 3).astype(np.float32)
+        ids, probs = orc.alt_tokens(l, cutoff, max_out)
+        rid, rprobs = _alt_numpy(l, cutoff, max_out)
+        assert np.array_equal(ids, rid), (vocab, cutoff)
+        assert np.allclose(probs, rprobs, rtol=1e-12, atol=1e-300)
+
+
+def test_alt_tokens_closed_forms(orc):
+    l = np.float32([1.0, 3.0, 3.0, 2.0, 0.5, 2.9, -np.inf])
+    # cutoff 0: only the maximum (its tie too), the lower index first
+    ids, probs = orc.alt_tokens(l, 0.0, 5)
+    assert list(ids) == [1, 2] and probs[0] == probs[1]
+    # p_i >= (1 - c) p_t  <=>  l_i >= l_t + ln(1 - c): c = 1 - e^-0.15 admits 2.9, not 2.0
+    ids, _ = orc.alt_tokens(l, 1 - math.exp(-0.15), 5)
+    assert list(ids) == [1, 2, 5]
+    # cutoff 1: every token by logit, the count capped by max_out
+    ids, probs = orc.alt_tokens(l, 1.0, 10)
+    assert list(ids) == [1, 2, 5, 3, 0, 4, 6] and probs[-1] == 0.0
+    assert list(orc.alt_tokens(l, 1.0, 3)[0]) == [1, 2, 5]
+    # probabilities are the softmax over the whole vocabulary
+    e = np.exp(l.astype(np.float64) - 3.0)
+    assert np.allclose(probs, e[[1, 2, 5, 3, 0, 4, 6]] / e.sum(), rtol=1e-14, atol=0)
+
+
+def test_alt_tokens_monotone_and_ratio(orc):
+    g = synth.generator(61)
+    l = (g.standard_normal(20000) * 2).astype(np.float32)
+    prev = set()
+    for c in (0.0, 0.3, 0.6, 0.9, 0.99, 0.999):
+        ids, probs = orc.alt_tokens(l, c, 20000)
+        assert prev <= set(ids.tolist())          # a higher cutoff keeps every earlier candidate
+        prev = set(ids.tolist())
+        assert np.all(probs / probs[0] >= (1 - c) * (1 - 1e-6))
+        assert np.all(np.diff(probs) <= 0)
