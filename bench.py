@@ -127,8 +127,8 @@ def timed(torch, stream, launch, copies, reps, replays=5):
 def kernels_leg(torch, synth, vox, dev, stream):
     """Per-kernel device times of the workloads beside the decoder step: the single 3072x3072
     GEMV, one decoder layer's linears, GQA attention at three ring fills, the encoder-chunk
-    GEMM set, the encoder's chunk attention, the GEMV over 16-bit weights, the adapter.  Every
-    measurement streams more than 1 GiB of distinct weights."""
+    GEMM set, the encoder's chunk attention, the GEMV over 16-bit weights, the alternative tokens,
+    the adapter.  The weight-streaming measurements rotate over more than 1 GiB of distinct copies."""
     GiB = 2 ** 30
     out = []
 
@@ -259,6 +259,20 @@ def kernels_leg(torch, synth, vox, dev, stream):
               "bytes": b, "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
         del chain, head
         torch.cuda.empty_cache()
+
+    # the greedy token and its alternatives from one step's logits (vocabulary 131072)
+    V = synth.VOXTRAL_DECODER.vocab
+    lg = (synth.normal_f32(synth.generator(synth.SEED_DECODER, 9), (V,)) * np.float32(3.0))
+    lgs = [torch.from_numpy(lg).to(dev) for _ in range(4)]
+    for max_out in (8, 32):
+        ids = torch.empty(max_out, dtype=torch.int32, device=dev)
+        probs = torch.empty(max_out, dtype=torch.float32, device=dev)
+        cnt = torch.empty(1, dtype=torch.int32, device=dev)
+        aws = torch.empty(vox.alt_tokens_workspace(V, max_out), dtype=torch.uint8, device=dev)
+        us = timed(torch, stream, lambda i: vox.alt_tokens(lgs[i], 0.9, max_out, ids, probs, cnt, aws), 4, 50)
+        emit({"kernel": "alt_tokens", "case": f"vocab {V}, cutoff 0.9, max_out {max_out}", "us": round(us, 3),
+              "bytes": V * 4, "gbs": round(V * 4 / us / 1e3, 1)})
+    del lgs
 
     # adapter (linear 5120 -> 3072, GELU, linear 3072 -> 3072) over the rows of one encoder chunk
     k, n_mid, n_out = synth.ADAPTER

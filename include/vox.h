@@ -134,6 +134,21 @@ int vox_gqa_decode_attn(const float *q, const float *k_cache, const float *v_cac
                         int n_q_heads, int n_kv_heads, int head_dim, int n_slots, int n_valid,
                         float scale, void *workspace, size_t workspace_bytes, void *stream);
 
+/* The greedy token and its alternatives from one step's logits ([VC] 사용 방법: --alt <cutoff>
+ * lists candidate tokens beside the chosen one, more for a higher cutoff; [VC] C API 구조: the
+ * number of alternatives is set per stream).  With t the largest logit (lowest index on a tie),
+ * token i is listed when logits[i] >= logits[t] + d, the sum taken in fp32 with d = ln(1 - cutoff)
+ * rounded to fp32 (every token when cutoff >= 1): its probability is at least (1 - cutoff) times
+ * t's.  The list (t first) runs by logit, higher first, ties to the lower index, at most max_out
+ * entries: ids[j] and probs[j] (softmax over all vocab logits, fp32), *count = its length; entries
+ * past the count are left untouched.  logits: vocab fp32 values, no NaN.  ids, probs: max_out
+ * entries; count: one int32; all device memory.  workspace: vox_alt_tokens_workspace(vocab,
+ * max_out) bytes, 8-byte aligned, contents irrelevant.  vocab < 1, cutoff < 0 or NaN, max_out < 1
+ * -> VOX_E_INVAL; vocab > 262144 or max_out > 32 -> VOX_E_UNSUPPORTED. */
+size_t vox_alt_tokens_workspace(int64_t vocab, int max_out);
+int vox_alt_tokens(const float *logits, int64_t vocab, float cutoff, int max_out, int32_t *ids, float *probs,
+                   int32_t *count, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------------------
  * Whole decoder step ([VC] 모델 아키텍처, 주요 기능, 성능 벤치마크).  Per token:
  *   h = dequant(tok_embd[token]);

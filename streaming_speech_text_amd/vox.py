@@ -60,6 +60,8 @@ _SIGS = {
     "vox_enc_attn": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _f32, _vp, _sz, _vp]),
     "vox_gqa_decode_attn_workspace": (_sz, [_int, _int, _int, _int]),
     "vox_gqa_decode_attn": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _f32, _vp, _sz, _vp]),
+    "vox_alt_tokens_workspace": (_sz, [_i64, _int]),
+    "vox_alt_tokens": (_int, [_vp, _i64, _f32, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "vox_decoder_workspace": (_int, [C.POINTER(DecoderConfig), C.POINTER(_sz), C.POINTER(_sz)]),
     "vox_decoder_create": (_int, [C.POINTER(DecoderConfig), C.POINTER(DecoderWeights), _vp, _sz, _vp, _sz, _vp,
                                   C.POINTER(_vp)]),
@@ -201,6 +203,20 @@ def enc_attn(q, k, v, out, n_heads, window, scale=None, workspace=None, stream=N
     _check(lib().vox_enc_attn(_ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
                               _ptr(out, torch.float32, "out"), m, n_ctx, n_heads, hd, window, scale,
                               _ptr(workspace, None, "workspace") if wsb else None, wsb, _stream(stream)))
+
+
+def alt_tokens_workspace(vocab, max_out) -> int:
+    return int(lib().vox_alt_tokens_workspace(vocab, max_out))
+
+
+def alt_tokens(logits, cutoff, max_out, ids, probs, count, workspace, stream=None):
+    """Greedy token and alternatives: logits fp32 [vocab]; ids int32 [max_out], probs fp32 [max_out],
+    count int32 [1] (device); workspace >= alt_tokens_workspace(vocab, max_out) bytes."""
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().vox_alt_tokens(_ptr(logits, torch.float32, "logits"), logits.numel(), float(cutoff), int(max_out),
+                                _ptr(ids, torch.int32, "ids"), _ptr(probs, torch.float32, "probs"),
+                                _ptr(count, torch.int32, "count"), _ptr(workspace, None, "workspace"), wsb,
+                                _stream(stream)))
 
 
 def gqa_decode_attn_workspace(n_q_heads, n_kv_heads, head_dim, n_slots) -> int:

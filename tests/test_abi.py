@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("vox_q4_dequant", "vox_q4_gemv", "vox_q4_gemm", "vox_q4_gemm_workspace", "vox_gqa_decode_attn",
                  "vox_gqa_decode_attn_workspace", "vox_adapter", "vox_adapter_workspace", "vox_enc_attn",
-                 "vox_enc_attn_workspace", "vox_w16_gemv", "vox_decoder_step",
+                 "vox_enc_attn_workspace", "vox_w16_gemv", "vox_alt_tokens", "vox_alt_tokens_workspace",
+                 "vox_decoder_step",
                  "vox_decoder_create", "vox_decoder_workspace", "vox_strerror", "vox_last_error"):
         assert name in fns
 
@@ -74,6 +75,13 @@ def test_validation_before_device_work(lib):
     assert lib.vox_w16_gemv(p, 2, p, C.c_void_p(0x800000), 10, 16, None) == vox.VOX_E_INVAL    # fmt
     assert lib.vox_w16_gemv(p, 1, p, C.c_void_p(0x800000), 0, 16, None) == vox.VOX_OK          # empty
     assert lib.vox_w16_gemv(C.c_void_p(0x1008), 0, p, C.c_void_p(0x800000), 10, 16, None) == vox.VOX_E_UNSUPPORTED
+    assert lib.vox_alt_tokens_workspace(131072, 8) == 256 * 8 * 8 + 256 * 8
+    assert lib.vox_alt_tokens_workspace(131072, 33) == 0 and lib.vox_alt_tokens_workspace(262145, 8) == 0
+    q4 = (p, C.c_void_p(0x200000), C.c_void_p(0x300000), C.c_void_p(0x400000))
+    assert lib.vox_alt_tokens(p, 1000, C.c_float(-0.5), 4, *q4[1:], C.c_void_p(0x500000), 4096, None) == vox.VOX_E_INVAL
+    assert lib.vox_alt_tokens(p, 1000, C.c_float(0.5), 40, *q4[1:], C.c_void_p(0x500000), 4096, None) == \
+        vox.VOX_E_UNSUPPORTED
+    assert lib.vox_alt_tokens(p, 1000, C.c_float(0.5), 4, *q4[1:], C.c_void_p(0x500000), 8, None) == vox.VOX_E_WORKSPACE
     # adapter: workspace holds the GELU pairs (2 x bf16 per value) plus the larger product's partials
     assert lib.vox_adapter_workspace(16, 5120, 3072, 3072) >= 16 * 3072 * 4
     assert lib.vox_adapter_workspace(16, 5120, 3072, 3072) % 16 == 0
