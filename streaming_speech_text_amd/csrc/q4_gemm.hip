@@ -72,16 +72,17 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t q)
 
 // GELU(v) = v * Phi(v) = v * erfc(-v / sqrt 2) / 2 in fp32, stored as hi = GELU(v) rounded to
 // bf16 and lo = the (exact fp32) remainder rounded to bf16, so hi + lo is within 2^-18 |GELU(v)|.
-// Layout: row `row` of hl is 2n values; column c of stage s = c / 256 puts hi at 512 s + c % 256
-// and lo 256 further, i.e. the stages of K alternate hi and lo halves.
+// Layout: row `row` of hl is 2n values; column c of 128-input stage s = c / 128 puts hi at
+// 256 s + c % 128 and lo 128 further, i.e. the stages of K alternate hi and lo halves.
+constexpr int GELU_STAGE = 128;
 __device__ __forceinline__ void store_gelu_pair(uint16_t *hl, int n, int64_t row, int col, float v)
 {
     const float g = 0.5f * v * erfcf(-0.70710678118654752f * v);
     const __bf16 hi = (__bf16)g;
     const __bf16 lo = (__bf16)(g - (float)hi);
-    uint16_t *p = hl + row * 2 * n + 2 * (col & ~255) + (col & 255);
+    uint16_t *p = hl + row * 2 * n + 2 * (col & ~(GELU_STAGE - 1)) + (col & (GELU_STAGE - 1));
     p[0] = __builtin_bit_cast(uint16_t, hi);
-    p[256] = __builtin_bit_cast(uint16_t, lo);
+    p[GELU_STAGE] = __builtin_bit_cast(uint16_t, lo);
 }
 
 template <int MI, int NJ>
@@ -200,25 +201,33 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
 }
 
 // ---------------------------------------------------------------------------------------
-// Tiled kernel for longer chunks (K of 1280 or 5120).  A workgroup of 8 waves owns a 64 x 64
-// tile of Y and walks K in stages of 8 Q4_0 blocks; in every stage wave w takes block w, so
-// each wave computes the whole tile over one eighth of K and no operand is shared:
-//  * the wave loads its A operands straight from memory one stage ahead: lane L's 16 bytes
+// Tiled kernel for longer chunks (K of 1280, 3072 or 5120).  A workgroup of 4 waves owns a
+// 64 x 64 tile of Y and walks K in stages of 4 Q4_0 blocks; in every stage wave w takes block w,
+// so each wave computes the whole tile over a quarter of K and no operand is shared:
+//  * the wave loads its A operands straight from memory two stages ahead: lane L's 16 bytes
 //    of a 16-row block are row L % 16, inputs 8(L/16) .. 8(L/16)+7 of the Q4_0 block;
-//  * the workgroup copies the stage's weight bytes (8 blocks = 144 contiguous, 16-byte aligned
-//    bytes per row) to LDS with 16-byte loads; each wave then reads the bytes of its block
+//  * the workgroup copies the stage's weight bytes (4 blocks = 72 contiguous, 8-byte aligned
+//    bytes per row) to LDS with 8-byte loads; each wave then reads the bytes of its block
 //    with aligned dword reads and unpacks the codes in registers to exact bf16: lane group g
 //    of a column takes inputs 8g .. 8g+7, i.e. the low (g < 2) or high (g >= 2) nibbles of
 //    code bytes 8(g%2) .. 8(g%2)+7;
 //  * per block the wave runs 4 x 4 matrix-core products of A with the exact (code - 8) values,
 //    each the block's sum of a * (code - 8) up to fp32 rounding; scale * product goes into fp32.
-// The eight waves' partial tiles are added through LDS in a fixed tree order at the end.
+// The four waves' partial tiles are added through LDS in a fixed tree order at the end.  Two
+// workgroups share a compute unit (at most 256 VGPRs per wave), so one's stage barrier overlaps
+// the other's work (measured on MI355X against eight-wave workgroups with 8-block stages, one
+// per compute unit: the encoder linear sets 6 % faster at 64-750 frames).
 // ---------------------------------------------------------------------------------------
-constexpr int GT_BM = 64, GT_BN = 64, GT_KC = 8, GT_THREADS = 512;
+constexpr int GT_BM = 64, GT_BN = 64, GT_KC = 4, GT_THREADS = 256;
+constexpr int GT_STAGE = GT_KC * 32;                        // inputs per stage
+constexpr int GT_WAVES = GT_THREADS / 64;
 constexpr int GT_RAW = GT_KC * 18;                          // weight bytes of one row per stage
-constexpr int GT_W_CHUNKS = GT_BN * GT_RAW / 16;            // 16-byte weight pieces per stage
-static_assert(GT_W_CHUNKS <= 2 * GT_THREADS, "two rounds of weight loads cover a stage");
+constexpr int GT_WB = 8;                                    // bytes per weight piece (72 = 9 x 8)
+constexpr int GT_W_CHUNKS = GT_BN * GT_RAW / GT_WB;         // weight pieces per stage
+constexpr int GT_WR = (GT_W_CHUNKS + GT_THREADS - 1) / GT_THREADS;   // load rounds per stage
+static_assert(GT_RAW % GT_WB == 0, "a row's stage bytes split into whole pieces");
 static_assert(GT_KC == GT_THREADS / 64, "one block per wave per stage");
+static_assert(GELU_STAGE == GT_STAGE, "a GELU pair stage is one weight stage of the second product");
 
 // Byte j of v as a float (one v_cvt_f32_ubyte{j}).
 __device__ __forceinline__ float ubyte_to_f(uint32_t v, int j)
@@ -249,8 +258,8 @@ __device__ __forceinline__ u32x4v nibbles_to_bf16(uint32_t lo, uint32_t hi, bool
     return p;
 }
 
-// Reads the bytes of block `blk` (0..7 of the stage) of the four 16-column blocks from the raw
-// stage copy (144 bytes per row) with aligned dword reads and unpacks this lane's operand
+// Reads the bytes of block `blk` (0..GT_KC-1 of the stage) of the four 16-column blocks from the
+// raw stage copy (GT_RAW bytes per row) with aligned dword reads and unpacks this lane's operand
 // (column 16j + l16, inputs 8*grp .. 8*grp+7) and scale.  ODD: blk is odd, so the block starts
 // at 2 mod 4 and its code bytes are 4-aligned; otherwise the block is 4-aligned and the code
 // bytes are 2 mod 4.
@@ -299,18 +308,18 @@ __device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, 
 //               reads weight stage st / 2, so each weight stage serves its hi and lo halves.
 enum { T_PLAIN = 0, T_GELU_OUT = 1, T_PAIR_IN = 2 };
 
-// NS: stages (of 256 inputs) per workgroup, fixed at compile time.  Workgroup z of the grid's
+// NS: stages (of GT_STAGE inputs) per workgroup, fixed at compile time.  Workgroup z of the grid's
 // third dimension takes stages z*NS .. z*NS+NS-1; with one slice it writes the output itself,
 // otherwise its fp32 partial tile goes to part[z][m][n] and q4_gemm_reduce_kernel adds the
 // slices.  k is the activations' row length.
 template <int NS, int MODE>
-__global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t *__restrict__ w,
+__global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_tiled_kernel(const uint8_t *__restrict__ w,
                                                                    const uint16_t *__restrict__ x,
                                                                    float *__restrict__ y, uint16_t *__restrict__ hl,
                                                                    float *__restrict__ part, int m, int n, int k)
 {
     __shared__ __attribute__((aligned(16))) uint32_t braw[2][GT_BN * GT_RAW / 4];
-    __shared__ f32x4v red[4][16][64];   // tree reduction of the waves' tiles
+    __shared__ f32x4v red[GT_WAVES / 2][16][64];   // tree reduction of the waves' tiles
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -327,31 +336,32 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         aoff[i] = (uint32_t)min(m0 + 16 * i + l16, m - 1) * (uint32_t)k + (uint32_t)(32 * wave + 8 * grp);
-    // weight pieces: chunk c -> row c / 9 of the tile, piece c % 9; the second round is clamped
-    // to the last chunk (a duplicate load and an identical LDS store)
-    uint32_t woff[2];
-    int wlds[2];
+    // weight pieces: chunk c -> row c / (GT_RAW / GT_WB) of the tile, piece c % (GT_RAW / GT_WB);
+    // rounds past the last chunk are clamped to it (a duplicate load and an identical LDS store)
+    uint32_t woff[GT_WR];
+    int wlds[GT_WR];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < GT_WR; ++r) {
         const int c = min(tid + GT_THREADS * r, GT_W_CHUNKS - 1);
-        const int col = min(n0 + c / (GT_RAW / 16), n - 1);
-        woff[r] = (uint32_t)col * row_bytes + (uint32_t)(16 * (c % (GT_RAW / 16)));
-        wlds[r] = 4 * c;
+        const int col = min(n0 + c / (GT_RAW / GT_WB), n - 1);
+        woff[r] = (uint32_t)col * row_bytes + (uint32_t)(GT_WB * (c % (GT_RAW / GT_WB)));
+        wlds[r] = (GT_WB / 4) * c;
     }
 
     // two stages of loads in flight: register slots 0 and 1 (compile-time indices)
-    u32x4v ar[2][4], wr[2][2];
+    u32x4v ar[2][4];
+    u32x2v wr[2][GT_WR];
     auto load_stage = [&](int st, auto slot) {
         constexpr int S = decltype(slot)::value;
         st = min(st, st_end - 1);   // past the slice: a harmless reload of its last stage
-        const uint16_t *xs = x + (size_t)st * (GT_KC * 32);
+        const uint16_t *xs = x + (size_t)st * GT_STAGE;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             ar[S][i] = *reinterpret_cast<const u32x4v *>(xs + aoff[i]);
         const uint8_t *ws = w + (size_t)(st >> KWS) * GT_RAW;
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-            wr[S][r] = *reinterpret_cast<const u32x4v *>(ws + woff[r]);
+        for (int r = 0; r < GT_WR; ++r)
+            wr[S][r] = *reinterpret_cast<const u32x2v *>(ws + woff[r]);
     };
 
     f32x4v acc[4][4];
@@ -365,15 +375,15 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
         constexpr int S = decltype(slot)::value;
         const int b = st & 1;
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-            *reinterpret_cast<u32x4v *>(&braw[b][wlds[r]]) = wr[S][r];
+        for (int r = 0; r < GT_WR; ++r)
+            *reinterpret_cast<u32x2v *>(&braw[b][wlds[r]]) = wr[S][r];
         bf16x8 af[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             af[i] = __builtin_bit_cast(bf16x8, ar[S][i]);
         __syncthreads();   // braw[b] complete; braw[b] is next written two stages later
         // B operands of block `wave` for the four 16-column blocks.  The block of column c
-        // starts at byte o = c*144 + 18*wave: 4-aligned for even waves, 2 mod 4 for odd ones
+        // starts at byte o = c*GT_RAW + 18*wave: 4-aligned for even waves, 2 mod 4 for odd ones
         // (the parity is uniform over a wave, so each wave runs one straight-line path).
         bf16x8 bf[4];
         float d[4];
@@ -410,9 +420,9 @@ __global__ __launch_bounds__(GT_THREADS) void q4_gemm_tiled_kernel(const uint8_t
     if constexpr (NS % 2)
         stage(st_end - 1, S0());
 
-    // tree: (w + 4) -> w, then (w + 2) -> w, then 1 -> 0; fixed order
+    // tree: (w + half) -> w for half = waves/2 .. 1; fixed order
 #pragma unroll
-    for (int half = 4; half >= 1; half >>= 1) {
+    for (int half = GT_WAVES / 2; half >= 1; half >>= 1) {
         if (wave >= half && wave < 2 * half) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -504,27 +514,24 @@ static bool tiled_shape(int64_t m, int64_t n, int64_t k)
 }
 
 // K slices for the tiled kernel (measured on MI355X at the encoder's shapes): none once the
-// output tiles alone give 160 workgroups; for 12 or 20 stages, the fewest slices (dividing the
-// stages, at least two stages each) that reach 160 workgroups, else the most; for 5 stages, one
-// stage per workgroup when there are at most 40 tiles, else none.  The slices' partial tiles are
-// added by q4_gemm_reduce_kernel.
+// output tiles alone give 160 workgroups, else the fewest slices (dividing the stages, at least
+// two stages each) that reach 160 workgroups, else the most (320 or 512 workgroups was slower).
+// The slices' partial tiles are added by q4_gemm_reduce_kernel.
+constexpr int GT_TARGET_WGS = 160;
 static int tiled_slices(int64_t m, int64_t n, int64_t k)
 {
     const int64_t tiles = ((n + GT_BN - 1) / GT_BN) * ((m + GT_BM - 1) / GT_BM);
-    const int nst = (int)(k / 256);
-    if (tiles >= 160)
+    const int nst = (int)(k / GT_STAGE);
+    if (tiles >= GT_TARGET_WGS)
         return 1;
-    if (nst >= 10) {
-        int most = 1;
-        for (int ks = 2; 2 * ks <= nst; ++ks)
-            if (nst % ks == 0) {
-                if (tiles * ks >= 160)
-                    return ks;
-                most = ks;
-            }
-        return most;
-    }
-    return tiles <= 40 ? nst : 1;
+    int most = 1;
+    for (int ks = 2; 2 * ks <= nst; ++ks)
+        if (nst % ks == 0) {
+            if (tiles * ks >= GT_TARGET_WGS)
+                return ks;
+            most = ks;
+        }
+    return most;
 }
 
 static size_t tiled_workspace(int64_t m, int64_t n, int slices)
@@ -549,10 +556,13 @@ static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_
                              int k, int slices, hipStream_t s)
 {
     constexpr bool gelu = MODE == T_GELU_OUT;
-    if ((slices > 1) != (part != nullptr) || (gelu ? (hl == nullptr || n % 256) : y == nullptr))
+    if ((slices > 1) != (part != nullptr) || (gelu ? (hl == nullptr || n % GELU_STAGE) : y == nullptr))
         return fail(VOX_E_INVAL, "q4 tiled product: one output, and a partial-tile buffer exactly when K is split");
-    switch ((k / 256) / slices) {   // stages per workgroup
+    switch ((k / GT_STAGE) / slices) {   // stages per workgroup
+    case 48: launch_tiled_slices<48, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 40: launch_tiled_slices<40, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
     case 24: launch_tiled_slices<24, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 16: launch_tiled_slices<16, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
     case 20: launch_tiled_slices<20, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
     case 12: launch_tiled_slices<12, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
     case 10: launch_tiled_slices<10, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
