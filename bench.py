@@ -304,8 +304,8 @@ def kernels_leg(torch, synth, vox, dev, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
-              "described in DESIGN.md and not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layout over several GPUs "
+              "is designed but not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch

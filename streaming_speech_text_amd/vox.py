@@ -78,8 +78,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with streaming_speech_text_amd/build.py "
-                              "(or __graft_entry__.build())")
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "python -m streaming_speech_text_amd.build")
         L = C.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             if not hasattr(L, name):
