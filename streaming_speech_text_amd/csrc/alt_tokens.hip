@@ -11,12 +11,19 @@
 // logit, higher first, ties to the lower index, at most max_out entries, each with its softmax
 // probability over the whole vocabulary.
 //
-// Two kernels.  Each wave of the first takes 512 logits: their max and the sum of exp(l - max)
-// (fixed order), and its max_out best (logit, index) keys from a bitonic sort held in registers
-// (VALU lane exchanges, no LDS, no barriers).  One workgroup of the second folds all partial lists into the best
-// max_out with the same in-wave sort, adds the partial sums rescaled to the global max (fixed
-// order), and writes the list.  Keys pack an order-preserving image of the
-// logit above the inverted index, so a larger key is a larger logit, then a lower index.
+// Three kernels, all selections on keys that pack an order-preserving image of the logit above
+// the inverted index (a larger key is a larger logit, then a lower index):
+//  * stats: each wave takes 512 logits: their max, the sum of exp(l - max) in a fixed order, and
+//    their largest key;
+//  * select: each wave finds the largest key of the whole vocabulary from the per-block ones
+//    (this is the greedy token t), forms the threshold and keeps its logits that pass it.  Up to
+//    max_out of them are written as they are; past that, a bitonic sort held in registers (VALU
+//    lane exchanges, no LDS or barriers) picks the best max_out;
+//  * final: one workgroup gathers the kept keys.  When at most 512 remain, one wave sorts them
+//    with the smallest power-of-two network that holds them (64 keys in the usual case, where a
+//    handful of tokens pass); otherwise the waves fold all per-block lists through 512-key sorts.
+//    The partial sums are rescaled to the global max (fixed order) and the list written.
+// The selected list is unique (the keys are distinct), so the gathering order does not matter.
 #include <cmath>
 
 #include "vox_common.h"
@@ -76,20 +83,21 @@ __device__ __forceinline__ void pair_minmax(u64 v, int m, u64 &mx, u64 &mn)
     mn = a > b ? b : a;
 }
 
-// Descending bitonic sort of a wave's 512 keys, element r * 64 + lane in v[r], without barriers
-// or LDS: pairs 64 or more apart are two registers of one lane, nearer pairs one register of two
-// lanes exchanged with VALU lane operations.
-__device__ __forceinline__ void wave_sort512_desc(u64 (&v)[8])
+// Descending bitonic sort of a wave's 64 R keys (R a power of two), element r * 64 + lane in v[r],
+// without barriers or LDS: pairs 64 or more apart are two registers of one lane, nearer pairs one
+// register of two lanes exchanged with VALU lane operations.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(u64 (&v)[R])
 {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int k = 2; k <= 512; k <<= 1) {
+    for (int k = 2; k <= 64 * R; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
             if (j >= 64) {
                 const int jr = j >> 6;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
+                for (int r = 0; r < R; ++r) {
                     if (r & jr)
                         continue;
                     const bool desc = ((r * 64 + lane) & k) == 0;   // the pair's run goes downwards
@@ -100,7 +108,7 @@ __device__ __forceinline__ void wave_sort512_desc(u64 (&v)[8])
                 }
             } else {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
+                for (int r = 0; r < R; ++r) {
                     u64 mx, mn;
                     pair_minmax(v[r], j, mx, mn);
                     const bool desc = ((r * 64 + lane) & k) == 0;
@@ -113,27 +121,50 @@ __device__ __forceinline__ void wave_sort512_desc(u64 (&v)[8])
     }
 }
 
-// One wave per 512 logits: their max, the sum of exp(l - max) (fixed order), and the kout best
-// keys (the first kout of the sorted 512).
-__global__ __launch_bounds__(64) void alt_partial_kernel(const float *__restrict__ logits, int vocab, int kout,
-                                                         u64 *__restrict__ pkeys, float *__restrict__ pm,
-                                                         float *__restrict__ ps)
+// Largest of the wave's keys, in every lane.
+__device__ __forceinline__ u64 wave_max_key(u64 v)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        u64 mx, mn;
+        pair_minmax(v, m, mx, mn);
+        v = mx;
+    }
+    return v;
+}
+
+// Largest key of the vocabulary from the per-block largest keys, in every lane of the wave.
+__device__ __forceinline__ u64 global_max_key(const u64 *__restrict__ pk, int nblk)
+{
+    const int lane = threadIdx.x & 63;
+    u64 m = 0ull;
+    for (int b = lane; b < nblk; b += 64)
+        m = pk[b] > m ? pk[b] : m;
+    return wave_max_key(m);
+}
+
+// One wave per 512 logits: their max, the sum of exp(l - max) (fixed order), their largest key.
+__global__ __launch_bounds__(64) void alt_stats_kernel(const float *__restrict__ logits, int vocab,
+                                                       float *__restrict__ pm, float *__restrict__ ps,
+                                                       u64 *__restrict__ pk)
 {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     float l[8];
-    u64 v[8];
     float mx = -INFINITY;
+    u64 km = 0ull;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int i = b * ALT_BLOCK + r * 64 + lane;
         const bool in = i < vocab;
         l[r] = in ? logits[i] : -INFINITY;
         // -0 keys as +0 so that equal logits tie on the index; key 0 ranks below every logit
-        v[r] = in ? argmax_key(l[r] == 0.0f ? 0.0f : l[r], (uint32_t)i) : 0ull;
+        const u64 key = in ? argmax_key(l[r] == 0.0f ? 0.0f : l[r], (uint32_t)i) : 0ull;
+        km = key > km ? key : km;
         mx = fmaxf(mx, l[r]);
     }
     mx = wave_max(mx);
+    km = wave_max_key(km);
     float sum = 0.0f;
     if (mx != -INFINITY) {
 #pragma unroll
@@ -141,58 +172,146 @@ __global__ __launch_bounds__(64) void alt_partial_kernel(const float *__restrict
             sum += expf(l[r] - mx);
     }
     sum = wave_sum(sum);
-    wave_sort512_desc(v);
-    if (lane < kout)
-        pkeys[(size_t)b * kout + lane] = v[0];
     if (lane == 0) {
         pm[b] = mx;
         ps[b] = sum;
+        pk[b] = km;
     }
 }
 
-// One workgroup: each wave folds chunks of the partial keys into its running best kout (kept in
-// the first kout slots, sorted with 512 - kout new keys at a time), wave 0 merges the 16 waves'
-// lists, then the sum is rescaled to the global max (fixed order) and the list written.
-__global__ __launch_bounds__(ALT_T2) void alt_final_kernel(const u64 *__restrict__ pkeys, const float *__restrict__ pm,
+// One wave per 512 logits: the keys of those at or above the threshold M + d (M the largest logit
+// of the vocabulary), at most kout of them (the best kout by a sort when more pass), into the
+// block's kout slots, the rest of the slots 0; their number into pc[b].
+__global__ __launch_bounds__(64) void alt_select_kernel(const float *__restrict__ logits, int vocab, int nblk,
+                                                        int kout, float d, const u64 *__restrict__ pk,
+                                                        u64 *__restrict__ pkeys, int32_t *__restrict__ pc)
+{
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    float l[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int i = b * ALT_BLOCK + r * 64 + lane;
+        l[r] = i < vocab ? logits[i] : -INFINITY;
+    }
+    const float tau = key_logit(global_max_key(pk, nblk)) + d;
+    u64 v[8];
+    bool pass[8];
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int i = b * ALT_BLOCK + r * 64 + lane;
+        pass[r] = i < vocab && l[r] >= tau;
+        v[r] = pass[r] ? argmax_key(l[r] == 0.0f ? 0.0f : l[r], (uint32_t)i) : 0ull;
+        c += __popcll(__ballot(pass[r]));
+    }
+    u64 *out = pkeys + (size_t)b * kout;
+    if (c <= kout) {
+        // in element order: a lane's slot is the count of passing elements before it
+        int base = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const u64 m = __ballot(pass[r]);
+            const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            if (pass[r])
+                out[base + before] = v[r];
+            base += __popcll(m);
+        }
+        if (lane >= c && lane < kout)
+            out[lane] = 0ull;
+    } else {
+        wave_sort_desc<8>(v);
+        if (lane < kout)
+            out[lane] = v[0];
+        c = kout;
+    }
+    if (lane == 0)
+        pc[b] = c;
+}
+
+// Sort of the first T <= 64 R keys of cand (the rest as key 0) by one wave; lane j of the result
+// holds the j-th largest.
+template <int R>
+__device__ __forceinline__ u64 sort_gathered(const u64 *cand, int T)
+{
+    const int lane = threadIdx.x & 63;
+    u64 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = r * 64 + lane;
+        v[r] = e < T ? cand[e] : 0ull;
+    }
+    wave_sort_desc<R>(v);
+    return v[0];
+}
+
+// One workgroup.  Each thread appends one block's kept keys to cand (the order does not matter).
+// At most 512 in all: wave 0 sorts them.  More: each wave folds chunks of all the blocks' slots
+// into its running best kout (kept in the first kout slots, sorted with 512 - kout new keys at a
+// time) and wave 0 merges the 16 waves' lists.  Then the sum is rescaled to the global max (fixed
+// order) and the list written.
+__global__ __launch_bounds__(ALT_T2) void alt_final_kernel(const u64 *__restrict__ pkeys, const int32_t *__restrict__ pc,
+                                                           const u64 *__restrict__ pk, const float *__restrict__ pm,
                                                            const float *__restrict__ ps, int nblk, int kout, float d,
-                                                           int max_out, int32_t *__restrict__ ids,
-                                                           float *__restrict__ probs, int32_t *__restrict__ count)
+                                                           int32_t *__restrict__ ids, float *__restrict__ probs,
+                                                           int32_t *__restrict__ count)
 {
     constexpr int WAVES = ALT_T2 / 64;
-    __shared__ u64 best[WAVES * ALT_MAX_OUT];
+    static_assert(WAVES * ALT_MAX_OUT <= ALT_BLOCK, "the waves' lists share the gathering buffer");
+    __shared__ u64 cand[ALT_BLOCK];
     __shared__ float red[WAVES];
     __shared__ float gmax;
+    __shared__ int total;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = nblk * kout;
-    const int fresh = ALT_BLOCK - kout;   // new keys per chunk
-    u64 v[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        v[r] = 0ull;
-    for (int c0 = wave * fresh; c0 < n; c0 += WAVES * fresh) {
-        // slots 0 .. kout-1 keep the running best; the others take keys c0 ...
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int e = r * 64 + lane;
-            if (e >= kout) {
-                const int i = c0 + e - kout;
-                v[r] = i < n ? pkeys[i] : 0ull;
-            }
-        }
-        wave_sort512_desc(v);
-    }
-    if (lane < kout)
-        best[wave * kout + lane] = v[0];
+    if (threadIdx.x == 0)
+        total = 0;
     __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int e = r * 64 + lane;
-            v[r] = e < WAVES * kout ? best[e] : 0ull;
+    for (int b = threadIdx.x; b < nblk; b += ALT_T2) {
+        const int c = pc[b];
+        if (c > 0) {
+            const int at = atomicAdd(&total, c);
+            for (int j = 0; j < c && at + j < ALT_BLOCK; ++j)
+                cand[at + j] = pkeys[(size_t)b * kout + j];
         }
-        wave_sort512_desc(v);   // the final list is v[0] of lanes 0 .. max_out-1
+    }
+    __syncthreads();
+    const int T = total;
+    u64 top = 0ull;   // in wave 0: lane j holds the j-th best kept key
+    if (T <= ALT_BLOCK) {
+        if (wave == 0)
+            top = T <= 64 ? sort_gathered<1>(cand, T)
+                : T <= 128 ? sort_gathered<2>(cand, T)
+                : T <= 256 ? sort_gathered<4>(cand, T)
+                           : sort_gathered<8>(cand, T);
+    } else {
+        const int n = nblk * kout;
+        const int fresh = ALT_BLOCK - kout;   // new keys per chunk
+        u64 v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            v[r] = 0ull;
+        for (int c0 = wave * fresh; c0 < n; c0 += WAVES * fresh) {
+            // slots 0 .. kout-1 keep the running best; the others take keys c0 ...
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int e = r * 64 + lane;
+                if (e >= kout) {
+                    const int i = c0 + e - kout;
+                    v[r] = i < n ? pkeys[i] : 0ull;
+                }
+            }
+            wave_sort_desc<8>(v);
+        }
+        if (lane < kout)
+            cand[wave * kout + lane] = v[0];
+        __syncthreads();
+        if (wave == 0)
+            top = sort_gathered<8>(cand, WAVES * kout);
+    }
+    if (wave == 0) {
+        const u64 gk = global_max_key(pk, nblk);   // the greedy token's key
         if (lane == 0)
-            gmax = key_logit(v[0]);
+            gmax = key_logit(gk);
     }
     __syncthreads();
     const float M = gmax;   // the greedy token's logit, the global max
@@ -208,9 +327,9 @@ __global__ __launch_bounds__(ALT_T2) void alt_final_kernel(const u64 *__restrict
         for (int w = 0; w < WAVES; ++w)
             zt += red[w];
         const float tau = M + d;
-        const u64 key = lane < max_out ? v[0] : 0ull;
+        const u64 key = lane < kout ? top : 0ull;
         const float lj = key_logit(key);
-        const bool take = lane < max_out && key != 0ull && lj >= tau;
+        const bool take = lane < kout && key != 0ull && lj >= tau;
         // the keys are sorted and the test is monotone in the logit: the taken ones are a prefix
         const u64 mask = __ballot(take);
         if (take) {
@@ -231,7 +350,8 @@ extern "C" size_t vox_alt_tokens_workspace(int64_t vocab, int max_out)
     if (vocab <= 0 || vocab > ALT_MAX_VOCAB || max_out < 1 || max_out > ALT_MAX_OUT)
         return 0;
     const int64_t nblk = (vocab + ALT_BLOCK - 1) / ALT_BLOCK;
-    return (size_t)nblk * max_out * 8 + (size_t)nblk * 8;
+    // kept keys, largest keys, maxima, sums, kept counts
+    return (size_t)nblk * max_out * 8 + (size_t)nblk * (8 + 4 + 4 + 4);
 }
 
 extern "C" int vox_alt_tokens(const float *logits, int64_t vocab, float cutoff, int max_out, int32_t *ids,
@@ -250,18 +370,24 @@ extern "C" int vox_alt_tokens(const float *logits, int64_t vocab, float cutoff, 
     if (!aligned(workspace, 8))
         return fail(VOX_E_INVAL, "vox_alt_tokens: workspace must be 8-byte aligned");
     const int nblk = (int)((vocab + ALT_BLOCK - 1) / ALT_BLOCK);
-    unsigned long long *pkeys = (unsigned long long *)workspace;
-    float *pm = (float *)(pkeys + (size_t)nblk * max_out);
+    u64 *pkeys = (u64 *)workspace;
+    u64 *pk = pkeys + (size_t)nblk * max_out;
+    float *pm = (float *)(pk + nblk);
     float *ps = pm + nblk;
+    int32_t *pc = (int32_t *)(ps + nblk);
     // d = ln(1 - cutoff) rounded to fp32 (computed here in double; every token when cutoff >= 1)
     const float d = cutoff >= 1.0f ? -INFINITY : (float)std::log(1.0 - (double)cutoff);
     hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(alt_partial_kernel, dim3((unsigned)nblk), dim3(64), 0, s, logits, (int)vocab, max_out, pkeys,
-                       pm, ps);
-    int st = check_launch("vox_alt_tokens partial");
+    hipLaunchKernelGGL(alt_stats_kernel, dim3((unsigned)nblk), dim3(64), 0, s, logits, (int)vocab, pm, ps, pk);
+    int st = check_launch("vox_alt_tokens stats");
     if (st)
         return st;
-    hipLaunchKernelGGL(alt_final_kernel, dim3(1), dim3(ALT_T2), 0, s, pkeys, pm, ps, nblk, max_out, d, max_out, ids,
+    hipLaunchKernelGGL(alt_select_kernel, dim3((unsigned)nblk), dim3(64), 0, s, logits, (int)vocab, nblk, max_out, d,
+                       pk, pkeys, pc);
+    st = check_launch("vox_alt_tokens select");
+    if (st)
+        return st;
+    hipLaunchKernelGGL(alt_final_kernel, dim3(1), dim3(ALT_T2), 0, s, pkeys, pc, pk, pm, ps, nblk, max_out, d, ids,
                        probs, count);
     st = check_launch("vox_alt_tokens final");
     return st ? st : ok();

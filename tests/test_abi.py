@@ -75,7 +75,7 @@ def test_validation_before_device_work(lib):
     assert lib.vox_w16_gemv(p, 2, p, C.c_void_p(0x800000), 10, 16, None) == vox.VOX_E_INVAL    # fmt
     assert lib.vox_w16_gemv(p, 1, p, C.c_void_p(0x800000), 0, 16, None) == vox.VOX_OK          # empty
     assert lib.vox_w16_gemv(C.c_void_p(0x1008), 0, p, C.c_void_p(0x800000), 10, 16, None) == vox.VOX_E_UNSUPPORTED
-    assert lib.vox_alt_tokens_workspace(131072, 8) == 256 * 8 * 8 + 256 * 8
+    assert lib.vox_alt_tokens_workspace(131072, 8) == 256 * 8 * 8 + 256 * 20
     assert lib.vox_alt_tokens_workspace(131072, 33) == 0 and lib.vox_alt_tokens_workspace(262145, 8) == 0
     q4 = (p, C.c_void_p(0x200000), C.c_void_p(0x300000), C.c_void_p(0x400000))
     assert lib.vox_alt_tokens(p, 1000, C.c_float(-0.5), 4, *q4[1:], C.c_void_p(0x500000), 4096, None) == vox.VOX_E_INVAL

@@ -78,3 +78,20 @@ def test_alt_tokens_on_decoder_logits(vx, orc):
     assert ids[0] == int(host(tok_out)[0])
     _check(vx, orc, lg, 0.99, 8, "alt on decoder logits")
     dec.close()
+
+
+@pytest.mark.parametrize("kept", [1, 40, 64, 65, 128, 129, 256, 257, 512, 513, 2000])
+@pytest.mark.parametrize("ties", [False, True])
+def test_alt_tokens_kept_counts(vx, orc, kept, ties):
+    # exactly `kept` tokens pass the threshold: 40 of them (or all, when fewer) in one 512-logit
+    # block, so that block keeps more than max_out, the others spread over the vocabulary.  The
+    # counts step over the sizes at which the gathered keys change sort network or overflow it.
+    g = synth.generator(954, kept)
+    vocab = 131072
+    logits = np.full(vocab, -5.0, np.float32) - g.random(vocab).astype(np.float32)
+    dense = np.arange(3 * 512, 3 * 512 + min(kept, 40))
+    rest = g.choice(np.setdiff1d(np.arange(vocab), dense), kept - dense.size, replace=False)
+    sel = np.concatenate([dense, rest])
+    logits[sel] = 5.0 if ties else (4.0 + g.random(sel.size)).astype(np.float32)
+    for max_out in (1, 8, 32):
+        _check(vx, orc, logits, 0.9999, max_out, f"alt kept={kept} ties={ties} max_out={max_out}")
