@@ -211,8 +211,10 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
 //    with aligned dword reads and unpacks the codes in registers to exact bf16: lane group g
 //    of a column takes inputs 8g .. 8g+7, i.e. the low (g < 2) or high (g >= 2) nibbles of
 //    code bytes 8(g%2) .. 8(g%2)+7;
-//  * per block the wave runs 4 x 4 matrix-core products of A with the exact (code - 8) values,
-//    each the block's sum of a * (code - 8) up to fp32 rounding; scale * product goes into fp32.
+//  * per block the wave runs 4 x 4 matrix-core products of A with the exact values
+//    16 (code - 8), each 16 times the block's sum of a * (code - 8) up to fp32 rounding (the
+//    factor 16 is exact and commutes with every rounding); scale * product goes into fp32, and
+//    the epilogue multiplies the tile by 1/16.
 // The four waves' partial tiles are added through LDS in a fixed tree order at the end.  Two
 // workgroups share a compute unit (at most 256 VGPRs per wave), so one's stage barrier overlaps
 // the other's work (measured on MI355X against eight-wave workgroups with 8-block stages, one
@@ -242,19 +244,22 @@ __device__ __forceinline__ float ubyte_to_f(uint32_t v, int j)
     return r;
 }
 
-// (code - 8) for 8 codes taken from one nibble of 8 bytes (lo: bytes 0-3, hi: 4-7), exact in bf16.
+// 16 (code - 8) for 8 codes taken from one nibble of 8 bytes (lo: bytes 0-3, hi: 4-7), exact in
+// bf16.  sh = 4 moves low nibbles to the top of their bytes (high nibbles: sh = 0); flipping the
+// top bit then leaves a byte that, read as a signed integer, is 16 (code - 8), because code ^ 8 is
+// code - 8 as a 4-bit two's complement number.  One sign-extending byte conversion per value.
 // (Feeding the raw codes and adding -8 times the activations' block sum through the accumulator
-// saves the subtractions but cancels two sums of size 8 sum|a|: measured on MI355X, no faster,
-// and its rounding shows where the weights are sparse.)
-__device__ __forceinline__ u32x4v nibbles_to_bf16(uint32_t lo, uint32_t hi, bool high_nibble)
+// saves more but cancels two sums of size 8 sum|a|: measured on MI355X, no faster, and its
+// rounding shows where the weights are sparse.)
+__device__ __forceinline__ u32x4v nibbles_to_bf16_x16(uint32_t lo, uint32_t hi, uint32_t sh)
 {
-    const uint32_t a = (high_nibble ? lo >> 4 : lo) & 0x0F0F0F0Fu;
-    const uint32_t b = (high_nibble ? hi >> 4 : hi) & 0x0F0F0F0Fu;
+    const uint32_t a = ((lo << sh) & 0xF0F0F0F0u) ^ 0x80808080u;
+    const uint32_t b = ((hi << sh) & 0xF0F0F0F0u) ^ 0x80808080u;
     u32x4v p;
-    p.x = pack_bf16_pair(ubyte_to_f(a, 0) - 8.0f, ubyte_to_f(a, 1) - 8.0f);
-    p.y = pack_bf16_pair(ubyte_to_f(a, 2) - 8.0f, ubyte_to_f(a, 3) - 8.0f);
-    p.z = pack_bf16_pair(ubyte_to_f(b, 0) - 8.0f, ubyte_to_f(b, 1) - 8.0f);
-    p.w = pack_bf16_pair(ubyte_to_f(b, 2) - 8.0f, ubyte_to_f(b, 3) - 8.0f);
+    p.x = pack_bf16_pair((float)(int8_t)a, (float)(int8_t)(a >> 8));
+    p.y = pack_bf16_pair((float)(int8_t)(a >> 16), (float)(int8_t)(a >> 24));
+    p.z = pack_bf16_pair((float)(int8_t)b, (float)(int8_t)(b >> 8));
+    p.w = pack_bf16_pair((float)(int8_t)(b >> 16), (float)(int8_t)(b >> 24));
     return p;
 }
 
@@ -296,8 +301,10 @@ __device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, 
             lo = __builtin_amdgcn_alignbyte(dw[j][2], dw[j][1], 2);
             hi = __builtin_amdgcn_alignbyte(dw[j][3], dw[j][2], 2);
         }
-        bf[j] = __builtin_bit_cast(bf16x8, nibbles_to_bf16(lo, hi, grp >= 2));
-        d[j] = half_bits_to_float(d16);
+        bf[j] = __builtin_bit_cast(bf16x8, nibbles_to_bf16_x16(lo, hi, grp >= 2 ? 0u : 4u));
+        float df = half_bits_to_float(d16);
+        asm volatile("" : "+v"(df));   // an fp32 scale, so the multiply-adds are v_fmac_f32, not v_fma_mix_f32
+        d[j] = df;
     }
 }
 
@@ -453,10 +460,11 @@ __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
                 for (int r = 0; r < 4; ++r) {
                     const int row = m0 + 16 * i + 4 * grp + r;
                     if (row < m && col < n) {
+                        const float yv = acc[i][j][r] * 0.0625f;   // the B operands were 16 (code - 8)
                         if (gelu)
-                            store_gelu_pair(hl, n, row, col, acc[i][j][r]);
+                            store_gelu_pair(hl, n, row, col, yv);
                         else
-                            dst[(size_t)row * n + col] = acc[i][j][r];
+                            dst[(size_t)row * n + col] = yv;
                     }
                 }
             }
