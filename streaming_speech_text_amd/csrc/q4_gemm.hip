@@ -213,8 +213,9 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
 //    code bytes 8(g%2) .. 8(g%2)+7;
 //  * per block the wave runs 4 x 4 matrix-core products of A with the exact values
 //    16 (code - 8), each 16 times the block's sum of a * (code - 8) up to fp32 rounding (the
-//    factor 16 is exact and commutes with every rounding); scale * product goes into fp32, and
-//    the epilogue multiplies the tile by 1/16.
+//    factor 16 is exact and commutes with every rounding while the sums stay below 2^124 in
+//    magnitude, i.e. for every output short of the top 1/16 of the fp32 range); scale * product
+//    goes into fp32, and the epilogue multiplies the tile by 1/16.
 // The four waves' partial tiles are added through LDS in a fixed tree order at the end.  Two
 // workgroups share a compute unit (at most 256 VGPRs per wave), so one's stage barrier overlaps
 // the other's work (measured on MI355X against eight-wave workgroups with 8-block stages, one
