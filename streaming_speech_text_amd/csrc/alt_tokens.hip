@@ -245,11 +245,14 @@ __device__ __forceinline__ u64 sort_gathered(const u64 *cand, int T)
     return v[0];
 }
 
-// One workgroup.  Each thread appends one block's kept keys to cand (the order does not matter).
-// At most 512 in all: wave 0 sorts them.  More: each wave folds chunks of all the blocks' slots
-// into its running best kout (kept in the first kout slots, sorted with 512 - kout new keys at a
-// time) and wave 0 merges the 16 waves' lists.  Then the sum is rescaled to the global max (fixed
-// order) and the list written.
+// One workgroup; thread b < nblk owns block b.  Every per-block value it needs (kept count, first
+// kept key, largest key, max, sum) is loaded at the start, so the kernel waits for one memory
+// round trip (two when a block keeps more than one key).  Each thread appends its block's kept keys
+// to cand (the order does not matter).  At most 512 in all: wave 0 sorts them.  More: each wave
+// folds chunks of all the blocks' slots into its running best kout (kept in the first kout slots,
+// sorted with 512 - kout new keys at a time) and wave 0 merges the 16 waves' lists.  Then the sum
+// is rescaled to the global max (fixed order) and the list written.
+static_assert(ALT_MAX_VOCAB / ALT_BLOCK <= ALT_T2, "one final-pass thread per block");
 __global__ __launch_bounds__(ALT_T2) void alt_final_kernel(const u64 *__restrict__ pkeys, const int32_t *__restrict__ pc,
                                                            const u64 *__restrict__ pk, const float *__restrict__ pm,
                                                            const float *__restrict__ ps, int nblk, int kout, float d,
@@ -259,21 +262,39 @@ __global__ __launch_bounds__(ALT_T2) void alt_final_kernel(const u64 *__restrict
     constexpr int WAVES = ALT_T2 / 64;
     static_assert(WAVES * ALT_MAX_OUT <= ALT_BLOCK, "the waves' lists share the gathering buffer");
     __shared__ u64 cand[ALT_BLOCK];
+    __shared__ u64 wmax[WAVES];
     __shared__ float red[WAVES];
-    __shared__ float gmax;
     __shared__ int total;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x == 0)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const bool own = tid < nblk;
+    const int c = own ? pc[tid] : 0;
+    const u64 k0 = own ? pkeys[(size_t)tid * kout] : 0ull;   // slot 0: the first kept key, or 0
+    const u64 kb = own ? pk[tid] : 0ull;
+    const float mb = own ? pm[tid] : -INFINITY;
+    const float sb = own ? ps[tid] : 0.0f;
+    if (tid == 0)
         total = 0;
+    const u64 wk = wave_max_key(kb);
+    if (lane == 0)
+        wmax[wave] = wk;
     __syncthreads();
-    for (int b = threadIdx.x; b < nblk; b += ALT_T2) {
-        const int c = pc[b];
-        if (c > 0) {
-            const int at = atomicAdd(&total, c);
-            for (int j = 0; j < c && at + j < ALT_BLOCK; ++j)
-                cand[at + j] = pkeys[(size_t)b * kout + j];
-        }
+    if (c > 0) {
+        const int at = atomicAdd(&total, c);
+        if (at < ALT_BLOCK)
+            cand[at] = k0;
+        for (int j = 1; j < c && at + j < ALT_BLOCK; ++j)
+            cand[at + j] = pkeys[(size_t)tid * kout + j];
     }
+    u64 gk = wmax[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w)
+        gk = wmax[w] > gk ? wmax[w] : gk;
+    const float M = key_logit(gk);   // the greedy token's logit, the global max
+    // this block's sum rescaled to M; the 16 waves' sums are added in order below
+    const float z = wave_sum(mb == -INFINITY ? 0.0f : sb * expf(mb - M));
+    if (lane == 0)
+        red[wave] = z;
     __syncthreads();
     const int T = total;
     u64 top = 0ull;   // in wave 0: lane j holds the j-th best kept key
@@ -308,20 +329,6 @@ __global__ __launch_bounds__(ALT_T2) void alt_final_kernel(const u64 *__restrict
         if (wave == 0)
             top = sort_gathered<8>(cand, WAVES * kout);
     }
-    if (wave == 0) {
-        const u64 gk = global_max_key(pk, nblk);   // the greedy token's key
-        if (lane == 0)
-            gmax = key_logit(gk);
-    }
-    __syncthreads();
-    const float M = gmax;   // the greedy token's logit, the global max
-    float z = 0.0f;
-    for (int b = threadIdx.x; b < nblk; b += ALT_T2)
-        z += pm[b] == -INFINITY ? 0.0f : ps[b] * expf(pm[b] - M);
-    z = wave_sum(z);
-    if (lane == 0)
-        red[wave] = z;
-    __syncthreads();
     if (wave == 0) {
         float zt = 0.0f;
         for (int w = 0; w < WAVES; ++w)
