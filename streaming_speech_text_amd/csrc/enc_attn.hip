@@ -279,7 +279,9 @@ __global__ __launch_bounds__(64 * EA_WAVES) void enc_attn_kernel(EncAttnArgs a)
 }
 
 // out[i][h*hd + d] = sum_z 2^(m_z - M) O_z[d] / sum_z 2^(m_z - M) l_z, splits in order z = 0, 1, ...
-// One thread per output value.
+// One thread per output value.  With NF > 0 (at least as many as the splits) every load is issued
+// before the first use (one memory round trip); NF = 0 takes two passes over the partials.
+template <int NF>
 __global__ __launch_bounds__(256) void enc_attn_merge_kernel(EncAttnArgs a, int splits)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -290,17 +292,42 @@ __global__ __launch_bounds__(256) void enc_attn_merge_kernel(EncAttnArgs a, int 
     const int64_t hi = t / a.hd;           // (i * n_heads + h)
     const int h = (int)(hi % a.n_heads);
     const int i = (int)(hi / a.n_heads);
-    float mx = -INFINITY;
-    for (int z = 0; z < splits; ++z)
-        mx = fmaxf(mx, a.pm[((size_t)z * a.n_heads + h) * a.m + i]);
-    float l = 0.0f, o = 0.0f;
-    for (int z = 0; z < splits; ++z) {
-        const size_t row = ((size_t)z * a.n_heads + h) * a.m + i;
-        const float w = __builtin_amdgcn_exp2f(a.pm[row] - mx);   // an empty split (max -inf) weighs 0
-        l += w * a.pl[row];
-        o += w * a.part[row * a.hd + d];
+    if constexpr (NF > 0) {
+        float pmv[NF], plv[NF], ov[NF];
+#pragma unroll
+        for (int z = 0; z < NF; ++z) {
+            const size_t row = ((size_t)(z < splits ? z : 0) * a.n_heads + h) * a.m + i;
+            pmv[z] = a.pm[row];
+            plv[z] = a.pl[row];
+            ov[z] = a.part[row * a.hd + d];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int z = 0; z < NF; ++z)
+            if (z < splits)
+                mx = fmaxf(mx, pmv[z]);
+        float l = 0.0f, o = 0.0f;
+#pragma unroll
+        for (int z = 0; z < NF; ++z)
+            if (z < splits) {
+                const float w = __builtin_amdgcn_exp2f(pmv[z] - mx);   // an empty split (max -inf) weighs 0
+                l += w * plv[z];
+                o += w * ov[z];
+            }
+        a.out[(size_t)i * a.width + (size_t)h * a.hd + d] = o / l;
+    } else {
+        float mx = -INFINITY;
+        for (int z = 0; z < splits; ++z)
+            mx = fmaxf(mx, a.pm[((size_t)z * a.n_heads + h) * a.m + i]);
+        float l = 0.0f, o = 0.0f;
+        for (int z = 0; z < splits; ++z) {
+            const size_t row = ((size_t)z * a.n_heads + h) * a.m + i;
+            const float w = __builtin_amdgcn_exp2f(a.pm[row] - mx);   // an empty split (max -inf) weighs 0
+            l += w * a.pl[row];
+            o += w * a.part[row * a.hd + d];
+        }
+        a.out[(size_t)i * a.width + (size_t)h * a.hd + d] = o / l;
     }
-    a.out[(size_t)i * a.width + (size_t)h * a.hd + d] = o / l;
 }
 
 struct EncAttnPlan {
@@ -411,7 +438,15 @@ extern "C" int vox_enc_attn(const float *q, const float *k, const float *v, floa
     if (st || p.splits == 1)
         return st ? st : ok();
     const int64_t total = m * width;
-    hipLaunchKernelGGL(enc_attn_merge_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, p.splits);
+    const dim3 mg((unsigned)((total + 255) / 256));
+    if (p.splits <= 2)
+        hipLaunchKernelGGL(enc_attn_merge_kernel<2>, mg, dim3(256), 0, s, a, p.splits);
+    else if (p.splits <= 4)
+        hipLaunchKernelGGL(enc_attn_merge_kernel<4>, mg, dim3(256), 0, s, a, p.splits);
+    else if (p.splits <= 8)
+        hipLaunchKernelGGL(enc_attn_merge_kernel<8>, mg, dim3(256), 0, s, a, p.splits);
+    else
+        hipLaunchKernelGGL(enc_attn_merge_kernel<0>, mg, dim3(256), 0, s, a, p.splits);
     st = check_launch("vox_enc_attn merge");
     return st ? st : ok();
 }

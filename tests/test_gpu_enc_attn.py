@@ -46,6 +46,9 @@ def test_enc_attn_chunk(vx, orc, m):
     (17, 749, 3, 44, 750),      # head size 44, ragged query block
     (33, 10, 5, 8, 16),         # head size 8 (one partial 16-wide block)
     (64, 900, 2, 48, 750),      # more earlier rows than the window needs
+    (40, 927, 1, 40, 907),      # 8 key splits: the merge's one-pass path at its limit
+    (16, 1075, 1, 40, 1055),    # 9 key splits: the merge's two-pass path
+    (5, 2000, 1, 40, 2000),     # 16 key splits
 ])
 def test_enc_attn_shapes(vx, orc, m, n_ctx, heads, hd, window):
     say(f"enc_attn m={m} n_ctx={n_ctx} heads={heads} hd={hd} window={window}")
