@@ -474,19 +474,36 @@ __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 
 // y = sum over z of part[z] (count values per slice, rows of n), slices added in order z = 0, 1,
 // ...; GELU: GELU pairs of the sums go to hl instead (store_gelu_pair).
-template <bool GELU>
+template <bool GELU, int NB>
 __global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__restrict__ part, float *__restrict__ y,
                                                              uint16_t *__restrict__ hl, int64_t count, int n,
                                                              int slices, bool vec4)
 {
+    // NB > 0 (at least the slice count): every slice's load is issued before the first add, so
+    // the kernel waits for one memory round trip; NB = 0: one load after another.
+    auto sum = [&](auto ld) {
+        auto a = ld(0);
+        if constexpr (NB > 0) {
+            decltype(a) v[NB];
+#pragma unroll
+            for (int z = 1; z < NB; ++z)
+                v[z] = ld(z < slices ? z : 0);
+#pragma unroll
+            for (int z = 1; z < NB; ++z)
+                if (z < slices)
+                    a += v[z];
+        } else {
+            for (int z = 1; z < slices; ++z)
+                a += ld(z);
+        }
+        return a;
+    };
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (vec4) {
         const int64_t i = 4 * t;
         if (i >= count)
             return;
-        f32x4v a = *reinterpret_cast<const f32x4v *>(part + i);
-        for (int z = 1; z < slices; ++z)
-            a += *reinterpret_cast<const f32x4v *>(part + (size_t)z * count + i);
+        const f32x4v a = sum([&](int z) { return *reinterpret_cast<const f32x4v *>(part + (size_t)z * count + i); });
         if constexpr (GELU) {
             const int64_t row = i / n;
             const int col = (int)(i - row * n);
@@ -499,9 +516,7 @@ __global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__rest
     } else {
         if (t >= count)
             return;
-        float a = part[t];
-        for (int z = 1; z < slices; ++z)
-            a += part[(size_t)z * count + t];
+        const float a = sum([&](int z) { return part[(size_t)z * count + t]; });
         if constexpr (GELU)
             store_gelu_pair(hl, n, t / n, (int)(t % n), a);
         else
@@ -590,8 +605,15 @@ static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_
     const int64_t count = (int64_t)m * n;
     const bool vec4 = count % 4 == 0 && (gelu ? n % 4 == 0 : aligned(y, 16));
     const int64_t threads = vec4 ? count / 4 : count;
-    hipLaunchKernelGGL(q4_gemm_reduce_kernel<gelu>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part,
-                       y, hl, count, n, slices, vec4);
+    const dim3 rg((unsigned)((threads + 255) / 256));
+    if (slices <= 2)
+        hipLaunchKernelGGL((q4_gemm_reduce_kernel<gelu, 2>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
+    else if (slices <= 4)
+        hipLaunchKernelGGL((q4_gemm_reduce_kernel<gelu, 4>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
+    else if (slices <= 8)
+        hipLaunchKernelGGL((q4_gemm_reduce_kernel<gelu, 8>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
+    else
+        hipLaunchKernelGGL((q4_gemm_reduce_kernel<gelu, 0>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
     return check_launch("q4 tiled product: slice sum");
 }
 
