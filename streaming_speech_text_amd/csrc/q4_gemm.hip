@@ -42,7 +42,7 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int GM_WAVES = 8;
 constexpr int GM_THREADS = 64 * GM_WAVES;
-constexpr int GM_PF = 4;           // K blocks in flight per wave
+constexpr int GM_PF = 4;           // K blocks in flight per wave (5 when a wave has exactly 5)
 
 // bf16 bits of two small integers given as exact fp32 values: the upper halves.
 __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi)
@@ -85,7 +85,7 @@ __device__ __forceinline__ void store_gelu_pair(uint16_t *hl, int n, int64_t row
     p[GELU_STAGE] = __builtin_bit_cast(uint16_t, lo);
 }
 
-template <int MI, int NJ>
+template <int MI, int NJ, int PF>
 __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x, float *__restrict__ y,
                                                             int m, int n, int k)
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
 
     // ring of GM_PF prefetched blocks; loads are unconditional (indices clamped), the scale of
     // a block past the wave's range is zeroed instead
-    u32x2v xa[GM_PF][MI][2];
-    uint32_t qv[GM_PF][NJ], dv[GM_PF][NJ];
+    u32x2v xa[PF][MI][2];
+    uint32_t qv[PF][NJ], dv[PF][NJ];
     auto load = [&](int slot, int b) {
         const int bb = b < kb1 ? b : (kb1 > kb0 ? kb1 - 1 : 0);
 #pragma unroll
@@ -146,12 +146,12 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
         }
     };
 #pragma unroll
-    for (int s = 0; s < GM_PF; ++s)
+    for (int s = 0; s < PF; ++s)
         load(s, kb0 + s);
 
-    for (int b0 = kb0; b0 < kb1; b0 += GM_PF) {
+    for (int b0 = kb0; b0 < kb1; b0 += PF) {
 #pragma unroll
-        for (int s = 0; s < GM_PF; ++s) {
+        for (int s = 0; s < PF; ++s) {
             const int b = b0 + s;
             bf16x8 afr[MI], bfr[NJ];
             float d[NJ];
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
                 bfr[j] = codes_to_bf16(qv[s][j]);
                 d[j] = b < kb1 ? half_bits_to_float(dv[s][j]) : 0.0f;
             }
-            load(s, b + GM_PF);   // refill: the ring stays GM_PF blocks ahead
+            load(s, b + PF);   // refill: the ring stays PF blocks ahead
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -528,13 +528,15 @@ __global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__rest
 static bool tiled_k(int64_t k) { return k == 1280 || k == 3072 || k == 5120; }
 
 // Whether the tiled kernel runs (given 16-byte aligned operands): a compiled K, offsets that fit
-// 32 bits, and either a long K or an output past about 48 x 1280 values - measured on MI355X at
-// the encoder's shapes, the split-K-over-waves kernel is the faster one below that for K = 1280.
+// 32 bits, and either a long K or an output past 64 x 1280 values (K = 1280) or 48 x 1280 (K =
+// 3072) - measured on MI355X at the encoder's shapes, the split-K-over-waves kernel is the faster
+// one below that (at K = 1280 with all five blocks of a wave in flight: 16 x 5120 and 64 x 1280
+// outputs 9.1 / 8.7 us against 10.0 / 9.5 tiled, 64 x 5120 19.1 against 12.4).
 static bool tiled_shape(int64_t m, int64_t n, int64_t k)
 {
     const size_t wbytes = (size_t)n * (size_t)(k / 32) * 18;
     return tiled_k(k) && (uint64_t)m * (uint64_t)k < (1ull << 31) && wbytes < (1ull << 31) &&
-           (k >= 5120 || m * n > 48 * 1280);
+           (k >= 5120 || m * n > (k == 1280 ? 64 : 48) * 1280);
 }
 
 // K slices for the tiled kernel (measured on MI355X at the encoder's shapes): none once the
@@ -617,11 +619,20 @@ static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_
     return check_launch("q4 tiled product: slice sum");
 }
 
+// Blocks in flight per wave: all of them when a wave has exactly five (K = 1280: the whole range
+// in one memory round trip; measured on MI355X, 16 x 1280 x 1280 took 5.5 us against 7.4 with
+// four), else four (five or eight for longer ranges was slower, e.g. 16 x 3072 x 3072: 15.6 us
+// against 13.0).
 template <int MI, int NJ>
 static int launch_gemm(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
 {
     const dim3 grid((unsigned)((n + 16 * NJ - 1) / (16 * NJ)), (unsigned)((m + 16 * MI - 1) / (16 * MI)));
-    hipLaunchKernelGGL((q4_gemm_kernel<MI, NJ>), grid, dim3(GM_THREADS), 0, s, (const uint8_t *)w, x, y, m, n, k);
+    const int per_wave = (k / 32 + GM_WAVES - 1) / GM_WAVES;
+    if (per_wave == 5)
+        hipLaunchKernelGGL((q4_gemm_kernel<MI, NJ, 5>), grid, dim3(GM_THREADS), 0, s, (const uint8_t *)w, x, y, m, n, k);
+    else
+        hipLaunchKernelGGL((q4_gemm_kernel<MI, NJ, GM_PF>), grid, dim3(GM_THREADS), 0, s, (const uint8_t *)w, x, y, m, n,
+                           k);
     return check_launch("vox_q4_gemm");
 }
 

@@ -118,3 +118,13 @@ def test_gemm_errors(vx):
         vx.q4_gemm(w, x, y, m=4, n=32, k=48)
     assert e.value.status == vx.VOX_E_INVAL
     vx.q4_gemm(w, x, y, m=0, n=32, k=64)
+
+
+@pytest.mark.parametrize("k", [1024, 1056, 1280, 1312])
+def test_gemm_small_kernel_block_ranges(vx, orc, k):
+    # the split-K-over-waves kernel keeps all five blocks of a wave in flight when a wave has
+    # exactly five (K = 1280, and 1056 where some waves have four); others run four at a time
+    m, n = 16, 200
+    w, xb = synth.gemm_inputs(615, m, n, k)
+    assert vx.q4_gemm_workspace(m, n, k) == 0
+    assert_close(_gemm(vx, w, xb, m, n, k, split=False), orc.q4_gemm(w, xb), f"gemm {m}x{n}x{k} small kernel")
