@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gemv-launches", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--leg", choices=["all", "gemv", "kernels"], default="all",
+    ap.add_argument("--leg", choices=["all", "gemv", "kernels", "probe"], default="all",
                     help="gemv: only the GEMV roofline leg and a copy of known size (for counter runs); "
                          "kernels: per-kernel timings of the other workloads, one JSON line each")
     return ap.parse_args()
@@ -82,6 +82,50 @@ def gemv_leg(args, torch, synth, vox, dev, stream):
     del ws
     torch.cuda.empty_cache()
     return {"n": n, "k": k, "us": gemv_us, "bytes": launch_bytes, "gbs": achieved}
+
+
+def probe_lib():
+    """The streaming-read probe (include/vox_probe.h), a library of its own beside libvox."""
+    import ctypes as C
+    path = os.path.join(ROOT, "streaming_speech_text_amd", "libvox_probe.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with python -m streaming_speech_text_amd.build")
+    L = C.CDLL(path)
+    L.vox_probe_sink_entries.restype = C.c_int
+    L.vox_probe_sink_entries.argtypes = [C.c_int]
+    L.vox_probe_stream_read.restype = C.c_int
+    L.vox_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    return L
+
+
+def probe_ceiling(torch, dev, stream, sizes, reps=100):
+    """Streaming-read rate (GB/s) of a plain 16-byte-load kernel for each byte count in `sizes`:
+    launches read consecutive windows of a buffer of more than 1 GiB (so no window is served from
+    the 256 MB Infinity Cache), captured in a graph and timed like the kernels; the best over
+    1, 2, 4 and 8 workgroups per compute unit.  Returns {bytes: (us, GB/s, wg_per_cu)}."""
+    L = probe_lib()
+    GiB = 2 ** 30
+    out = {}
+    sink = torch.empty(8 * 1024, dtype=torch.int32, device=dev)
+    for size in sizes:
+        size = (size + 255) // 256 * 256
+        n_win = max(2, int(np.ceil(1.1 * GiB / size)))
+        buf = torch.empty(n_win * size, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        best = None
+        for wg in (1, 2, 4, 8):
+            def launch(i, wg=wg):
+                st = L.vox_probe_stream_read(buf.data_ptr() + i * size, size, sink.data_ptr(), wg,
+                                             torch.cuda.current_stream().cuda_stream)
+                if st:
+                    raise RuntimeError(f"probe launch failed ({st})")
+            us = timed(torch, stream, launch, n_win, reps)
+            if best is None or us < best[0]:
+                best = (us, size / us / 1e3, wg)
+        out[size] = best
+        del buf
+        torch.cuda.empty_cache()
+    return out
 
 
 def copy_calibration(torch, dev):
@@ -322,6 +366,14 @@ def main():
         return
     if args.leg == "kernels":
         kernels_leg(torch, synth, vox, dev, stream)
+        return
+    if args.leg == "probe":
+        # the decoder kernels' byte counts (O, QKV, down, gate/up, LM head), config 1, and a sweep
+        sizes = [7077888, 10616832, 15925248, 31850496, 226492416, 5308416, 1 << 20, 4 << 20, 16 << 20,
+                 64 << 20, 256 << 20]
+        for b, (us, gbs, wg) in probe_ceiling(torch, dev, stream, sizes).items():
+            print(json.dumps({"leg": "probe", "bytes": b, "us": round(us, 3), "gbs": round(gbs, 1),
+                              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "wg_per_cu": wg}), flush=True)
         return
     s = synth.VOXTRAL_DECODER
     print(f"[bench] generating weights ({s.n_layers} layers, vocab {s.vocab})", file=sys.stderr, flush=True)

@@ -114,7 +114,7 @@ int vox_adapter(const void *w1_q4, const void *w2_q4, const uint16_t *x_bf16, fl
  * fp32 throughout (fp32 matrix cores).  workspace: vox_enc_attn_workspace(...) bytes of device
  * memory, 16-byte aligned, apart from the other buffers (0 bytes -> may be NULL), contents
  * irrelevant.  m == 0 is a no-op.  head_dim not a multiple of 4 or above 48 ->
- * VOX_E_UNSUPPORTED; q, k not 16-byte aligned -> VOX_E_UNSUPPORTED; out overlapping an input ->
+ * VOX_E_UNSUPPORTED; q, k, v not 16-byte aligned -> VOX_E_UNSUPPORTED; out overlapping an input ->
  * VOX_E_INVAL; a smaller workspace -> VOX_E_WORKSPACE. */
 size_t vox_enc_attn_workspace(int64_t m, int64_t n_ctx, int n_heads, int head_dim, int window);
 int vox_enc_attn(const float *q, const float *k, const float *v, float *out, int64_t m, int64_t n_ctx, int n_heads,
@@ -195,6 +195,13 @@ int vox_decoder_create(const vox_decoder_config *c, const vox_decoder_weights *w
                        vox_decoder_t **out);
 /* Position back to 0 (the KV window is logically emptied); enqueued on `stream`. */
 int vox_decoder_reset(vox_decoder_t *d, void *stream);
+/* Resumes a stream at absolute position pos (0 <= pos <= VOX_DECODER_MAX_POS, else VOX_E_INVAL),
+ * e.g. one whose KV ring the caller saved and copied back ([VC] 주요 기능: the window rolls over an
+ * unbounded stream).  The ring must then hold the keys (after rotation) and values of positions
+ * max(0, pos - n_slots) .. pos - 1, position p at slot p % n_slots; the next step is token pos.
+ * vox_decoder_reset is vox_decoder_seek(d, 0).  Enqueued on `stream`. */
+#define VOX_DECODER_MAX_POS ((int64_t)1 << 40)
+int vox_decoder_seek(vox_decoder_t *d, int64_t pos, void *stream);
 /* One token: reads token_in[0] (device int32 in [0, vocab); an id outside is clamped to the
  * range), writes token_out[0] (device int32) and, when logits is not NULL, logits[vocab] fp32.
  * token_out may equal token_in. */

@@ -477,6 +477,26 @@ void orc_decoder_reset(orc_decoder *d)
 
 int64_t orc_decoder_position(const orc_decoder *d) { return d->pos; }
 
+static void ensure_capacity(orc_decoder *d, int64_t need);
+
+/* Resumes a stream at absolute position pos with a given window ([VC] section 주요 기능: the
+ * window rolls over an unbounded stream, keeping the last 8192 positions).  k and v hold, per
+ * layer, the keys (already rotated) and values of positions pos - len .. pos - 1, oldest first,
+ * len = min(pos, n_slots), each row n_kv*head_dim floats: layout [n_layers][len][n_kv][hd]. */
+void orc_decoder_load_window(orc_decoder *d, int64_t pos, const float *k, const float *v)
+{
+    const int64_t len = pos < d->c.n_slots ? pos : d->c.n_slots;
+    const int64_t row = d->c.n_kv_heads * d->c.head_dim;
+    ensure_capacity(d, len);
+    for (int64_t l = 0; l < d->c.n_layers; l++)
+        for (int64_t i = 0; i < len * row; i++) {
+            d->kcache[l][i] = (double)k[(l * len) * row + i];
+            d->vcache[l][i] = (double)v[(l * len) * row + i];
+        }
+    d->pos = pos;
+    d->len = len;
+}
+
 const double *orc_decoder_hidden(const orc_decoder *d) { return d->h; }
 
 /* Rolling KV window ([VC] section 주요 기능: an 8192-position sliding window whose cache

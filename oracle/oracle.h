@@ -76,6 +76,9 @@ orc_decoder *orc_decoder_create(const orc_decoder_config *c, const uint8_t *tok_
 void orc_decoder_destroy(orc_decoder *d);
 void orc_decoder_reset(orc_decoder *d);
 int64_t orc_decoder_position(const orc_decoder *d);
+/* Resumes at position pos with the window given as k, v [n_layers][len][n_kv][hd] (fp32),
+ * oldest first, len = min(pos, n_slots). */
+void orc_decoder_load_window(orc_decoder *d, int64_t pos, const float *k, const float *v);
 /* One step on `token`.  Writes logits[vocab] (double) when non-NULL and returns the
  * greedy next token: the first index of the largest logit, taken over fp32 logits. */
 int64_t orc_decoder_step(orc_decoder *d, int64_t token, double *logits);

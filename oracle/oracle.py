@@ -60,6 +60,7 @@ def lib():
             "orc_enc_attn": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _dbl, _vp],
             "orc_decoder_destroy": [_vp],
             "orc_decoder_reset": [_vp],
+            "orc_decoder_load_window": [_vp, _i64, _vp, _vp],
         }.items():
             f = getattr(L, name)
             f.restype = None
@@ -296,6 +297,16 @@ class Decoder:
 
     def reset(self):
         lib().orc_decoder_reset(self._h)
+
+    def load_window(self, pos: int, k, v):
+        """Resume at position `pos`; k, v fp32 [n_layers, len, n_kv*head_dim], oldest first,
+        len = min(pos, n_slots)."""
+        s = self.shape
+        n = min(pos, s.n_slots)
+        k = _c(k, np.float32)
+        v = _c(v, np.float32)
+        assert k.shape == v.shape == (s.n_layers, n, s.n_kv_heads * s.head_dim)
+        lib().orc_decoder_load_window(self._h, int(pos), _p(k), _p(v))
 
     @property
     def position(self) -> int:

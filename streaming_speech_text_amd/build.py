@@ -1,7 +1,9 @@
-"""Builds libvox.so (HIP, gfx950 only) in-tree from csrc/.
+"""Builds libvox.so (HIP, gfx950 only) in-tree from csrc/, and the measurement aid
+libvox_probe.so from probe/.
 
 Every source is compiled by hipcc for gfx950 with packed FP32 instructions disabled, then
-linked into streaming_speech_text_amd/libvox.so.  Objects go to streaming_speech_text_amd/_build/.
+linked into streaming_speech_text_amd/libvox.so (libvox_probe.so).  Objects go to
+streaming_speech_text_amd/_build/.
 """
 from __future__ import annotations
 
@@ -15,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvox.so")
+PROBE_SRC = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libvox_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -41,17 +45,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    probe_srcs = sorted(glob.glob(os.path.join(PROBE_SRC, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs) + len(probe_srcs)))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], PROBE_LIB, verbose)
     return LIB
 
 

@@ -399,11 +399,12 @@ __global__ void dec_rope_table_kernel(double *freq, float theta)
         freq[i] = pow((double)theta, -2.0 * (double)i / (double)ATTN_HD) / 3.14159265358979323846;
 }
 
-__global__ void dec_reset_kernel(DecCtl *ctl, const double *freq_pi)
+// Sets the position of the next token (0 for a reset) and its rotation table.
+__global__ void dec_seek_kernel(DecCtl *ctl, const double *freq_pi, int64_t pos)
 {
-    rope_fill(ctl, freq_pi, 0);
+    rope_fill(ctl, freq_pi, pos);
     if (threadIdx.x == 0)
-        ctl->pos = 0;
+        ctl->pos = pos;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -804,7 +805,8 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     st = check_hip(hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking), "vox_decoder_create: stream");
     if (!st) {
         hipLaunchKernelGGL(dec_rope_table_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->rope, c->rope_theta);
-        hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl, (const double *)d->rope);
+        hipLaunchKernelGGL(dec_seek_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl, (const double *)d->rope,
+                           (int64_t)0);
         st = check_launch("vox_decoder_create: init");
     }
     if (st) {
@@ -821,11 +823,20 @@ extern "C" int vox_decoder_reset(vox_decoder_t *d, void *stream)
 {
     if (!d)
         return fail(VOX_E_INVAL, "vox_decoder_reset: null handle");
-    hipLaunchKernelGGL(dec_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl, (const double *)d->rope);
-    int st = check_launch("vox_decoder_reset");
+    return vox_decoder_seek(d, 0, stream);
+}
+
+extern "C" int vox_decoder_seek(vox_decoder_t *d, int64_t pos, void *stream)
+{
+    if (!d)
+        return fail(VOX_E_INVAL, "vox_decoder_seek: null handle");
+    if (pos < 0 || pos > VOX_DECODER_MAX_POS)
+        return fail(VOX_E_INVAL, "vox_decoder_seek: position %lld outside [0, 2^40]", (long long)pos);
+    hipLaunchKernelGGL(dec_seek_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, d->ctl, (const double *)d->rope, pos);
+    int st = check_launch("vox_decoder_seek");
     if (st)
         return st;
-    d->host_pos = 0;
+    d->host_pos = pos;
     return ok();
 }
 

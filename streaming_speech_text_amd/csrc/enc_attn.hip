@@ -387,8 +387,8 @@ extern "C" int vox_enc_attn(const float *q, const float *k, const float *v, floa
         return fail(VOX_E_UNSUPPORTED, "vox_enc_attn: sizes beyond the grid or 32-bit element offsets");
     if (!q || !k || !v || !out)
         return fail(VOX_E_INVAL, "vox_enc_attn: null pointer");
-    if (!aligned(q, 16) || !aligned(k, 16))
-        return fail(VOX_E_UNSUPPORTED, "vox_enc_attn: q and k must be 16-byte aligned");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(VOX_E_UNSUPPORTED, "vox_enc_attn: q, k and v must be 16-byte aligned");
     const size_t qbytes = (size_t)m * width * 4, kvbytes = (size_t)T * width * 4;
     if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) || overlaps(out, qbytes, v, kvbytes))
         return fail(VOX_E_INVAL, "vox_enc_attn: out overlaps an input");

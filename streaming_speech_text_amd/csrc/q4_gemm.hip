@@ -149,7 +149,9 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
     for (int s = 0; s < PF; ++s)
         load(s, kb0 + s);
 
-    for (int b0 = kb0; b0 < kb1; b0 += PF) {
+    // one pass over the PF blocks of the ring starting at block b0; REFILL: load the blocks PF
+    // further into the slots as they are consumed (the ring stays PF blocks ahead)
+    auto ring_pass = [&](int b0, auto refill) {
 #pragma unroll
         for (int s = 0; s < PF; ++s) {
             const int b = b0 + s;
@@ -165,7 +167,8 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
                 bfr[j] = codes_to_bf16(qv[s][j]);
                 d[j] = b < kb1 ? half_bits_to_float(dv[s][j]) : 0.0f;
             }
-            load(s, b + PF);   // refill: the ring stays PF blocks ahead
+            if constexpr (decltype(refill)::value)
+                load(s, b + PF);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -174,7 +177,14 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
                     acc[i][j] += d[j] * t;
                 }
         }
-    }
+    };
+    // every pass but the last refills; the last one issues no loads (a wave whose range holds at
+    // most PF blocks, e.g. K = 1280 with PF = 5, loads each block once)
+    int b0 = kb0;
+    for (; b0 + PF < kb1; b0 += PF)
+        ring_pass(b0, std::true_type{});
+    if (b0 < kb1)
+        ring_pass(b0, std::false_type{});
 
     // add the eight waves' partial tiles in wave order
 #pragma unroll

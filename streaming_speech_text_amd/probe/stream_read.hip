@@ -1,0 +1,70 @@
+// stream_read.hip - streaming-read probe: the HBM read rate a plain kernel reaches on this GPU.
+//
+// Not an operation of the decoder.  It reads a buffer once with 16-byte loads and keeps a
+// checksum per workgroup, so the loads cannot be dropped.  The rate it reaches at a given size
+// is the practical ceiling for a kernel that must stream that many bytes once (the decoder's
+// GEMVs stream their Q4_0 weights exactly once per token).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vox_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int PROBE_THREADS = 256;
+constexpr int PROBE_UNROLL = 8;   // 16-byte loads in flight per thread per round
+
+// Workgroup i reads 16-byte chunks i*T + t, then every gridDim*T further, PROBE_UNROLL rounds
+// at a time (all loads of a round issued before their first use).
+__global__ __launch_bounds__(PROBE_THREADS) void stream_read_kernel(const u32x4 *__restrict__ src, int64_t n16,
+                                                                    uint32_t *__restrict__ sink)
+{
+    const int64_t stride = (int64_t)gridDim.x * PROBE_THREADS;
+    int64_t i = (int64_t)blockIdx.x * PROBE_THREADS + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + (PROBE_UNROLL - 1) * stride < n16; i += PROBE_UNROLL * stride) {
+        u32x4 v[PROBE_UNROLL];
+#pragma unroll
+        for (int u = 0; u < PROBE_UNROLL; ++u)
+            v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < PROBE_UNROLL; ++u)
+            acc ^= v[u];
+    }
+    for (; i < n16; i += stride)
+        acc ^= src[i];
+    __shared__ uint32_t red[PROBE_THREADS];
+    red[threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int t = 0; t < PROBE_THREADS; ++t)
+            r ^= red[t];
+        sink[blockIdx.x] = r;
+    }
+}
+
+}  // namespace
+
+extern "C" int vox_probe_sink_entries(int wg_per_cu)
+{
+    int dev = 0, cus = 0;
+    if (wg_per_cu < 1 || wg_per_cu > 8 || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return -1;
+    return wg_per_cu * cus;
+}
+
+extern "C" int vox_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream)
+{
+    if (!buf || !sink || bytes == 0 || bytes % 16 || ((uintptr_t)buf % 16))
+        return -1;
+    const int grid = vox_probe_sink_entries(wg_per_cu);
+    if (grid < 1)
+        return -1;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(PROBE_THREADS), 0, (hipStream_t)stream,
+                       (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}

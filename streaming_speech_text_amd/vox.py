@@ -66,6 +66,7 @@ _SIGS = {
     "vox_decoder_create": (_int, [C.POINTER(DecoderConfig), C.POINTER(DecoderWeights), _vp, _sz, _vp, _sz, _vp,
                                   C.POINTER(_vp)]),
     "vox_decoder_reset": (_int, [_vp, _vp]),
+    "vox_decoder_seek": (_int, [_vp, _i64, _vp]),
     "vox_decoder_step": (_int, [_vp, _vp, _vp, _vp, _vp]),
     "vox_decoder_position": (_int, [_vp, C.POINTER(_i64)]),
     "vox_decoder_set_graph": (_int, [_vp, _int]),
@@ -272,6 +273,11 @@ class Decoder:
 
     def reset(self, stream=None):
         _check(lib().vox_decoder_reset(self._h, _stream(stream)))
+
+    def seek(self, pos: int, stream=None):
+        """Resume at absolute position `pos`; the KV ring must hold positions max(0, pos - n_slots) ..
+        pos - 1 at slots p % n_slots."""
+        _check(lib().vox_decoder_seek(self._h, int(pos), _stream(stream)))
 
     def set_graph(self, enable: bool):
         _check(lib().vox_decoder_set_graph(self._h, 1 if enable else 0))

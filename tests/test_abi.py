@@ -10,8 +10,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vox.h")
 
 
-def header_functions():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "vox_probe.h")
+
+
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(vox_[a-z0-9_]+)\s*\(", text)))
 
@@ -35,11 +38,26 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_function(lib):
     missing = [f for f in header_functions() if not hasattr(lib, f)]
     assert not missing, f"declared in vox.h but not exported: {missing}"
+    assert "vox_decoder_seek" in header_functions()
+
+
+def test_probe_library_exports_its_header():
+    # the streaming-read probe (measurement aid) is a library of its own
+    path = os.path.join(ROOT, "streaming_speech_text_amd", "libvox_probe.so")
+    plib = C.CDLL(path)
+    fns = header_functions(PROBE_HEADER)
+    assert fns == ["vox_probe_sink_entries", "vox_probe_stream_read"]
+    assert all(hasattr(plib, f) for f in fns)
+    plib.vox_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    # bad arguments are refused before any HIP call
+    assert plib.vox_probe_stream_read(None, 16, C.c_void_p(0x1000), 1, None) == -1
+    assert plib.vox_probe_stream_read(C.c_void_p(0x1000), 24, C.c_void_p(0x1000), 1, None) == -1
+    assert plib.vox_probe_stream_read(C.c_void_p(0x1008), 32, C.c_void_p(0x1000), 1, None) == -1
 
 
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "vox.h"\nint main(void) { return vox_strerror(0) == 0; }\n')
+    src.write_text('#include "vox.h"\n#include "vox_probe.h"\nint main(void) { return vox_strerror(0) == 0; }\n')
     import subprocess
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
                         str(src)], capture_output=True, text=True)
@@ -108,6 +126,9 @@ def test_validation_before_device_work(lib):
     assert lib.vox_enc_attn(p, p, p, C.c_void_p(0x800000), 4, -1, 32, 40, 750, 0.1, None, 0, None) == vox.VOX_E_INVAL
     assert lib.vox_enc_attn(p, C.c_void_p(0x200000), C.c_void_p(0x400000), C.c_void_p(0x800000), 16, 749, 32, 40,
                             750, 0.1, None, 0, None) == vox.VOX_E_WORKSPACE
+    # v is read with 16-byte loads like q and k: a v offset by 4 bytes is refused before any launch
+    assert lib.vox_enc_attn(p, C.c_void_p(0x200000), C.c_void_p(0x400004), C.c_void_p(0x800000), 4, 5, 32, 40,
+                            750, 0.1, None, 0, None) == vox.VOX_E_UNSUPPORTED
     ws = lib.vox_gqa_decode_attn_workspace(32, 8, 128, 8192)
     assert ws > 0 and lib.vox_gqa_decode_attn_workspace(32, 8, 64, 8192) == 0
     args = (p, C.c_void_p(0x200000), C.c_void_p(0x400000), C.c_void_p(0x800000))

@@ -376,8 +376,9 @@ TINY = synth.DecoderShape(n_layers=2, dim=64, n_heads=4, n_kv_heads=2, head_dim=
                           vocab=512, n_slots=16, norm_eps=1e-5, rope_theta=1e6)
 
 
-def _torch_decoder_reference(shape, weights, tokens):
-    """Second, independent composition from library routines (torch float64)."""
+def _torch_decoder_reference(shape, weights, tokens, start_pos=0, window=None):
+    """Second, independent composition from library routines (torch float64).  window: None, or
+    (k, v) fp32 [n_layers, len, n_kv*head_dim] holding positions start_pos - len .. start_pos - 1."""
     s = shape
     t = torch.float64
 
@@ -407,8 +408,13 @@ def _torch_decoder_reference(shape, weights, tokens):
         return torch.view_as_real(z).reshape(-1)
 
     cache = [([], []) for _ in layers]
+    if window is not None:
+        for li in range(len(layers)):
+            for row_k, row_v in zip(window[0][li], window[1][li]):
+                cache[li][0].append(torch.from_numpy(row_k.astype(np.float64)).reshape(s.n_kv_heads, s.head_dim))
+                cache[li][1].append(torch.from_numpy(row_v.astype(np.float64)).reshape(s.n_kv_heads, s.head_dim))
     outs = []
-    for pos, tok in enumerate(tokens):
+    for pos, tok in enumerate(tokens, start=start_pos):
         h = E[tok].clone()
         for li, L in enumerate(layers):
             x = F.rms_norm(h, (s.dim,), L["an"], s.norm_eps)
@@ -448,6 +454,29 @@ def test_decoder_tiny_vs_torch_composition(orc):
     dec.reset()
     nxt, lg = dec.step(tokens[0])
     assert dec.position == 1 and np.allclose(lg, ref[0], rtol=1e-10, atol=1e-10)
+    dec.close()
+
+
+@pytest.mark.parametrize("pos", [5, 16, 1_000_003])
+def test_decoder_resume_from_window_vs_torch_composition(orc, pos):
+    # a stream resumed at position pos with a given window (fewer entries than the ring holds, a
+    # full ring, and a position far past any test's step count, where the rotary angles are large)
+    w = synth.decoder_weights(43, TINY)
+    n = min(pos, TINY.n_slots)
+    kw = synth.normal_f32(synth.generator(43, 10), (TINY.n_layers, n, TINY.n_kv_heads * TINY.head_dim))
+    vw = synth.normal_f32(synth.generator(43, 11), (TINY.n_layers, n, TINY.n_kv_heads * TINY.head_dim))
+    tokens = synth.generator(43, 9).integers(0, TINY.vocab, size=20).tolist()
+    dec = orc.Decoder(TINY, w)
+    dec.step(tokens[-1])                      # a state that loading the window must replace
+    dec.load_window(pos, kw, vw)
+    assert dec.position == pos
+    got = [dec.step(t)[1] for t in tokens]
+    ref = _torch_decoder_reference(TINY, w, tokens, start_pos=pos, window=(kw, vw))
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, rtol=1e-9, atol=1e-9)
+    # the loaded window matters: a different window changes the first step's logits
+    dec.load_window(pos, kw, vw * np.float32(0.5))
+    assert not np.allclose(dec.step(tokens[0])[1], ref[0])
     dec.close()
 
 
