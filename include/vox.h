@@ -134,6 +134,20 @@ int vox_gqa_decode_attn(const float *q, const float *k_cache, const float *v_cac
                         int n_q_heads, int n_kv_heads, int head_dim, int n_slots, int n_valid,
                         float scale, void *workspace, size_t workspace_bytes, void *stream);
 
+/* The same attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace argument and no
+ * allocation of any kind.  The split partials live in a fixed device array of the library,
+ * 1 MiB (1,048,576 bytes), one copy per GPU, held until the process ends; the partials need
+ * n_q_heads * min(32, ceil(n_slots / 128)) * 528 bytes (540,672 at 32 heads over 8192 slots),
+ * and a request beyond the array returns VOX_E_UNSUPPORTED before any device work.  Every call
+ * on one GPU shares that array: calls that overlap in time on one GPU (different streams, or
+ * other host threads) race and their results are undefined; calls on one stream are ordered.
+ * Arguments, results and other errors as vox_gqa_decode_attn; the first call on a device also
+ * looks up the array's device address (VOX_E_HIP if that fails). */
+int vox_gqa_decode_attn_noalloc(const float *q, const float *k_cache, const float *v_cache, float *out,
+                                int n_q_heads, int n_kv_heads, int head_dim, int n_slots, int n_valid,
+                                float scale, void *stream);
+
 /* The greedy token and its alternatives from one step's logits ([VC] 사용 방법: --alt <cutoff>
  * lists candidate tokens beside the chosen one, more for a higher cutoff; [VC] C API 구조: the
  * number of alternatives is set per stream).  With t the largest logit (lowest index on a tie),

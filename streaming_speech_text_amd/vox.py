@@ -60,6 +60,7 @@ _SIGS = {
     "vox_enc_attn": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _f32, _vp, _sz, _vp]),
     "vox_gqa_decode_attn_workspace": (_sz, [_int, _int, _int, _int]),
     "vox_gqa_decode_attn": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _f32, _vp, _sz, _vp]),
+    "vox_gqa_decode_attn_noalloc": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _f32, _vp]),
     "vox_alt_tokens_workspace": (_sz, [_i64, _int]),
     "vox_alt_tokens": (_int, [_vp, _i64, _f32, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "vox_decoder_workspace": (_int, [C.POINTER(DecoderConfig), C.POINTER(_sz), C.POINTER(_sz)]),
@@ -231,6 +232,15 @@ def gqa_decode_attn(q, k_cache, v_cache, out, n_q_heads, n_kv_heads, head_dim, n
                                      _ptr(v_cache, torch.float32, "v_cache"), _ptr(out, torch.float32, "out"),
                                      n_q_heads, n_kv_heads, head_dim, n_slots, n_valid, float(scale),
                                      _ptr(workspace, None, "workspace"), wsb, _stream(stream)))
+
+
+def gqa_decode_attn_noalloc(q, k_cache, v_cache, out, n_q_heads, n_kv_heads, head_dim, n_slots, n_valid, scale,
+                            stream=None):
+    """gqa_decode_attn without a workspace: the library's fixed per-GPU scratch holds the split partials."""
+    _check(lib().vox_gqa_decode_attn_noalloc(_ptr(q, torch.float32, "q"), _ptr(k_cache, torch.float32, "k_cache"),
+                                             _ptr(v_cache, torch.float32, "v_cache"), _ptr(out, torch.float32, "out"),
+                                             n_q_heads, n_kv_heads, head_dim, n_slots, n_valid, float(scale),
+                                             _stream(stream)))
 
 
 def decoder_workspace(cfg: DecoderConfig):

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_function(lib):
     missing = [f for f in header_functions() if not hasattr(lib, f)]
     assert not missing, f"declared in vox.h but not exported: {missing}"
-    assert "vox_decoder_seek" in header_functions()
+    assert "vox_gqa_decode_attn_noalloc" in header_functions() and "vox_decoder_seek" in header_functions()
 
 
 def test_probe_library_exports_its_header():
