@@ -6,9 +6,17 @@ GQA 32 query / 8 KV heads of 128, SwiGLU 9216, tied Q4_0 embedding / LM head of 
 prefix is teacher-forced (untimed), then K greedy steps run back to back with the token fed
 back on the device; each step replays the captured HIP graph of the step.
 
-Printed: one JSON line with decoder ms/token, the roofline of the dominant kernel (the Q4_0
-GEMV, timed with HIP events at the LM-head shape over rotating weight copies so that every
-launch streams from HBM), and the CPU oracle timed on a bounded sample on the host.
+Printed: one JSON line with decoder ms/token (median of five sequences of K steps, each timed
+with HIP events on the stream the steps run on), the decoder at a full, wrapped 8192-position
+window, the roofline of the dominant kernel (the Q4_0 GEMV, timed with HIP events at the LM-head
+shape over rotating weight copies so that every launch streams from HBM) next to the read ceiling
+of the streaming probe at the same byte count, a GEMV sweep over row counts at K = 3072, the
+decoder's own dominant kernel from the committed kernel trace, and the CPU oracle timed on
+bounded samples on the host (at all its threads and at one).
+
+Other modes: --leg kernels (per-kernel timings of the other workloads), --leg gemv (the GEMV leg
+alone, for counter runs), --leg probe (read ceilings and the grid-handoff probe), and
+--summarize-trace CSV (per-kernel statistics of a rocprofv3 kernel trace).
 """
 from __future__ import annotations
 
@@ -35,9 +43,21 @@ def parse():
     ap.add_argument("--gemv-launches", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--leg", choices=["all", "gemv", "kernels", "probe"], default="all",
+    ap.add_argument("--sequences", type=int, default=5, help="decoder sequences timed (median reported)")
+    ap.add_argument("--leg", choices=["all", "decoder", "gemv", "kernels", "probe"], default="all",
                     help="gemv: only the GEMV roofline leg and a copy of known size (for counter runs); "
-                         "kernels: per-kernel timings of the other workloads, one JSON line each")
+                         "kernels: per-kernel timings of the other workloads, one JSON line each; "
+                         "probe: read ceilings and the grid-handoff probe; decoder: only the decoder at the "
+                         "bench configuration (for kernel traces)")
+    ap.add_argument("--summarize-trace", metavar="CSV", help="print per-kernel statistics of a rocprofv3 "
+                    "kernel_trace.csv (calls, mean, p10/p50/p90, min, max in us) and exit")
+    ap.add_argument("--trace-json", metavar="OUT", help="with --summarize-trace: also write the statistics with "
+                    "the digest of the decoder sources (the decoder_roofline input) to OUT")
+    ap.add_argument("--decoder-steps", type=int, default=0, help="with --trace-json: decoder steps in the trace")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="HBM bytes per launch of the LM-head-shape GEMV from two rocprofv3 --pmc runs of "
+                         "--leg gemv (FETCH_SIZE, then WRITE_SIZE), scaled by what the same counters read for "
+                         "the leg's 256 MiB copies; prints the JSON that bench.py reads as `traffic`")
     return ap.parse_args()
 
 
@@ -75,13 +95,16 @@ def gemv_leg(args, torch, synth, vox, dev, stream):
     ws = [torch.from_numpy(gw).to(dev) for _ in range(copies)]
     xd = torch.from_numpy(gx).to(dev)
     y = torch.empty(n, dtype=torch.float32, device=dev)
-    gemv_us = timed(torch, stream, lambda i: vox.q4_gemv(ws[i], xd, y), copies, args.gemv_launches)
+    per = timed_all(torch, stream, lambda i: vox.q4_gemv(ws[i], xd, y), copies, args.gemv_launches, replays=10)
+    gemv_us = float(np.median(per))
     launch_bytes = n * synth.q4_row_bytes(k) + 4 * (n + k)
     achieved = launch_bytes / (gemv_us * 1e-6) / 1e9
     print(f"[bench] q4 gemv {n}x{k}: {gemv_us:.2f} us/launch, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
     del ws
     torch.cuda.empty_cache()
-    return {"n": n, "k": k, "us": gemv_us, "bytes": launch_bytes, "gbs": achieved}
+    return {"n": n, "k": k, "us": gemv_us, "bytes": launch_bytes, "gbs": achieved,
+            "spread": {"p10": round(float(np.percentile(per, 10)), 3), "p90": round(float(np.percentile(per, 90)), 3),
+                       "replays": len(per), "launches_per_replay": args.gemv_launches}}
 
 
 def probe_lib():
@@ -128,6 +151,67 @@ def probe_ceiling(torch, dev, stream, sizes, reps=100):
     return out
 
 
+def probe_leg(torch, dev, stream):
+    """Read ceilings at the decoder kernels' byte counts (O, QKV, down, gate/up, LM head), config 1
+    and a size sweep; then the grid-handoff probe: a persistent kernel with a grid barrier per
+    phase (two barrier forms) against one launch per phase, with 0, 8, 16 and 32 MB of weights
+    streamed per phase."""
+    sizes = [7077888, 10616832, 15925248, 31850496, 226492416, 5308416, 1 << 20, 4 << 20, 16 << 20,
+             64 << 20, 256 << 20]
+    for b, (us, gbs, wg) in probe_ceiling(torch, dev, stream, sizes).items():
+        print(json.dumps({"leg": "probe", "bytes": b, "us": round(us, 3), "gbs": round(gbs, 1),
+                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "wg_per_cu": wg}), flush=True)
+    import ctypes as C
+    L = probe_lib()
+    L.vox_probe_handoff_work_bytes.restype = C.c_size_t
+    L.vox_probe_handoff_work_bytes.argtypes = []
+    L.vox_probe_handoff_reset.argtypes = [C.c_void_p, C.c_void_p]
+    L.vox_probe_handoff_persistent.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p,
+                                               C.c_void_p]
+    L.vox_probe_handoff_phase.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
+    work = torch.empty(L.vox_probe_handoff_work_bytes(), dtype=torch.uint8, device=dev)
+    wbytes = 1200 << 20
+    wts = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    wts.fill_(1)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nphase = 300
+
+    def cur():
+        return torch.cuda.current_stream().cuda_stream
+
+    def status():
+        torch.cuda.synchronize()
+        c = work[:16].view(torch.int32).cpu().tolist()
+        return {"expired_waits": c[1], "values_wrong": c[2]}
+
+    for nch in (0, 4, 8, 16):
+        phase_bytes = 8192 * nch * cus
+        for mode, name in ((0, "persistent, gathered flags"), (1, "persistent, eight counters")):
+            per = []
+            for _ in range(5):
+                L.vox_probe_handoff_reset(work.data_ptr(), cur())
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                st = L.vox_probe_handoff_persistent(mode, nch, nphase, wts.data_ptr(), wbytes, work.data_ptr(), cur())
+                e1.record(stream)
+                if st:
+                    raise RuntimeError(f"handoff probe failed ({st})")
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3 / nphase)
+            print(json.dumps({"leg": "handoff", "mode": name, "phase_bytes": phase_bytes,
+                              "us_per_phase": round(float(np.median(per)), 3), **status()}), flush=True)
+        L.vox_probe_handoff_reset(work.data_ptr(), cur())
+
+        def launch(i, nch=nch):
+            if L.vox_probe_handoff_phase(nch, i + 1, wts.data_ptr(), wbytes, work.data_ptr(), cur()):
+                raise RuntimeError("handoff phase launch failed")
+        us = timed(torch, stream, launch, nphase, nphase)
+        print(json.dumps({"leg": "handoff", "mode": "one launch per phase (graph)", "phase_bytes": phase_bytes,
+                          "us_per_phase": round(us, 3), **status()}), flush=True)
+
+
 def copy_calibration(torch, dev):
     """A plain device copy of known size (256 MiB read + 256 MiB written), the reference the
     HBM byte counters are scaled by."""
@@ -140,9 +224,15 @@ def copy_calibration(torch, dev):
 
 def timed(torch, stream, launch, copies, reps, replays=5):
     """Device time (us) of `launch(i)` (which enqueues on the current stream), averaged over `reps`
-    launches rotating over `copies`.  The launches are captured once in a HIP graph, so host
-    launch cost is not measured; after two warm replays, `replays` replays are timed one by one
-    with HIP events on the stream the graph runs on, and the median is returned."""
+    launches rotating over `copies`: the median over `replays` timed graph replays (timed_all)."""
+    return float(np.median(timed_all(torch, stream, launch, copies, reps, replays)))
+
+
+def timed_all(torch, stream, launch, copies, reps, replays=5):
+    """Per-launch device times (us) of `launch(i)` (which enqueues on the current stream), one per
+    timed replay, each averaged over `reps` launches rotating over `copies`.  The launches are
+    captured once in a HIP graph, so host launch cost is not measured; after two warm replays,
+    `replays` replays are timed one by one with HIP events on the stream the graph runs on."""
     for i in range(min(copies, 4)):
         launch(i % copies)
     torch.cuda.synchronize()
@@ -165,7 +255,7 @@ def timed(torch, stream, launch, copies, reps, replays=5):
         e1.record(stream)
         torch.cuda.synchronize()
         per.append(e0.elapsed_time(e1) * 1e3 / reps)
-    return float(np.median(per))
+    return per
 
 
 def kernels_leg(torch, synth, vox, dev, stream):
@@ -195,6 +285,8 @@ def kernels_leg(torch, synth, vox, dev, stream):
     gemv_case("single 3072x3072", 3072, 3072, synth.SEED_GEMV)
     for i, (name, (n, k)) in enumerate(synth.LAYER_LINEARS.items()):
         gemv_case(f"layer {name}", n, k, 100 * synth.SEED_LAYER + i)
+    for name, n, k in synth.ENCODER_LINEARS[3:]:
+        gemv_case(f"encoder width {name}", n, k, 8100 + n + k)
     torch.cuda.empty_cache()
 
     # attention over an 8192-slot ring
@@ -345,8 +437,345 @@ def kernels_leg(torch, synth, vox, dev, stream):
     return out
 
 
+DECODER_SOURCES = ("decoder.hip", "gemv_core.h", "gqa_attn.h", "vox_common.h")
+
+
+def source_digest(names) -> str:
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "streaming_speech_text_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_trace(path: str):
+    """Per-kernel statistics of a rocprofv3 kernel_trace.csv: one JSON line per kernel name, in
+    order of total time (calls, mean, p10, p50, p90, min, max; microseconds)."""
+    import csv
+    durs = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("KernelName") or r.get("Name")
+            t0 = int(r.get("Start_Timestamp") or r.get("BeginNs") or r["Start"])
+            t1 = int(r.get("End_Timestamp") or r.get("EndNs") or r["End"])
+            durs.setdefault(name, []).append((t1 - t0) / 1e3)
+    rows = []
+    for name, d in durs.items():
+        a = np.asarray(d)
+        rows.append({"kernel": name, "calls": int(a.size), "total_us": round(float(a.sum()), 2),
+                     "mean_us": round(float(a.mean()), 3), "p10_us": round(float(np.percentile(a, 10)), 3),
+                     "p50_us": round(float(np.percentile(a, 50)), 3), "p90_us": round(float(np.percentile(a, 90)), 3),
+                     "min_us": round(float(a.min()), 3), "max_us": round(float(a.max()), 3)})
+    rows.sort(key=lambda r: -r["total_us"])
+    for r in rows:
+        print(json.dumps(r), flush=True)
+    return rows
+
+
+def counter_summary(fetch_csv: str, write_csv: str):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMV of --leg gemv, scaled by the values the
+    same counters read for the leg's calibration copies (256 MiB read and written each)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+                vals.setdefault(r["Kernel_Name"], {})
+                vals[r["Kernel_Name"]][key] = vals[r["Kernel_Name"]].get(key, 0.0) + float(r["Counter_Value"])
+        return {k: list(v.values()) for k, v in vals.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, needle, big_only=False):
+        for k, v in d.items():
+            if needle in k:
+                if big_only:
+                    v = [x for x in v if x > 0.5 * max(v)]
+                return float(np.mean(v)), len(v)
+        raise KeyError(needle)
+
+    cf, _ = pick(fetch, "copyBuffer", big_only=True)
+    cw, _ = pick(write, "copyBuffer", big_only=True)
+    gf, nd = pick(fetch, "q4_gemv_tiled_kernel")
+    gw, _ = pick(write, "q4_gemv_tiled_kernel")
+    copy_kib = 256 * 1024
+    ffac, wfac = copy_kib / cf, copy_kib / cw
+    n, k = 131072, 3072
+    alg = n * (k // 32) * 18 + 4 * (n + k)
+    hbm = int(round((gf * ffac + gw * wfac) * 1024))
+    return {"kernel": "q4_gemv_tiled_kernel (vox_q4_gemv, 131072 x 3072, LM-head shape)",
+            "kernel_source_digest": kernel_source_digest(),
+            "digest_of": "sha256 of csrc/gemv_core.h + csrc/q4_gemv.hip + csrc/vox_common.h, first 16 hex digits",
+            "calibration": {"reference": "torch copy of 256 MiB (__amd_rocclr_copyBuffer) in --leg gemv",
+                            "fetch_size_kib_read_by_copy": round(cf, 2), "write_size_kib_written_by_copy": round(cw, 2),
+                            "fetch_factor": round(ffac, 5), "write_factor": round(wfac, 5)},
+            "per_dispatch_kib": {"FETCH_SIZE": round(gf, 2), "WRITE_SIZE": round(gw, 2), "dispatches": nd},
+            "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": round(hbm / alg, 4)}
+
+
+def decoder_kernel_bytes(name: str, s, q4_row_bytes):
+    """Algorithmic bytes of one launch of a decoder kernel at shape s, from the kernel's policy name:
+    its Q4_0 weights once plus the fp32 vectors it must read and write."""
+    qd, kvd = s.n_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    name = name.replace("vox::", "")
+    if "GateUpPolicy" in name:
+        return 2 * s.hidden * q4_row_bytes(s.dim) + 4 * (2 * s.dim + s.hidden)
+    if "QkvPolicy" in name:
+        return (qd + 2 * kvd) * q4_row_bytes(s.dim) + 4 * (2 * s.dim + qd + 2 * kvd)
+    if "ResidualPolicy<GemvGeom<9216" in name:
+        return s.dim * q4_row_bytes(s.hidden) + 4 * (s.hidden + 2 * s.dim)
+    if "ResidualPolicy<GemvGeom<4096" in name:
+        return s.dim * q4_row_bytes(qd) + 4 * (qd + 2 * s.dim)
+    if "LmHeadPolicy" in name:
+        return s.vocab * q4_row_bytes(s.dim) + 4 * 2 * s.dim
+    return None
+
+
+def decoder_trace_roofline(synth):
+    """The decoder's dominant kernel (largest share of a token's time) from the committed kernel
+    trace of the default bench workload, if that trace was taken on the current decoder sources:
+    its algorithmic bytes per launch, mean duration in the trace and fraction of HBM peak."""
+    p = os.path.join(ROOT, "profiles", "decoder_step_kernels.json")
+    try:
+        with open(p) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != source_digest(DECODER_SOURCES):
+        return {"stale": True, "note": "kernel trace taken on other decoder sources"}
+    s = synth.VOXTRAL_DECODER
+    steps = d["decoder_steps"]
+    cands = [k for k in d["kernels"] if k["kernel"].replace("vox::", "").startswith(("void dec_", "dec_"))]
+    top = max(cands, key=lambda k: k["total_us"])
+    b = decoder_kernel_bytes(top["kernel"], s, synth.q4_row_bytes)
+    out = {"kernel": top["kernel"], "us_per_launch": top["mean_us"], "p10_us": top["p10_us"], "p90_us": top["p90_us"],
+           "launches_per_token": round(top["calls"] / steps, 2),
+           "share_of_token": round(top["total_us"] / sum(k["total_us"] for k in cands), 4),
+           "source": "profiles/decoder_step_kernels.json (rocprofv3 kernel trace)"}
+    if b:
+        gbs = b / top["mean_us"] / 1e3
+        out.update({"bound": "hbm", "bytes_per_launch": b, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    return out
+
+
+def decoder_device_weights(torch, synth, w, dev):
+    return {"tok_embd": torch.from_numpy(w["tok_embd"]).to(dev), "out_norm": torch.from_numpy(w["out_norm"]).to(dev),
+            "layers": [{k: torch.from_numpy(v).to(dev) for k, v in L.items()} for L in w["layers"]]}
+
+
+def time_sequences(torch, stream, dec, tok, n_seq, steps, before):
+    """n_seq sequences of `steps` greedy steps (token fed back on the device); before(q) prepares
+    sequence q untimed.  Each sequence is bracketed by synchronisations and timed with HIP events
+    on the stream the steps run on (and by the host clock).  Returns (device ms/token, wall
+    ms/token) lists."""
+    dev_ms, wall_ms = [], []
+    for q in range(n_seq):
+        before(q)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            dec.step(tok, tok)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall_ms.append((time.perf_counter() - t0) * 1e3 / steps)
+        dev_ms.append(e0.elapsed_time(e1) / steps)
+    return dev_ms, wall_ms
+
+
+def spread(v):
+    a = np.asarray(v, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "min": round(float(a.min()), 4),
+            "max": round(float(a.max()), 4), "n": int(a.size)}
+
+
+def decoder_legs(args, torch, synth, vox, dev, stream, w, full_window=True):
+    """The decoder at the bench configuration (38-position prefix, then K greedy steps) and at a
+    full, wrapped 8192-position window (ring filled with N(0, 1) keys and values, stream resumed
+    at position 8192 + 3000)."""
+    s = synth.VOXTRAL_DECODER
+    wd = decoder_device_weights(torch, synth, w, dev)
+    cfg = vox.DecoderConfig(s.n_layers, s.dim, s.n_heads, s.n_kv_heads, s.head_dim, s.hidden, s.vocab, s.n_slots,
+                            s.norm_eps, s.rope_theta)
+    dec = vox.Decoder(cfg, wd)
+    prefix, start = synth.decoder_tokens(synth.SEED_DECODER, s.vocab)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run_prefix(_q=0):
+        dec.reset()
+        for t in prefix:
+            tok.fill_(int(t))
+            dec.step(tok, tok)
+        tok.fill_(start)
+
+    # warmup: captures the graph of every attention bucket the timed positions use
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    run_prefix()
+    for _ in range(max(args.warmup, args.steps)):
+        dec.step(tok, tok)
+    torch.cuda.synchronize()
+    dev_ms, wall_ms = time_sequences(torch, stream, dec, tok, args.sequences, args.steps, run_prefix)
+    last_token = int(tok.item())
+    weight_bytes = (s.n_layers * sum(o * synth.q4_row_bytes(i) for o, i in synth.LAYER_LINEARS.values())
+                    + s.vocab * synth.q4_row_bytes(s.dim) + synth.q4_row_bytes(s.dim))
+    kv_row = s.n_layers * 2 * s.n_kv_heads * s.head_dim * 4
+    kv_bytes = sum(kv_row * min(p + 1, s.n_slots) for p in range(len(prefix), len(prefix) + args.steps)) / args.steps
+    main = {"dev_ms": dev_ms, "wall_ms": wall_ms, "bytes": weight_bytes + kv_bytes, "last_token": last_token,
+            "positions": [len(prefix), len(prefix) + args.steps], "prefix": prefix}
+    print(f"[bench] decoder {np.median(dev_ms):.4f} ms/token (median of {len(dev_ms)} sequences; host clock "
+          f"{np.median(wall_ms):.4f})", file=sys.stderr, flush=True)
+    if not full_window:
+        dec.close()
+        return main, None
+
+    # full window: every step reads all 8192 positions of every layer's K and V
+    dec.kv.view(torch.float32).normal_()
+    pos0 = s.n_slots + 3000
+    dec.seek(pos0)
+    tok.fill_(start)
+    for _ in range(max(args.warmup, 2)):
+        dec.step(tok, tok)
+    torch.cuda.synchronize()
+    f_dev, f_wall = time_sequences(torch, stream, dec, tok, args.sequences, args.steps, lambda q: None)
+    full_bytes = weight_bytes + kv_row * s.n_slots
+    fm = float(np.median(f_dev))
+    full = {"ms_per_token": spread(f_dev), "host_clock_ms_per_token": round(float(np.median(f_wall)), 4),
+            "positions": [pos0, pos0 + (max(args.warmup, 2) + args.sequences * args.steps)],
+            "live_positions": s.n_slots, "bytes_per_token": int(full_bytes),
+            "kv_bytes_per_token": int(kv_row * s.n_slots), "achieved_gbs": round(full_bytes / fm / 1e6, 1),
+            "frac_hbm": round(full_bytes / fm / 1e6 / HBM_PEAK_GBS, 4),
+            "note": "ring filled with N(0,1) keys and values, stream resumed past a wrapped window"}
+    print(f"[bench] decoder full window {fm:.4f} ms/token, {full['achieved_gbs']:.0f} GB/s", file=sys.stderr,
+          flush=True)
+    dec.close()
+    del wd
+    torch.cuda.empty_cache()
+    return main, full
+
+
+def gemv_sweep(torch, synth, vox, dev, stream, k=3072, rows=(1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)):
+    """The Q4_0 GEMV over row counts at K = 3072 (the decoder width), rotating over more than
+    1 GiB of weight copies per point."""
+    out = []
+    w_all, x = synth.gemv_inputs(synth.SEED_GEMV, max(rows), k)
+    xd = torch.from_numpy(x).to(dev)
+    for n in rows:
+        w = w_all[:n]
+        copies = max(2, int(np.ceil(1.1 * 2 ** 30 / w.nbytes)))
+        base = torch.from_numpy(np.ascontiguousarray(w)).to(dev)
+        ws = [base] + [base.clone() for _ in range(copies - 1)]
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        us = timed(torch, stream, lambda i: vox.q4_gemv(ws[i], xd, y), copies, 200 if n <= 16384 else 100)
+        b = n * synth.q4_row_bytes(k) + 4 * (n + k)
+        out.append({"n": n, "k": k, "us": round(us, 3), "gbs": round(b / us / 1e3, 1),
+                    "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del ws, base
+        torch.cuda.empty_cache()
+    return out
+
+
+def lscpu_model() -> str:
+    try:
+        import subprocess
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in r.stdout.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, ValueError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_leg(args, synth, w):
+    """The oracle (fp64 C, OpenMP over output rows or heads) on the host: the decoder step at the
+    full shape (first teacher-forced steps of the prefix) and the single workloads, at the
+    oracle's default thread count and at one thread.  Bounded samples: a few seconds each."""
+    import oracle
+    s = synth.VOXTRAL_DECODER
+    prefix, _ = synth.decoder_tokens(synth.SEED_DECODER, s.vocab)
+    n_threads = oracle.max_threads()
+
+    def clock(fn, reps):
+        t = []
+        for _ in range(reps):
+            a = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - a)
+        return 1e3 * float(np.median(t))
+
+    gw, gx = synth.gemv_inputs(synth.SEED_GEMV, 3072, 3072)
+    hw = w["tok_embd"]
+    hx = synth.normal_f32(synth.generator(synth.SEED_GEMV, 2), (s.dim,))
+    q, kc, vc = synth.attention_inputs(synth.SEED_ATTN, 32, 8, 128, 8192)
+    qd, kd, vd = q.astype(np.float64), kc.astype(np.float64), vc.astype(np.float64)
+    gemm = [synth.gemm_inputs(synth.SEED_GEMM, 16, n, k) for _, n, k in synth.ENCODER_LINEARS]
+    work = {}
+    dec = {}
+    for threads, budget in ((n_threads, args.cpu_seconds), (1, args.cpu_seconds / 2)):
+        oracle.set_num_threads(threads)
+        od = oracle.Decoder(s, w)
+        times = []
+        t_start = time.perf_counter()
+        for t in prefix:
+            a = time.perf_counter()
+            od.step(int(t), want_logits=False)
+            times.append(time.perf_counter() - a)
+            if time.perf_counter() - t_start > budget and len(times) >= (3 if threads > 1 else 1):
+                break
+        od.close()
+        dec[threads] = (1e3 * float(np.mean(times)), len(times))
+        reps = 3 if threads > 1 else 1
+        work.setdefault("gemv 3072x3072", {})[threads] = clock(lambda: oracle.q4_gemv(gw, gx), reps)
+        work.setdefault("gemv 131072x3072 (LM-head shape)", {})[threads] = clock(lambda: oracle.q4_gemv(hw, hx), 1)
+        work.setdefault("gqa attention, 8192 positions", {})[threads] = clock(
+            lambda: oracle.gqa_attn(qd, kd, vd, 1 / np.sqrt(128)), reps)
+        work.setdefault("encoder linears set, M=16", {})[threads] = clock(
+            lambda: [oracle.q4_gemm(gw_, xb_) for gw_, xb_ in gemm], 1)
+    oracle.set_num_threads(n_threads)
+    nbytes = {"gemv 3072x3072": 3072 * synth.q4_row_bytes(3072) + 8 * 3072,
+              "gemv 131072x3072 (LM-head shape)": s.vocab * synth.q4_row_bytes(s.dim) + 4 * (s.vocab + s.dim),
+              "gqa attention, 8192 positions": 8192 * 8192 + 2 * 32 * 128 * 4,
+              "encoder linears set, M=16": sum(n * synth.q4_row_bytes(k) + 16 * (2 * k + 4 * n)
+                                               for _, n, k in synth.ENCODER_LINEARS)}
+    per = {name: {"ms": {str(t): round(v, 3) for t, v in d.items()},
+                  "gbs": {str(t): round(nbytes[name] / (v * 1e-3) / 1e9, 2) for t, v in d.items()}}
+           for name, d in work.items()}
+    return {"value": round(dec[n_threads][0], 3), "unit": "ms/token", "cores": n_threads, "kind": "oracle",
+            "sample": f"first {dec[n_threads][1]} teacher-forced steps of the 38-token prefix at the full decoder "
+                      f"shape (fp64 oracle, OpenMP over output rows); at 1 thread the first {dec[1][1]}",
+            "threads": n_threads, "cpu_model": lscpu_model(), "host_cpus": os.cpu_count(),
+            "value_1_thread": round(dec[1][0], 3), "workloads": per}
+
+
 def main():
     args = parse()
+    if args.counter_summary:
+        print(json.dumps(counter_summary(*args.counter_summary), indent=1), flush=True)
+        return
+    if args.summarize_trace:
+        rows = summarize_trace(args.summarize_trace)
+        if args.trace_json:
+            with open(args.trace_json, "w") as f:
+                json.dump({"source_digest": source_digest(DECODER_SOURCES), "decoder_steps": args.decoder_steps,
+                           "trace": os.path.basename(args.summarize_trace), "kernels": rows}, f, indent=1)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layout over several GPUs "
               "is designed but not built.", file=sys.stderr)
@@ -366,87 +795,31 @@ def main():
         return
     if args.leg == "kernels":
         kernels_leg(torch, synth, vox, dev, stream)
+        for r in gemv_sweep(torch, synth, vox, dev, stream):
+            print(json.dumps({"kernel": "q4_gemv", "case": "row sweep at K=3072", **r}), flush=True)
         return
     if args.leg == "probe":
-        # the decoder kernels' byte counts (O, QKV, down, gate/up, LM head), config 1, and a sweep
-        sizes = [7077888, 10616832, 15925248, 31850496, 226492416, 5308416, 1 << 20, 4 << 20, 16 << 20,
-                 64 << 20, 256 << 20]
-        for b, (us, gbs, wg) in probe_ceiling(torch, dev, stream, sizes).items():
-            print(json.dumps({"leg": "probe", "bytes": b, "us": round(us, 3), "gbs": round(gbs, 1),
-                              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "wg_per_cu": wg}), flush=True)
+        probe_leg(torch, dev, stream)
         return
     s = synth.VOXTRAL_DECODER
     print(f"[bench] generating weights ({s.n_layers} layers, vocab {s.vocab})", file=sys.stderr, flush=True)
     w = synth.decoder_weights(synth.SEED_DECODER, s)
-    wd = {"tok_embd": torch.from_numpy(w["tok_embd"]).to(dev), "out_norm": torch.from_numpy(w["out_norm"]).to(dev),
-          "layers": [{k: torch.from_numpy(v).to(dev) for k, v in L.items()} for L in w["layers"]]}
-    cfg = vox.DecoderConfig(s.n_layers, s.dim, s.n_heads, s.n_kv_heads, s.head_dim, s.hidden, s.vocab, s.n_slots,
-                            s.norm_eps, s.rope_theta)
-    dec = vox.Decoder(cfg, wd)
-    prefix, start = synth.decoder_tokens(synth.SEED_DECODER, s.vocab)
-    tok = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    def run_prefix():
-        dec.reset()
-        for t in prefix:
-            tok.fill_(int(t))
-            dec.step(tok, tok)
-        tok.fill_(start)
-
-    # warmup: captures the graphs of every attention bucket the timed positions use
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    run_prefix()
-    for _ in range(max(args.warmup, args.steps)):
-        dec.step(tok, tok)
-    torch.cuda.synchronize()
-
-    run_prefix()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        dec.step(tok, tok)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_token = wall * 1e3 / args.steps
-    dev_ms = ev0.elapsed_time(ev1) / args.steps
-    last_token = int(tok.item())
-    step_weight_bytes = (s.n_layers * sum(o * synth.q4_row_bytes(i) for o, i in synth.LAYER_LINEARS.values())
-                         + s.vocab * synth.q4_row_bytes(s.dim) + synth.q4_row_bytes(s.dim))
-    kv_bytes = sum(s.n_layers * 2 * s.n_kv_heads * s.head_dim * 4 * min(p + 1, s.n_slots)
-                   for p in range(len(prefix), len(prefix) + args.steps)) / args.steps
-    step_bytes = step_weight_bytes + kv_bytes
-    print(f"[bench] decoder {ms_per_token:.4f} ms/token (device {dev_ms:.4f}), "
-          f"{step_bytes / (ms_per_token * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
-    dec.close()
-    del wd
-    torch.cuda.empty_cache()
+    dm, full = decoder_legs(args, torch, synth, vox, dev, stream, w, full_window=args.leg == "all")
+    if args.leg == "decoder":
+        n_steps = (args.sequences + 1) * len(dm["prefix"]) + max(args.warmup, args.steps) + args.sequences * args.steps
+        print(json.dumps({"leg": "decoder", "ms_per_token": spread(dm["dev_ms"]), "decoder_steps": n_steps}),
+              flush=True)
+        return
+    ms_per_token = float(np.median(dm["dev_ms"]))
 
     gemv = gemv_leg(args, torch, synth, vox, dev, stream)
     traffic = measured_traffic(kernel_source_digest(), gemv["bytes"])
+    ceil = probe_ceiling(torch, dev, stream, [gemv["bytes"] // 256 * 256], reps=50)
+    c_us, c_gbs, c_wg = next(iter(ceil.values()))
+    sweep = gemv_sweep(torch, synth, vox, dev, stream)
+    print(f"[bench] gemv sweep: " + ", ".join(f"{r['n']}:{r['gbs']:.0f}" for r in sweep), file=sys.stderr, flush=True)
 
-    # CPU baseline: the oracle on the host cores, bounded sample of the same decoder workload
-    cpu = None
-    if not args.no_cpu:
-        import oracle
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        od = oracle.Decoder(s, w)
-        times = []
-        t_start = time.perf_counter()
-        for t in list(prefix):
-            a = time.perf_counter()
-            od.step(int(t), want_logits=False)
-            times.append(time.perf_counter() - a)
-            if time.perf_counter() - t_start > args.cpu_seconds and len(times) >= 3:
-                break
-        od.close()
-        cpu = {"value": round(1e3 * float(np.mean(times)), 3), "unit": "ms/token", "cores": threads,
-               "kind": "oracle",
-               "sample": f"first {len(times)} teacher-forced steps of the 38-token prefix at the full decoder "
-                         f"shape (fp64 oracle, OpenMP over output rows)"}
+    cpu = None if args.no_cpu else cpu_leg(args, synth, w)
 
     out = {
         "metric": "decoder ms/token + Q4_0 GEMV achieved HBM GB/s (% of peak), 1 MI355X",
@@ -463,15 +836,23 @@ def main():
         "data": "synthetic (seeded random-init Q4_0 weights, seeded token ids)",
         "config": {"workload": "Voxtral decoder step: 26 layers, dim 3072, GQA 32/8 x 128, SwiGLU 9216, "
                                "tied Q4_0 head 131072, 8192-slot KV ring, 38-token prefix then greedy steps",
-                   "tokens_timed": args.steps, "kv_positions": [len(prefix), len(prefix) + args.steps]},
+                   "tokens_timed": args.steps, "sequences": args.sequences, "kv_positions": dm["positions"]},
         "roofline": {"bound": "hbm", "achieved": round(gemv["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gemv["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": f"q4_gemv {gemv['n']}x{gemv['k']} (LM-head shape)", "bytes_per_launch": gemv["bytes"],
-                     "us_per_launch": round(gemv["us"], 3)},
-        "decoder_device_ms_per_token": round(dev_ms, 4),
-        "decoder_hbm_gbs": round(step_bytes / (ms_per_token * 1e-3) / 1e9, 1),
-        "decoder_bytes_per_token": int(step_bytes),
-        "last_token": last_token,
+                     "us_per_launch": round(gemv["us"], 3), "us_per_launch_spread": gemv["spread"],
+                     "ceiling": {"gbs": round(c_gbs, 1), "frac_hbm": round(c_gbs / HBM_PEAK_GBS, 4),
+                                 "us": round(c_us, 3), "probe": "streaming read of the same byte count "
+                                 "(libvox_probe.so)", "workgroups_per_cu": c_wg},
+                     "frac_of_ceiling": round(gemv["gbs"] / c_gbs, 4)},
+        "decoder_ms_per_token": spread(dm["dev_ms"]),
+        "decoder_host_clock_ms_per_token": spread(dm["wall_ms"]),
+        "decoder_hbm_gbs": round(dm["bytes"] / (ms_per_token * 1e-3) / 1e9, 1),
+        "decoder_bytes_per_token": int(dm["bytes"]),
+        "decoder_full_window": full,
+        "decoder_roofline": decoder_trace_roofline(synth),
+        "gemv_sweep_k3072": sweep,
+        "last_token": dm["last_token"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -25,6 +25,25 @@ int vox_probe_sink_entries(int wg_per_cu);
  * hipStream_t; NULL = the null stream).  Returns 0, -1 on a bad argument, -4 if the launch failed. */
 int vox_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream);
 
+/* Grid-wide handoff probe: the cost of passing a 3072-float vector between phases inside one
+ * persistent kernel (one 512-thread workgroup per compute unit, a grid barrier per phase, each
+ * workgroup's next weight share of 8192 * nch bytes prefetched before the barrier) against one
+ * launch per phase.  nch: 0, 4, 8 or 16 (0: the handoff alone).  Work buffer: device memory of
+ * vox_probe_handoff_work_bytes() bytes, 256-byte aligned; its first 16 bytes are four uint32
+ * (abort flag, expired waits, vector values read wrong, unused), cleared by vox_probe_handoff_reset.
+ * weights: at least 8192 * nch * (number of compute units) bytes, 16-byte aligned (phases read
+ * consecutive windows of it).  Every wait inside the persistent kernel is bounded (2^20 polls);
+ * one expired wait ends all others.  Returns 0, -1 on a bad argument, -2 if a workgroup per
+ * compute unit cannot be resident, -4 if the launch failed. */
+size_t vox_probe_handoff_work_bytes(void);
+int vox_probe_handoff_reset(void *work, void *stream);
+/* mode 0: every workgroup stores a flag, one workgroup gathers them and releases the grid;
+ * mode 1: eight counters, every workgroup polls their sum.  Runs nphase phases (1..100000). */
+int vox_probe_handoff_persistent(int mode, int nch, int nphase, const void *weights, size_t weight_bytes, void *work,
+                                 void *stream);
+/* Phase `phase` (1..100000) of the same work as its own launch, no prefetch, no barrier. */
+int vox_probe_handoff_phase(int nch, int phase, const void *weights, size_t weight_bytes, void *work, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

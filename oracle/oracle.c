@@ -22,8 +22,13 @@
 #include "oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads of the OpenMP loops below (for timing the oracle at a chosen thread count). */
+void orc_set_num_threads(int64_t n) { omp_set_num_threads(n > 0 ? (int)n : 1); }
+int64_t orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------------------
  * Number formats

@@ -58,6 +58,10 @@ int64_t orc_argmax_f64(const double *v, int64_t n);
 int64_t orc_alt_tokens(const float *logits, int64_t vocab, double cutoff, int64_t max_out, int64_t *ids,
                        double *probs);
 
+/* OpenMP threads used by the loops (timing only; results do not depend on it). */
+void orc_set_num_threads(int64_t n);
+int64_t orc_max_threads(void);
+
 /* Whole decoder step */
 typedef struct {
     int64_t n_layers, dim, n_heads, n_kv_heads, head_dim, hidden, vocab, n_slots;

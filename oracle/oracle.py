@@ -71,6 +71,10 @@ def lib():
         L.orc_argmax_f32.argtypes = [_vp, _i64]
         L.orc_argmax_f64.restype = _i64
         L.orc_argmax_f64.argtypes = [_vp, _i64]
+        L.orc_set_num_threads.restype = None
+        L.orc_set_num_threads.argtypes = [_i64]
+        L.orc_max_threads.restype = _i64
+        L.orc_max_threads.argtypes = []
         L.orc_decoder_create.restype = _vp
         L.orc_decoder_create.argtypes = [C.POINTER(DecoderConfig), _vp, _vp, C.POINTER(LayerWeights)]
         L.orc_decoder_position.restype = _i64
@@ -263,6 +267,15 @@ def argmax_f32(v) -> int:
 def argmax_f64(v) -> int:
     v = _c(v, np.float64)
     return int(lib().orc_argmax_f64(_p(v), v.size))
+
+
+def set_num_threads(n: int):
+    """OpenMP threads of the oracle's loops (timing only; results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 class Decoder:

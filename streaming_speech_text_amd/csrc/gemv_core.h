@@ -201,20 +201,22 @@ __device__ __forceinline__ void gemv_tile_rows(const u32x4 *tile, float *red, fl
         red[rr * Gm::TR + c] = q4_pair_dot(D, px.x, px.n8a, px.n8b);
     }
     __syncthreads();
-    // Each row's TR partials are added by a row of 16 lanes (TR/16 each, then a DPP tree), in
-    // a fixed order; rows beyond NT/16 take a second pass.
-    static_assert(Gm::TR % 16 == 0, "row partials split over 16 lanes");
-    constexpr int ROWS_PER_PASS = Gm::NT / 16;
+    // Each row's TR partials are added by RL lanes (TR/RL each, then a DPP tree): a row of 16
+    // lanes when TR is a multiple of 16, else a quad; in a fixed order.  Rows beyond NT/RL take
+    // another pass.
+    constexpr int RL = Gm::TR % 16 == 0 ? 16 : 4;
+    static_assert(Gm::TR % RL == 0, "row partials split over 16 or 4 lanes");
+    constexpr int ROWS_PER_PASS = Gm::NT / RL;
 #pragma unroll
     for (int r0 = 0; r0 < Gm::R; r0 += ROWS_PER_PASS) {
-        const int row = r0 + tid / 16;
-        if (row < Gm::R) {   // uniform over each 16-lane row
-            const int j = tid % 16;
+        const int row = r0 + tid / RL;
+        if (row < Gm::R) {   // uniform over each group of RL lanes
+            const int j = tid % RL;
             float s = 0.0f;
 #pragma unroll
-            for (int i = 0; i < Gm::TR / 16; ++i)
-                s += red[row * Gm::TR + i * 16 + j];
-            s = row16_sum(s);
+            for (int i = 0; i < Gm::TR / RL; ++i)
+                s += red[row * Gm::TR + i * RL + j];
+            s = RL == 16 ? row16_sum(s) : quad_sum(s);
             if (j == 0)
                 rowsum[row] = s * px.scale;
         }

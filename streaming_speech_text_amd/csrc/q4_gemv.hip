@@ -63,7 +63,8 @@ __global__ __launch_bounds__(256) void q4_gemv_generic_kernel(const uint8_t *__r
 }
 
 // ---------------------------------------------------------------------------------------
-// Tiled fast path (K in {3072, 4096, 9216}: the decoder's linear widths).
+// Tiled fast path (K in {3072, 4096, 9216}: the decoder's linear widths; 1280, 5120: the
+// encoder's).
 // ---------------------------------------------------------------------------------------
 template <class Gm>
 struct PlainGemvPolicy {
@@ -136,6 +137,13 @@ int q4_gemv_launch(const void *w, const float *x, float *y, int64_t n, int64_t k
     if (fast_layout && k == 9216)
         return tall ? launch_tiled<GemvGeom<9216, 576, 8>>(w, x, y, n, s)
                     : launch_tiled<GemvGeom<9216, 576, 4>>(w, x, y, n, s);
+    // the encoder widths ([VC] 모델 아키텍처: width 1280, feed-forward 5120): 20 or 80 threads per
+    // row, five-wave workgroups; at K = 1280 a workgroup holds 16 row groups, so 16-row tiles
+    if (fast_layout && k == 1280)
+        return launch_tiled<GemvGeom<1280, 320, 16>>(w, x, y, n, s);
+    if (fast_layout && k == 5120)
+        return tall ? launch_tiled<GemvGeom<5120, 320, 8>>(w, x, y, n, s)
+                    : launch_tiled<GemvGeom<5120, 320, 4>>(w, x, y, n, s);
     const int64_t grid = (n + 3) / 4;
     hipLaunchKernelGGL(q4_gemv_generic_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)w, x, y, n,
                        k);

@@ -43,6 +43,14 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
+// Sum over each quad of lanes (fixed order); every lane of the quad gets the quad's total.
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += dpp_f<DPP_QUAD_XOR1>(v);
+    v += dpp_f<DPP_QUAD_XOR2>(v);
+    return v;
+}
+
 __device__ __forceinline__ float row16_max(float v)
 {
     v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));

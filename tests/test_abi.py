@@ -46,7 +46,8 @@ def test_probe_library_exports_its_header():
     path = os.path.join(ROOT, "streaming_speech_text_amd", "libvox_probe.so")
     plib = C.CDLL(path)
     fns = header_functions(PROBE_HEADER)
-    assert fns == ["vox_probe_sink_entries", "vox_probe_stream_read"]
+    assert fns == ["vox_probe_handoff_persistent", "vox_probe_handoff_phase", "vox_probe_handoff_reset",
+                   "vox_probe_handoff_work_bytes", "vox_probe_sink_entries", "vox_probe_stream_read"]
     assert all(hasattr(plib, f) for f in fns)
     plib.vox_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
     # bad arguments are refused before any HIP call

@@ -70,13 +70,20 @@ def test_gemv_lm_head_shape(vx, orc):
     _gemv_case(vx, orc, 131072, 3072, 61, "lm-head")
 
 
-@pytest.mark.parametrize("k", [3072, 4096, 9216])
+@pytest.mark.parametrize("k", [3072, 4096, 9216, 1280, 5120])
 @pytest.mark.parametrize("n", [1, 3, 17, 65, 1000, 4097])
 def test_gemv_ragged_rows(vx, orc, n, k):
     _gemv_case(vx, orc, n, k, 7000 + n + k, "ragged")
 
 
-@pytest.mark.parametrize("k", [32, 96, 1280, 5120, 2080])
+def test_gemv_encoder_linears(vx, orc):
+    # the encoder's linears (width 1280, feed-forward 5120) at one activation vector: the tiled
+    # path at K = 1280 (16-row tiles, quad reductions) and K = 5120
+    for i, (name, n, k) in enumerate(synth.ENCODER_LINEARS):
+        _gemv_case(vx, orc, n, k, 8100 + i, f"encoder {name}")
+
+
+@pytest.mark.parametrize("k", [32, 96, 1312, 2080])
 def test_gemv_generic_widths(vx, orc, k):
     _gemv_case(vx, orc, 77, k, 8000 + k, "generic-k")
 
@@ -96,7 +103,7 @@ def test_gemv_unaligned_pointers(vx, orc):
 def test_gemv_exact_dyadic(vx, orc):
     # power-of-two scales and small integer activations: every partial sum is exact in fp32,
     # so the GPU must agree with the oracle bit for bit whatever the summation order
-    for n, k in [(64, 3072), (40, 4096), (12, 9216), (9, 1280)]:
+    for n, k in [(64, 3072), (40, 4096), (12, 9216), (9, 1280), (33, 1280), (21, 5120), (9, 1312)]:
         g = synth.generator(92, n, k)
         w = synth.q4_matrix(g, n, k).reshape(n, k // 32, 18)
         e = g.integers(-3, 1, size=(n, k // 32)).astype(np.float64)
