@@ -11,7 +11,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# VOX_ORACLE_LIB selects another build of the same source (the sanitizer build, oracle/build.py)
+_LIB_PATH = os.environ.get("VOX_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _i64 = C.c_int64
