@@ -308,18 +308,23 @@ def kernels_leg(torch, synth, vox, dev, stream):
     del ks, vs
     torch.cuda.empty_cache()
 
-    # encoder-chunk GEMM set: the six linears of one layer, each M
-    for m in synth.ENCODER_M:
+    # encoder-chunk GEMM set: the six linears of one layer, each M; then the same set with q, k and v
+    # as one 3840-row product over their concatenated weights (the rows of a Q4_0 matrix are
+    # independent, so stacking Wq, Wk, Wv gives q, k, v side by side in one output)
+    for m, fused in [(m_, f_) for m_ in synth.ENCODER_M for f_ in (False, True)]:
         sets = []
         for name, n, k in synth.ENCODER_LINEARS:
             w, xb = synth.gemm_inputs(synth.SEED_GEMM, m, n, k)
             sets.append((name, n, k, w, torch.from_numpy(xb.view(np.int16)).to(dev)))
+        if fused:
+            qkv_w = np.concatenate([sets[0][3], sets[1][3], sets[2][3]], axis=0)
+            sets = [("qkv", 3 * sets[0][1], sets[0][2], qkv_w, sets[0][4])] + sets[3:]
         wbytes = sum(s_[3].nbytes for s_ in sets)
         copies = max(2, int(np.ceil(1.1 * GiB / wbytes)))
         wdev = [[torch.from_numpy(s_[3]).to(dev) for s_ in sets] for _ in range(copies)]
         ys = [torch.empty(m, s_[1], dtype=torch.float32, device=dev) for s_ in sets]
         # one workspace serves the set (the launches run one after another on the stream)
-        wsb = max(vox.q4_gemm_workspace(m, n, k) for _, n, k in synth.ENCODER_LINEARS)
+        wsb = max(vox.q4_gemm_workspace(m, n_, k_) for _, n_, k_, _, _ in sets)
         gws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
         def launch(i):
@@ -328,8 +333,9 @@ def kernels_leg(torch, synth, vox, dev, stream):
                                                  vox._ptr(gws) if wsb else None, wsb, vox._stream(None)))
         us = timed(torch, stream, launch, copies, 50)
         flops = 2 * m * sum(n * k for _, n, k in synth.ENCODER_LINEARS)
-        b = wbytes + sum(m * k * 2 + m * n * 4 for _, n, k in synth.ENCODER_LINEARS)
-        emit({"kernel": "q4_gemm", "case": f"encoder linears set, M={m}", "us": round(us, 3), "flops": flops,
+        b = wbytes + sum(m * k_ * 2 + m * n_ * 4 for _, n_, k_, _, _ in sets)
+        emit({"kernel": "q4_gemm", "case": f"encoder linears set, M={m}" + (", q/k/v as one 3840-row call" if fused
+                                                                             else ""), "us": round(us, 3), "flops": flops,
               "tflops": round(flops / us / 1e6, 2), "frac_mfma_bf16": round(flops / us / 1e6 / 2500.0, 4),
               "bytes": b, "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
         del wdev

@@ -11,7 +11,7 @@
 // in bf16 and whose A operand holds the bf16 activations; the fp32 result is multiplied by the
 // block's scale d and accumulated in fp32 on the vector units.
 //
-// Two kernels:
+// Three kernels:
 //  * small outputs: a workgroup of 8 waves owns a (16*MI) x (16*NJ) tile; the waves
 //    split the K blocks into eight contiguous ranges, load their operands straight from memory
 //    with GM_PF blocks in flight, and the eight partial tiles are added in LDS in wave order.
@@ -22,6 +22,9 @@
 //  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS),
 //    optionally with K split over workgroups (partial tiles in the caller's workspace, added in
 //    a fixed order by a second kernel).
+//  * long chunks with many output tiles: the split product (128 x 128 tiles), whose B operands
+//    are the exact hi and lo bf16 parts of each dequantised weight, so the scale needs no vector
+//    work per output.
 //
 // The adapter between encoder and decoder (voxtral.c page, section 모델 아키텍처: a linear from
 // 5120 to 3072 inputs, GELU, a linear from 3072 to 3072) is two tiled products.  The first one's
@@ -85,12 +88,15 @@ __device__ __forceinline__ void store_gelu_pair(uint16_t *hl, int n, int64_t row
     p[GELU_STAGE] = __builtin_bit_cast(uint16_t, lo);
 }
 
-template <int MI, int NJ, int PF>
-__global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__restrict__ w,
+// WAVES: waves splitting K.  (Sixteen waves with all ten blocks of each in flight for 16 x 1280 x
+// 5120 were measured on MI355X at 19.3 us against 13 us for the tiled kernel and its slice sum:
+// the lanes' 4-byte pieces of 16 weight rows make every load touch 16 cache lines.)
+template <int MI, int NJ, int PF, int WAVES = GM_WAVES>
+__global__ __launch_bounds__(64 * WAVES) void q4_gemm_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x, float *__restrict__ y,
                                                             int m, int n, int k)
 {
-    __shared__ float red[GM_WAVES][MI * NJ][4][64];
+    __shared__ float red[WAVES][MI * NJ][4][64];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -101,8 +107,8 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
     const int m0 = blockIdx.y * 16 * MI;
     const int nb = k / 32;
     const size_t row_bytes = (size_t)nb * 18;
-    const int kb0 = (int)((int64_t)wave * nb / GM_WAVES);
-    const int kb1 = (int)((int64_t)(wave + 1) * nb / GM_WAVES);
+    const int kb0 = (int)((int64_t)wave * nb / WAVES);
+    const int kb1 = (int)((int64_t)(wave + 1) * nb / WAVES);
 
     // operand rows of this lane (past the edge: the last valid row; masked at the store)
     const uint16_t *xrow[MI];
@@ -196,12 +202,12 @@ __global__ __launch_bounds__(GM_THREADS) void q4_gemm_kernel(const uint8_t *__re
                 red[wave][i * NJ + j][r][lane] = acc[i][j][r];
     __syncthreads();
     // D layout of a 16x16 MFMA block: lane holds rows 4*(lane/16) .. +3 of column lane%16
-    for (int e = tid; e < MI * NJ * 4 * 64; e += GM_THREADS) {
+    for (int e = tid; e < MI * NJ * 4 * 64; e += 64 * WAVES) {
         const int ln = e & 63, r = (e >> 6) & 3, blk = e >> 8;
         const int i = blk / NJ, j = blk % NJ;
         float v = red[0][blk][r][ln];
 #pragma unroll
-        for (int wv = 1; wv < GM_WAVES; ++wv)
+        for (int wv = 1; wv < WAVES; ++wv)
             v += red[wv][blk][r][ln];
         const int row = m0 + 16 * i + 4 * (ln >> 4) + r;
         const int col = n0 + 16 * j + (ln & 15);
@@ -534,6 +540,204 @@ __global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__rest
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Long chunks without per-block scale arithmetic (the split product).  A dequantised weight
+// w = (code - 8) * d is exact in fp32 with at most 14 significant bits, so it is the exact sum of
+// two bf16 values: hi = w with the low 16 bits of its fp32 pattern cleared (8 significant bits)
+// and lo = w - hi (at most 6 significant bits, exact).  Y = X W^T then runs as two bf16 products
+// per Q4_0 block, X HI^T + X LO^T, every product exact and accumulated in fp32: the scale sits
+// inside the operands, so no vector instruction runs per output and block, and a weight costs a
+// handful of vector instructions once per 128 rows of X.  The price is twice the matrix-core
+// work of the product as defined.
+//
+// Workgroup: 4 waves, a 128 x 128 tile of Y.  Wave w owns columns 32w .. 32w+31 for all 128 rows
+// (four 32 x 32 output blocks of v_mfma_f32_32x32x16_bf16), so each weight is unpacked once, in
+// the registers of the wave that uses it.  K runs in stages of 4 Q4_0 blocks (128 inputs): the
+// stage's activations (128 rows x 128 bf16, rows padded by 16 bytes) and raw weight bytes (128
+// columns x 72 bytes) go through LDS, and the next stage's loads are in flight in registers while
+// the current one is computed.  Operand layouts of the 32 x 32 x 16 product: lane L of A holds row
+// L % 32, inputs 8(L/32) .. 8(L/32)+7 of a 16-input step; lane L of B holds column L % 32 and the
+// same inputs; result register r of lane L is row 8(r/4) + 4(L/32) + r % 4, column L % 32.  A Q4_0
+// block is two steps, its low nibbles (inputs 0-15) then its high nibbles (16-31); lane group g
+// takes code bytes 8g .. 8g+7 in both.  Workgroup z of the grid's third dimension takes stages
+// z*NS .. z*NS+NS-1 and, when part is set, writes its partial tile to part[z] instead of y.
+// ---------------------------------------------------------------------------------------
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+
+constexpr int GH_BM = 128, GH_BN = 128, GH_THREADS = 256;
+constexpr int GH_KC = 4, GH_STAGE = GH_KC * 32;                   // Q4_0 blocks / inputs per stage
+constexpr int GH_AROW = GH_STAGE + 8;                              // bf16 per LDS row of A (16-byte pad)
+constexpr int GH_RAW = GH_KC * 18;                                 // weight bytes of a column per stage
+constexpr int GH_A_PER = GH_BM * GH_STAGE * 2 / 16 / GH_THREADS;   // 16-byte pieces of A per thread: 8
+constexpr int GH_W_PIECES = GH_BN * GH_RAW / 8;                    // 8-byte pieces of the weights: 1152
+constexpr int GH_W_PER = (GH_W_PIECES + GH_THREADS - 1) / GH_THREADS;   // 5
+static_assert(GH_A_PER * GH_THREADS * 8 == GH_BM * GH_STAGE, "the threads cover a stage of A");
+static_assert(GH_RAW % 8 == 0, "a column's stage bytes are whole 8-byte pieces");
+
+// hi and lo bf16 parts of w = (code - 8) * d for the four codes of bytes 0..3 of c (nibble values
+// 0..15 in the low 4 bits of each byte), packed in weight order: two dwords each.
+__device__ __forceinline__ void split_pairs(uint32_t c, float d, float m8d, uint32_t &h01, uint32_t &h23, uint32_t &l01,
+                                            uint32_t &l23)
+{
+    float wv[4], lv[4];
+    uint32_t hb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        wv[j] = fmaf(ubyte_to_f(c, j), d, m8d);   // (code - 8) * d, exact
+        hb[j] = __builtin_bit_cast(uint32_t, wv[j]) & 0xFFFF0000u;
+        lv[j] = wv[j] - __builtin_bit_cast(float, hb[j]);   // exact, at most 6 significant bits
+    }
+    h01 = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
+    h23 = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
+    l01 = pack_bf16_pair(lv[0], lv[1]);
+    l23 = pack_bf16_pair(lv[2], lv[3]);
+}
+
+// B operands (hi and lo, both 16-input steps) of block `blk` of the stage for this lane's column,
+// from the column's raw stage bytes in LDS (dword aligned, GH_RAW bytes).
+__device__ __forceinline__ void unpack_split(const uint32_t *col, int blk, int g, bf16x8 (&bhi)[2], bf16x8 (&blo)[2])
+{
+    const int base = 18 * blk;   // first byte of the block: 4-aligned for even blocks, 2 mod 4 for odd
+    uint32_t d16, c0, c1;
+    if ((blk & 1) == 0) {
+        d16 = col[base >> 2] & 0xFFFFu;
+        const uint32_t *q = col + ((base + 2 + 8 * g) >> 2);   // code bytes start 2 mod 4
+        const uint32_t q0 = q[0], q1 = q[1], q2 = q[2];
+        c0 = __builtin_amdgcn_alignbyte(q1, q0, 2);
+        c1 = __builtin_amdgcn_alignbyte(q2, q1, 2);
+    } else {
+        d16 = col[(base - 2) >> 2] >> 16;
+        const uint32_t *q = col + ((base + 2 + 8 * g) >> 2);   // code bytes 4-aligned
+        c0 = q[0];
+        c1 = q[1];
+    }
+    const float d = half_bits_to_float(d16);
+    const float m8d = -8.0f * d;
+    uint32_t h[4], l[4];
+    // low nibbles: the block's inputs 8g .. 8g+7 of the first step
+    split_pairs(c0 & 0x0F0F0F0Fu, d, m8d, h[0], h[1], l[0], l[1]);
+    split_pairs(c1 & 0x0F0F0F0Fu, d, m8d, h[2], h[3], l[2], l[3]);
+    bhi[0] = __builtin_bit_cast(bf16x8, u32x4v{h[0], h[1], h[2], h[3]});
+    blo[0] = __builtin_bit_cast(bf16x8, u32x4v{l[0], l[1], l[2], l[3]});
+    // high nibbles: inputs 16 + 8g .. of the second step
+    split_pairs((c0 >> 4) & 0x0F0F0F0Fu, d, m8d, h[0], h[1], l[0], l[1]);
+    split_pairs((c1 >> 4) & 0x0F0F0F0Fu, d, m8d, h[2], h[3], l[2], l[3]);
+    bhi[1] = __builtin_bit_cast(bf16x8, u32x4v{h[0], h[1], h[2], h[3]});
+    blo[1] = __builtin_bit_cast(bf16x8, u32x4v{l[0], l[1], l[2], l[3]});
+}
+
+// WM: waves along M (1: four waves, each 32 columns x 128 rows; 2: eight waves, each 32 columns x
+// 64 rows - twice the waves to hide latency, each weight unpacked by the two waves that use it).
+template <int NS, int WM>
+__global__ __launch_bounds__(GH_THREADS * WM) __attribute__((amdgpu_waves_per_eu(2 * WM))) void q4_gemm_split_kernel(
+    const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, float *__restrict__ part,
+    int m, int n, int k)
+{
+    constexpr int NT = GH_THREADS * WM;
+    constexpr int A_PER = GH_A_PER / WM;                        // 16-byte pieces of A per thread
+    constexpr int W_PER = (GH_W_PIECES + NT - 1) / NT;          // 8-byte weight pieces per thread
+    constexpr int MI = 4 / WM;                                   // 32-row blocks per wave
+    __shared__ __attribute__((aligned(16))) uint16_t as[GH_BM * GH_AROW];
+    __shared__ __attribute__((aligned(16))) uint32_t wraw[GH_BN * GH_RAW / 4];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int wn = wave & 3, wm = wave >> 2;   // column quarter, row part
+    const int lane = tid & 63;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int m0 = blockIdx.y * GH_BM;
+    const int n0 = blockIdx.x * GH_BN;
+    const int st0 = blockIdx.z * NS;
+    const uint32_t row_bytes = (uint32_t)(k / 32) * 18;
+
+    // activations: piece p = tid + NT j is row p / 16, inputs 8 (p % 16) .. of the stage (rows past
+    // m repeat the last row; their outputs are not stored)
+    uint32_t aoff[A_PER];
+    int alds[A_PER];
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j) {
+        const int p = tid + NT * j, r = p >> 4, c = p & 15;
+        aoff[j] = (uint32_t)min(m0 + r, m - 1) * (uint32_t)k + (uint32_t)(8 * c);
+        alds[j] = r * GH_AROW + 8 * c;
+    }
+    // weights: piece q is column q / 9, bytes 8 (q % 9) .. of its stage bytes; pieces past the last
+    // repeat it (a duplicate load and an identical LDS store); columns past n repeat the last one
+    uint32_t woff[W_PER];
+    int wlds[W_PER];
+#pragma unroll
+    for (int j = 0; j < W_PER; ++j) {
+        const int q = min(tid + NT * j, GH_W_PIECES - 1);
+        const int col = min(n0 + q / (GH_RAW / 8), n - 1);
+        woff[j] = (uint32_t)col * row_bytes + (uint32_t)(8 * (q % (GH_RAW / 8)));
+        wlds[j] = (q / (GH_RAW / 8)) * (GH_RAW / 4) + 2 * (q % (GH_RAW / 8));
+    }
+
+    u32x4v ar[A_PER];
+    u32x2v wr[W_PER];
+    auto load_stage = [&](int st) {
+        const uint16_t *xs = x + (size_t)st * GH_STAGE;
+#pragma unroll
+        for (int j = 0; j < A_PER; ++j)
+            ar[j] = *reinterpret_cast<const u32x4v *>(xs + aoff[j]);
+        const uint8_t *ws = w + (size_t)st * GH_RAW;
+#pragma unroll
+        for (int j = 0; j < W_PER; ++j)
+            wr[j] = *reinterpret_cast<const u32x2v *>(ws + woff[j]);
+    };
+
+    f32x16v acc[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+        acc[i] = 0.0f;
+
+    const uint32_t *colw = wraw + (32 * wn + l32) * (GH_RAW / 4);
+    const int arow0 = 32 * MI * wm + l32;
+    load_stage(st0);
+    for (int s = 0; s < NS; ++s) {
+        __syncthreads();   // every wave is done with the previous stage's LDS
+#pragma unroll
+        for (int j = 0; j < A_PER; ++j)
+            *reinterpret_cast<u32x4v *>(&as[alds[j]]) = ar[j];
+#pragma unroll
+        for (int j = 0; j < W_PER; ++j)
+            *reinterpret_cast<u32x2v *>(&wraw[wlds[j]]) = wr[j];
+        __syncthreads();
+        if (s + 1 < NS)
+            load_stage(st0 + s + 1);   // in flight during the products
+#pragma unroll
+        for (int b = 0; b < GH_KC; ++b) {
+            bf16x8 bhi[2], blo[2];
+            unpack_split(colw, b, g, bhi, blo);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8 af[MI];
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    af[i] = *reinterpret_cast<const bf16x8 *>(&as[(arow0 + 32 * i) * GH_AROW + 32 * b + 16 * h + 8 * g]);
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bhi[h], acc[i], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], blo[h], acc[i], 0, 0, 0);
+            }
+        }
+    }
+
+    float *const dst = part ? part + (size_t)blockIdx.z * m * n : y;
+    const int col = n0 + 32 * wn + l32;
+    if (col < n) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + 32 * (MI * wm + i) + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (row < m)
+                    dst[(size_t)row * n + col] = acc[i][r];
+            }
+    }
+}
+
 // K values with a compiled stage sequence (the encoder's widths and the decoder's)
 static bool tiled_k(int64_t k) { return k == 1280 || k == 3072 || k == 5120; }
 
@@ -629,6 +833,45 @@ static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_
     return check_launch("q4 tiled product: slice sum");
 }
 
+// The split product (q4_gemm_split_kernel) runs where its 128 x 128 tiles alone give at least
+// SPLIT_MIN_WGS workgroups and the chunk has at least SPLIT_MIN_M rows (the unpack of a weight is
+// repaid over 128 rows).  Measured on MI355X against the tiled kernel: 750 x 5120 x 1280 28.5
+// against 34.4 us; with K split over the grid to reach the workgroup count (750 x 1280 x 1280, five
+// slices of two stages, and the slice sum) 22 against 12.9 us, so it never splits K.  Four waves
+// (each 32 columns x 128 rows) beat eight (each 32 x 64, every weight unpacked twice): 28.5 against
+// 30.5 us; eight-block stages: no faster.
+constexpr int64_t SPLIT_MIN_M = 256;
+constexpr int SPLIT_MIN_WGS = 240;
+constexpr int SPLIT_WM = 1;   // waves along M per workgroup
+
+static bool split_shape(int64_t m, int64_t n, int64_t k)
+{
+    const size_t wbytes = (size_t)n * (size_t)(k / 32) * 18;
+    const int64_t tiles = ((n + GH_BN - 1) / GH_BN) * ((m + GH_BM - 1) / GH_BM);
+    return tiled_k(k) && m >= SPLIT_MIN_M && tiles >= SPLIT_MIN_WGS && (uint64_t)m * (uint64_t)k < (1ull << 31) &&
+           wbytes < (1ull << 31) && (m + GH_BM - 1) / GH_BM <= 65535;
+}
+
+template <int NS>
+static void launch_split_ns(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
+{
+    const dim3 grid((unsigned)((n + GH_BN - 1) / GH_BN), (unsigned)((m + GH_BM - 1) / GH_BM), 1u);
+    hipLaunchKernelGGL((q4_gemm_split_kernel<NS, SPLIT_WM>), grid, dim3(GH_THREADS * SPLIT_WM), 0, s,
+                       (const uint8_t *)w, x, y, (float *)nullptr, m, n, k);
+}
+
+// y = X W^T through the split product (K = 1280, 3072 or 5120: 10, 24 or 40 stages).
+static int launch_gemm_split(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
+{
+    switch (k / GH_STAGE) {
+    case 40: launch_split_ns<40>(w, x, y, m, n, k, s); break;
+    case 24: launch_split_ns<24>(w, x, y, m, n, k, s); break;
+    case 10: launch_split_ns<10>(w, x, y, m, n, k, s); break;
+    default: return fail(VOX_E_UNSUPPORTED, "q4 split product: no compiled stage count for k=%d", k);
+    }
+    return check_launch("q4 split product");
+}
+
 // Blocks in flight per wave: all of them when a wave has exactly five (K = 1280: the whole range
 // in one memory round trip; measured on MI355X, 16 x 1280 x 1280 took 5.5 us against 7.4 with
 // four), else four (five or eight for longer ranges was slower, e.g. 16 x 3072 x 3072: 15.6 us
@@ -652,8 +895,11 @@ using namespace vox;
 
 extern "C" size_t vox_q4_gemm_workspace(int64_t m, int64_t n, int64_t k)
 {
-    if (m <= 0 || n <= 0 || k <= 0 || k % 32 || m > 65535 * 16 || n > (1 << 24) || k > (1 << 24) ||
-        !tiled_shape(m, n, k))
+    if (m <= 0 || n <= 0 || k <= 0 || k % 32 || m > 65535 * 16 || n > (1 << 24) || k > (1 << 24))
+        return 0;
+    if (split_shape(m, n, k))
+        return 0;
+    if (!tiled_shape(m, n, k))
         return 0;
     return tiled_workspace(m, n, tiled_slices(m, n, k));
 }
@@ -679,7 +925,9 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
         return fail(VOX_E_INVAL, "vox_q4_gemm: workspace and workspace_bytes must be both set or both zero");
     hipStream_t s = (hipStream_t)stream;
     int st;
-    if (aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_shape(m, n, k)) {
+    if (aligned(x_bf16, 16) && aligned(w_q4, 16) && split_shape(m, n, k)) {
+        st = launch_gemm_split(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
+    } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_shape(m, n, k)) {
         int slices = workspace ? tiled_slices(m, n, k) : 1;
         const size_t need = tiled_workspace(m, n, slices);
         if (need > workspace_bytes)

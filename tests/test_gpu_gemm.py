@@ -51,7 +51,7 @@ def test_gemm_split_repeatable(vx):
     assert np.array_equal(host(y), a)
 
 
-@pytest.mark.parametrize("m,n,k", [(200, 5120, 1280), (750, 1280, 5120), (16, 1280, 1280)])
+@pytest.mark.parametrize("m,n,k", [(200, 5120, 1280), (750, 5120, 1280), (16, 1280, 1280)])
 def test_gemm_workspace_on_unsplit_shape(vx, orc, m, n, k):
     # a workspace handed to a call that does not split K must leave y as the result (regression:
     # the single-slice tiled launch once wrote its tile into the workspace)
@@ -84,7 +84,8 @@ def test_gemm_ragged(vx, orc, m, n, k):
     assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm ragged {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(70, 96, 1280), (64, 1280, 5120)])
+@pytest.mark.parametrize("m,n,k", [(70, 96, 1280), (64, 1280, 5120), (300, 200, 1280), (257, 130, 5120),
+                                   (750, 1280, 1280), (256, 3072, 3072), (260, 10300, 1280), (16, 1280, 5120)])
 def test_gemm_exact_dyadic(vx, orc, m, n, k):
     # small-integer activations and power-of-two scales: every product and partial sum is exact,
     # so the matrix-core result must equal the oracle bit for bit (also when K is split)
@@ -95,8 +96,40 @@ def test_gemm_exact_dyadic(vx, orc, m, n, k):
     w = w.reshape(n, -1)
     xi = g.integers(-4, 5, size=(m, k)).astype(np.float32)
     xb = synth.bf16_bits(xi)
-    got = _gemm(vx, w, xb, m, n, k)
-    assert np.array_equal(got.astype(np.float64), orc.q4_gemm(w, xb))
+    ref = orc.q4_gemm(w, xb)
+    say(f"gemm exact dyadic m={m} n={n} k={k}")
+    assert np.array_equal(_gemm(vx, w, xb, m, n, k).astype(np.float64), ref)
+    if vx.q4_gemm_workspace(m, n, k):
+        assert np.array_equal(_gemm(vx, w, xb, m, n, k, split=False).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(750, 5120, 1280), (770, 5120, 3072), (1023, 3850, 5120), (260, 10300, 1280)])
+def test_gemm_split_product_ragged(vx, orc, m, n, k):
+    # long chunks with many 128 x 128 tiles run the split product (hi + lo bf16 parts of every
+    # weight): edges in both dimensions, every K
+    w, xb = synth.gemm_inputs(620 + m, m, n, k)
+    say(f"gemm split product m={m} n={n} k={k}")
+    assert vx.q4_gemm_workspace(m, n, k) == 0
+    assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm split {m}x{n}x{k}")
+
+
+def test_gemm_fused_qkv_equals_separate(vx, orc):
+    # q, k and v as one product over the stacked weights (rows of a Q4_0 matrix are independent):
+    # the same values as three calls, within the bound of the oracle for each
+    for m in (16, 64, 750):
+        ws_ = [synth.gemm_inputs(640 + i, m, 1280, 1280) for i in range(3)]
+        xb = ws_[0][1]
+        wqkv = np.concatenate([w for w, _ in ws_], axis=0)
+        say(f"gemm fused qkv m={m}")
+        got = _gemm(vx, wqkv, xb, m, 3840, 1280)
+        for i, (w, _) in enumerate(ws_):
+            assert_close(got[:, 1280 * i:1280 * (i + 1)], orc.q4_gemm(w, xb), f"fused qkv part {i} m={m}")
+
+
+def test_gemm_split_product_repeatable(vx):
+    m, n, k = 750, 5120, 1280
+    w, xb = synth.gemm_inputs(616, m, n, k)
+    assert np.array_equal(_gemm(vx, w, xb, m, n, k), _gemm(vx, w, xb, m, n, k))
 
 
 def test_gemm_row_matches_gemv(vx):
