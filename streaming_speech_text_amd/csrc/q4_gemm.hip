@@ -550,12 +550,12 @@ __global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__rest
 // handful of vector instructions once per 128 rows of X.  The price is twice the matrix-core
 // work of the product as defined.
 //
-// Workgroup: 4 waves, a 128 x 128 tile of Y.  Wave w owns columns 32w .. 32w+31 for all 128 rows
-// (four 32 x 32 output blocks of v_mfma_f32_32x32x16_bf16), so each weight is unpacked once, in
-// the registers of the wave that uses it.  K runs in stages of 4 Q4_0 blocks (128 inputs): the
-// stage's activations (128 rows x 128 bf16, rows padded by 16 bytes) and raw weight bytes (128
-// columns x 72 bytes) go through LDS, and the next stage's loads are in flight in registers while
-// the current one is computed.  Operand layouts of the 32 x 32 x 16 product: lane L of A holds row
+// Workgroup: 4 waves per K group, a 128 x 128 tile of Y.  Wave w of a group owns columns 32w ..
+// 32w+31 for all 128 rows (four 32 x 32 output blocks of v_mfma_f32_32x32x16_bf16) over the group's
+// blocks of each stage, so each weight is unpacked once, in the registers of the wave that uses it.
+// K runs in stages of 4 Q4_0 blocks (128 inputs): the stage's activations (128 rows x 128 bf16,
+// rows padded by 16 bytes) and raw weight bytes (128 columns x 72 bytes) go through LDS, and the
+// loads of a later stage are in flight in registers while the current one is computed.  Operand layouts of the 32 x 32 x 16 product: lane L of A holds row
 // L % 32, inputs 8(L/32) .. 8(L/32)+7 of a 16-input step; lane L of B holds column L % 32 and the
 // same inputs; result register r of lane L is row 8(r/4) + 4(L/32) + r % 4, column L % 32.  A Q4_0
 // block is two steps, its low nibbles (inputs 0-15) then its high nibbles (16-31); lane group g
@@ -626,23 +626,33 @@ __device__ __forceinline__ void unpack_split(const uint32_t *col, int blk, int g
     blo[1] = __builtin_bit_cast(bf16x8, u32x4v{l[0], l[1], l[2], l[3]});
 }
 
-// WM: waves along M (1: four waves, each 32 columns x 128 rows; 2: eight waves, each 32 columns x
-// 64 rows - twice the waves to hide latency, each weight unpacked by the two waves that use it).
-template <int NS, int WM>
-__global__ __launch_bounds__(GH_THREADS * WM) __attribute__((amdgpu_waves_per_eu(2 * WM))) void q4_gemm_split_kernel(
+// KW: wave groups splitting K inside the workgroup.  Group kg (waves 4 kg .. 4 kg + 3) takes
+// blocks kg * GH_KC / KW .. of every stage, so each weight is still unpacked once, by the one wave
+// that uses it; with KW = 2 every SIMD runs two waves, one's MFMAs covering the other's unpacking
+// and LDS reads.  The groups' partial tiles are added through LDS at the end, group 0's first.
+// LDS holds two stages: the waves store stage s + 1 (loaded from memory during stage s - 1) into
+// the other buffer after their first block of stage s, then issue the loads of stage s + 2, so one
+// barrier per stage suffices.
+template <int NS, int KW>
+__global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_split_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, float *__restrict__ part,
     int m, int n, int k)
 {
-    constexpr int NT = GH_THREADS * WM;
-    constexpr int A_PER = GH_A_PER / WM;                        // 16-byte pieces of A per thread
+    constexpr int NT = GH_THREADS * KW;
+    constexpr int A_PER = GH_A_PER / KW;                        // 16-byte pieces of A per thread
     constexpr int W_PER = (GH_W_PIECES + NT - 1) / NT;          // 8-byte weight pieces per thread
-    constexpr int MI = 4 / WM;                                   // 32-row blocks per wave
-    __shared__ __attribute__((aligned(16))) uint16_t as[GH_BM * GH_AROW];
-    __shared__ __attribute__((aligned(16))) uint32_t wraw[GH_BN * GH_RAW / 4];
+    constexpr int MI = 4;                                        // 32-row blocks per wave
+    constexpr int BPW = GH_KC / KW;                              // blocks per wave and stage
+    constexpr int A_BUF = GH_BM * GH_AROW;                       // bf16 per stage of A
+    constexpr int W_BUF = GH_BN * GH_RAW / 4;                    // dwords per stage of weights
+    static_assert(GH_A_PER % KW == 0 && GH_KC % KW == 0, "the wave groups share the stage evenly");
+    static_assert(KW == 1 || (KW - 1) * 4 * MI * 16 * 64 * 4 <= 2 * A_BUF * 2, "the partial tiles fit in LDS");
+    __shared__ __attribute__((aligned(16))) uint16_t as[2 * A_BUF];
+    __shared__ __attribute__((aligned(16))) uint32_t wraw[2 * W_BUF];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
-    const int wn = wave & 3, wm = wave >> 2;   // column quarter, row part
+    const int wn = wave & 3, kg = wave >> 2;   // column quarter, K group
     const int lane = tid & 63;
     const int l32 = lane & 31, g = lane >> 5;
     const int m0 = blockIdx.y * GH_BM;
@@ -684,28 +694,32 @@ __global__ __launch_bounds__(GH_THREADS * WM) __attribute__((amdgpu_waves_per_eu
         for (int j = 0; j < W_PER; ++j)
             wr[j] = *reinterpret_cast<const u32x2v *>(ws + woff[j]);
     };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < A_PER; ++j)
+            *reinterpret_cast<u32x4v *>(&as[buf * A_BUF + alds[j]]) = ar[j];
+#pragma unroll
+        for (int j = 0; j < W_PER; ++j)
+            *reinterpret_cast<u32x2v *>(&wraw[buf * W_BUF + wlds[j]]) = wr[j];
+    };
 
     f32x16v acc[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
         acc[i] = 0.0f;
 
-    const uint32_t *colw = wraw + (32 * wn + l32) * (GH_RAW / 4);
-    const int arow0 = 32 * MI * wm + l32;
     load_stage(st0);
+    store_stage(0);
+    if (NS > 1)
+        load_stage(st0 + 1);
+    __syncthreads();
     for (int s = 0; s < NS; ++s) {
-        __syncthreads();   // every wave is done with the previous stage's LDS
+        const int cur = s & 1;
+        const uint32_t *colw = wraw + cur * W_BUF + (32 * wn + l32) * (GH_RAW / 4);
+        const uint16_t *arow = as + cur * A_BUF + l32 * GH_AROW + 8 * g;
 #pragma unroll
-        for (int j = 0; j < A_PER; ++j)
-            *reinterpret_cast<u32x4v *>(&as[alds[j]]) = ar[j];
-#pragma unroll
-        for (int j = 0; j < W_PER; ++j)
-            *reinterpret_cast<u32x2v *>(&wraw[wlds[j]]) = wr[j];
-        __syncthreads();
-        if (s + 1 < NS)
-            load_stage(st0 + s + 1);   // in flight during the products
-#pragma unroll
-        for (int b = 0; b < GH_KC; ++b) {
+        for (int bb = 0; bb < BPW; ++bb) {
+            const int b = kg * BPW + bb;
             bf16x8 bhi[2], blo[2];
             unpack_split(colw, b, g, bhi, blo);
 #pragma unroll
@@ -713,7 +727,7 @@ __global__ __launch_bounds__(GH_THREADS * WM) __attribute__((amdgpu_waves_per_eu
                 bf16x8 af[MI];
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
-                    af[i] = *reinterpret_cast<const bf16x8 *>(&as[(arow0 + 32 * i) * GH_AROW + 32 * b + 16 * h + 8 * g]);
+                    af[i] = *reinterpret_cast<const bf16x8 *>(arow + 32 * i * GH_AROW + 32 * b + 16 * h);
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bhi[h], acc[i], 0, 0, 0);
@@ -721,7 +735,36 @@ __global__ __launch_bounds__(GH_THREADS * WM) __attribute__((amdgpu_waves_per_eu
                 for (int i = 0; i < MI; ++i)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], blo[h], acc[i], 0, 0, 0);
             }
+            if (bb == 0 && s + 1 < NS) {
+                store_stage(cur ^ 1);   // the other buffer was last read in stage s - 1
+                if (s + 2 < NS)
+                    load_stage(st0 + s + 2);
+            }
         }
+        __syncthreads();
+    }
+
+    if constexpr (KW > 1) {
+        // groups 1.. leave their partial tiles in LDS (the stage buffers are free after the last
+        // barrier); group 0 adds them in group order
+        float *red = reinterpret_cast<float *>(as);
+        if (kg > 0) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    red[((((kg - 1) * 4 + wn) * MI + i) * 16 + r) * 64 + lane] = acc[i][r];
+        }
+        __syncthreads();
+        if (kg > 0)
+            return;
+#pragma unroll
+        for (int q = 1; q < KW; ++q)
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][r] += red[((((q - 1) * 4 + wn) * MI + i) * 16 + r) * 64 + lane];
     }
 
     float *const dst = part ? part + (size_t)blockIdx.z * m * n : y;
@@ -731,7 +774,7 @@ __global__ __launch_bounds__(GH_THREADS * WM) __attribute__((amdgpu_waves_per_eu
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + 32 * (MI * wm + i) + 8 * (r >> 2) + 4 * g + (r & 3);
+                const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
                 if (row < m)
                     dst[(size_t)row * n + col] = acc[i][r];
             }
@@ -837,12 +880,16 @@ static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_
 // SPLIT_MIN_WGS workgroups and the chunk has at least SPLIT_MIN_M rows (the unpack of a weight is
 // repaid over 128 rows).  Measured on MI355X against the tiled kernel: 750 x 5120 x 1280 28.5
 // against 34.4 us; with K split over the grid to reach the workgroup count (750 x 1280 x 1280, five
-// slices of two stages, and the slice sum) 22 against 12.9 us, so it never splits K.  Four waves
-// (each 32 columns x 128 rows) beat eight (each 32 x 64, every weight unpacked twice): 28.5 against
-// 30.5 us; eight-block stages: no faster.
+// slices of two stages, and the slice sum) 22 against 12.9 us, so it never splits K.  Two wave
+// groups splitting K inside the workgroup (two waves per SIMD) with one barrier per stage: 27.6 to
+// 28.0 us against 29.3 for four waves with two barriers per stage (30.4 with one); eight waves
+// each 32 x 64 (every weight unpacked twice): 30.5 us; eight-block stages: no faster.  Timed over
+// K at 750 x 5120, a stage costs 1.89 us (its 64 matrix-core products per SIMD take about 1.0 us
+// at the 37-40 cycles per v_mfma_f32_32x32x16_bf16 measured in a loop of independent products)
+// and a launch 9 us besides (the 15.4 MB output store alone about 3 us).
 constexpr int64_t SPLIT_MIN_M = 256;
 constexpr int SPLIT_MIN_WGS = 240;
-constexpr int SPLIT_WM = 1;   // waves along M per workgroup
+constexpr int SPLIT_KW = 2;   // wave groups splitting K per workgroup
 
 static bool split_shape(int64_t m, int64_t n, int64_t k)
 {
@@ -856,7 +903,7 @@ template <int NS>
 static void launch_split_ns(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
 {
     const dim3 grid((unsigned)((n + GH_BN - 1) / GH_BN), (unsigned)((m + GH_BM - 1) / GH_BM), 1u);
-    hipLaunchKernelGGL((q4_gemm_split_kernel<NS, SPLIT_WM>), grid, dim3(GH_THREADS * SPLIT_WM), 0, s,
+    hipLaunchKernelGGL((q4_gemm_split_kernel<NS, SPLIT_KW>), grid, dim3(GH_THREADS * SPLIT_KW), 0, s,
                        (const uint8_t *)w, x, y, (float *)nullptr, m, n, k);
 }
 
