@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--trace-json", metavar="OUT", help="with --summarize-trace: also write the statistics with "
                     "the digest of the decoder sources (the decoder_roofline input) to OUT")
     ap.add_argument("--decoder-steps", type=int, default=0, help="with --trace-json: decoder steps in the trace")
+    ap.add_argument("--summarize-counters", metavar="CSV", help="print per-dispatch counter means of a rocprofv3 "
+                    "--pmc counter_collection.csv per kernel and launch shape and exit")
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="HBM bytes per launch of the LM-head-shape GEMV from two rocprofv3 --pmc runs of "
                          "--leg gemv (FETCH_SIZE, then WRITE_SIZE), scaled by what the same counters read for "
@@ -210,6 +212,37 @@ def probe_leg(torch, dev, stream):
         us = timed(torch, stream, launch, nphase, nphase)
         print(json.dumps({"leg": "handoff", "mode": "one launch per phase (graph)", "phase_bytes": phase_bytes,
                           "us_per_phase": round(us, 3), **status()}), flush=True)
+
+    # matrix-core rate: four independent bf16 products per round, alone and with 16/32/64
+    # independent fp32 multiply-adds per round, at one and two waves per SIMD
+    L.vox_probe_mfma_rate_entries.restype = C.c_int
+    L.vox_probe_mfma_rate_entries.argtypes = [C.c_int]
+    L.vox_probe_mfma_rate.restype = C.c_int
+    L.vox_probe_mfma_rate.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    iters = 2048
+    for wps in (1, 2):
+        out = torch.empty(L.vox_probe_mfma_rate_entries(wps), dtype=torch.float32, device=dev)
+        for kind, name, flop in ((0, "v_mfma_f32_32x32x16_bf16", 32768), (1, "v_mfma_f32_16x16x32_bf16", 16384)):
+            for nv in (0, 16, 32, 64):
+                per = []
+                for rep in range(4):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    if L.vox_probe_mfma_rate(kind, nv, wps, iters, out.data_ptr(), cur()):
+                        raise RuntimeError("matrix-core rate probe launch failed")
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if rep:   # the first launch warms up
+                        per.append(e0.elapsed_time(e1) * 1e3)
+                us = float(np.median(per))
+                products = cus * 4 * wps * iters * 4   # waves x rounds x 4
+                print(json.dumps({"leg": "mfma_rate", "product": name, "waves_per_simd": wps, "fma_per_round": nv,
+                                  "us": round(us, 2), "tflops": round(products * flop / us / 1e6, 1),
+                                  "frac_bf16_peak": round(products * flop / us / 1e6 / 2500.0, 4),
+                                  "cycles_per_round_per_wave_at_2.4GHz": round(us * 2400.0 / (iters * wps), 1)}),
+                      flush=True)
+        del out
 
 
 def copy_calibration(torch, dev):
@@ -473,6 +506,36 @@ def summarize_trace(path: str):
                      "p50_us": round(float(np.percentile(a, 50)), 3), "p90_us": round(float(np.percentile(a, 90)), 3),
                      "min_us": round(float(a.min()), 3), "max_us": round(float(a.max()), 3)})
     rows.sort(key=lambda r: -r["total_us"])
+    for r in rows:
+        print(json.dumps(r), flush=True)
+    return rows
+
+
+def summarize_counters(path: str):
+    """Per-dispatch means of every counter in a rocprofv3 --pmc counter_collection.csv, grouped by
+    kernel name and launch shape (grid and workgroup size): one JSON line per group, in order of
+    dispatch count.  Where the counters allow: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x
+    GRBM_GUI_ACTIVE / XCDs) with 1024 SIMDs and 8 XCDs, and vector instructions per matrix-core
+    instruction."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            d = per.setdefault(key, {}).setdefault(r.get("Dispatch_Id") or r["Correlation_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = []
+    for (name, grid, wg), disp in per.items():
+        names = sorted({c for d in disp.values() for c in d})
+        mean = {c: float(np.mean([d[c] for d in disp.values() if c in d])) for c in names}
+        row = {"kernel": name, "grid_threads": grid, "workgroup": wg, "dispatches": len(disp),
+               "mean": {c: round(v, 1) for c, v in mean.items()}}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE"):
+            row["mfma_busy"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * mean["GRBM_GUI_ACTIVE"] / 8), 4)
+        if mean.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in mean:
+            row["valu_per_mfma"] = round(mean["SQ_INSTS_VALU"] / mean["SQ_INSTS_MFMA"], 2)
+        rows.append(row)
+    rows.sort(key=lambda r: -r["dispatches"])
     for r in rows:
         print(json.dumps(r), flush=True)
     return rows
@@ -774,6 +837,9 @@ def main():
     args = parse()
     if args.counter_summary:
         print(json.dumps(counter_summary(*args.counter_summary), indent=1), flush=True)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.summarize_trace:
         rows = summarize_trace(args.summarize_trace)

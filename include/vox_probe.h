@@ -1,9 +1,10 @@
-/* vox_probe.h - measurement aid beside libvox (built as libvox_probe.so).
+/* vox_probe.h - measurement aids beside libvox (built as libvox_probe.so).
  *
- * Not an operation of the decoder step: the streaming-read probe gives the HBM read rate a
- * plain kernel reaches on this GPU for a given number of bytes, the practical ceiling next to
- * the 8 TB/s nominal peak for kernels that stream their data once (the Q4_0 GEMVs of vox.h,
- * whose fused dequantisation follows the Rust port page, GeekNews 26595, section 아키텍처).
+ * Not operations of the decoder step: the streaming-read probe gives the HBM read rate a plain
+ * kernel reaches on this GPU for a given number of bytes, the practical ceiling next to the
+ * 8 TB/s nominal peak for kernels that stream their data once (the Q4_0 GEMVs of vox.h, whose
+ * fused dequantisation follows the Rust port page, GeekNews 26595, section 아키텍처); the
+ * matrix-core rate probe gives the same for the bf16 products of the Q4_0 GEMMs.
  */
 #ifndef VOX_PROBE_H
 #define VOX_PROBE_H
@@ -43,6 +44,17 @@ int vox_probe_handoff_persistent(int mode, int nch, int nphase, const void *weig
                                  void *stream);
 /* Phase `phase` (1..100000) of the same work as its own launch, no prefetch, no barrier. */
 int vox_probe_handoff_phase(int nch, int phase, const void *weights, size_t weight_bytes, void *work, void *stream);
+
+/* Matrix-core rate probe.  Output entries (floats) of a launch with waves_per_simd (1..4) waves
+ * per SIMD on the current device (workgroups of four waves, one per compute unit and wave per
+ * SIMD); -1 on a bad argument or a HIP failure. */
+int vox_probe_mfma_rate_entries(int waves_per_simd);
+/* Every wave runs `iters` (1..2^24) rounds of four independent bf16 matrix-core products (kind 0:
+ * v_mfma_f32_32x32x16_bf16, 32768 flop each; kind 1: v_mfma_f32_16x16x32_bf16, 16384 flop each)
+ * plus nv (0, 16, 32 or 64) independent fp32 multiply-adds, then writes one value per lane to the
+ * device array out (vox_probe_mfma_rate_entries(waves_per_simd) floats).  Enqueued on `stream`.
+ * Returns 0, -1 on a bad argument, -4 if the launch failed. */
+int vox_probe_mfma_rate(int kind, int nv, int waves_per_simd, int iters, float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -47,13 +47,21 @@ def test_probe_library_exports_its_header():
     plib = C.CDLL(path)
     fns = header_functions(PROBE_HEADER)
     assert fns == ["vox_probe_handoff_persistent", "vox_probe_handoff_phase", "vox_probe_handoff_reset",
-                   "vox_probe_handoff_work_bytes", "vox_probe_sink_entries", "vox_probe_stream_read"]
+                   "vox_probe_handoff_work_bytes", "vox_probe_mfma_rate", "vox_probe_mfma_rate_entries",
+                   "vox_probe_sink_entries", "vox_probe_stream_read"]
     assert all(hasattr(plib, f) for f in fns)
     plib.vox_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
     # bad arguments are refused before any HIP call
     assert plib.vox_probe_stream_read(None, 16, C.c_void_p(0x1000), 1, None) == -1
     assert plib.vox_probe_stream_read(C.c_void_p(0x1000), 24, C.c_void_p(0x1000), 1, None) == -1
     assert plib.vox_probe_stream_read(C.c_void_p(0x1008), 32, C.c_void_p(0x1000), 1, None) == -1
+    plib.vox_probe_mfma_rate.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    out = C.c_void_p(0x1000)
+    assert plib.vox_probe_mfma_rate(2, 0, 1, 16, out, None) == -1     # no such product
+    assert plib.vox_probe_mfma_rate(0, 8, 1, 16, out, None) == -1     # fp32 work not in 0/16/32/64
+    assert plib.vox_probe_mfma_rate(0, 0, 5, 16, out, None) == -1     # waves per SIMD past 4
+    assert plib.vox_probe_mfma_rate(0, 0, 1, 0, out, None) == -1      # no rounds
+    assert plib.vox_probe_mfma_rate(1, 0, 1, 16, None, None) == -1    # no output
 
 
 def test_header_compiles_as_c(tmp_path):
