@@ -374,6 +374,32 @@ def kernels_leg(torch, synth, vox, dev, stream):
         del wdev
         torch.cuda.empty_cache()
 
+    # one product per launch at 750 frames (each linear of the set, q/k/v stacked), then the split
+    # product over K at 750 x 5120 (the cost of a stage and of a launch)
+    def gemm_case(case, m, n, k):
+        w, xb = synth.gemm_inputs(synth.SEED_GEMM, m, n, k)
+        copies = max(2, int(np.ceil(1.1 * GiB / w.nbytes)))
+        ws_ = [torch.from_numpy(w).to(dev) for _ in range(copies)]
+        xd = torch.from_numpy(xb.view(np.int16)).to(dev)
+        y = torch.empty(m, n, dtype=torch.float32, device=dev)
+        wsb_ = vox.q4_gemm_workspace(m, n, k)
+        gws_ = torch.empty(max(wsb_, 1), dtype=torch.uint8, device=dev)
+
+        def launch(i):
+            vox._check(vox.lib().vox_q4_gemm(vox._ptr(ws_[i]), vox._ptr(xd), vox._ptr(y), m, n, k,
+                                             vox._ptr(gws_) if wsb_ else None, wsb_, vox._stream(None)))
+        us = timed(torch, stream, launch, copies, 50)
+        fl = 2 * m * n * k
+        emit({"kernel": "q4_gemm", "case": case, "m": m, "n": n, "k": k, "us": round(us, 3),
+              "tflops": round(fl / us / 1e6, 2), "frac_mfma_bf16": round(fl / us / 1e6 / 2500.0, 4)})
+        del ws_
+        torch.cuda.empty_cache()
+
+    for name, n, k in synth.ENCODER_LINEARS[3:] + [("q/k/v stacked", 3840, 1280)]:
+        gemm_case(f"encoder {name}, M=750", 750, n, k)
+    for k in (1280, 3072, 5120):
+        gemm_case("split product over K at 750 x 5120", 750, 5120, k)
+
     # encoder self-attention over a chunk (32 heads x 40, window 750, a full window of earlier rows)
     H, W = synth.ENC_HEADS, synth.ENC_WINDOW
     hd, n_ctx = synth.ENC_HEAD_DIM, synth.ENC_WINDOW - 1
