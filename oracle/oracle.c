@@ -433,6 +433,7 @@ int64_t orc_alt_tokens(const float *logits, int64_t vocab, double cutoff, int64_
 
 struct orc_decoder {
     orc_decoder_config c;
+    int64_t wfmt;      /* -1: Q4_0 weights; 0: bf16; 1: IEEE binary16 */
     const uint8_t *tok_embd;
     const float *out_norm;
     orc_layer_weights *layers;
@@ -449,6 +450,7 @@ orc_decoder *orc_decoder_create(const orc_decoder_config *c, const uint8_t *tok_
 {
     orc_decoder *d = (orc_decoder *)calloc(1, sizeof *d);
     d->c = *c;
+    d->wfmt = -1;
     d->tok_embd = tok_embd;
     d->out_norm = out_norm;
     d->layers = (orc_layer_weights *)malloc(sizeof(orc_layer_weights) * (size_t)c->n_layers);
@@ -456,6 +458,18 @@ orc_decoder *orc_decoder_create(const orc_decoder_config *c, const uint8_t *tok_
     d->kcache = (double **)calloc((size_t)c->n_layers, sizeof(double *));
     d->vcache = (double **)calloc((size_t)c->n_layers, sizeof(double *));
     d->h = (double *)calloc((size_t)c->dim, sizeof(double));
+    return d;
+}
+
+/* The same decoder over 16-bit weights (voxtral.c page, section 모델 다운로드 및 구성: BF16
+ * weights; section 메모리 요구사항: converted to F16 for the GPU).  Every matrix (the layers'
+ * linears and the tied embedding / LM head) holds n x k 16-bit patterns, row-major: fmt 0 bf16,
+ * fmt 1 IEEE binary16; the layer pointers of orc_layer_weights point at those uint16 arrays. */
+orc_decoder *orc_decoder_create_w16(const orc_decoder_config *c, int64_t fmt, const uint16_t *tok_embd,
+                                    const float *out_norm, const orc_layer_weights *layers)
+{
+    orc_decoder *d = orc_decoder_create(c, (const uint8_t *)tok_embd, out_norm, layers);
+    d->wfmt = fmt ? 1 : 0;
     return d;
 }
 
@@ -540,6 +554,25 @@ static void ensure_capacity(orc_decoder *d, int64_t need)
     d->cap = cap;
 }
 
+/* y = W x in double for the decoder's weight format: Q4_0 rows, or 16-bit rows widened exactly. */
+static void dec_linear(const orc_decoder *d, const uint8_t *w, const double *x, double *y, int64_t n, int64_t k)
+{
+    if (d->wfmt < 0) {
+        orc_q4_gemv_f64(w, x, y, n, k);
+        return;
+    }
+    const uint16_t *w16 = (const uint16_t *)w;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < k; i++) {
+            const uint16_t b = w16[r * k + i];
+            acc += (d->wfmt ? orc_fp16_to_double(b) : orc_bf16_to_double(b)) * x[i];
+        }
+        y[r] = acc;
+    }
+}
+
 int64_t orc_decoder_step(orc_decoder *d, int64_t token, double *logits)
 {
     const orc_decoder_config *c = &d->c;
@@ -560,43 +593,49 @@ int64_t orc_decoder_step(orc_decoder *d, int64_t token, double *logits)
     double *a = (double *)malloc(sizeof(double) * (size_t)c->hidden);
     double *lg = logits ? logits : (double *)malloc(sizeof(double) * (size_t)c->vocab);
 
-    /* Input: the token's row of the tied Q4_0 embedding table ([RS] section 브라우저 실행을
-     * 위한 기술적 해결: the embedding stays on the GPU as Q4 and a row is looked up per token). */
-    for (int64_t b = 0; b < dim / 32; b++)
-        q4_block_values(d->tok_embd + token * row_bytes + b * 18, d->h + b * 32);
+    /* Input: the token's row of the tied embedding table ([RS] section 브라우저 실행을 위한 기술적
+     * 해결: the embedding stays on the GPU as Q4 and a row is looked up per token), Q4_0 or 16-bit. */
+    if (d->wfmt < 0) {
+        for (int64_t b = 0; b < dim / 32; b++)
+            q4_block_values(d->tok_embd + token * row_bytes + b * 18, d->h + b * 32);
+    } else {
+        const uint16_t *row = (const uint16_t *)d->tok_embd + token * dim;
+        for (int64_t i = 0; i < dim; i++)
+            d->h[i] = d->wfmt ? orc_fp16_to_double(row[i]) : orc_bf16_to_double(row[i]);
+    }
 
     const double scale = 1.0 / sqrt((double)hd);
     for (int64_t l = 0; l < c->n_layers; l++) {
         const orc_layer_weights *L = &d->layers[l];
         /* attention block */
         orc_rmsnorm(d->h, L->attn_norm, dim, c->norm_eps, xn);
-        orc_q4_gemv_f64(L->wq, xn, q, qd, dim);
-        orc_q4_gemv_f64(L->wk, xn, k, kvd, dim);
-        orc_q4_gemv_f64(L->wv, xn, v, kvd, dim);
+        dec_linear(d, L->wq, xn, q, qd, dim);
+        dec_linear(d, L->wk, xn, k, kvd, dim);
+        dec_linear(d, L->wv, xn, v, kvd, dim);
         orc_rope(q, c->n_heads, hd, d->pos, c->rope_theta);
         orc_rope(k, c->n_kv_heads, hd, d->pos, c->rope_theta);
         kv_append(d, l, k, v);
         /* cached rows are [t][n_kv][hd]: head stride hd, time stride n_kv*hd */
         gqa_attn_strided(q, d->kcache[l], d->vcache[l], c->n_heads, c->n_kv_heads, hd, new_len,
                          hd, kvd, scale, o);
-        orc_q4_gemv_f64(L->wo, o, y, dim, qd);
+        dec_linear(d, L->wo, o, y, dim, qd);
         for (int64_t i = 0; i < dim; i++)
             d->h[i] += y[i];
         /* feed-forward block */
         orc_rmsnorm(d->h, L->ffn_norm, dim, c->norm_eps, xn);
-        orc_q4_gemv_f64(L->w_gate, xn, gt, c->hidden, dim);
-        orc_q4_gemv_f64(L->w_up, xn, up, c->hidden, dim);
+        dec_linear(d, L->w_gate, xn, gt, c->hidden, dim);
+        dec_linear(d, L->w_up, xn, up, c->hidden, dim);
         orc_swiglu(gt, up, c->hidden, a);
-        orc_q4_gemv_f64(L->w_down, a, y, dim, c->hidden);
+        dec_linear(d, L->w_down, a, y, dim, c->hidden);
         for (int64_t i = 0; i < dim; i++)
             d->h[i] += y[i];
     }
     d->len = new_len;
 
-    /* Output: final RMSNorm, then the tied Q4_0 table as LM head, then the greedy choice
-     * taken over fp32 logits (the precision the GPU path decides in). */
+    /* Output: final RMSNorm, then the tied table as LM head, then the greedy choice taken over
+     * fp32 logits (the precision the GPU path decides in). */
     orc_rmsnorm(d->h, d->out_norm, dim, c->norm_eps, xn);
-    orc_q4_gemv_f64(d->tok_embd, xn, lg, c->vocab, dim);
+    dec_linear(d, d->tok_embd, xn, lg, c->vocab, dim);
     float *lf = (float *)malloc(sizeof(float) * (size_t)c->vocab);
     for (int64_t i = 0; i < c->vocab; i++)
         lf[i] = (float)lg[i];

@@ -77,6 +77,10 @@ typedef struct orc_decoder orc_decoder;
 
 orc_decoder *orc_decoder_create(const orc_decoder_config *c, const uint8_t *tok_embd,
                                 const float *out_norm, const orc_layer_weights *layers);
+/* The same step over 16-bit weights: every matrix n x k uint16, row-major, fmt 0 bf16, fmt 1
+ * IEEE binary16 (the orc_layer_weights pointers then point at uint16 arrays). */
+orc_decoder *orc_decoder_create_w16(const orc_decoder_config *c, int64_t fmt, const uint16_t *tok_embd,
+                                    const float *out_norm, const orc_layer_weights *layers);
 void orc_decoder_destroy(orc_decoder *d);
 void orc_decoder_reset(orc_decoder *d);
 int64_t orc_decoder_position(const orc_decoder *d);

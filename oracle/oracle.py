@@ -78,6 +78,8 @@ def lib():
         L.orc_max_threads.argtypes = []
         L.orc_decoder_create.restype = _vp
         L.orc_decoder_create.argtypes = [C.POINTER(DecoderConfig), _vp, _vp, C.POINTER(LayerWeights)]
+        L.orc_decoder_create_w16.restype = _vp
+        L.orc_decoder_create_w16.argtypes = [C.POINTER(DecoderConfig), _i64, _vp, _vp, C.POINTER(LayerWeights)]
         L.orc_decoder_position.restype = _i64
         L.orc_decoder_position.argtypes = [_vp]
         L.orc_decoder_step.restype = _i64
@@ -280,9 +282,10 @@ def max_threads() -> int:
 
 
 class Decoder:
-    """Oracle decoder over host weights (as produced by the synthetic generator)."""
+    """Oracle decoder over host weights (as produced by the synthetic generator): Q4_0 matrices,
+    or with fmt "bf16" / "f16" 16-bit matrices (uint16 [n, k]) for every linear and the table."""
 
-    def __init__(self, shape, weights):
+    def __init__(self, shape, weights, fmt=None):
         s = shape
         self.shape = s
         self._keep = []
@@ -296,13 +299,19 @@ class Decoder:
                                  s.vocab, s.n_slots, s.norm_eps, s.rope_theta)
         arr = (LayerWeights * s.n_layers)()
         for i, L in enumerate(weights["layers"]):
+            wt = np.uint8 if fmt is None else np.uint16
             arr[i] = LayerWeights(keep(L["attn_norm"], np.float32), keep(L["ffn_norm"], np.float32),
-                                  keep(L["wq"], np.uint8), keep(L["wk"], np.uint8), keep(L["wv"], np.uint8),
-                                  keep(L["wo"], np.uint8), keep(L["w_gate"], np.uint8),
-                                  keep(L["w_up"], np.uint8), keep(L["w_down"], np.uint8))
+                                  keep(L["wq"], wt), keep(L["wk"], wt), keep(L["wv"], wt),
+                                  keep(L["wo"], wt), keep(L["w_gate"], wt),
+                                  keep(L["w_up"], wt), keep(L["w_down"], wt))
         self._layers = arr
-        self._h = lib().orc_decoder_create(C.byref(self.cfg), keep(weights["tok_embd"], np.uint8),
-                                           keep(weights["out_norm"], np.float32), arr)
+        if fmt is None:
+            self._h = lib().orc_decoder_create(C.byref(self.cfg), keep(weights["tok_embd"], np.uint8),
+                                               keep(weights["out_norm"], np.float32), arr)
+        else:
+            code = {"bf16": 0, "f16": 1}[fmt]
+            self._h = lib().orc_decoder_create_w16(C.byref(self.cfg), code, keep(weights["tok_embd"], np.uint16),
+                                                   keep(weights["out_norm"], np.float32), arr)
 
     def step(self, token: int, want_logits: bool = True):
         logits = np.empty(self.shape.vocab, np.float64) if want_logits else None

@@ -199,6 +199,33 @@ def decoder_weights(seed: int, s: DecoderShape):
     }
 
 
+def decoder_weights_w16(seed: int, s: DecoderShape, fmt: str):
+    """The same structure over 16-bit weights ("bf16" or "f16"): every linear and the tied table
+    uint16 [n, k] (w16_matrix: N(0, 0.02^2) rounded to the format); norms as decoder_weights."""
+    qd = s.n_heads * s.head_dim
+    kvd = s.n_kv_heads * s.head_dim
+    layers = []
+    for li in range(s.n_layers):
+        def g(t):
+            return generator(seed, 3, li, t)
+        layers.append({
+            "attn_norm": uniform_f32(g(0), (s.dim,), 0.5, 1.5),
+            "ffn_norm": uniform_f32(g(1), (s.dim,), 0.5, 1.5),
+            "wq": w16_matrix(g(2), qd, s.dim, fmt),
+            "wk": w16_matrix(g(3), kvd, s.dim, fmt),
+            "wv": w16_matrix(g(4), kvd, s.dim, fmt),
+            "wo": w16_matrix(g(5), s.dim, qd, fmt),
+            "w_gate": w16_matrix(g(6), s.hidden, s.dim, fmt),
+            "w_up": w16_matrix(g(7), s.hidden, s.dim, fmt),
+            "w_down": w16_matrix(g(8), s.dim, s.hidden, fmt),
+        })
+    return {
+        "tok_embd": w16_matrix(generator(seed, 3, 0), s.vocab, s.dim, fmt),
+        "out_norm": uniform_f32(generator(seed, 3, 1), (s.dim,), 0.5, 1.5),
+        "layers": layers,
+    }
+
+
 def decoder_tokens(seed: int, vocab: int, prefix: int = DECODER_PREFIX):
     """(prefix token ids [prefix] int32, start id int) for a decoder run."""
     g = generator(seed, 2)

@@ -376,14 +376,24 @@ TINY = synth.DecoderShape(n_layers=2, dim=64, n_heads=4, n_kv_heads=2, head_dim=
                           vocab=512, n_slots=16, norm_eps=1e-5, rope_theta=1e6)
 
 
-def _torch_decoder_reference(shape, weights, tokens, start_pos=0, window=None):
+def _np_w16(w, n, k, fmt):
+    """Independent numpy decode of 16-bit weight patterns (bf16: the upper half of an fp32;
+    f16: numpy's IEEE half), used only as a cross-check."""
+    b = np.ascontiguousarray(w, dtype=np.uint16).reshape(n, k)
+    if fmt == "bf16":
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return b.view(np.float16).astype(np.float64)
+
+
+def _torch_decoder_reference(shape, weights, tokens, start_pos=0, window=None, fmt=None):
     """Second, independent composition from library routines (torch float64).  window: None, or
-    (k, v) fp32 [n_layers, len, n_kv*head_dim] holding positions start_pos - len .. start_pos - 1."""
+    (k, v) fp32 [n_layers, len, n_kv*head_dim] holding positions start_pos - len .. start_pos - 1.
+    fmt: None for Q4_0 weights, "bf16" / "f16" for 16-bit ones."""
     s = shape
     t = torch.float64
 
     def deq(w, n, k):
-        return torch.from_numpy(_np_dequant(w, n, k))
+        return torch.from_numpy(_np_dequant(w, n, k) if fmt is None else _np_w16(w, n, k, fmt))
 
     E = deq(weights["tok_embd"], s.vocab, s.dim)
     layers = []
@@ -454,6 +464,45 @@ def test_decoder_tiny_vs_torch_composition(orc):
     dec.reset()
     nxt, lg = dec.step(tokens[0])
     assert dec.position == 1 and np.allclose(lg, ref[0], rtol=1e-10, atol=1e-10)
+    dec.close()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_decoder_w16_tiny_vs_torch_composition(orc, fmt):
+    # the step over 16-bit weights (voxtral.c page, sections 모델 다운로드 및 구성 / 메모리 요구사항:
+    # BF16 weights, F16 on the GPU) against the torch composition on its own decode of the bits
+    w = synth.decoder_weights_w16(41, TINY, fmt)
+    n_steps = 40  # window of 16 wraps twice
+    tokens = synth.generator(41, 9).integers(0, TINY.vocab, size=n_steps).tolist()
+    dec = orc.Decoder(TINY, w, fmt=fmt)
+    got = []
+    for tok in tokens:
+        nxt, lg = dec.step(tok)
+        got.append(lg)
+        assert nxt == int(np.argmax(lg.astype(np.float32)))
+    ref = _torch_decoder_reference(TINY, w, tokens, fmt=fmt)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, rtol=1e-10, atol=1e-10)
+    dec.close()
+    # the format flag is read: the same bits taken as the other format give other logits
+    other = "f16" if fmt == "bf16" else "bf16"
+    dec = orc.Decoder(TINY, w, fmt=other)
+    assert not np.allclose(dec.step(tokens[0])[1], ref[0])
+    dec.close()
+
+
+def test_decoder_w16_resume_from_window(orc):
+    w = synth.decoder_weights_w16(44, TINY, "f16")
+    pos = 1_000_003
+    kw = synth.normal_f32(synth.generator(44, 10), (TINY.n_layers, TINY.n_slots, TINY.n_kv_heads * TINY.head_dim))
+    vw = synth.normal_f32(synth.generator(44, 11), (TINY.n_layers, TINY.n_slots, TINY.n_kv_heads * TINY.head_dim))
+    tokens = synth.generator(44, 9).integers(0, TINY.vocab, size=12).tolist()
+    dec = orc.Decoder(TINY, w, fmt="f16")
+    dec.load_window(pos, kw, vw)
+    got = [dec.step(t)[1] for t in tokens]
+    ref = _torch_decoder_reference(TINY, w, tokens, start_pos=pos, window=(kw, vw), fmt="f16")
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, rtol=1e-9, atol=1e-9)
     dec.close()
 
 
