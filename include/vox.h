@@ -207,6 +207,13 @@ int vox_decoder_workspace(const vox_decoder_config *c, size_t *kv_bytes, size_t 
 int vox_decoder_create(const vox_decoder_config *c, const vox_decoder_weights *w, void *kv,
                        size_t kv_bytes, void *scratch, size_t scratch_bytes, void *stream,
                        vox_decoder_t **out);
+/* The same decoder over 16-bit weights (voxtral.c page, GeekNews 26608, section 모델 다운로드 및
+ * 구성: BF16 weights; section 메모리 요구사항: converted to F16 for the GPU): every layer matrix and
+ * the tied table tok_embd are n x k row-major 16-bit values, fmt VOX_W16_BF16 or VOX_W16_F16 (the
+ * vox_layer_weights pointers then point at them; 16-byte aligned).  Everything else as
+ * vox_decoder_create; another fmt -> VOX_E_INVAL. */
+int vox_decoder_create_w16(const vox_decoder_config *c, const vox_decoder_weights *w, int fmt, void *kv,
+                           size_t kv_bytes, void *scratch, size_t scratch_bytes, void *stream, vox_decoder_t **out);
 /* Position back to 0 (the KV window is logically emptied); enqueued on `stream`. */
 int vox_decoder_reset(vox_decoder_t *d, void *stream);
 /* Resumes a stream at absolute position pos (0 <= pos <= VOX_DECODER_MAX_POS, else VOX_E_INVAL),

@@ -75,15 +75,16 @@ struct QkvArgs {
     int n_slots;
 };
 
-// xs = RMSNorm(row) * gain for the token's row of the Q4_0 embedding table; the workgroup that
-// passes h_out also stores the raw row there (it is the first residual stream).
-template <int NT, int K>
+// xs = RMSNorm(row) * gain for the token's row of the embedding table (Q4_0 or 16-bit); the
+// workgroup that passes h_out also stores the raw row there (it is the first residual stream).
+template <int NT, int K, int FMT = FMT_Q4>
 struct EmbedRmsNormX {
     static constexpr int PAIRS = K / 64;
     static constexpr int PER = (PAIRS + NT - 1) / NT;
     static constexpr int GPER = (K / 4) / NT;
+    static constexpr int WORDS = FMT == FMT_Q4 ? 9 : 32;   // dwords of 64 values
     static_assert((K / 4) % NT == 0, "the workgroup must cover the vector evenly");
-    uint32_t raw[PER][9];
+    uint32_t raw[PER][WORDS];
     f32x4 gv[GPER];
 
     __device__ __forceinline__ void issue(const uint8_t *__restrict__ row, const float *__restrict__ gain)
@@ -91,9 +92,9 @@ struct EmbedRmsNormX {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int c = min((int)threadIdx.x + j * NT, PAIRS - 1);   // unconditional load
-            const uint32_t *p = reinterpret_cast<const uint32_t *>(row + 36 * c);
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(row + 4 * WORDS * c);
 #pragma unroll
-            for (int i = 0; i < 9; ++i)
+            for (int i = 0; i < WORDS; ++i)
                 raw[j][i] = p[i];
         }
         const f32x4 *g4 = reinterpret_cast<const f32x4 *>(gain);
@@ -109,7 +110,21 @@ struct EmbedRmsNormX {
             const int c = threadIdx.x + j * NT;
             if (c < PAIRS) {
                 float v[64];
-                dequant_pair_words(raw[j], v);
+                if constexpr (FMT == FMT_Q4) {
+                    dequant_pair_words(raw[j], v);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) {
+                        const uint32_t u = raw[j][i];
+                        if constexpr (FMT == FMT_BF16) {
+                            v[2 * i] = __builtin_bit_cast(float, u << 16);
+                            v[2 * i + 1] = __builtin_bit_cast(float, u & 0xFFFF0000u);
+                        } else {
+                            v[2 * i] = half_bits_to_float(u & 0xFFFFu);
+                            v[2 * i + 1] = half_bits_to_float(u >> 16);
+                        }
+                    }
+                }
                 float4 *d4 = reinterpret_cast<float4 *>(xs + XS_ROW * c);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -143,7 +158,7 @@ struct QkvPolicy {
 
     __host__ __device__ static int tiles(const QkvArgs &a) { return (a.qrows + 2 * a.kvrows) / Gm::R; }
 
-    typedef std::conditional_t<EMBED, EmbedRmsNormX<Gm::NT, Gm::K>, RmsNormX<Gm::NT, Gm::K>> XRegs;
+    typedef std::conditional_t<EMBED, EmbedRmsNormX<Gm::NT, Gm::K, Gm::FMT>, RmsNormX<Gm::NT, Gm::K>> XRegs;
     __device__ void x_issue(XRegs &x)
     {
         if constexpr (EMBED) {
@@ -417,8 +432,8 @@ constexpr int nt_for()
     return K == 1024 ? 128 : K == 2048 ? 128 : K == 3072 ? 192 : K == 4096 ? 256 : 576;
 }
 
-template <int K, int R, int NPART = 1>
-using DGeom = GemvGeom<K, nt_for<K>(), R, NPART>;
+template <int K, int R, int NPART = 1, int FMT = FMT_Q4>
+using DGeom = GemvGeom<K, nt_for<K>(), R, NPART, FMT>;
 
 template <class Gm, class Policy, class Args>
 static int launch_gemv(const Args &args, hipStream_t s, const char *what, int *grid_out = nullptr)
@@ -444,42 +459,66 @@ constexpr int min_rows()
     return nt_for<K>() / (K / 64);
 }
 
-template <int K, bool EMBED>
+// 16-bit rows take the shortest tile the row groups allow (4 rows, 8 at width 1024): a row is
+// 3.6 times the bytes of a Q4_0 row, so these tiles carry about as many bytes as the Q4_0 ones.
+template <int K, int FMT>
+constexpr int w16_rows()
+{
+    return min_rows<K>() > 4 ? min_rows<K>() : 4;
+}
+
+template <int K, bool EMBED, int FMT>
 static int run_qkv(const QkvArgs &a, int, hipStream_t s)
 {
-    return launch_gemv<DGeom<K, 8>, QkvPolicy<DGeom<K, 8>, EMBED>>(a, s, "decoder qkv");
+    constexpr int R = FMT == FMT_Q4 ? 8 : w16_rows<K, FMT>();
+    return launch_gemv<DGeom<K, R, 1, FMT>, QkvPolicy<DGeom<K, R, 1, FMT>, EMBED>>(a, s, "decoder qkv");
 }
 
-template <int K>
+template <int K, int FMT>
 static int run_residual(const ResidualArgs &a, int R, hipStream_t s)
 {
-    if (R == 16)
-        return launch_gemv<DGeom<K, 16>, ResidualPolicy<DGeom<K, 16>>>(a, s, "decoder residual gemv");
-    if constexpr (12 % min_rows<K>() == 0) {
-        if (R == 12)
-            return launch_gemv<DGeom<K, 12>, ResidualPolicy<DGeom<K, 12>>>(a, s, "decoder residual gemv");
+    if constexpr (FMT != FMT_Q4) {
+        constexpr int RW = w16_rows<K, FMT>();
+        return launch_gemv<DGeom<K, RW, 1, FMT>, ResidualPolicy<DGeom<K, RW, 1, FMT>>>(a, s, "decoder residual gemv");
+    } else {
+        if (R == 16)
+            return launch_gemv<DGeom<K, 16>, ResidualPolicy<DGeom<K, 16>>>(a, s, "decoder residual gemv");
+        if constexpr (12 % min_rows<K>() == 0) {
+            if (R == 12)
+                return launch_gemv<DGeom<K, 12>, ResidualPolicy<DGeom<K, 12>>>(a, s, "decoder residual gemv");
+        }
+        if (R == 8 || min_rows<K>() > 4)
+            return launch_gemv<DGeom<K, 8>, ResidualPolicy<DGeom<K, 8>>>(a, s, "decoder residual gemv");
+        if constexpr (min_rows<K>() <= 4)
+            return launch_gemv<DGeom<K, 4>, ResidualPolicy<DGeom<K, 4>>>(a, s, "decoder residual gemv");
+        return VOX_E_UNSUPPORTED;
     }
-    if (R == 8 || min_rows<K>() > 4)
-        return launch_gemv<DGeom<K, 8>, ResidualPolicy<DGeom<K, 8>>>(a, s, "decoder residual gemv");
-    if constexpr (min_rows<K>() <= 4)
-        return launch_gemv<DGeom<K, 4>, ResidualPolicy<DGeom<K, 4>>>(a, s, "decoder residual gemv");
-    return VOX_E_UNSUPPORTED;
 }
 
-template <int K>
+template <int K, int FMT>
 static int run_gateup(const GateUpArgs &a, int R, hipStream_t s)
 {
-    if (R == 16)
-        return launch_gemv<DGeom<K, 16, 2>, GateUpPolicy<DGeom<K, 16, 2>>>(a, s, "decoder gate/up");
-    return launch_gemv<DGeom<K, 8, 2>, GateUpPolicy<DGeom<K, 8, 2>>>(a, s, "decoder gate/up");
+    if constexpr (FMT != FMT_Q4) {
+        constexpr int RW = w16_rows<K, FMT>();
+        return launch_gemv<DGeom<K, RW, 2, FMT>, GateUpPolicy<DGeom<K, RW, 2, FMT>>>(a, s, "decoder gate/up");
+    } else {
+        if (R == 16)
+            return launch_gemv<DGeom<K, 16, 2>, GateUpPolicy<DGeom<K, 16, 2>>>(a, s, "decoder gate/up");
+        return launch_gemv<DGeom<K, 8, 2>, GateUpPolicy<DGeom<K, 8, 2>>>(a, s, "decoder gate/up");
+    }
 }
 
-template <int K>
+template <int K, int FMT>
 static int run_lmhead(const LmHeadArgs &a, int R, hipStream_t s, int *grid)
 {
-    if (R == 16)
-        return launch_gemv<DGeom<K, 16>, LmHeadPolicy<DGeom<K, 16>>>(a, s, "decoder lm head", grid);
-    return launch_gemv<DGeom<K, 8>, LmHeadPolicy<DGeom<K, 8>>>(a, s, "decoder lm head", grid);
+    if constexpr (FMT != FMT_Q4) {
+        constexpr int RW = w16_rows<K, FMT>();
+        return launch_gemv<DGeom<K, RW, 1, FMT>, LmHeadPolicy<DGeom<K, RW, 1, FMT>>>(a, s, "decoder lm head", grid);
+    } else {
+        if (R == 16)
+            return launch_gemv<DGeom<K, 16>, LmHeadPolicy<DGeom<K, 16>>>(a, s, "decoder lm head", grid);
+        return launch_gemv<DGeom<K, 8>, LmHeadPolicy<DGeom<K, 8>>>(a, s, "decoder lm head", grid);
+    }
 }
 
 static bool model_width(int k) { return k == 1024 || k == 3072; }
@@ -570,6 +609,7 @@ struct vox_decoder {
     unsigned long long *keys;
     double *rope;
     float *h, *q, *o, *act, *part;
+    int fmt;   // FMT_Q4, FMT_BF16 or FMT_F16: the format of every matrix
     int group, s_cap;
     int r_qkv, r_o, r_ffn, r_down, r_head;
     int64_t host_pos;
@@ -622,8 +662,9 @@ static int launch_attn(const AttnArgs &a, int width, int n_kv, hipStream_t s)
     return check_launch("decoder attention merge");
 }
 
-static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out, float *logits, int bucket,
-                        hipStream_t s)
+template <int FMT>
+static int enqueue_step_fmt(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out, float *logits, int bucket,
+                            hipStream_t s)
 {
     const vox_decoder_config &c = d->c;
     const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
@@ -656,9 +697,9 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
         qa.ctl = d->ctl;
         qa.n_slots = c.n_slots;
         if (c.dim == 3072)
-            st = l == 0 ? run_qkv<3072, true>(qa, d->r_qkv, s) : run_qkv<3072, false>(qa, d->r_qkv, s);
+            st = l == 0 ? run_qkv<3072, true, FMT>(qa, d->r_qkv, s) : run_qkv<3072, false, FMT>(qa, d->r_qkv, s);
         else
-            st = l == 0 ? run_qkv<1024, true>(qa, d->r_qkv, s) : run_qkv<1024, false>(qa, d->r_qkv, s);
+            st = l == 0 ? run_qkv<1024, true, FMT>(qa, d->r_qkv, s) : run_qkv<1024, false, FMT>(qa, d->r_qkv, s);
         if (st)
             break;
 
@@ -683,29 +724,39 @@ static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out,
             break;
 
         ResidualArgs oa{(const uint8_t *)L.wo, d->o, d->h, c.dim};
-        st = qd == 4096 ? run_residual<4096>(oa, d->r_o, s) : run_residual<1024>(oa, d->r_o, s);
+        st = qd == 4096 ? run_residual<4096, FMT>(oa, d->r_o, s) : run_residual<1024, FMT>(oa, d->r_o, s);
         if (st)
             break;
 
         GateUpArgs ga{(const uint8_t *)L.w_gate, (const uint8_t *)L.w_up, c.hidden, d->h, L.ffn_norm, c.norm_eps,
                       d->act};
-        st = c.dim == 3072 ? run_gateup<3072>(ga, d->r_ffn, s) : run_gateup<1024>(ga, d->r_ffn, s);
+        st = c.dim == 3072 ? run_gateup<3072, FMT>(ga, d->r_ffn, s) : run_gateup<1024, FMT>(ga, d->r_ffn, s);
         if (st)
             break;
 
         ResidualArgs da{(const uint8_t *)L.w_down, d->act, d->h, c.dim};
-        st = c.hidden == 9216 ? run_residual<9216>(da, d->r_down, s) : run_residual<2048>(da, d->r_down, s);
+        st = c.hidden == 9216 ? run_residual<9216, FMT>(da, d->r_down, s) : run_residual<2048, FMT>(da, d->r_down, s);
     }
     if (st)
         return st;
     LmHeadArgs la{d->tok_embd, c.vocab, d->h, d->out_norm, c.norm_eps, logits, d->keys};
     int grid = 0;
-    int st2 = c.dim == 3072 ? run_lmhead<3072>(la, d->r_head, s, &grid) : run_lmhead<1024>(la, d->r_head, s, &grid);
+    int st2 = c.dim == 3072 ? run_lmhead<3072, FMT>(la, d->r_head, s, &grid) : run_lmhead<1024, FMT>(la, d->r_head, s, &grid);
     if (st2)
         return st2;
     hipLaunchKernelGGL(dec_finalize_kernel, dim3(1), dim3(256), 0, s, d->ctl, (const unsigned long long *)d->keys, grid,
                        tok_out, (const double *)d->rope);
     return check_launch("decoder finalize");
+}
+
+static int enqueue_step(vox_decoder *d, const int32_t *tok_in, int32_t *tok_out, float *logits, int bucket,
+                        hipStream_t s)
+{
+    switch (d->fmt) {
+    case FMT_BF16: return enqueue_step_fmt<FMT_BF16>(d, tok_in, tok_out, logits, bucket, s);
+    case FMT_F16: return enqueue_step_fmt<FMT_F16>(d, tok_in, tok_out, logits, bucket, s);
+    default: return enqueue_step_fmt<FMT_Q4>(d, tok_in, tok_out, logits, bucket, s);
+    }
 }
 
 static void drop_graphs(vox_decoder *d)
@@ -731,8 +782,10 @@ extern "C" int vox_decoder_workspace(const vox_decoder_config *c, size_t *kv_byt
     return ok();
 }
 
-extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder_weights *w, void *kv, size_t kv_bytes,
-                                  void *scratch, size_t scratch_bytes, void *stream, vox_decoder_t **out)
+namespace vox {
+
+static int create_decoder(const vox_decoder_config *c, const vox_decoder_weights *w, int fmt, void *kv,
+                          size_t kv_bytes, void *scratch, size_t scratch_bytes, void *stream, vox_decoder_t **out)
 {
     if (!out)
         return fail(VOX_E_INVAL, "vox_decoder_create: null output handle");
@@ -765,6 +818,7 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     if (!d)
         return fail(VOX_E_INVAL, "vox_decoder_create: out of host memory");
     d->c = *c;
+    d->fmt = fmt;
     d->layers.assign(w->layers, w->layers + c->n_layers);
     d->tok_embd = (const uint8_t *)w->tok_embd;
     d->out_norm = w->out_norm;
@@ -817,6 +871,26 @@ extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder
     }
     *out = d;
     return ok();
+}
+
+}  // namespace vox
+
+extern "C" int vox_decoder_create(const vox_decoder_config *c, const vox_decoder_weights *w, void *kv, size_t kv_bytes,
+                                  void *scratch, size_t scratch_bytes, void *stream, vox_decoder_t **out)
+{
+    return create_decoder(c, w, FMT_Q4, kv, kv_bytes, scratch, scratch_bytes, stream, out);
+}
+
+extern "C" int vox_decoder_create_w16(const vox_decoder_config *c, const vox_decoder_weights *w, int fmt, void *kv,
+                                      size_t kv_bytes, void *scratch, size_t scratch_bytes, void *stream,
+                                      vox_decoder_t **out)
+{
+    if (out)
+        *out = nullptr;
+    if (fmt != VOX_W16_BF16 && fmt != VOX_W16_F16)
+        return fail(VOX_E_INVAL, "vox_decoder_create_w16: fmt %d is neither VOX_W16_BF16 nor VOX_W16_F16", fmt);
+    return create_decoder(c, w, fmt == VOX_W16_BF16 ? FMT_BF16 : FMT_F16, kv, kv_bytes, scratch, scratch_bytes, stream,
+                          out);
 }
 
 extern "C" int vox_decoder_reset(vox_decoder_t *d, void *stream)

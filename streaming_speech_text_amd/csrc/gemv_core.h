@@ -22,6 +22,10 @@
 //    share of the masks (no separate integer-to-float conversion).
 //  * The K/64 partial sums of a row are combined through LDS in a fixed order (the result is
 //    deterministic run to run).
+//  * The same pipeline streams rows of 16-bit weights (bf16 or IEEE binary16, the formats of
+//    voxtral.c's weights and of its GPU path: page GeekNews 26608, sections 모델 다운로드 및 구성
+//    and 메모리 요구사항): 2K bytes per row, thread c of a row group taking its 16-byte chunks c,
+//    c + K/64, ... of every row with the activations of the same elements.
 #pragma once
 
 #include "vox_common.h"
@@ -33,14 +37,18 @@ namespace vox {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int K_, int NT_, int R_, int NPART_ = 1>
+// Weight formats of a matrix row: GGUF Q4_0 blocks, or 16-bit values (bf16 or IEEE binary16).
+enum { FMT_Q4 = 0, FMT_BF16 = 1, FMT_F16 = 2 };
+
+template <int K_, int NT_, int R_, int NPART_ = 1, int FMT_ = FMT_Q4>
 struct GemvGeom {
     static constexpr int K = K_;
     static constexpr int NT = NT_;
     static constexpr int R = R_;
     static constexpr int NPART = NPART_;        // tile = NPART slices of R/NPART rows
+    static constexpr int FMT = FMT_;
     static constexpr int NB = K / 32;           // Q4_0 blocks per row
-    static constexpr int RB = NB * 18;          // bytes per row
+    static constexpr int RB = FMT == FMT_Q4 ? NB * 18 : K * 2;   // bytes per row
     static constexpr int TR = K / 64;           // threads per row (one block pair each)
     static constexpr int G = NT / TR;           // row groups per workgroup
     static constexpr int RPP = R / NPART;       // rows per slice
@@ -116,6 +124,32 @@ __device__ __forceinline__ float q4_pair_dot(const uint32_t (&D)[9], const float
     return fmaf(d0, s0, d1 * s1);
 }
 
+// Dot product of 64 16-bit weights (eight 16-byte chunks, eight values each, in order) with
+// their activations x[64].  bf16: a value is the upper half of an fp32 (one shift or mask);
+// fp16: widened exactly inside v_fma_mix_f32.  Four partial sums over the chunks j % 4, added in a
+// fixed order.
+template <int FMT>
+__device__ __forceinline__ float w16_dot64(const u32x4 (&W)[8], const float (&x)[64])
+{
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t u[4] = {W[j].x, W[j].y, W[j].z, W[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x0 = x[8 * j + 2 * i], x1 = x[8 * j + 2 * i + 1];
+            if constexpr (FMT == FMT_BF16) {
+                acc[j & 3] = fmaf(__builtin_bit_cast(float, u[i] << 16), x0, acc[j & 3]);
+                acc[j & 3] = fmaf(__builtin_bit_cast(float, u[i] & 0xFFFF0000u), x1, acc[j & 3]);
+            } else {
+                acc[j & 3] = fma_f16h<false>(u[i], x0, acc[j & 3]);
+                acc[j & 3] = fma_f16h<true>(u[i], x1, acc[j & 3]);
+            }
+        }
+    }
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // Per-kernel prologue result: the thread's 64 activations and the two -8*sum terms.
 struct PairX {
     float x[64];
@@ -189,16 +223,31 @@ __device__ __forceinline__ void gemv_tile_rows(const u32x4 *tile, float *red, fl
     const int tid = threadIdx.x;
     const int c = tid % Gm::TR;
     const int g = tid / Gm::TR;
-    const uint32_t *lds32 = reinterpret_cast<const uint32_t *>(tile);
+    if constexpr (Gm::FMT == FMT_Q4) {
+        const uint32_t *lds32 = reinterpret_cast<const uint32_t *>(tile);
 #pragma unroll
-    for (int j = 0; j < Gm::R / Gm::G; ++j) {
-        const int rr = g + j * Gm::G;
-        const uint32_t *p = lds32 + rr * (Gm::RB / 4) + 9 * c;
-        uint32_t D[9];
+        for (int j = 0; j < Gm::R / Gm::G; ++j) {
+            const int rr = g + j * Gm::G;
+            const uint32_t *p = lds32 + rr * (Gm::RB / 4) + 9 * c;
+            uint32_t D[9];
 #pragma unroll
-        for (int i = 0; i < 9; ++i)
-            D[i] = p[i];
-        red[rr * Gm::TR + c] = q4_pair_dot(D, px.x, px.n8a, px.n8b);
+            for (int i = 0; i < 9; ++i)
+                D[i] = p[i];
+            red[rr * Gm::TR + c] = q4_pair_dot(D, px.x, px.n8a, px.n8b);
+        }
+    } else {
+        // 16-bit rows: thread c takes the row's 16-byte chunks c, c + TR, ... (eight of them), so a
+        // wave's LDS reads are consecutive; px.x holds the matching activations (w16_load_x)
+#pragma unroll
+        for (int j = 0; j < Gm::R / Gm::G; ++j) {
+            const int rr = g + j * Gm::G;
+            const u32x4 *p = tile + rr * (Gm::RB / 16) + c;
+            u32x4 W[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                W[i] = p[i * Gm::TR];
+            red[rr * Gm::TR + c] = w16_dot64<Gm::FMT>(W, px.x);
+        }
     }
     __syncthreads();
     // Each row's TR partials are added by RL lanes (TR/RL each, then a DPP tree): a row of 16
@@ -231,20 +280,38 @@ template <class Gm, class Policy>
 __device__ __forceinline__ void gemv_load_x(Policy &P, typename Policy::XRegs &xr, float *xs, float *wsum, PairX &px)
 {
     px.scale = P.x_stage(xr, xs, wsum);
-    const float4 *x4 = reinterpret_cast<const float4 *>(xs + XS_ROW * (threadIdx.x % Gm::TR));
+    if constexpr (Gm::FMT == FMT_Q4) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(xs + XS_ROW * (threadIdx.x % Gm::TR));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float4 v = x4[i];
-        px.x[4 * i + 0] = v.x;
-        px.x[4 * i + 1] = v.y;
-        px.x[4 * i + 2] = v.z;
-        px.x[4 * i + 3] = v.w;
+        for (int i = 0; i < 16; ++i) {
+            const float4 v = x4[i];
+            px.x[4 * i + 0] = v.x;
+            px.x[4 * i + 1] = v.y;
+            px.x[4 * i + 2] = v.z;
+            px.x[4 * i + 3] = v.w;
+        }
+        px.finish();
+    } else {
+        // the activations of the thread's chunks c, c + TR, ...: elements 8 (c + j TR) .. + 7
+        const int c = threadIdx.x % Gm::TR;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float4 *x4 = reinterpret_cast<const float4 *>(xs + xs_index(8 * (c + j * Gm::TR)));
+            const float4 a = x4[0], b = x4[1];
+            px.x[8 * j + 0] = a.x;
+            px.x[8 * j + 1] = a.y;
+            px.x[8 * j + 2] = a.z;
+            px.x[8 * j + 3] = a.w;
+            px.x[8 * j + 4] = b.x;
+            px.x[8 * j + 5] = b.y;
+            px.x[8 * j + 6] = b.z;
+            px.x[8 * j + 7] = b.w;
+        }
     }
-    px.finish();
     __syncthreads();
 }
 
-// The tile pipeline shared by every Q4_0 GEMV flavour.  Policy supplies:
+// The tile pipeline shared by every GEMV flavour (Q4_0 or 16-bit rows).  Policy supplies:
 //   XRegs, x_issue(XRegs&)                 issue the activation loads into registers
 //   x_stage(XRegs&, float* xs, float* wsum) fill xs with the activations, element i at
 //                                          xs[xs_index(i)] (all threads call it; it ends with a

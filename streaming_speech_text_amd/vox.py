@@ -66,6 +66,8 @@ _SIGS = {
     "vox_decoder_workspace": (_int, [C.POINTER(DecoderConfig), C.POINTER(_sz), C.POINTER(_sz)]),
     "vox_decoder_create": (_int, [C.POINTER(DecoderConfig), C.POINTER(DecoderWeights), _vp, _sz, _vp, _sz, _vp,
                                   C.POINTER(_vp)]),
+    "vox_decoder_create_w16": (_int, [C.POINTER(DecoderConfig), C.POINTER(DecoderWeights), _int, _vp, _sz, _vp, _sz, _vp,
+                                  C.POINTER(_vp)]),
     "vox_decoder_reset": (_int, [_vp, _vp]),
     "vox_decoder_seek": (_int, [_vp, _i64, _vp]),
     "vox_decoder_step": (_int, [_vp, _vp, _vp, _vp, _vp]),
@@ -254,9 +256,10 @@ class Decoder:
     """Owns a vox_decoder_t over device weights and caller-allocated buffers.
 
     `weights` holds device tensors: tok_embd (uint8), out_norm (fp32), and a list of layer
-    dicts with attn_norm, ffn_norm, wq, wk, wv, wo, w_gate, w_up, w_down."""
+    dicts with attn_norm, ffn_norm, wq, wk, wv, wo, w_gate, w_up, w_down.  fmt None: Q4_0
+    matrices (uint8 bytes); "bf16" / "f16": 16-bit matrices (uint16 / int16 [n, k])."""
 
-    def __init__(self, cfg: DecoderConfig, weights, kv=None, scratch=None, stream=None):
+    def __init__(self, cfg: DecoderConfig, weights, kv=None, scratch=None, stream=None, fmt=None):
         self.cfg = cfg
         kv_bytes, sc_bytes = decoder_workspace(cfg)
         dev = weights["tok_embd"].device
@@ -269,11 +272,16 @@ class Decoder:
             self._layers[i] = LayerWeights(*[_ptr(L[f], None, f) for f in
                                              ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo",
                                               "w_gate", "w_up", "w_down")])
-        self._w = DecoderWeights(_ptr(weights["tok_embd"], torch.uint8, "tok_embd"),
+        self._w = DecoderWeights(_ptr(weights["tok_embd"], torch.uint8 if fmt is None else None, "tok_embd"),
                                  _ptr(weights["out_norm"], torch.float32, "out_norm"), self._layers)
         h = _vp()
-        _check(lib().vox_decoder_create(C.byref(cfg), C.byref(self._w), _ptr(self.kv), kv_bytes,
-                                        _ptr(self.scratch), sc_bytes, _stream(stream), C.byref(h)))
+        if fmt is None:
+            _check(lib().vox_decoder_create(C.byref(cfg), C.byref(self._w), _ptr(self.kv), kv_bytes,
+                                            _ptr(self.scratch), sc_bytes, _stream(stream), C.byref(h)))
+        else:
+            code = {"bf16": VOX_W16_BF16, "f16": VOX_W16_F16}[fmt]
+            _check(lib().vox_decoder_create_w16(C.byref(cfg), C.byref(self._w), code, _ptr(self.kv), kv_bytes,
+                                                _ptr(self.scratch), sc_bytes, _stream(stream), C.byref(h)))
         self._h = h
 
     def step(self, token_in, token_out, logits=None, stream=None):

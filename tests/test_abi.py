@@ -167,3 +167,7 @@ def test_decoder_workspace_matches_page_kv_figure(lib):
     assert lib.vox_decoder_step(None, None, None, None, None) == vox.VOX_E_INVAL
     pos = C.c_int64()
     assert lib.vox_decoder_position(None, C.byref(pos)) == vox.VOX_E_INVAL
+    # the 16-bit decoder refuses a format other than bf16 / f16 before looking at anything else
+    h = C.c_void_p(0x1234)
+    assert lib.vox_decoder_create_w16(C.byref(cfg), None, 2, None, 0, None, 0, None, C.byref(h)) == vox.VOX_E_INVAL
+    assert not h.value
