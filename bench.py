@@ -44,11 +44,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sequences", type=int, default=5, help="decoder sequences timed (median reported)")
-    ap.add_argument("--leg", choices=["all", "decoder", "gemv", "kernels", "probe"], default="all",
+    ap.add_argument("--leg", choices=["all", "decoder", "decoder_w16", "gemv", "kernels", "probe"], default="all",
                     help="gemv: only the GEMV roofline leg and a copy of known size (for counter runs); "
                          "kernels: per-kernel timings of the other workloads, one JSON line each; "
                          "probe: read ceilings and the grid-handoff probe; decoder: only the decoder at the "
-                         "bench configuration (for kernel traces)")
+                         "bench configuration (for kernel traces); decoder_w16: only the decoder over f16 weights")
     ap.add_argument("--summarize-trace", metavar="CSV", help="print per-kernel statistics of a rocprofv3 "
                     "kernel_trace.csv (calls, mean, p10/p50/p90, min, max in us) and exit")
     ap.add_argument("--trace-json", metavar="OUT", help="with --summarize-trace: also write the statistics with "
@@ -758,6 +758,54 @@ def decoder_legs(args, torch, synth, vox, dev, stream, w, full_window=True):
     return main, full
 
 
+def decoder_w16_leg(args, torch, synth, vox, dev, stream, fmt="f16", n_seq=3):
+    """The decoder over 16-bit weights (the format voxtral.c's GPU path runs, F16) at the bench
+    configuration: 38-token prefix untimed, then args.steps greedy steps per sequence, median of
+    n_seq sequences."""
+    s = synth.VOXTRAL_DECODER
+    print(f"[bench] generating {fmt} weights", file=sys.stderr, flush=True)
+    w = synth.decoder_weights_w16(synth.SEED_DECODER, s, fmt)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    wd = {"tok_embd": d(w["tok_embd"]), "out_norm": d(w["out_norm"]),
+          "layers": [{k: d(v) for k, v in L.items()} for L in w["layers"]]}
+    wbytes = sum(int(v.nbytes) for L in w["layers"] for k, v in L.items() if k.startswith("w")) + w["tok_embd"].nbytes
+    del w
+    cfg = vox.DecoderConfig(s.n_layers, s.dim, s.n_heads, s.n_kv_heads, s.head_dim, s.hidden, s.vocab, s.n_slots,
+                            s.norm_eps, s.rope_theta)
+    dec = vox.Decoder(cfg, wd, fmt=fmt)
+    prefix, start = synth.decoder_tokens(synth.SEED_DECODER, s.vocab)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run_prefix(_q=0):
+        dec.reset()
+        for t in prefix:
+            tok.fill_(int(t))
+            dec.step(tok, tok)
+        tok.fill_(start)
+
+    run_prefix()
+    for _ in range(max(args.warmup, args.steps)):
+        dec.step(tok, tok)
+    torch.cuda.synchronize()
+    dev_ms, wall_ms = time_sequences(torch, stream, dec, tok, n_seq, args.steps, run_prefix)
+    kv_row = s.n_layers * 2 * s.n_kv_heads * s.head_dim * 4
+    kv_bytes = sum(kv_row * min(p + 1, s.n_slots) for p in range(len(prefix), len(prefix) + args.steps)) / args.steps
+    m = float(np.median(dev_ms))
+    out = {"format": fmt, "ms_per_token": spread(dev_ms), "host_clock_ms_per_token": round(float(np.median(wall_ms)), 4),
+           "bytes_per_token": int(wbytes + kv_bytes), "achieved_gbs": round((wbytes + kv_bytes) / m / 1e6, 1),
+           "frac_hbm": round((wbytes + kv_bytes) / m / 1e6 / HBM_PEAK_GBS, 4),
+           "note": "16-bit weights ~ N(0, 0.02^2); the pages' F16 step on Metal (M3 Max) is 23.5 ms"}
+    print(f"[bench] decoder over {fmt} weights {m:.4f} ms/token, {out['achieved_gbs']:.0f} GB/s", file=sys.stderr,
+          flush=True)
+    dec.close()
+    del wd
+    torch.cuda.empty_cache()
+    return out
+
+
 def gemv_sweep(torch, synth, vox, dev, stream, k=3072, rows=(1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)):
     """The Q4_0 GEMV over row counts at K = 3072 (the decoder width), rotating over more than
     1 GiB of weight copies per point."""
@@ -899,6 +947,9 @@ def main():
     if args.leg == "probe":
         probe_leg(torch, dev, stream)
         return
+    if args.leg == "decoder_w16":
+        print(json.dumps({"leg": "decoder_w16", **decoder_w16_leg(args, torch, synth, vox, dev, stream)}), flush=True)
+        return
     s = synth.VOXTRAL_DECODER
     print(f"[bench] generating weights ({s.n_layers} layers, vocab {s.vocab})", file=sys.stderr, flush=True)
     w = synth.decoder_weights(synth.SEED_DECODER, s)
@@ -909,6 +960,7 @@ def main():
               flush=True)
         return
     ms_per_token = float(np.median(dm["dev_ms"]))
+    w16 = decoder_w16_leg(args, torch, synth, vox, dev, stream)
 
     gemv = gemv_leg(args, torch, synth, vox, dev, stream)
     traffic = measured_traffic(kernel_source_digest(), gemv["bytes"])
@@ -948,6 +1000,7 @@ def main():
         "decoder_hbm_gbs": round(dm["bytes"] / (ms_per_token * 1e-3) / 1e9, 1),
         "decoder_bytes_per_token": int(dm["bytes"]),
         "decoder_full_window": full,
+        "decoder_w16": w16,
         "decoder_roofline": decoder_trace_roofline(synth),
         "gemv_sweep_k3072": sweep,
         "last_token": dm["last_token"],
