@@ -11,7 +11,7 @@
 // in bf16 and whose A operand holds the bf16 activations; the fp32 result is multiplied by the
 // block's scale d and accumulated in fp32 on the vector units.
 //
-// Three kernels:
+// Four kernels:
 //  * small outputs: a workgroup of 8 waves owns a (16*MI) x (16*NJ) tile; the waves
 //    split the K blocks into eight contiguous ranges, load their operands straight from memory
 //    with GM_PF blocks in flight, and the eight partial tiles are added in LDS in wave order.
@@ -19,6 +19,8 @@
 //    B holds (code - 8).  Lane group g (= lane / 16) takes code bytes 4g..4g+3, i.e. inputs
 //    {4g..4g+3} (low nibbles) then {16+4g..16+4g+3} (high nibbles), and the activations of
 //    the same inputs (the MFMA's k slots may hold the inputs in any order A and B agree on).
+//  * at most 16 rows at K = 1280 or 3072: the skinny kernel (16-column tiles whose weights for the
+//    whole of K are staged through LDS in one round trip, the same per-block products);
 //  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS),
 //    optionally with K split over workgroups (partial tiles in the caller's workspace, added in
 //    a fixed order by a second kernel).
@@ -213,6 +215,107 @@ __global__ __launch_bounds__(64 * WAVES) void q4_gemm_kernel(const uint8_t *__re
         const int col = n0 + 16 * j + (ln & 15);
         if (row < m && col < n)
             y[(size_t)row * n + col] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Skinny products (at most 16 rows of X, K of 1280 or 3072): one workgroup of 8 waves per 16
+// columns of Y.  The workgroup copies its 16 weight rows for the whole of K into LDS with
+// coalesced 16-byte loads (one memory round trip, at most 28 KB), while each wave loads the
+// activations of its eighth of K straight into registers; then every wave unpacks its blocks from
+// LDS and runs one v_mfma_f32_16x16x32_bf16 per block with the operand layout of q4_gemm_kernel,
+// and the eight partial tiles are added in LDS in wave order.  (q4_gemm_kernel reads the same
+// weights with 2-byte loads that each touch 16 rows.)
+// ---------------------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__restrict__ w,
+                                                             const uint16_t *__restrict__ x, float *__restrict__ y,
+                                                             int m, int n)
+{
+    constexpr int K = NB * 32;
+    constexpr int RB = NB * 18;              // bytes per weight row
+    constexpr int RW = RB / 4 + 1;           // LDS dwords per row: odd, so the 16 rows fall in 16 banks
+    constexpr int CH = RB / 16;              // 16-byte chunks per row
+    constexpr int PER = (16 * CH + 511) / 512;
+    constexpr int BPW = NB / 8;              // blocks per wave
+    static_assert(RB % 16 == 0 && NB % 8 == 0, "whole chunks per row, whole blocks per wave");
+    __shared__ uint32_t wt[16 * RW];
+    __shared__ float red[8][4][64];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int grp = lane >> 4;
+    const int l16 = lane & 15;
+    const int n0 = blockIdx.x * 16;
+    const int kb0 = wave * BPW;
+
+    // activations of this lane: row l16 (past m: the last row, not stored), inputs 4g..4g+3 and
+    // 16+4g..16+4g+3 of each of the wave's blocks
+    const uint16_t *xr = x + (size_t)min(l16, m - 1) * K;
+    u32x2v xa[BPW][2];
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+        const uint16_t *xp = xr + (size_t)(kb0 + b) * 32 + 4 * grp;
+        xa[b][0] = *reinterpret_cast<const u32x2v *>(xp);
+        xa[b][1] = *reinterpret_cast<const u32x2v *>(xp + 16);
+    }
+    // the 16 weight rows (rows past n repeat row n - 1): chunk q -> row q / CH, chunk q % CH;
+    // threads past the last chunk reload it (an identical LDS store)
+    u32x4v wr[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int q = min(tid + 512 * p, 16 * CH - 1);
+        const int col = min(n0 + q / CH, n - 1);
+        wr[p] = *reinterpret_cast<const u32x4v *>(w + (size_t)col * RB + (size_t)16 * (q % CH));
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int q = min(tid + 512 * p, 16 * CH - 1);
+        uint32_t *dst = wt + (q / CH) * RW + 4 * (q % CH);
+        dst[0] = wr[p].x;
+        dst[1] = wr[p].y;
+        dst[2] = wr[p].z;
+        dst[3] = wr[p].w;
+    }
+    __syncthreads();
+
+    const uint32_t *row = wt + l16 * RW;
+    f32x4v acc = 0.0f;
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+        const int kb = kb0 + b;
+        const int o = 18 * kb;   // byte offset of the block in its row: 4-aligned for even kb
+        uint32_t q, d16;
+        if ((kb & 1) == 0) {     // uniform over the wave
+            d16 = row[o >> 2] & 0xFFFFu;
+            q = __builtin_amdgcn_alignbyte(row[(o >> 2) + grp + 1], row[(o >> 2) + grp], 2);
+        } else {
+            d16 = row[(o - 2) >> 2] >> 16;
+            q = row[((o + 2) >> 2) + grp];
+        }
+        const u32x4v av = {xa[b][0].x, xa[b][0].y, xa[b][1].x, xa[b][1].y};
+        const f32x4v t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), codes_to_bf16(q),
+                                                                 (f32x4v)0.0f, 0, 0, 0);
+        acc += half_bits_to_float(d16) * t;
+    }
+
+    // add the eight waves' partial tiles in wave order
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        red[wave][r][lane] = acc[r];
+    __syncthreads();
+    // D layout of a 16x16 MFMA block: lane holds rows 4*(lane/16) .. +3 of column lane%16
+    if (tid < 256) {
+        const int ln = tid & 63, r = tid >> 6;
+        float v = red[0][r][ln];
+#pragma unroll
+        for (int wv = 1; wv < 8; ++wv)
+            v += red[wv][r][ln];
+        const int rowi = 4 * (ln >> 4) + r;
+        const int col = n0 + (ln & 15);
+        if (rowi < m && col < n)
+            y[(size_t)rowi * n + col] = v;
     }
 }
 
@@ -919,6 +1022,29 @@ static int launch_gemm_split(const void *w, const uint16_t *x, float *y, int m, 
     return check_launch("q4 split product");
 }
 
+// The skinny kernel takes the products of at most 16 rows at K = 1280 or 3072 (one 16-row tile;
+// the weights of a 16-column tile fit in LDS for the whole of K).  Measured on MI355X at 16
+// frames: 16 x 1280 x 1280 5.0 us against 5.6 with the split-K-over-waves kernel, 16 x 5120 x 1280
+// 7.4 against 9.0, q/k/v stacked 5.1 against 5.7; at K = 3072 16 x 3072 x 3072 9.4 against 13.0
+// (tiled) and 8 x 9216 x 3072 14.9 against 18.5; at K = 5120 (16 x 1280 x 5120: 80 workgroups)
+// 13.0 against 10.1 us for the tiled kernel with K split over the grid, which keeps that shape.
+static bool skinny_shape(int64_t m, int64_t n, int64_t k)
+{
+    return m >= 1 && m <= 16 && (k == 1280 || k == 3072) &&
+           (uint64_t)n * (uint64_t)(k / 32) * 18 < (1ull << 31) && (n + 15) / 16 <= 0x7FFFFFFF;
+}
+
+static int launch_gemm_skinny(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
+{
+    const dim3 grid((unsigned)((n + 15) / 16));
+    switch (k) {
+    case 1280: hipLaunchKernelGGL(q4_gemm_skinny_kernel<40>, grid, dim3(512), 0, s, (const uint8_t *)w, x, y, m, n); break;
+    case 3072: hipLaunchKernelGGL(q4_gemm_skinny_kernel<96>, grid, dim3(512), 0, s, (const uint8_t *)w, x, y, m, n); break;
+    default: return fail(VOX_E_UNSUPPORTED, "q4 skinny product: no compiled K for k=%d", k);
+    }
+    return check_launch("q4 skinny product");
+}
+
 // Blocks in flight per wave: all of them when a wave has exactly five (K = 1280: the whole range
 // in one memory round trip; measured on MI355X, 16 x 1280 x 1280 took 5.5 us against 7.4 with
 // four), else four (five or eight for longer ranges was slower, e.g. 16 x 3072 x 3072: 15.6 us
@@ -944,7 +1070,7 @@ extern "C" size_t vox_q4_gemm_workspace(int64_t m, int64_t n, int64_t k)
 {
     if (m <= 0 || n <= 0 || k <= 0 || k % 32 || m > 65535 * 16 || n > (1 << 24) || k > (1 << 24))
         return 0;
-    if (split_shape(m, n, k))
+    if (split_shape(m, n, k) || skinny_shape(m, n, k))
         return 0;
     if (!tiled_shape(m, n, k))
         return 0;
@@ -974,6 +1100,8 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
     int st;
     if (aligned(x_bf16, 16) && aligned(w_q4, 16) && split_shape(m, n, k)) {
         st = launch_gemm_split(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
+    } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && skinny_shape(m, n, k)) {
+        st = launch_gemm_skinny(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
     } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_shape(m, n, k)) {
         int slices = workspace ? tiled_slices(m, n, k) : 1;
         const size_t need = tiled_workspace(m, n, slices);

@@ -153,6 +153,29 @@ def test_gemm_errors(vx):
     vx.q4_gemm(w, x, y, m=0, n=32, k=64)
 
 
+@pytest.mark.parametrize("m,n,k", [(5, 1283, 1280), (11, 77, 3072), (16, 3840, 1280), (2, 1280, 3072), (16, 1, 3072),
+                                   (1, 5120, 1280), (13, 2000, 3072)])
+def test_gemm_skinny(vx, orc, m, n, k):
+    # at most 16 rows at K = 1280 / 3072: the whole K of a 16-column tile staged in LDS;
+    # ragged column counts (the last tile repeats the last weight row) and rows below 16
+    w, xb = synth.gemm_inputs(620 + m, m, n, k)
+    assert vx.q4_gemm_workspace(m, n, k) == 0
+    say(f"gemm skinny m={m} n={n} k={k}")
+    assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm skinny {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(7, 130, 3072), (16, 1283, 1280), (3, 64, 1280)])
+def test_gemm_skinny_exact_dyadic(vx, orc, m, n, k):
+    # exact inputs: the skinny kernel's sum (eight waves' partial tiles added in order) is exact
+    g = synth.generator(621)
+    w = synth.q4_matrix(g, n, k).reshape(n, k // 32, 18)
+    e = g.integers(-3, 1, size=(n, k // 32)).astype(np.float64)
+    w[:, :, 0:2] = (2.0 ** e).astype("<f2").view(np.uint8).reshape(n, k // 32, 2)
+    w = w.reshape(n, -1)
+    xb = synth.bf16_bits(g.integers(-4, 5, size=(m, k)).astype(np.float32))
+    assert np.array_equal(_gemm(vx, w, xb, m, n, k).astype(np.float64), orc.q4_gemm(w, xb))
+
+
 @pytest.mark.parametrize("k", [1024, 1056, 1280, 1312])
 def test_gemm_small_kernel_block_ranges(vx, orc, k):
     # the split-K-over-waves kernel keeps all five blocks of a wave in flight when a wave has
