@@ -1028,6 +1028,8 @@ static int launch_gemm_split(const void *w, const uint16_t *x, float *y, int m, 
 // 7.4 against 9.0, q/k/v stacked 5.1 against 5.7; at K = 3072 16 x 3072 x 3072 9.4 against 13.0
 // (tiled) and 8 x 9216 x 3072 14.9 against 18.5; at K = 5120 (16 x 1280 x 5120: 80 workgroups)
 // 13.0 against 10.1 us for the tiled kernel with K split over the grid, which keeps that shape.
+// Four 16-row blocks per wave for up to 64 rows at K = 1280 were slower than the kernels those
+// shapes keep (64 x 1280 x 1280 11.3 against 8.9 us, 64 x 5120 x 1280 20.2 against 11.7).
 static bool skinny_shape(int64_t m, int64_t n, int64_t k)
 {
     return m >= 1 && m <= 16 && (k == 1280 || k == 3072) &&
