@@ -90,6 +90,13 @@ __device__ __forceinline__ void store_gelu_pair(uint16_t *hl, int n, int64_t row
     p[GELU_STAGE] = __builtin_bit_cast(uint16_t, lo);
 }
 
+// Modes of the tiled and skinny kernels (compile-time, so the plain product carries no code of the others):
+//  T_PLAIN      fp32 output y;
+//  T_GELU_OUT   the unsplit output goes through GELU into hl as store_gelu_pair lays it out;
+//  T_PAIR_IN    the activations are GELU pairs (row length k = 2 x the weights' K): stage st
+//               reads weight stage st / 2, so each weight stage serves its hi and lo halves.
+enum { T_PLAIN = 0, T_GELU_OUT = 1, T_PAIR_IN = 2 };
+
 // WAVES: waves splitting K.  (Sixteen waves with all ten blocks of each in flight for 16 x 1280 x
 // 5120 were measured on MI355X at 19.3 us against 13 us for the tiled kernel and its slice sum:
 // the lanes' 4-byte pieces of 16 weight rows make every load touch 16 cache lines.)
@@ -227,12 +234,16 @@ __global__ __launch_bounds__(64 * WAVES) void q4_gemm_kernel(const uint8_t *__re
 // and the eight partial tiles are added in LDS in wave order.  (q4_gemm_kernel reads the same
 // weights with 2-byte loads that each touch 16 rows.)
 // ---------------------------------------------------------------------------------------
-template <int NB>
+// MODE (T_PLAIN, T_GELU_OUT, T_PAIR_IN): as for the tiled kernel; with T_PAIR_IN a block's hi and
+// lo activations (128 apart in the pair layout) go through two products into one result before its
+// scale, and with T_GELU_OUT the outputs go to hl as GELU pairs.
+template <int NB, int MODE = T_PLAIN>
 __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__restrict__ w,
                                                              const uint16_t *__restrict__ x, float *__restrict__ y,
-                                                             int m, int n)
+                                                             uint16_t *__restrict__ hl, int m, int n)
 {
-    constexpr int K = NB * 32;
+    constexpr int K = NB * 32 * (MODE == T_PAIR_IN ? 2 : 1);   // the activations' row length
+    constexpr int NA = MODE == T_PAIR_IN ? 2 : 1;              // activation halves per block
     constexpr int RB = NB * 18;              // bytes per weight row
     constexpr int RW = RB / 4 + 1;           // LDS dwords per row: odd, so the 16 rows fall in 16 banks
     constexpr int CH = RB / 16;              // 16-byte chunks per row
@@ -253,12 +264,19 @@ __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__re
     // activations of this lane: row l16 (past m: the last row, not stored), inputs 4g..4g+3 and
     // 16+4g..16+4g+3 of each of the wave's blocks
     const uint16_t *xr = x + (size_t)min(l16, m - 1) * K;
-    u32x2v xa[BPW][2];
+    u32x2v xa[BPW][NA][2];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
-        const uint16_t *xp = xr + (size_t)(kb0 + b) * 32 + 4 * grp;
-        xa[b][0] = *reinterpret_cast<const u32x2v *>(xp);
-        xa[b][1] = *reinterpret_cast<const u32x2v *>(xp + 16);
+        const int kb = kb0 + b;
+        // plain: inputs 32 kb ..; pairs: block kb is columns 32 (kb % 4) .. of 128-input stage kb / 4,
+        // its hi half at 256 (kb / 4) + 32 (kb % 4) and its lo half 128 further
+        const uint16_t *xp = xr + (MODE == T_PAIR_IN ? (size_t)(256 * (kb >> 2) + 32 * (kb & 3)) : (size_t)kb * 32) +
+                             4 * grp;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            xa[b][a][0] = *reinterpret_cast<const u32x2v *>(xp + 128 * a);
+            xa[b][a][1] = *reinterpret_cast<const u32x2v *>(xp + 128 * a + 16);
+        }
     }
     // the 16 weight rows (rows past n repeat row n - 1): chunk q -> row q / CH, chunk q % CH;
     // threads past the last chunk reload it (an identical LDS store)
@@ -294,9 +312,13 @@ __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__re
             d16 = row[(o - 2) >> 2] >> 16;
             q = row[((o + 2) >> 2) + grp];
         }
-        const u32x4v av = {xa[b][0].x, xa[b][0].y, xa[b][1].x, xa[b][1].y};
-        const f32x4v t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), codes_to_bf16(q),
-                                                                 (f32x4v)0.0f, 0, 0, 0);
+        const bf16x8 bq = codes_to_bf16(q);
+        f32x4v t = 0.0f;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            const u32x4v av = {xa[b][a][0].x, xa[b][a][0].y, xa[b][a][1].x, xa[b][a][1].y};
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bq, t, 0, 0, 0);
+        }
         acc += half_bits_to_float(d16) * t;
     }
 
@@ -314,8 +336,12 @@ __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__re
             v += red[wv][r][ln];
         const int rowi = 4 * (ln >> 4) + r;
         const int col = n0 + (ln & 15);
-        if (rowi < m && col < n)
-            y[(size_t)rowi * n + col] = v;
+        if (rowi < m && col < n) {
+            if constexpr (MODE == T_GELU_OUT)
+                store_gelu_pair(hl, n, rowi, col, v);
+            else
+                y[(size_t)rowi * n + col] = v;
+        }
     }
 }
 
@@ -428,12 +454,6 @@ __device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, 
     }
 }
 
-// Modes of the tiled kernel (compile-time, so the plain product carries no code of the others):
-//  T_PLAIN      fp32 output y;
-//  T_GELU_OUT   the unsplit output goes through GELU into hl as store_gelu_pair lays it out;
-//  T_PAIR_IN    the activations are GELU pairs (row length k = 2 x the weights' K): stage st
-//               reads weight stage st / 2, so each weight stage serves its hi and lo halves.
-enum { T_PLAIN = 0, T_GELU_OUT = 1, T_PAIR_IN = 2 };
 
 // NS: stages (of GT_STAGE inputs) per workgroup, fixed at compile time.  Workgroup z of the grid's
 // third dimension takes stages z*NS .. z*NS+NS-1; with one slice it writes the output itself,
@@ -1040,8 +1060,8 @@ static int launch_gemm_skinny(const void *w, const uint16_t *x, float *y, int m,
 {
     const dim3 grid((unsigned)((n + 15) / 16));
     switch (k) {
-    case 1280: hipLaunchKernelGGL(q4_gemm_skinny_kernel<40>, grid, dim3(512), 0, s, (const uint8_t *)w, x, y, m, n); break;
-    case 3072: hipLaunchKernelGGL(q4_gemm_skinny_kernel<96>, grid, dim3(512), 0, s, (const uint8_t *)w, x, y, m, n); break;
+    case 1280: hipLaunchKernelGGL((q4_gemm_skinny_kernel<40>), grid, dim3(512), 0, s, (const uint8_t *)w, x, y, nullptr, m, n); break;
+    case 3072: hipLaunchKernelGGL((q4_gemm_skinny_kernel<96>), grid, dim3(512), 0, s, (const uint8_t *)w, x, y, nullptr, m, n); break;
     default: return fail(VOX_E_UNSUPPORTED, "q4 skinny product: no compiled K for k=%d", k);
     }
     return check_launch("q4 skinny product");
@@ -1152,6 +1172,29 @@ static bool adapter_shape(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
 
 }  // namespace vox
 
+// At most 16 rows: both products through the skinny kernel (no K slices), the first writing the
+// GELU pairs, the second reading them.  Measured on MI355X: 4 rows 18.6 us against 28.7 with the
+// tiled products and their slice sums, 16 rows 27.3 against 29.5.
+static int adapter_skinny(const void *w1, const void *w2, const uint16_t *x, float *y, uint16_t *h, int m, int k,
+                          int n_mid, int n_out, hipStream_t s)
+{
+    const dim3 g1((unsigned)((n_mid + 15) / 16)), g2((unsigned)((n_out + 15) / 16));
+    switch (k) {
+    case 1280: hipLaunchKernelGGL((q4_gemm_skinny_kernel<40, T_GELU_OUT>), g1, dim3(512), 0, s, (const uint8_t *)w1, x, nullptr, h, m, n_mid); break;
+    case 3072: hipLaunchKernelGGL((q4_gemm_skinny_kernel<96, T_GELU_OUT>), g1, dim3(512), 0, s, (const uint8_t *)w1, x, nullptr, h, m, n_mid); break;
+    default: hipLaunchKernelGGL((q4_gemm_skinny_kernel<160, T_GELU_OUT>), g1, dim3(512), 0, s, (const uint8_t *)w1, x, nullptr, h, m, n_mid); break;
+    }
+    int st = check_launch("adapter, first product");
+    if (st)
+        return st;
+    if (n_mid == 1280)
+        hipLaunchKernelGGL((q4_gemm_skinny_kernel<40, T_PAIR_IN>), g2, dim3(512), 0, s, (const uint8_t *)w2, h, y, nullptr, m, n_out);
+    else
+        hipLaunchKernelGGL((q4_gemm_skinny_kernel<96, T_PAIR_IN>), g2, dim3(512), 0, s, (const uint8_t *)w2, h, y, nullptr, m, n_out);
+    st = check_launch("adapter, second product");
+    return st ? st : ok();
+}
+
 extern "C" size_t vox_adapter_workspace(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
 {
     if (m <= 0 || n_out <= 0 || !adapter_shape(m, k, n_mid, n_out))
@@ -1191,6 +1234,8 @@ extern "C" int vox_adapter(const void *w1_q4, const void *w2_q4, const uint16_t 
         return fail(VOX_E_INVAL, "vox_adapter: y overlaps an input");
     hipStream_t s = (hipStream_t)stream;
     uint16_t *h = (uint16_t *)workspace;
+    if (m <= 16)
+        return adapter_skinny(w1_q4, w2_q4, x_bf16, y, h, (int)m, (int)k, (int)n_mid, (int)n_out, s);
     float *part = (float *)((char *)workspace + adapter_h_bytes(m, n_mid));
     const int s1 = tiled_slices(m, n_mid, k), s2 = tiled_slices(m, n_out, 2 * n_mid);
     int st = launch_gemm_tiled<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, s1 > 1 ? part : nullptr, (int)m, (int)n_mid,

@@ -38,18 +38,20 @@ def test_adapter_chunk_rows(vx, orc, m):
 
 
 @pytest.mark.parametrize("m,k,n_mid,n_out", [(1, 1280, 1280, 64), (17, 1280, 3072, 100), (65, 3072, 1280, 33),
-                                             (130, 5120, 1280, 1283), (3, 5120, 3072, 7), (200, 1280, 1280, 1280)])
+                                             (130, 5120, 1280, 1283), (3, 5120, 3072, 7), (200, 1280, 1280, 1280),
+                                             (16, 3072, 3072, 1283), (11, 5120, 1280, 100)])
 def test_adapter_ragged(vx, orc, m, k, n_mid, n_out):
     say(f"adapter ragged m={m} {k}->{n_mid}->{n_out}")
     w1, w2, xb = synth.adapter_inputs(700 + m, m, k, n_mid, n_out)
     assert_close(_adapter(vx, w1, w2, xb, n_out), orc.adapter(w1, w2, xb), f"adapter {m} {k}->{n_mid}->{n_out}")
 
 
-def test_adapter_gelu_between_the_linears(vx, orc):
+@pytest.mark.parametrize("m", [40, 9])
+def test_adapter_gelu_between_the_linears(vx, orc, m):
     # W2 = identity (code 9 on the diagonal, 8 elsewhere, scale 1): Y = GELU(X W1^T).  The GELU
     # value travels as a bf16 pair within 2^-18 of its fp32 value, so this holds well inside the
-    # usual bound.
-    m, k, n_mid = 40, 5120, 1280
+    # usual bound (m = 9: both products through the kernel for at most 16 rows).
+    k, n_mid = 5120, 1280
     g = synth.generator(720)
     w1 = synth.q4_matrix(g, n_mid, k)
     xb = synth.bf16_normal(g, (m, k))
