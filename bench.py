@@ -188,7 +188,8 @@ def probe_leg(torch, dev, stream):
 
     for nch in (0, 4, 8, 16):
         phase_bytes = 8192 * nch * cus
-        for mode, name in ((0, "persistent, gathered flags"), (1, "persistent, eight counters")):
+        for mode, name in ((0, "persistent, gathered flags"), (1, "persistent, eight counters"),
+                           (2, "persistent, poller wave")):
             per = []
             for _ in range(5):
                 L.vox_probe_handoff_reset(work.data_ptr(), cur())

@@ -39,7 +39,9 @@ int vox_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_
 size_t vox_probe_handoff_work_bytes(void);
 int vox_probe_handoff_reset(void *work, void *stream);
 /* mode 0: every workgroup stores a flag, one workgroup gathers them and releases the grid;
- * mode 1: eight counters, every workgroup polls their sum.  Runs nphase phases (1..100000). */
+ * mode 1: eight counters, every workgroup polls their sum; mode 2: eight counters polled by a
+ * ninth wave per workgroup that holds no weight loads, while the eight working waves keep the
+ * next phase's loads in flight across the barrier.  Runs nphase phases (1..100000). */
 int vox_probe_handoff_persistent(int mode, int nch, int nphase, const void *weights, size_t weight_bytes, void *work,
                                  void *stream);
 /* Phase `phase` (1..100000) of the same work as its own launch, no prefetch, no barrier. */

@@ -13,7 +13,9 @@
 // stores), then waits at the grid barrier.  The vectors are double-buffered by phase parity.
 // Barriers: mode 0 - every workgroup stores its own flag, workgroup 0 gathers them and releases
 // the grid with one flag; mode 1 - eight counters (workgroup i adds to counter i % 8), every
-// workgroup polls their sum.  Every wait is bounded; one expired wait sets an abort flag that
+// workgroup polls their sum; mode 2 - the eight counters polled by a ninth wave that holds no
+// weight loads, so the working waves keep the next phase's loads in flight across the barrier.
+// Every wait is bounded; one expired wait sets an abort flag that
 // ends all others, so every workgroup exits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -181,6 +183,102 @@ __global__ __launch_bounds__(HT) void handoff_persistent_kernel(const u32x4 *__r
         atomicAdd(&W.ctl->sink, 1u);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int WAIT_LGKM0 = 0xC07F;   // LDS and scalar memory done; vector memory untouched
+constexpr int WAIT_ALL0 = 0;         // everything done
+
+// Mode 2: the same phases with the next phase's weight loads in flight across the barrier.  A
+// ninth wave in each workgroup keeps no weight loads: it stores the workgroup's share of the
+// phase's vector (agent scope), waits for its own stores, adds the workgroup to the eight
+// counters, polls their sum, reads the grid's vector for the next phase (agent scope) into LDS,
+// and releases the eight working waves.  Those check every value of that vector, fold their
+// prefetched weights, hand their share of the next vector to the poller through LDS, issue the
+// next phase's loads and wait
+// at workgroup barriers that wait on no memory, so their loads stay in flight while the grid
+// synchronises (memory returns in order per wave: the poller's loads never queue behind them).
+template <int NCH>
+__global__ __launch_bounds__(HT + 64) void handoff_poller_kernel(const u32x4 *__restrict__ wts, int64_t win16, int nwin,
+                                                                 uint8_t *work, int nphase)
+{
+    __shared__ float vin[HVEC];   // the previous phase's vector
+    __shared__ float vout[64];    // this workgroup's share of the phase's vector
+    const Work W = work_of(work);
+    const int G = gridDim.x;
+    const int per = HVEC / G;
+    const int tid = threadIdx.x;
+    const bool poller = tid >= HT;
+    const int lane = tid & 63;
+    u32x4 pf[NCH > 0 ? NCH : 1];
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    auto issue = [&](int p) {
+        const u32x4 *base = wts + (int64_t)(p % nwin) * win16 + (int64_t)blockIdx.x * NCH * HT;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            pf[c] = base[c * HT + tid];
+    };
+    if (!poller && NCH > 0)
+        issue(1);
+    for (int p = 1; p <= nphase; ++p) {
+        if (!poller) {
+            float sum = 0.0f;
+            if (p > 1) {
+                unsigned bad = 0;   // values the poller read before they were visible
+                for (int i = tid; i < HVEC; i += HT) {
+                    bad += vin[i] != (float)((p - 1) * 4096 + i / per);
+                    sum += vin[i];
+                }
+                if (bad)
+                    __hip_atomic_fetch_add(&W.ctl->mismatches, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+                acc ^= pf[c];
+            if (tid < per)
+                vout[tid] = (float)(p * 4096 + (int)blockIdx.x) + 0.0f * sum;
+            if constexpr (NCH > 0)
+                issue(p + 1);   // in flight until the next phase folds it (past the last phase: unused)
+        }
+        __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);   // vout written
+        __builtin_amdgcn_s_barrier();
+        if (poller) {
+            if (lane < per)
+                __hip_atomic_store(W.vec + (size_t)(p & 1) * HVEC + blockIdx.x * per + lane, vout[lane], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(WAIT_ALL0);   // the poller's stores are complete (it has no loads in flight)
+            if (lane == 0)
+                __hip_atomic_fetch_add(W.counters + (blockIdx.x & 7) * 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            unsigned n = 0;
+            for (;;) {
+                unsigned c = lane < 8 ? ld_agent(W.counters + lane * 64) : 0u;
+                c += __shfl_xor(c, 1);
+                c += __shfl_xor(c, 2);
+                c += __shfl_xor(c, 4);
+                if (__shfl(c, 0) >= (unsigned)p * (unsigned)G)
+                    break;
+                if (++n > SPIN_LIMIT || ld_agent(&W.ctl->abort_flag)) {
+                    give_up(W, lane);
+                    break;
+                }
+            }
+            if (p < nphase) {
+                // a lane's 48 loads all issued before the first is used: one memory round trip
+                const float *v = W.vec + (size_t)(p & 1) * HVEC + lane;
+                float xs[HVEC / 64];
+#pragma unroll
+                for (int j = 0; j < HVEC / 64; ++j)
+                    xs[j] = __hip_atomic_load(v + 64 * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int j = 0; j < HVEC / 64; ++j)
+                    vin[lane + 64 * j] = xs[j];
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);   // vin written
+        __builtin_amdgcn_s_barrier();
+    }
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u)
+        atomicAdd(&W.ctl->sink, 1u);
+}
+
 // One phase as its own launch (the same work, without a prefetch or a barrier).
 template <int NCH>
 __global__ __launch_bounds__(HT) void handoff_phase_kernel(const u32x4 *__restrict__ wts, int64_t win16, int nwin,
@@ -235,12 +333,15 @@ template <int NCH>
 int launch_persistent(int mode, const void *w, int64_t win16, int nwin, void *work, int nphase, int G, hipStream_t s)
 {
     int occ = 0;
-    const bool fits = mode == 0
-                          ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, handoff_persistent_kernel<0, NCH>, HT, 0) == hipSuccess
-                          : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, handoff_persistent_kernel<1, NCH>, HT, 0) == hipSuccess;
+    const bool fits = mode == 0   ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, handoff_persistent_kernel<0, NCH>, HT, 0) == hipSuccess
+                      : mode == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, handoff_persistent_kernel<1, NCH>, HT, 0) == hipSuccess
+                                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, handoff_poller_kernel<NCH>, HT + 64, 0) == hipSuccess;
     if (!fits || occ < 1)
         return -2;   // one workgroup per compute unit must be resident at once
-    if (mode == 0)
+    if (mode == 2)
+        hipLaunchKernelGGL((handoff_poller_kernel<NCH>), dim3(G), dim3(HT + 64), 0, s, (const u32x4 *)w, win16, nwin,
+                           (uint8_t *)work, nphase);
+    else if (mode == 0)
         hipLaunchKernelGGL((handoff_persistent_kernel<0, NCH>), dim3(G), dim3(HT), 0, s, (const u32x4 *)w, win16, nwin,
                            (uint8_t *)work, nphase);
     else
@@ -267,8 +368,9 @@ extern "C" int vox_probe_handoff_persistent(int mode, int nch, int nphase, const
     const int G = grid_size();
     int64_t win16 = 0;
     int nwin = 0;
-    if ((mode != 0 && mode != 1) || nphase < 1 || nphase > 100000 || !work || (uintptr_t)work % 256 || G < 1 ||
-        (nch > 0 && (!weights || (uintptr_t)weights % 16)) || !windows(nch, G, weight_bytes, win16, nwin))
+    if ((mode != 0 && mode != 1 && mode != 2) || nphase < 1 || nphase > 100000 || !work || (uintptr_t)work % 256 || G < 1 ||
+        (nch > 0 && (!weights || (uintptr_t)weights % 16)) || !windows(nch, G, weight_bytes, win16, nwin) ||
+        (mode == 2 && (HVEC % G || HVEC / G > 64)))   // the poller stores a share of at most 64 values
         return -1;
     hipStream_t s = (hipStream_t)stream;
     switch (nch) {
