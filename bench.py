@@ -375,7 +375,7 @@ def kernels_leg(torch, synth, vox, dev, stream):
         del wdev
         torch.cuda.empty_cache()
 
-    # one product per launch at 750 frames (each linear of the set, q/k/v stacked), then the split
+    # one product per launch at 750 frames (each linear of the set, q/k/v stacked), then the wide
     # product over K at 750 x 5120 (the cost of a stage and of a launch)
     def gemm_case(case, m, n, k):
         w, xb = synth.gemm_inputs(synth.SEED_GEMM, m, n, k)
@@ -399,7 +399,7 @@ def kernels_leg(torch, synth, vox, dev, stream):
     for name, n, k in synth.ENCODER_LINEARS[3:] + [("q/k/v stacked", 3840, 1280)]:
         gemm_case(f"encoder {name}, M=750", 750, n, k)
     for k in (1280, 3072, 5120):
-        gemm_case("split product over K at 750 x 5120", 750, 5120, k)
+        gemm_case("wide product over K at 750 x 5120", 750, 5120, k)
 
     # encoder self-attention over a chunk (32 heads x 40, window 750, a full window of earlier rows)
     H, W = synth.ENC_HEADS, synth.ENC_WINDOW

@@ -6,12 +6,13 @@
 // dequantisation fused into the product (Rust port page, GeekNews 26595, section 아키텍처).
 //
 // Exactness: a dequantised weight (code - 8) * d needs up to 15 significant bits, more than
-// bf16 holds, so the matrix cores never see it.  Each 32-input Q4_0 block is one
-// v_mfma_f32_16x16x32_bf16 per 16 x 16 output block whose B operand holds exact small integers
-// in bf16 and whose A operand holds the bf16 activations; the fp32 result is multiplied by the
-// block's scale d and accumulated in fp32 on the vector units.
+// bf16 holds, so the matrix cores never see it.  Each 32-input Q4_0 block is one product per
+// output block (v_mfma_f32_16x16x32_bf16, or two v_mfma_f32_32x32x16_bf16 in the wide product)
+// whose B operand holds exact small integers in bf16 and whose A operand holds the bf16
+// activations; the fp32 result is multiplied by the block's scale d and accumulated in fp32 on
+// the vector units.
 //
-// Four kernels:
+// Four products:
 //  * small outputs: a workgroup of 8 waves owns a (16*MI) x (16*NJ) tile; the waves
 //    split the K blocks into eight contiguous ranges, load their operands straight from memory
 //    with GM_PF blocks in flight, and the eight partial tiles are added in LDS in wave order.
@@ -24,9 +25,8 @@
 //  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS),
 //    optionally with K split over workgroups (partial tiles in the caller's workspace, added in
 //    a fixed order by a second kernel).
-//  * long chunks with many output tiles: the split product (128 x 128 tiles), whose B operands
-//    are the exact hi and lo bf16 parts of each dequantised weight, so the scale needs no vector
-//    work per output.
+//  * long chunks: the wide product (128 x 128 tiles on v_mfma_f32_32x32x16_bf16, the same
+//    exact operands and per-block scale), K split over the grid where its tiles are too few.
 //
 // The adapter between encoder and decoder (voxtral.c page, section 모델 아키텍처: a linear from
 // 5120 to 3072 inputs, GELU, a linear from 3072 to 3072) is two tiled products.  The first one's
@@ -664,26 +664,24 @@ __global__ __launch_bounds__(256) void q4_gemm_reduce_kernel(const float *__rest
 }
 
 // ---------------------------------------------------------------------------------------
-// Long chunks without per-block scale arithmetic (the split product).  A dequantised weight
-// w = (code - 8) * d is exact in fp32 with at most 14 significant bits, so it is the exact sum of
-// two bf16 values: hi = w with the low 16 bits of its fp32 pattern cleared (8 significant bits)
-// and lo = w - hi (at most 6 significant bits, exact).  Y = X W^T then runs as two bf16 products
-// per Q4_0 block, X HI^T + X LO^T, every product exact and accumulated in fp32: the scale sits
-// inside the operands, so no vector instruction runs per output and block, and a weight costs a
-// handful of vector instructions once per 128 rows of X.  The price is twice the matrix-core
-// work of the product as defined.
+// Long chunks on 128 x 128 tiles (the wide product).  Each Q4_0 block of a 32 x 32 output block
+// is two v_mfma_f32_32x32x16_bf16 products on the exact operands 16 (code - 8) into a zeroed
+// temporary, which 16 fp32 multiply-adds per lane scale by the block's d / 16 into the
+// accumulator.  The 32 x 32 x 16 product does twice the work of a 16 x 16 x 32 one in about the
+// same issue time, and a wave's unpacked block serves 128 rows.
 //
 // Workgroup: 4 waves per K group, a 128 x 128 tile of Y.  Wave w of a group owns columns 32w ..
-// 32w+31 for all 128 rows (four 32 x 32 output blocks of v_mfma_f32_32x32x16_bf16) over the group's
-// blocks of each stage, so each weight is unpacked once, in the registers of the wave that uses it.
-// K runs in stages of 4 Q4_0 blocks (128 inputs): the stage's activations (128 rows x 128 bf16,
-// rows padded by 16 bytes) and raw weight bytes (128 columns x 72 bytes) go through LDS, and the
-// loads of a later stage are in flight in registers while the current one is computed.  Operand layouts of the 32 x 32 x 16 product: lane L of A holds row
-// L % 32, inputs 8(L/32) .. 8(L/32)+7 of a 16-input step; lane L of B holds column L % 32 and the
-// same inputs; result register r of lane L is row 8(r/4) + 4(L/32) + r % 4, column L % 32.  A Q4_0
-// block is two steps, its low nibbles (inputs 0-15) then its high nibbles (16-31); lane group g
-// takes code bytes 8g .. 8g+7 in both.  Workgroup z of the grid's third dimension takes stages
-// z*NS .. z*NS+NS-1 and, when part is set, writes its partial tile to part[z] instead of y.
+// 32w+31 for all 128 rows (four 32 x 32 output blocks) over the group's blocks of each stage, so
+// each weight is unpacked once, in the registers of the wave that uses it.  K runs in stages of 4
+// Q4_0 blocks (128 inputs): the stage's activations (128 rows x 128 bf16, rows padded by 16 bytes)
+// and raw weight bytes (128 columns x 72 bytes) go through LDS, and the loads of a later stage are
+// in flight in registers while the current one is computed.  Operand layouts of the 32 x 32 x 16
+// product: lane L of A holds row L % 32, inputs 8(L/32) .. 8(L/32)+7 of a 16-input step; lane L of
+// B holds column L % 32 and the same inputs; result register r of lane L is row 8(r/4) + 4(L/32) +
+// r % 4, column L % 32, so a lane's 16 results share one column and one scale.  A Q4_0 block is
+// two steps, its low nibbles (inputs 0-15) then its high nibbles (16-31); lane group g takes code
+// bytes 8g .. 8g+7 in both.  Workgroup z of the grid's third dimension takes stages z*NS ..
+// z*NS+NS-1 and, when part is set, writes its partial tile to part[z] instead of y.
 // ---------------------------------------------------------------------------------------
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 
@@ -697,67 +695,40 @@ constexpr int GH_W_PER = (GH_W_PIECES + GH_THREADS - 1) / GH_THREADS;   // 5
 static_assert(GH_A_PER * GH_THREADS * 8 == GH_BM * GH_STAGE, "the threads cover a stage of A");
 static_assert(GH_RAW % 8 == 0, "a column's stage bytes are whole 8-byte pieces");
 
-// hi and lo bf16 parts of w = (code - 8) * d for the four codes of bytes 0..3 of c (nibble values
-// 0..15 in the low 4 bits of each byte), packed in weight order: two dwords each.
-__device__ __forceinline__ void split_pairs(uint32_t c, float d, float m8d, uint32_t &h01, uint32_t &h23, uint32_t &l01,
-                                            uint32_t &l23)
+// Exact B operands 16 (code - 8) of block `blk` for this lane's column (both 16-input steps) and the
+// block's scale d / 16, from the column's raw stage bytes in LDS.
+__device__ __forceinline__ void unpack_codes(const uint32_t *col, int blk, int g, bf16x8 (&bq)[2], float &ds)
 {
-    float wv[4], lv[4];
-    uint32_t hb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        wv[j] = fmaf(ubyte_to_f(c, j), d, m8d);   // (code - 8) * d, exact
-        hb[j] = __builtin_bit_cast(uint32_t, wv[j]) & 0xFFFF0000u;
-        lv[j] = wv[j] - __builtin_bit_cast(float, hb[j]);   // exact, at most 6 significant bits
-    }
-    h01 = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
-    h23 = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
-    l01 = pack_bf16_pair(lv[0], lv[1]);
-    l23 = pack_bf16_pair(lv[2], lv[3]);
-}
-
-// B operands (hi and lo, both 16-input steps) of block `blk` of the stage for this lane's column,
-// from the column's raw stage bytes in LDS (dword aligned, GH_RAW bytes).
-__device__ __forceinline__ void unpack_split(const uint32_t *col, int blk, int g, bf16x8 (&bhi)[2], bf16x8 (&blo)[2])
-{
-    const int base = 18 * blk;   // first byte of the block: 4-aligned for even blocks, 2 mod 4 for odd
+    const int base = 18 * blk;
     uint32_t d16, c0, c1;
     if ((blk & 1) == 0) {
         d16 = col[base >> 2] & 0xFFFFu;
-        const uint32_t *q = col + ((base + 2 + 8 * g) >> 2);   // code bytes start 2 mod 4
+        const uint32_t *q = col + ((base + 2 + 8 * g) >> 2);
         const uint32_t q0 = q[0], q1 = q[1], q2 = q[2];
         c0 = __builtin_amdgcn_alignbyte(q1, q0, 2);
         c1 = __builtin_amdgcn_alignbyte(q2, q1, 2);
     } else {
         d16 = col[(base - 2) >> 2] >> 16;
-        const uint32_t *q = col + ((base + 2 + 8 * g) >> 2);   // code bytes 4-aligned
+        const uint32_t *q = col + ((base + 2 + 8 * g) >> 2);
         c0 = q[0];
         c1 = q[1];
     }
-    const float d = half_bits_to_float(d16);
-    const float m8d = -8.0f * d;
-    uint32_t h[4], l[4];
-    // low nibbles: the block's inputs 8g .. 8g+7 of the first step
-    split_pairs(c0 & 0x0F0F0F0Fu, d, m8d, h[0], h[1], l[0], l[1]);
-    split_pairs(c1 & 0x0F0F0F0Fu, d, m8d, h[2], h[3], l[2], l[3]);
-    bhi[0] = __builtin_bit_cast(bf16x8, u32x4v{h[0], h[1], h[2], h[3]});
-    blo[0] = __builtin_bit_cast(bf16x8, u32x4v{l[0], l[1], l[2], l[3]});
-    // high nibbles: inputs 16 + 8g .. of the second step
-    split_pairs((c0 >> 4) & 0x0F0F0F0Fu, d, m8d, h[0], h[1], l[0], l[1]);
-    split_pairs((c1 >> 4) & 0x0F0F0F0Fu, d, m8d, h[2], h[3], l[2], l[3]);
-    bhi[1] = __builtin_bit_cast(bf16x8, u32x4v{h[0], h[1], h[2], h[3]});
-    blo[1] = __builtin_bit_cast(bf16x8, u32x4v{l[0], l[1], l[2], l[3]});
+    bq[0] = __builtin_bit_cast(bf16x8, nibbles_to_bf16_x16(c0, c1, 4u));   // low nibbles: first step
+    bq[1] = __builtin_bit_cast(bf16x8, nibbles_to_bf16_x16(c0, c1, 0u));   // high nibbles: second step
+    float d = half_bits_to_float(d16) * 0.0625f;   // exact: the operands were 16 (code - 8)
+    asm volatile("" : "+v"(d));   // an fp32 scale, so the multiply-adds are v_fmac_f32
+    ds = d;
 }
 
 // KW: wave groups splitting K inside the workgroup.  Group kg (waves 4 kg .. 4 kg + 3) takes
 // blocks kg * GH_KC / KW .. of every stage, so each weight is still unpacked once, by the one wave
-// that uses it; with KW = 2 every SIMD runs two waves, one's MFMAs covering the other's unpacking
-// and LDS reads.  The groups' partial tiles are added through LDS at the end, group 0's first.
+// that uses it; with KW = 2 every SIMD runs two waves, one's products covering the other's vector
+// work and LDS reads.  The groups' partial tiles are added through LDS at the end, group 0's first.
 // LDS holds two stages: the waves store stage s + 1 (loaded from memory during stage s - 1) into
 // the other buffer after their first block of stage s, then issue the loads of stage s + 2, so one
 // barrier per stage suffices.
 template <int NS, int KW>
-__global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_split_kernel(
+__global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_wide_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, float *__restrict__ part,
     int m, int n, int k)
 {
@@ -785,12 +756,14 @@ __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu
 
     // activations: piece p = tid + NT j is row p / 16, inputs 8 (p % 16) .. of the stage (rows past
     // m repeat the last row; their outputs are not stored)
+    // (32-bit byte offsets, the stage's added each time: below 2^32 since m k and the weight bytes
+    // are below 2^31, so a load takes the uniform base and one offset register)
     uint32_t aoff[A_PER];
     int alds[A_PER];
 #pragma unroll
     for (int j = 0; j < A_PER; ++j) {
         const int p = tid + NT * j, r = p >> 4, c = p & 15;
-        aoff[j] = (uint32_t)min(m0 + r, m - 1) * (uint32_t)k + (uint32_t)(8 * c);
+        aoff[j] = 2u * ((uint32_t)min(m0 + r, m - 1) * (uint32_t)k + (uint32_t)(8 * c));
         alds[j] = r * GH_AROW + 8 * c;
     }
     // weights: piece q is column q / 9, bytes 8 (q % 9) .. of its stage bytes; pieces past the last
@@ -807,15 +780,15 @@ __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu
 
     u32x4v ar[A_PER];
     u32x2v wr[W_PER];
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
     auto load_stage = [&](int st) {
-        const uint16_t *xs = x + (size_t)st * GH_STAGE;
+        const uint32_t xo = (uint32_t)st * (GH_STAGE * 2), wo = (uint32_t)st * GH_RAW;
 #pragma unroll
         for (int j = 0; j < A_PER; ++j)
-            ar[j] = *reinterpret_cast<const u32x4v *>(xs + aoff[j]);
-        const uint8_t *ws = w + (size_t)st * GH_RAW;
+            ar[j] = *reinterpret_cast<const u32x4v *>(xb + (aoff[j] + xo));
 #pragma unroll
         for (int j = 0; j < W_PER; ++j)
-            wr[j] = *reinterpret_cast<const u32x2v *>(ws + woff[j]);
+            wr[j] = *reinterpret_cast<const u32x2v *>(w + (woff[j] + wo));
     };
     auto store_stage = [&](int buf) {
 #pragma unroll
@@ -826,46 +799,66 @@ __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu
             *reinterpret_cast<u32x2v *>(&wraw[buf * W_BUF + wlds[j]]) = wr[j];
     };
 
-    f32x16v acc[MI];
+    f32x16v acc[MI], t[MI];   // t: the last block's unscaled products
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
         acc[i] = 0.0f;
+        t[i] = 0.0f;
+    }
+    float dprev = 0.0f;   // the last block's scale
 
     load_stage(st0);
     store_stage(0);
     if (NS > 1)
         load_stage(st0 + 1);
     __syncthreads();
-    for (int s = 0; s < NS; ++s) {
-        const int cur = s & 1;
+    // block b of the stage in buffer cur.  The previous block's products are scaled into the
+    // accumulators while this block's products of the tile before are in flight.
+    auto block = [&](int cur, int b) {
         const uint32_t *colw = wraw + cur * W_BUF + (32 * wn + l32) * (GH_RAW / 4);
         const uint16_t *arow = as + cur * A_BUF + l32 * GH_AROW + 8 * g;
+        bf16x8 bq[2];
+        float ds;
+        unpack_codes(colw, b, g, bq, ds);
+        bf16x8 af[MI][2];
 #pragma unroll
-        for (int bb = 0; bb < BPW; ++bb) {
-            const int b = kg * BPW + bb;
-            bf16x8 bhi[2], blo[2];
-            unpack_split(colw, b, g, bhi, blo);
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bf16x8 af[MI];
+            for (int h = 0; h < 2; ++h)
+                af[i][h] = *reinterpret_cast<const bf16x8 *>(arow + 32 * i * GH_AROW + 32 * b + 16 * h);
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    af[i] = *reinterpret_cast<const bf16x8 *>(arow + 32 * i * GH_AROW + 32 * b + 16 * h);
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bhi[h], acc[i], 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], blo[h], acc[i], 0, 0, 0);
-            }
-            if (bb == 0 && s + 1 < NS) {
-                store_stage(cur ^ 1);   // the other buffer was last read in stage s - 1
-                if (s + 2 < NS)
-                    load_stage(st0 + s + 2);
-            }
+        for (int i = 0; i < MI; ++i) {
+            acc[i] += dprev * t[i];
+            t[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][0], bq[0], (f32x16v)0.0f, 0, 0, 0);
+            t[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][1], bq[1], t[i], 0, 0, 0);
         }
+        dprev = ds;
+        // one product, then eight vector instructions
+#pragma unroll
+        for (int i = 0; i < 2 * MI; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+    };
+    // one straight-line body per stage: after its first block the waves store the next stage
+    // (loaded during the stage before) into the other buffer, last read in the stage before, and
+    // load the one after (past the last stage: a harmless reload of it)
+    for (int s = 0; s + 1 < NS; ++s) {
+        const int cur = s & 1;
+        block(cur, kg * BPW);
+        store_stage(cur ^ 1);
+        load_stage(min(st0 + s + 2, st0 + NS - 1));
+#pragma unroll
+        for (int bb = 1; bb < BPW; ++bb)
+            block(cur, kg * BPW + bb);
         __syncthreads();
     }
+#pragma unroll
+    for (int bb = 0; bb < BPW; ++bb)
+        block((NS - 1) & 1, kg * BPW + bb);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+        acc[i] += dprev * t[i];
 
     if constexpr (KW > 1) {
         // groups 1.. leave their partial tiles in LDS (the stage buffers are free after the last
@@ -957,6 +950,25 @@ static void launch_tiled_slices(const void *w, const uint16_t *x, float *y, uint
 // Output: y (fp32), or for T_GELU_OUT GELU pairs in hl (n a multiple of 256).  part: slices x m x n
 // floats when slices > 1, else null (the kernel then writes the output itself).  k: the
 // activations' row length.
+// y (or GELU pairs in hl) = the sum of `slices` partial tiles part[z][m][n], added in order z = 0, 1, ...
+template <bool GELU>
+static int launch_slice_sum(const float *part, float *y, uint16_t *hl, int m, int n, int slices, hipStream_t s)
+{
+    const int64_t count = (int64_t)m * n;
+    const bool vec4 = count % 4 == 0 && (GELU ? n % 4 == 0 : aligned(y, 16));
+    const int64_t threads = vec4 ? count / 4 : count;
+    const dim3 rg((unsigned)((threads + 255) / 256));
+    if (slices <= 2)
+        hipLaunchKernelGGL((q4_gemm_reduce_kernel<GELU, 2>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
+    else if (slices <= 4)
+        hipLaunchKernelGGL((q4_gemm_reduce_kernel<GELU, 4>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
+    else if (slices <= 8)
+        hipLaunchKernelGGL((q4_gemm_reduce_kernel<GELU, 8>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
+    else
+        hipLaunchKernelGGL((q4_gemm_reduce_kernel<GELU, 0>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
+    return check_launch("q4 product: slice sum");
+}
+
 template <int MODE>
 static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_t *hl, float *part, int m, int n,
                              int k, int slices, hipStream_t s)
@@ -981,65 +993,66 @@ static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_
     case 1: launch_tiled_slices<1, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
     default: return fail(VOX_E_UNSUPPORTED, "q4 tiled product: no compiled stage count for k=%d in %d slices", k, slices);
     }
-    int st = check_launch("q4 tiled product");
-    if (st || slices == 1)
-        return st;
-    const int64_t count = (int64_t)m * n;
-    const bool vec4 = count % 4 == 0 && (gelu ? n % 4 == 0 : aligned(y, 16));
-    const int64_t threads = vec4 ? count / 4 : count;
-    const dim3 rg((unsigned)((threads + 255) / 256));
-    if (slices <= 2)
-        hipLaunchKernelGGL((q4_gemm_reduce_kernel<gelu, 2>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
-    else if (slices <= 4)
-        hipLaunchKernelGGL((q4_gemm_reduce_kernel<gelu, 4>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
-    else if (slices <= 8)
-        hipLaunchKernelGGL((q4_gemm_reduce_kernel<gelu, 8>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
-    else
-        hipLaunchKernelGGL((q4_gemm_reduce_kernel<gelu, 0>), rg, dim3(256), 0, s, part, y, hl, count, n, slices, vec4);
-    return check_launch("q4 tiled product: slice sum");
+    const int st = check_launch("q4 tiled product");
+    return st || slices == 1 ? st : launch_slice_sum<gelu>(part, y, hl, m, n, slices, s);
 }
 
-// The split product (q4_gemm_split_kernel) runs where its 128 x 128 tiles alone give at least
-// SPLIT_MIN_WGS workgroups and the chunk has at least SPLIT_MIN_M rows (the unpack of a weight is
-// repaid over 128 rows).  Measured on MI355X against the tiled kernel: 750 x 5120 x 1280 28.5
-// against 34.4 us; with K split over the grid to reach the workgroup count (750 x 1280 x 1280, five
-// slices of two stages, and the slice sum) 22 against 12.9 us, so it never splits K.  Two wave
-// groups splitting K inside the workgroup (two waves per SIMD) with one barrier per stage: 27.6 to
-// 28.0 us against 29.3 for four waves with two barriers per stage (30.4 with one); eight waves
-// each 32 x 64 (every weight unpacked twice): 30.5 us; eight-block stages: no faster.  Timed over
-// K at 750 x 5120, a stage costs 1.89 us (its 64 matrix-core products per SIMD take about 1.0 us
-// at the 37-40 cycles per v_mfma_f32_32x32x16_bf16 measured in a loop of independent products)
-// and a launch 9 us besides (the 15.4 MB output store alone about 3 us).
-constexpr int64_t SPLIT_MIN_M = 256;
-constexpr int SPLIT_MIN_WGS = 240;
-constexpr int SPLIT_KW = 2;   // wave groups splitting K per workgroup
+// The wide product (q4_gemm_wide_kernel) takes chunks of at least WIDE_MIN_M rows whose 128 x 128
+// tiles, with K split over the grid into slices of at least WIDE_MIN_STAGES stages where needed
+// (the partial tiles in the caller's workspace, then the slice sum), give at least WIDE_MIN_WGS
+// workgroups.  Measured on MI355X: 750 x 5120 x 1280 22.4 us, 750 x 5120 x 5120 64.1 us (a stage
+// 1.39 us, a launch about 8.5 us besides); the same tiles with the exact hi and lo bf16 parts of
+// every weight as B operands (twice the products, no per-block scale) took 27.4 and 83.7 us.
+// Two wave groups splitting K inside the workgroup (two waves per SIMD) with one barrier per
+// stage: 27.6 to 28.0 us against 29.3 for four waves with two barriers per stage (30.4 with one)
+// in the hi/lo form; eight waves each 32 x 64 (every weight unpacked twice): 30.5 us; eight-block
+// stages: no faster.
+constexpr int64_t WIDE_MIN_M = 256;
+constexpr int WIDE_MIN_WGS = 160;
+constexpr int WIDE_MIN_STAGES = 10;
+constexpr int WIDE_KW = 2;   // wave groups splitting K per workgroup
 
-static bool split_shape(int64_t m, int64_t n, int64_t k)
+// Slices of K over the grid for the wide product: 1 (unsplit), more (a workspace of that many
+// partial tiles), or 0 where the wide product does not take the shape.
+static int wide_slices(int64_t m, int64_t n, int64_t k)
 {
     const size_t wbytes = (size_t)n * (size_t)(k / 32) * 18;
+    if (!tiled_k(k) || m < WIDE_MIN_M || (uint64_t)m * (uint64_t)k >= (1ull << 31) || wbytes >= (1ull << 31) ||
+        (m + GH_BM - 1) / GH_BM > 65535)
+        return 0;
     const int64_t tiles = ((n + GH_BN - 1) / GH_BN) * ((m + GH_BM - 1) / GH_BM);
-    return tiled_k(k) && m >= SPLIT_MIN_M && tiles >= SPLIT_MIN_WGS && (uint64_t)m * (uint64_t)k < (1ull << 31) &&
-           wbytes < (1ull << 31) && (m + GH_BM - 1) / GH_BM <= 65535;
+    const int nst = (int)(k / GH_STAGE);
+    for (int ks = 1; nst / ks >= WIDE_MIN_STAGES; ++ks)
+        if (nst % ks == 0 && tiles * ks >= WIDE_MIN_WGS)
+            return ks;
+    return 0;
 }
 
 template <int NS>
-static void launch_split_ns(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
+static void launch_wide_ns(const void *w, const uint16_t *x, float *y, float *part, int m, int n, int k, int slices,
+                           hipStream_t s)
 {
-    const dim3 grid((unsigned)((n + GH_BN - 1) / GH_BN), (unsigned)((m + GH_BM - 1) / GH_BM), 1u);
-    hipLaunchKernelGGL((q4_gemm_split_kernel<NS, SPLIT_KW>), grid, dim3(GH_THREADS * SPLIT_KW), 0, s,
-                       (const uint8_t *)w, x, y, (float *)nullptr, m, n, k);
+    const dim3 grid((unsigned)((n + GH_BN - 1) / GH_BN), (unsigned)((m + GH_BM - 1) / GH_BM), (unsigned)slices);
+    hipLaunchKernelGGL((q4_gemm_wide_kernel<NS, WIDE_KW>), grid, dim3(GH_THREADS * WIDE_KW), 0, s,
+                       (const uint8_t *)w, x, y, part, m, n, k);
 }
 
-// y = X W^T through the split product (K = 1280, 3072 or 5120: 10, 24 or 40 stages).
-static int launch_gemm_split(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
+// y = X W^T through the wide product; part holds `slices` partial tiles when K is split.
+static int launch_gemm_wide(const void *w, const uint16_t *x, float *y, float *part, int m, int n, int k, int slices,
+                            hipStream_t s)
 {
-    switch (k / GH_STAGE) {
-    case 40: launch_split_ns<40>(w, x, y, m, n, k, s); break;
-    case 24: launch_split_ns<24>(w, x, y, m, n, k, s); break;
-    case 10: launch_split_ns<10>(w, x, y, m, n, k, s); break;
-    default: return fail(VOX_E_UNSUPPORTED, "q4 split product: no compiled stage count for k=%d", k);
+    if ((slices > 1) != (part != nullptr))
+        return fail(VOX_E_INVAL, "q4 wide product: a partial-tile buffer exactly when K is split");
+    switch ((k / GH_STAGE) / slices) {   // stages per workgroup
+    case 40: launch_wide_ns<40>(w, x, y, part, m, n, k, slices, s); break;
+    case 24: launch_wide_ns<24>(w, x, y, part, m, n, k, slices, s); break;
+    case 20: launch_wide_ns<20>(w, x, y, part, m, n, k, slices, s); break;
+    case 12: launch_wide_ns<12>(w, x, y, part, m, n, k, slices, s); break;
+    case 10: launch_wide_ns<10>(w, x, y, part, m, n, k, slices, s); break;
+    default: return fail(VOX_E_UNSUPPORTED, "q4 wide product: no compiled stage count for k=%d in %d slices", k, slices);
     }
-    return check_launch("q4 split product");
+    const int st = check_launch("q4 wide product");
+    return st || slices == 1 ? st : launch_slice_sum<false>(part, y, nullptr, m, n, slices, s);
 }
 
 // The skinny kernel takes the products of at most 16 rows at K = 1280 or 3072 (one 16-row tile;
@@ -1092,7 +1105,9 @@ extern "C" size_t vox_q4_gemm_workspace(int64_t m, int64_t n, int64_t k)
 {
     if (m <= 0 || n <= 0 || k <= 0 || k % 32 || m > 65535 * 16 || n > (1 << 24) || k > (1 << 24))
         return 0;
-    if (split_shape(m, n, k) || skinny_shape(m, n, k))
+    if (const int ws = wide_slices(m, n, k))
+        return ws > 1 ? tiled_workspace(m, n, ws) : 0;
+    if (skinny_shape(m, n, k))
         return 0;
     if (!tiled_shape(m, n, k))
         return 0;
@@ -1120,8 +1135,15 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
         return fail(VOX_E_INVAL, "vox_q4_gemm: workspace and workspace_bytes must be both set or both zero");
     hipStream_t s = (hipStream_t)stream;
     int st;
-    if (aligned(x_bf16, 16) && aligned(w_q4, 16) && split_shape(m, n, k)) {
-        st = launch_gemm_split(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
+    const int wide = aligned(x_bf16, 16) && aligned(w_q4, 16) ? wide_slices(m, n, k) : 0;
+    if (wide == 1 || (wide > 1 && workspace)) {
+        const size_t need = wide > 1 ? tiled_workspace(m, n, wide) : 0;
+        if (need > workspace_bytes)
+            return fail(VOX_E_WORKSPACE, "vox_q4_gemm: workspace of %zu bytes, need %zu", workspace_bytes, need);
+        if (need && (!aligned(workspace, 16) || overlaps(workspace, need, y, ybytes) ||
+                     overlaps(workspace, need, x_bf16, xbytes) || overlaps(workspace, need, w_q4, wbytes)))
+            return fail(VOX_E_INVAL, "vox_q4_gemm: workspace must be 16-byte aligned and apart from x, y and w");
+        st = launch_gemm_wide(w_q4, x_bf16, y, wide > 1 ? (float *)workspace : nullptr, (int)m, (int)n, (int)k, wide, s);
     } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && skinny_shape(m, n, k)) {
         st = launch_gemm_skinny(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
     } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_shape(m, n, k)) {

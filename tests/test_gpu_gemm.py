@@ -85,7 +85,8 @@ def test_gemm_ragged(vx, orc, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(70, 96, 1280), (64, 1280, 5120), (300, 200, 1280), (257, 130, 5120),
-                                   (750, 1280, 1280), (256, 3072, 3072), (260, 10300, 1280), (16, 1280, 5120)])
+                                   (750, 1280, 1280), (256, 3072, 3072), (260, 10300, 1280), (16, 1280, 5120),
+                                   (750, 1280, 5120), (600, 2000, 3072)])
 def test_gemm_exact_dyadic(vx, orc, m, n, k):
     # small-integer activations and power-of-two scales: every product and partial sum is exact,
     # so the matrix-core result must equal the oracle bit for bit (also when K is split)
@@ -103,14 +104,28 @@ def test_gemm_exact_dyadic(vx, orc, m, n, k):
         assert np.array_equal(_gemm(vx, w, xb, m, n, k, split=False).astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("m,n,k", [(750, 5120, 1280), (770, 5120, 3072), (1023, 3850, 5120), (260, 10300, 1280)])
-def test_gemm_split_product_ragged(vx, orc, m, n, k):
-    # long chunks with many 128 x 128 tiles run the split product (hi + lo bf16 parts of every
-    # weight): edges in both dimensions, every K
+@pytest.mark.parametrize("m,n,k", [(750, 5120, 1280), (770, 5120, 3072), (1023, 3850, 5120), (260, 10300, 1280),
+                                   (750, 3840, 1280)])
+def test_gemm_wide_ragged(vx, orc, m, n, k):
+    # long chunks with many 128 x 128 tiles run the wide product unsplit: edges in both
+    # dimensions, every K
     w, xb = synth.gemm_inputs(620 + m, m, n, k)
-    say(f"gemm split product m={m} n={n} k={k}")
+    say(f"gemm wide m={m} n={n} k={k}")
     assert vx.q4_gemm_workspace(m, n, k) == 0
-    assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm split {m}x{n}x{k}")
+    assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm wide {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k,slices", [(750, 1280, 5120, 4), (1000, 1100, 5120, 4), (400, 3000, 5120, 2),
+                                          (600, 2000, 3072, 2)])
+def test_gemm_wide_k_slices(vx, orc, m, n, k, slices):
+    # the wide product with K split over the grid (10, 20 and 12 stages per slice) and the slice
+    # sum; without a workspace the same call runs unsplit on the tiled kernel
+    assert vx.q4_gemm_workspace(m, n, k) == slices * m * n * 4
+    w, xb = synth.gemm_inputs(630 + m, m, n, k)
+    say(f"gemm wide sliced m={m} n={n} k={k}")
+    ref = orc.q4_gemm(w, xb)
+    assert_close(_gemm(vx, w, xb, m, n, k), ref, f"gemm wide sliced {m}x{n}x{k}")
+    assert_close(_gemm(vx, w, xb, m, n, k, split=False), ref, f"gemm {m}x{n}x{k} without workspace")
 
 
 def test_gemm_fused_qkv_equals_separate(vx, orc):
@@ -126,10 +141,19 @@ def test_gemm_fused_qkv_equals_separate(vx, orc):
             assert_close(got[:, 1280 * i:1280 * (i + 1)], orc.q4_gemm(w, xb), f"fused qkv part {i} m={m}")
 
 
-def test_gemm_split_product_repeatable(vx):
+def test_gemm_wide_repeatable(vx):
     m, n, k = 750, 5120, 1280
     w, xb = synth.gemm_inputs(616, m, n, k)
     assert np.array_equal(_gemm(vx, w, xb, m, n, k), _gemm(vx, w, xb, m, n, k))
+    # sliced: fixed slice order, also with a dirty, larger workspace
+    m, n, k = 750, 1280, 5120
+    w, xb = synth.gemm_inputs(617, m, n, k)
+    a = _gemm(vx, w, xb, m, n, k)
+    assert np.array_equal(a, _gemm(vx, w, xb, m, n, k))
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    big = torch.full((vx.q4_gemm_workspace(m, n, k) + 4096,), 0x7F, dtype=torch.uint8, device="cuda")
+    vx.q4_gemm(dev(w), dev(xb), y, m=m, n=n, k=k, workspace=big)
+    assert np.array_equal(host(y), a)
 
 
 def test_gemm_row_matches_gemv(vx):
