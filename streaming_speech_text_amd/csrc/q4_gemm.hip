@@ -727,10 +727,12 @@ __device__ __forceinline__ void unpack_codes(const uint32_t *col, int blk, int g
 // LDS holds two stages: the waves store stage s + 1 (loaded from memory during stage s - 1) into
 // the other buffer after their first block of stage s, then issue the loads of stage s + 2, so one
 // barrier per stage suffices.
-template <int NS, int KW>
+// MODE: T_PLAIN, T_GELU_OUT or T_PAIR_IN as for the tiled kernel (a pair stage reads weight stage
+// st / 2; with K split over the grid a GELU output goes through the slice sum).
+template <int NS, int KW, int MODE>
 __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_wide_kernel(
-    const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, float *__restrict__ part,
-    int m, int n, int k)
+    const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, uint16_t *__restrict__ hl,
+    float *__restrict__ part, int m, int n, int k)
 {
     constexpr int NT = GH_THREADS * KW;
     constexpr int A_PER = GH_A_PER / KW;                        // 16-byte pieces of A per thread
@@ -752,7 +754,8 @@ __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu
     const int m0 = blockIdx.y * GH_BM;
     const int n0 = blockIdx.x * GH_BN;
     const int st0 = blockIdx.z * NS;
-    const uint32_t row_bytes = (uint32_t)(k / 32) * 18;
+    constexpr int KWS = MODE == T_PAIR_IN ? 1 : 0;   // weight stage = activation stage >> KWS
+    const uint32_t row_bytes = (uint32_t)((k >> KWS) / 32) * 18;
 
     // activations: piece p = tid + NT j is row p / 16, inputs 8 (p % 16) .. of the stage (rows past
     // m repeat the last row; their outputs are not stored)
@@ -782,7 +785,7 @@ __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu
     u32x2v wr[W_PER];
     const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
     auto load_stage = [&](int st) {
-        const uint32_t xo = (uint32_t)st * (GH_STAGE * 2), wo = (uint32_t)st * GH_RAW;
+        const uint32_t xo = (uint32_t)st * (GH_STAGE * 2), wo = (uint32_t)(st >> KWS) * GH_RAW;
 #pragma unroll
         for (int j = 0; j < A_PER; ++j)
             ar[j] = *reinterpret_cast<const u32x4v *>(xb + (aoff[j] + xo));
@@ -883,6 +886,7 @@ __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu
                     acc[i][r] += red[((((q - 1) * 4 + wn) * MI + i) * 16 + r) * 64 + lane];
     }
 
+    const bool gelu = MODE == T_GELU_OUT && !part;   // uniform over the grid
     float *const dst = part ? part + (size_t)blockIdx.z * m * n : y;
     const int col = n0 + 32 * wn + l32;
     if (col < n) {
@@ -891,8 +895,12 @@ __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (row < m)
-                    dst[(size_t)row * n + col] = acc[i][r];
+                if (row < m) {
+                    if (gelu)
+                        store_gelu_pair(hl, n, row, col, acc[i][r]);
+                    else
+                        dst[(size_t)row * n + col] = acc[i][r];
+                }
             }
     }
 }
@@ -1007,17 +1015,18 @@ static int launch_gemm_tiled(const void *w, const uint16_t *x, float *y, uint16_
 // stage: 27.6 to 28.0 us against 29.3 for four waves with two barriers per stage (30.4 with one)
 // in the hi/lo form; eight waves each 32 x 64 (every weight unpacked twice): 30.5 us; eight-block
 // stages: no faster.
-constexpr int64_t WIDE_MIN_M = 256;
+constexpr int64_t WIDE_MIN_M = 128;
 constexpr int WIDE_MIN_WGS = 160;
 constexpr int WIDE_MIN_STAGES = 10;
 constexpr int WIDE_KW = 2;   // wave groups splitting K per workgroup
 
 // Slices of K over the grid for the wide product: 1 (unsplit), more (a workspace of that many
-// partial tiles), or 0 where the wide product does not take the shape.
-static int wide_slices(int64_t m, int64_t n, int64_t k)
+// partial tiles), or 0 where the wide product does not take the shape.  k is the activations' row
+// length; kws = 1 for GELU-pair activations (weights of k / 2 inputs).
+static int wide_slices(int64_t m, int64_t n, int64_t k, int kws = 0)
 {
-    const size_t wbytes = (size_t)n * (size_t)(k / 32) * 18;
-    if (!tiled_k(k) || m < WIDE_MIN_M || (uint64_t)m * (uint64_t)k >= (1ull << 31) || wbytes >= (1ull << 31) ||
+    const size_t wbytes = (size_t)n * (size_t)((k >> kws) / 32) * 18;
+    if (!tiled_k(k >> kws) || m < WIDE_MIN_M || (uint64_t)m * (uint64_t)k >= (1ull << 31) || wbytes >= (1ull << 31) ||
         (m + GH_BM - 1) / GH_BM > 65535)
         return 0;
     const int64_t tiles = ((n + GH_BN - 1) / GH_BN) * ((m + GH_BM - 1) / GH_BM);
@@ -1028,31 +1037,36 @@ static int wide_slices(int64_t m, int64_t n, int64_t k)
     return 0;
 }
 
-template <int NS>
-static void launch_wide_ns(const void *w, const uint16_t *x, float *y, float *part, int m, int n, int k, int slices,
-                           hipStream_t s)
+template <int NS, int MODE>
+static void launch_wide_ns(const void *w, const uint16_t *x, float *y, uint16_t *hl, float *part, int m, int n, int k,
+                           int slices, hipStream_t s)
 {
     const dim3 grid((unsigned)((n + GH_BN - 1) / GH_BN), (unsigned)((m + GH_BM - 1) / GH_BM), (unsigned)slices);
-    hipLaunchKernelGGL((q4_gemm_wide_kernel<NS, WIDE_KW>), grid, dim3(GH_THREADS * WIDE_KW), 0, s,
-                       (const uint8_t *)w, x, y, part, m, n, k);
+    hipLaunchKernelGGL((q4_gemm_wide_kernel<NS, WIDE_KW, MODE>), grid, dim3(GH_THREADS * WIDE_KW), 0, s,
+                       (const uint8_t *)w, x, y, hl, part, m, n, k);
 }
 
-// y = X W^T through the wide product; part holds `slices` partial tiles when K is split.
-static int launch_gemm_wide(const void *w, const uint16_t *x, float *y, float *part, int m, int n, int k, int slices,
-                            hipStream_t s)
+// The wide product; part holds `slices` partial tiles when K is split, and a GELU output (into hl)
+// then goes through the slice sum.
+template <int MODE>
+static int launch_gemm_wide(const void *w, const uint16_t *x, float *y, uint16_t *hl, float *part, int m, int n, int k,
+                            int slices, hipStream_t s)
 {
-    if ((slices > 1) != (part != nullptr))
-        return fail(VOX_E_INVAL, "q4 wide product: a partial-tile buffer exactly when K is split");
+    constexpr bool gelu = MODE == T_GELU_OUT;
+    if ((slices > 1) != (part != nullptr) || (gelu ? (hl == nullptr || n % GELU_STAGE) : y == nullptr))
+        return fail(VOX_E_INVAL, "q4 wide product: one output, and a partial-tile buffer exactly when K is split");
     switch ((k / GH_STAGE) / slices) {   // stages per workgroup
-    case 40: launch_wide_ns<40>(w, x, y, part, m, n, k, slices, s); break;
-    case 24: launch_wide_ns<24>(w, x, y, part, m, n, k, slices, s); break;
-    case 20: launch_wide_ns<20>(w, x, y, part, m, n, k, slices, s); break;
-    case 12: launch_wide_ns<12>(w, x, y, part, m, n, k, slices, s); break;
-    case 10: launch_wide_ns<10>(w, x, y, part, m, n, k, slices, s); break;
+    case 48: launch_wide_ns<48, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 40: launch_wide_ns<40, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 24: launch_wide_ns<24, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 20: launch_wide_ns<20, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 16: launch_wide_ns<16, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 12: launch_wide_ns<12, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
+    case 10: launch_wide_ns<10, MODE>(w, x, y, hl, part, m, n, k, slices, s); break;
     default: return fail(VOX_E_UNSUPPORTED, "q4 wide product: no compiled stage count for k=%d in %d slices", k, slices);
     }
     const int st = check_launch("q4 wide product");
-    return st || slices == 1 ? st : launch_slice_sum<false>(part, y, nullptr, m, n, slices, s);
+    return st || slices == 1 ? st : launch_slice_sum<gelu>(part, y, hl, m, n, slices, s);
 }
 
 // The skinny kernel takes the products of at most 16 rows at K = 1280 or 3072 (one 16-row tile;
@@ -1143,7 +1157,8 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
         if (need && (!aligned(workspace, 16) || overlaps(workspace, need, y, ybytes) ||
                      overlaps(workspace, need, x_bf16, xbytes) || overlaps(workspace, need, w_q4, wbytes)))
             return fail(VOX_E_INVAL, "vox_q4_gemm: workspace must be 16-byte aligned and apart from x, y and w");
-        st = launch_gemm_wide(w_q4, x_bf16, y, wide > 1 ? (float *)workspace : nullptr, (int)m, (int)n, (int)k, wide, s);
+        st = launch_gemm_wide<T_PLAIN>(w_q4, x_bf16, y, nullptr, wide > 1 ? (float *)workspace : nullptr, (int)m,
+                                       (int)n, (int)k, wide, s);
     } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && skinny_shape(m, n, k)) {
         st = launch_gemm_skinny(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
     } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_shape(m, n, k)) {
@@ -1176,10 +1191,28 @@ static size_t adapter_h_bytes(int64_t m, int64_t n_mid)
     return ((size_t)m * (size_t)n_mid * 4 + 255) & ~(size_t)255;
 }
 
+// K slices of the adapter's two products: the wide product's where it takes the shape (wide set),
+// else the tiled kernel's.
+struct AdapterPlan {
+    bool wide1, wide2;
+    int s1, s2;
+};
+static AdapterPlan adapter_plan(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
+{
+    AdapterPlan p;
+    const int w1 = wide_slices(m, n_mid, k), w2 = wide_slices(m, n_out, 2 * n_mid, 1);
+    p.wide1 = w1 > 0;
+    p.wide2 = w2 > 0;
+    p.s1 = w1 > 0 ? w1 : tiled_slices(m, n_mid, k);
+    p.s2 = w2 > 0 ? w2 : tiled_slices(m, n_out, 2 * n_mid);
+    return p;
+}
+
 static size_t adapter_part_bytes(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
 {
-    const size_t a = tiled_workspace(m, n_mid, tiled_slices(m, n_mid, k));
-    const size_t b = tiled_workspace(m, n_out, tiled_slices(m, n_out, 2 * n_mid));
+    const AdapterPlan p = adapter_plan(m, k, n_mid, n_out);
+    const size_t a = tiled_workspace(m, n_mid, p.s1);
+    const size_t b = tiled_workspace(m, n_out, p.s2);
     return a > b ? a : b;
 }
 
@@ -1259,11 +1292,13 @@ extern "C" int vox_adapter(const void *w1_q4, const void *w2_q4, const uint16_t 
     if (m <= 16)
         return adapter_skinny(w1_q4, w2_q4, x_bf16, y, h, (int)m, (int)k, (int)n_mid, (int)n_out, s);
     float *part = (float *)((char *)workspace + adapter_h_bytes(m, n_mid));
-    const int s1 = tiled_slices(m, n_mid, k), s2 = tiled_slices(m, n_out, 2 * n_mid);
-    int st = launch_gemm_tiled<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, s1 > 1 ? part : nullptr, (int)m, (int)n_mid,
-                                           (int)k, s1, s);
+    const AdapterPlan p = adapter_plan(m, k, n_mid, n_out);
+    float *p1 = p.s1 > 1 ? part : nullptr, *p2 = p.s2 > 1 ? part : nullptr;
+    int st = p.wide1 ? launch_gemm_wide<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, p1, (int)m, (int)n_mid, (int)k, p.s1, s)
+                     : launch_gemm_tiled<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, p1, (int)m, (int)n_mid, (int)k, p.s1, s);
     if (!st)
-        st = launch_gemm_tiled<T_PAIR_IN>(w2_q4, h, y, nullptr, s2 > 1 ? part : nullptr, (int)m, (int)n_out,
-                                          (int)(2 * n_mid), s2, s);
+        st = p.wide2 ? launch_gemm_wide<T_PAIR_IN>(w2_q4, h, y, nullptr, p2, (int)m, (int)n_out, (int)(2 * n_mid), p.s2, s)
+                     : launch_gemm_tiled<T_PAIR_IN>(w2_q4, h, y, nullptr, p2, (int)m, (int)n_out, (int)(2 * n_mid),
+                                                    p.s2, s);
     return st ? st : ok();
 }

@@ -46,12 +46,23 @@ def test_adapter_ragged(vx, orc, m, k, n_mid, n_out):
     assert_close(_adapter(vx, w1, w2, xb, n_out), orc.adapter(w1, w2, xb), f"adapter {m} {k}->{n_mid}->{n_out}")
 
 
-@pytest.mark.parametrize("m", [40, 9])
-def test_adapter_gelu_between_the_linears(vx, orc, m):
+@pytest.mark.parametrize("m,k,n_mid,n_out", [(190, 5120, 3072, 3000), (520, 5120, 1280, 2000),
+                                             (800, 1280, 3072, 3072)])
+def test_adapter_wide(vx, orc, m, k, n_mid, n_out):
+    # longer chunks through the 128 x 128 tile product: GELU output with K split over the grid
+    # (through the slice sum) and unsplit (stored by the product), pair input split and unsplit
+    say(f"adapter wide m={m} {k}->{n_mid}->{n_out}")
+    w1, w2, xb = synth.adapter_inputs(710 + m, m, k, n_mid, n_out)
+    assert_close(_adapter(vx, w1, w2, xb, n_out), orc.adapter(w1, w2, xb), f"adapter {m} {k}->{n_mid}->{n_out}")
+
+
+@pytest.mark.parametrize("m,n_mid", [(40, 1280), (9, 1280), (187, 3072)])
+def test_adapter_gelu_between_the_linears(vx, orc, m, n_mid):
     # W2 = identity (code 9 on the diagonal, 8 elsewhere, scale 1): Y = GELU(X W1^T).  The GELU
     # value travels as a bf16 pair within 2^-18 of its fp32 value, so this holds well inside the
-    # usual bound (m = 9: both products through the kernel for at most 16 rows).
-    k, n_mid = 5120, 1280
+    # usual bound (m = 9: both products through the kernel for at most 16 rows; m = 187: through
+    # the 128 x 128 tile product).
+    k = 5120
     g = synth.generator(720)
     w1 = synth.q4_matrix(g, n_mid, k)
     xb = synth.bf16_normal(g, (m, k))
@@ -69,9 +80,10 @@ def test_adapter_gelu_between_the_linears(vx, orc, m):
     assert (h < -2).any() and np.all(np.abs(got[h < -2]) < 0.1)
 
 
-def test_adapter_repeatable(vx):
+@pytest.mark.parametrize("m", [16, 187])
+def test_adapter_repeatable(vx, m):
     # fixed summation order: two calls agree bit for bit, also with a larger, differently dirty workspace
-    m, (k, n_mid, n_out) = 16, synth.ADAPTER
+    k, n_mid, n_out = synth.ADAPTER
     w1, w2, xb = synth.adapter_inputs(721, m, k, n_mid, n_out)
     a = _adapter(vx, w1, w2, xb, n_out)
     b = _adapter(vx, w1, w2, xb, n_out, extra=4096, fill=0x3C)
