@@ -20,8 +20,8 @@
 //    B holds (code - 8).  Lane group g (= lane / 16) takes code bytes 4g..4g+3, i.e. inputs
 //    {4g..4g+3} (low nibbles) then {16+4g..16+4g+3} (high nibbles), and the activations of
 //    the same inputs (the MFMA's k slots may hold the inputs in any order A and B agree on).
-//  * at most 16 rows at K = 1280 or 3072: the skinny kernel (16-column tiles whose weights for the
-//    whole of K are staged through LDS in one round trip, the same per-block products);
+//  * at most 16 rows at K = 1280, 3072 or 5120: the skinny kernel (16-column tiles whose weights for
+//    the whole of K are staged through LDS in one round trip, the same per-block products);
 //  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS),
 //    optionally with K split over workgroups (partial tiles in the caller's workspace, added in
 //    a fixed order by a second kernel).
@@ -225,14 +225,38 @@ __global__ __launch_bounds__(64 * WAVES) void q4_gemm_kernel(const uint8_t *__re
     }
 }
 
+// 16 (code - 8) for 8 codes taken from one nibble of 8 bytes (lo: bytes 0-3, hi: 4-7), exact in
+// bf16.  sh = 4 moves low nibbles to the top of their bytes (high nibbles: sh = 0); flipping the
+// top bit then leaves a byte that, read as a signed integer, is 16 (code - 8), because code ^ 8 is
+// code - 8 as a 4-bit two's complement number.  One sign-extending byte conversion per value.
+// (Feeding the raw codes and adding -8 times the activations' block sum through the accumulator
+// saves more but cancels two sums of size 8 sum|a|: measured on MI355X, no faster, and its
+// rounding shows where the weights are sparse.)
+__device__ __forceinline__ u32x4v nibbles_to_bf16_x16(uint32_t lo, uint32_t hi, uint32_t sh)
+{
+    const uint32_t a = ((lo << sh) & 0xF0F0F0F0u) ^ 0x80808080u;
+    const uint32_t b = ((hi << sh) & 0xF0F0F0F0u) ^ 0x80808080u;
+    u32x4v p;
+    p.x = pack_bf16_pair((float)(int8_t)a, (float)(int8_t)(a >> 8));
+    p.y = pack_bf16_pair((float)(int8_t)(a >> 16), (float)(int8_t)(a >> 24));
+    p.z = pack_bf16_pair((float)(int8_t)b, (float)(int8_t)(b >> 8));
+    p.w = pack_bf16_pair((float)(int8_t)(b >> 16), (float)(int8_t)(b >> 24));
+    return p;
+}
+
 // ---------------------------------------------------------------------------------------
-// Skinny products (at most 16 rows of X, K of 1280 or 3072): one workgroup of 8 waves per 16
+// Skinny products (at most 16 rows of X, K of 1280, 3072 or 5120): one workgroup of 8 waves per 16
 // columns of Y.  The workgroup copies its 16 weight rows for the whole of K into LDS with
-// coalesced 16-byte loads (one memory round trip, at most 28 KB), while each wave loads the
-// activations of its eighth of K straight into registers; then every wave unpacks its blocks from
-// LDS and runs one v_mfma_f32_16x16x32_bf16 per block with the operand layout of q4_gemm_kernel,
-// and the eight partial tiles are added in LDS in wave order.  (q4_gemm_kernel reads the same
-// weights with 2-byte loads that each touch 16 rows.)
+// coalesced 16-byte loads (one memory round trip, at most 46 KB), while each wave loads the
+// activations of its eighth of K straight into registers, one 16-byte load per block and lane
+// (row L % 16, inputs 8(L/16) .. 8(L/16)+7: a wave's load covers 64 contiguous bytes of each of
+// the 16 rows); then every wave unpacks its blocks from LDS to the exact values 16 (code - 8)
+// (lane group g: the low (g < 2) or high (g >= 2) nibbles of code bytes 8(g%2) .. 8(g%2)+7, as in
+// the tiled kernel) and runs one v_mfma_f32_16x16x32_bf16 per block with the scale d / 16, and the
+// eight partial tiles are added in LDS in wave order.  (Two 8-byte activation loads per block,
+// each covering 32 bytes of the 16 rows, took 10.1 / 5.0 / 9.5 us at 16 x 1280 x 5120 / 1280 x
+// 1280 / 3072 x 3072 on MI355X against 8.4 / 4.2 / 6.2: a compute unit's load throughput, not
+// the bytes, bounds these shapes.)
 // ---------------------------------------------------------------------------------------
 // MODE (T_PLAIN, T_GELU_OUT, T_PAIR_IN): as for the tiled kernel; with T_PAIR_IN a block's hi and
 // lo activations (128 apart in the pair layout) go through two products into one result before its
@@ -261,22 +285,18 @@ __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__re
     const int n0 = blockIdx.x * 16;
     const int kb0 = wave * BPW;
 
-    // activations of this lane: row l16 (past m: the last row, not stored), inputs 4g..4g+3 and
-    // 16+4g..16+4g+3 of each of the wave's blocks
+    // activations of this lane: row l16 (past m: the last row, not stored), inputs 8g..8g+7 of
+    // each of the wave's blocks (one 16-byte load per block; pairs: the hi and lo halves)
     const uint16_t *xr = x + (size_t)min(l16, m - 1) * K;
-    u32x2v xa[BPW][NA][2];
+    u32x4v xa[BPW][NA];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
         const int kb = kb0 + b;
-        // plain: inputs 32 kb ..; pairs: block kb is columns 32 (kb % 4) .. of 128-input stage kb / 4,
-        // its hi half at 256 (kb / 4) + 32 (kb % 4) and its lo half 128 further
         const uint16_t *xp = xr + (MODE == T_PAIR_IN ? (size_t)(256 * (kb >> 2) + 32 * (kb & 3)) : (size_t)kb * 32) +
-                             4 * grp;
+                             8 * grp;
 #pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            xa[b][a][0] = *reinterpret_cast<const u32x2v *>(xp + 128 * a);
-            xa[b][a][1] = *reinterpret_cast<const u32x2v *>(xp + 128 * a + 16);
-        }
+        for (int a = 0; a < NA; ++a)
+            xa[b][a] = *reinterpret_cast<const u32x4v *>(xp + 128 * a);
     }
     // the 16 weight rows (rows past n repeat row n - 1): chunk q -> row q / CH, chunk q % CH;
     // threads past the last chunk reload it (an identical LDS store)
@@ -304,22 +324,26 @@ __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__re
     for (int b = 0; b < BPW; ++b) {
         const int kb = kb0 + b;
         const int o = 18 * kb;   // byte offset of the block in its row: 4-aligned for even kb
-        uint32_t q, d16;
+        // lane group g: inputs 8g .. 8g+7 = the low (g < 2) or high (g >= 2) nibbles of code bytes
+        // 8 (g % 2) .. 8 (g % 2) + 7, as 16 (code - 8)
+        uint32_t lo, hi, d16;
+        const int c = 8 * (grp & 1);
+        const uint32_t *q = row + ((o + 2 + c) >> 2);
         if ((kb & 1) == 0) {     // uniform over the wave
             d16 = row[o >> 2] & 0xFFFFu;
-            q = __builtin_amdgcn_alignbyte(row[(o >> 2) + grp + 1], row[(o >> 2) + grp], 2);
+            lo = __builtin_amdgcn_alignbyte(q[1], q[0], 2);
+            hi = __builtin_amdgcn_alignbyte(q[2], q[1], 2);
         } else {
             d16 = row[(o - 2) >> 2] >> 16;
-            q = row[((o + 2) >> 2) + grp];
+            lo = q[0];
+            hi = q[1];
         }
-        const bf16x8 bq = codes_to_bf16(q);
+        const bf16x8 bq = __builtin_bit_cast(bf16x8, nibbles_to_bf16_x16(lo, hi, grp >= 2 ? 0u : 4u));
         f32x4v t = 0.0f;
 #pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            const u32x4v av = {xa[b][a][0].x, xa[b][a][0].y, xa[b][a][1].x, xa[b][a][1].y};
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bq, t, 0, 0, 0);
-        }
-        acc += half_bits_to_float(d16) * t;
+        for (int a = 0; a < NA; ++a)
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[b][a]), bq, t, 0, 0, 0);
+        acc += (half_bits_to_float(d16) * 0.0625f) * t;
     }
 
     // add the eight waves' partial tiles in wave order
@@ -388,25 +412,6 @@ __device__ __forceinline__ float ubyte_to_f(uint32_t v, int j)
     default: asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v)); break;
     }
     return r;
-}
-
-// 16 (code - 8) for 8 codes taken from one nibble of 8 bytes (lo: bytes 0-3, hi: 4-7), exact in
-// bf16.  sh = 4 moves low nibbles to the top of their bytes (high nibbles: sh = 0); flipping the
-// top bit then leaves a byte that, read as a signed integer, is 16 (code - 8), because code ^ 8 is
-// code - 8 as a 4-bit two's complement number.  One sign-extending byte conversion per value.
-// (Feeding the raw codes and adding -8 times the activations' block sum through the accumulator
-// saves more but cancels two sums of size 8 sum|a|: measured on MI355X, no faster, and its
-// rounding shows where the weights are sparse.)
-__device__ __forceinline__ u32x4v nibbles_to_bf16_x16(uint32_t lo, uint32_t hi, uint32_t sh)
-{
-    const uint32_t a = ((lo << sh) & 0xF0F0F0F0u) ^ 0x80808080u;
-    const uint32_t b = ((hi << sh) & 0xF0F0F0F0u) ^ 0x80808080u;
-    u32x4v p;
-    p.x = pack_bf16_pair((float)(int8_t)a, (float)(int8_t)(a >> 8));
-    p.y = pack_bf16_pair((float)(int8_t)(a >> 16), (float)(int8_t)(a >> 24));
-    p.z = pack_bf16_pair((float)(int8_t)b, (float)(int8_t)(b >> 8));
-    p.w = pack_bf16_pair((float)(int8_t)(b >> 16), (float)(int8_t)(b >> 24));
-    return p;
 }
 
 // Reads the bytes of block `blk` (0..GT_KC-1 of the stage) of the four 16-column blocks from the
@@ -1069,17 +1074,17 @@ static int launch_gemm_wide(const void *w, const uint16_t *x, float *y, uint16_t
     return st || slices == 1 ? st : launch_slice_sum<gelu>(part, y, hl, m, n, slices, s);
 }
 
-// The skinny kernel takes the products of at most 16 rows at K = 1280 or 3072 (one 16-row tile;
-// the weights of a 16-column tile fit in LDS for the whole of K).  Measured on MI355X at 16
-// frames: 16 x 1280 x 1280 5.0 us against 5.6 with the split-K-over-waves kernel, 16 x 5120 x 1280
-// 7.4 against 9.0, q/k/v stacked 5.1 against 5.7; at K = 3072 16 x 3072 x 3072 9.4 against 13.0
-// (tiled) and 8 x 9216 x 3072 14.9 against 18.5; at K = 5120 (16 x 1280 x 5120: 80 workgroups)
-// 13.0 against 10.1 us for the tiled kernel with K split over the grid, which keeps that shape.
-// Four 16-row blocks per wave for up to 64 rows at K = 1280 were slower than the kernels those
-// shapes keep (64 x 1280 x 1280 11.3 against 8.9 us, 64 x 5120 x 1280 20.2 against 11.7).
+// The skinny kernel takes the products of at most 16 rows at K = 1280, 3072 or 5120 (one 16-row
+// tile; the weights of a 16-column tile fit in LDS for the whole of K).  Measured on MI355X at 16
+// frames: 16 x 1280 x 1280 4.2 us, 16 x 5120 x 1280 5.4, q/k/v stacked 4.2, 16 x 3072 x 3072 6.2,
+// 16 x 1280 x 5120 8.4 against 10.1 for the tiled kernel with K split over the grid and its slice
+// sum (and 5.6 / 9.0 / 5.7 / 13.0 us for the first shapes on the split-K-over-waves or tiled
+// kernels).  Four 16-row blocks per wave for up to 64 rows at K = 1280 were slower than the
+// kernels those shapes keep (64 x 1280 x 1280 11.3 against 8.9 us, 64 x 5120 x 1280 20.2 against
+// 11.7).
 static bool skinny_shape(int64_t m, int64_t n, int64_t k)
 {
-    return m >= 1 && m <= 16 && (k == 1280 || k == 3072) &&
+    return m >= 1 && m <= 16 && (k == 1280 || k == 3072 || k == 5120) &&
            (uint64_t)n * (uint64_t)(k / 32) * 18 < (1ull << 31) && (n + 15) / 16 <= 0x7FFFFFFF;
 }
 
@@ -1089,6 +1094,7 @@ static int launch_gemm_skinny(const void *w, const uint16_t *x, float *y, int m,
     switch (k) {
     case 1280: hipLaunchKernelGGL((q4_gemm_skinny_kernel<40>), grid, dim3(512), 0, s, (const uint8_t *)w, x, y, nullptr, m, n); break;
     case 3072: hipLaunchKernelGGL((q4_gemm_skinny_kernel<96>), grid, dim3(512), 0, s, (const uint8_t *)w, x, y, nullptr, m, n); break;
+    case 5120: hipLaunchKernelGGL((q4_gemm_skinny_kernel<160>), grid, dim3(512), 0, s, (const uint8_t *)w, x, y, nullptr, m, n); break;
     default: return fail(VOX_E_UNSUPPORTED, "q4 skinny product: no compiled K for k=%d", k);
     }
     return check_launch("q4 skinny product");
