@@ -20,8 +20,9 @@
 //    B holds (code - 8).  Lane group g (= lane / 16) takes code bytes 4g..4g+3, i.e. inputs
 //    {4g..4g+3} (low nibbles) then {16+4g..16+4g+3} (high nibbles), and the activations of
 //    the same inputs (the MFMA's k slots may hold the inputs in any order A and B agree on).
-//  * at most 16 rows at K = 1280, 3072 or 5120: the skinny kernel (16-column tiles whose weights for
-//    the whole of K are staged through LDS in one round trip, the same per-block products);
+//  * at most 64 rows at K = 1280 or 3072, 16 at K = 5120: the skinny kernel (16 x 16 tiles whose
+//    weights for the whole of K are staged through LDS in one round trip, the same per-block
+//    products);
 //  * longer chunks: the tiled kernel further down (64 x 64 tiles, weights staged through LDS),
 //    optionally with K split over workgroups (partial tiles in the caller's workspace, added in
 //    a fixed order by a second kernel).
@@ -245,8 +246,8 @@ __device__ __forceinline__ u32x4v nibbles_to_bf16_x16(uint32_t lo, uint32_t hi, 
 }
 
 // ---------------------------------------------------------------------------------------
-// Skinny products (at most 16 rows of X, K of 1280, 3072 or 5120): one workgroup of 8 waves per 16
-// columns of Y.  The workgroup copies its 16 weight rows for the whole of K into LDS with
+// Skinny products (16-row tiles of up to 64 rows of X, K of 1280, 3072 or 5120): one workgroup of 8
+// waves per 16 columns and 16 rows of Y.  The workgroup copies its 16 weight rows for the whole of K into LDS with
 // coalesced 16-byte loads (one memory round trip, at most 46 KB), while each wave loads the
 // activations of its eighth of K straight into registers, one 16-byte load per block and lane
 // (row L % 16, inputs 8(L/16) .. 8(L/16)+7: a wave's load covers 64 contiguous bytes of each of
@@ -283,11 +284,12 @@ __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__re
     const int grp = lane >> 4;
     const int l16 = lane & 15;
     const int n0 = blockIdx.x * 16;
+    const int m0 = blockIdx.y * 16;   // the workgroup's 16-row tile
     const int kb0 = wave * BPW;
 
-    // activations of this lane: row l16 (past m: the last row, not stored), inputs 8g..8g+7 of
+    // activations of this lane: row m0 + l16 (past m: the last row, not stored), inputs 8g..8g+7 of
     // each of the wave's blocks (one 16-byte load per block; pairs: the hi and lo halves)
-    const uint16_t *xr = x + (size_t)min(l16, m - 1) * K;
+    const uint16_t *xr = x + (size_t)min(m0 + l16, m - 1) * K;
     u32x4v xa[BPW][NA];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__re
 #pragma unroll
         for (int wv = 1; wv < 8; ++wv)
             v += red[wv][r][ln];
-        const int rowi = 4 * (ln >> 4) + r;
+        const int rowi = m0 + 4 * (ln >> 4) + r;
         const int col = n0 + (ln & 15);
         if (rowi < m && col < n) {
             if constexpr (MODE == T_GELU_OUT)
@@ -1074,23 +1076,25 @@ static int launch_gemm_wide(const void *w, const uint16_t *x, float *y, uint16_t
     return st || slices == 1 ? st : launch_slice_sum<gelu>(part, y, hl, m, n, slices, s);
 }
 
-// The skinny kernel takes the products of at most 16 rows at K = 1280, 3072 or 5120 (one 16-row
-// tile; the weights of a 16-column tile fit in LDS for the whole of K).  Measured on MI355X at 16
-// frames: 16 x 1280 x 1280 4.2 us, 16 x 5120 x 1280 5.4, q/k/v stacked 4.2, 16 x 3072 x 3072 6.2,
-// 16 x 1280 x 5120 8.4 against 10.1 for the tiled kernel with K split over the grid and its slice
-// sum (and 5.6 / 9.0 / 5.7 / 13.0 us for the first shapes on the split-K-over-waves or tiled
-// kernels).  Four 16-row blocks per wave for up to 64 rows at K = 1280 were slower than the
-// kernels those shapes keep (64 x 1280 x 1280 11.3 against 8.9 us, 64 x 5120 x 1280 20.2 against
-// 11.7).
+// The skinny kernel takes the products of at most 64 rows at K = 1280 or 3072 and of at most 16
+// rows at K = 5120 (a workgroup per 16-row tile; the weights of a 16-column tile fit in LDS for
+// the whole of K).  Measured on MI355X: 16 x 1280 x 1280 4.2 us, 16 x 5120 x 1280 5.4,
+// q/k/v stacked 4.2, 16 x 3072 x 3072 6.2, 16 x 1280 x 5120 8.4 against 10.1 for the tiled kernel
+// with K split over the grid and its slice sum (and 5.6 / 9.0 / 5.7 / 13.0 us for the first shapes
+// on the split-K-over-waves or tiled kernels); 64 x 1280 x 1280 5.4 against 8.9 us (split-K over
+// waves), 64 x 3840 x 1280 8.1 against 12.6, 64 x 5120 x 1280 9.4 against 11.8 and 24 / 64 x 3072 x
+// 3072 8.2 / 12.5 against 11.5 / 13.5 (tiled and slice sum), but 64 x 1280 x 5120 13.2 against
+// 12.0 and 64 x 3072 x 5120 19.3 against 17.5, where every 16-row tile reads all of K of its
+// activations once per 16 columns.
 static bool skinny_shape(int64_t m, int64_t n, int64_t k)
 {
-    return m >= 1 && m <= 16 && (k == 1280 || k == 3072 || k == 5120) &&
+    return m >= 1 && (k == 1280 || k == 3072 || (k == 5120 && m <= 16)) && m <= 64 &&
            (uint64_t)n * (uint64_t)(k / 32) * 18 < (1ull << 31) && (n + 15) / 16 <= 0x7FFFFFFF;
 }
 
 static int launch_gemm_skinny(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t s)
 {
-    const dim3 grid((unsigned)((n + 15) / 16));
+    const dim3 grid((unsigned)((n + 15) / 16), (unsigned)((m + 15) / 16));
     switch (k) {
     case 1280: hipLaunchKernelGGL((q4_gemm_skinny_kernel<40>), grid, dim3(512), 0, s, (const uint8_t *)w, x, y, nullptr, m, n); break;
     case 3072: hipLaunchKernelGGL((q4_gemm_skinny_kernel<96>), grid, dim3(512), 0, s, (const uint8_t *)w, x, y, nullptr, m, n); break;

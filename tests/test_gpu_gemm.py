@@ -178,9 +178,11 @@ def test_gemm_errors(vx):
 
 
 @pytest.mark.parametrize("m,n,k", [(5, 1283, 1280), (11, 77, 3072), (16, 3840, 1280), (2, 1280, 3072), (16, 1, 3072),
-                                   (1, 5120, 1280), (13, 2000, 3072), (16, 1280, 5120), (3, 77, 5120)])
+                                   (1, 5120, 1280), (13, 2000, 3072), (16, 1280, 5120), (3, 77, 5120), (40, 1283, 1280),
+                                   (17, 77, 1280), (64, 3840, 1280), (40, 1000, 3072)])
 def test_gemm_skinny(vx, orc, m, n, k):
-    # at most 16 rows at K = 1280 / 3072 / 5120: the whole K of a 16-column tile staged in LDS;
+    # at most 64 rows at K = 1280 / 3072 and 16 at K = 5120 (16-row tiles): the whole K of a
+    # 16-column tile staged in LDS;
     # ragged column counts (the last tile repeats the last weight row) and rows below 16
     w, xb = synth.gemm_inputs(620 + m, m, n, k)
     assert vx.q4_gemm_workspace(m, n, k) == 0
@@ -188,7 +190,7 @@ def test_gemm_skinny(vx, orc, m, n, k):
     assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm skinny {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(7, 130, 3072), (16, 1283, 1280), (3, 64, 1280), (9, 200, 5120)])
+@pytest.mark.parametrize("m,n,k", [(7, 130, 3072), (16, 1283, 1280), (3, 64, 1280), (9, 200, 5120), (33, 200, 1280)])
 def test_gemm_skinny_exact_dyadic(vx, orc, m, n, k):
     # exact inputs: the skinny kernel's sum (eight waves' partial tiles added in order) is exact
     g = synth.generator(621)
