@@ -1204,17 +1204,18 @@ static size_t adapter_h_bytes(int64_t m, int64_t n_mid)
 // K slices of the adapter's two products: the wide product's where it takes the shape (wide set),
 // else the tiled kernel's.
 struct AdapterPlan {
-    bool wide1, wide2;
-    int s1, s2;
+    bool skinny1, skinny2, wide1, wide2;
+    int s1, s2;   // K slices (1: unsplit)
 };
 static AdapterPlan adapter_plan(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
 {
     AdapterPlan p;
+    p.skinny1 = p.skinny2 = m <= 16;
     const int w1 = wide_slices(m, n_mid, k), w2 = wide_slices(m, n_out, 2 * n_mid, 1);
-    p.wide1 = w1 > 0;
-    p.wide2 = w2 > 0;
-    p.s1 = w1 > 0 ? w1 : tiled_slices(m, n_mid, k);
-    p.s2 = w2 > 0 ? w2 : tiled_slices(m, n_out, 2 * n_mid);
+    p.wide1 = !p.skinny1 && w1 > 0;
+    p.wide2 = !p.skinny2 && w2 > 0;
+    p.s1 = p.skinny1 ? 1 : p.wide1 ? w1 : tiled_slices(m, n_mid, k);
+    p.s2 = p.skinny2 ? 1 : p.wide2 ? w2 : tiled_slices(m, n_out, 2 * n_mid);
     return p;
 }
 
@@ -1237,27 +1238,30 @@ static bool adapter_shape(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
 
 }  // namespace vox
 
-// At most 16 rows: both products through the skinny kernel (no K slices), the first writing the
-// GELU pairs, the second reading them.  Measured on MI355X: 4 rows 18.6 us against 28.7 with the
-// tiled products and their slice sums, 16 rows 27.3 against 29.5.
-static int adapter_skinny(const void *w1, const void *w2, const uint16_t *x, float *y, uint16_t *h, int m, int k,
-                          int n_mid, int n_out, hipStream_t s)
+// The adapter's products through the skinny kernel at most 16 rows (no K slices), the first
+// writing the GELU pairs, the second reading them.  Measured on MI355X: 4 rows 18.6 us against
+// 28.7 with the tiled products and their slice sums, 16 rows 27.3 against 29.5 (before the skinny
+// kernel's 16-byte activation loads; with them 14.0 and 18.8 us).  The second product through it
+// at 50 rows as well: 37.8 against 36.4 us.
+static int adapter_skinny_first(const void *w1, const uint16_t *x, uint16_t *h, int m, int k, int n_mid, hipStream_t s)
 {
-    const dim3 g1((unsigned)((n_mid + 15) / 16)), g2((unsigned)((n_out + 15) / 16));
+    const dim3 g1((unsigned)((n_mid + 15) / 16), (unsigned)((m + 15) / 16));
     switch (k) {
     case 1280: hipLaunchKernelGGL((q4_gemm_skinny_kernel<40, T_GELU_OUT>), g1, dim3(512), 0, s, (const uint8_t *)w1, x, nullptr, h, m, n_mid); break;
     case 3072: hipLaunchKernelGGL((q4_gemm_skinny_kernel<96, T_GELU_OUT>), g1, dim3(512), 0, s, (const uint8_t *)w1, x, nullptr, h, m, n_mid); break;
     default: hipLaunchKernelGGL((q4_gemm_skinny_kernel<160, T_GELU_OUT>), g1, dim3(512), 0, s, (const uint8_t *)w1, x, nullptr, h, m, n_mid); break;
     }
-    int st = check_launch("adapter, first product");
-    if (st)
-        return st;
+    return check_launch("adapter, first product");
+}
+
+static int adapter_skinny_second(const void *w2, const uint16_t *h, float *y, int m, int n_mid, int n_out, hipStream_t s)
+{
+    const dim3 g2((unsigned)((n_out + 15) / 16), (unsigned)((m + 15) / 16));
     if (n_mid == 1280)
         hipLaunchKernelGGL((q4_gemm_skinny_kernel<40, T_PAIR_IN>), g2, dim3(512), 0, s, (const uint8_t *)w2, h, y, nullptr, m, n_out);
     else
         hipLaunchKernelGGL((q4_gemm_skinny_kernel<96, T_PAIR_IN>), g2, dim3(512), 0, s, (const uint8_t *)w2, h, y, nullptr, m, n_out);
-    st = check_launch("adapter, second product");
-    return st ? st : ok();
+    return check_launch("adapter, second product");
 }
 
 extern "C" size_t vox_adapter_workspace(int64_t m, int64_t k, int64_t n_mid, int64_t n_out)
@@ -1299,16 +1303,16 @@ extern "C" int vox_adapter(const void *w1_q4, const void *w2_q4, const uint16_t 
         return fail(VOX_E_INVAL, "vox_adapter: y overlaps an input");
     hipStream_t s = (hipStream_t)stream;
     uint16_t *h = (uint16_t *)workspace;
-    if (m <= 16)
-        return adapter_skinny(w1_q4, w2_q4, x_bf16, y, h, (int)m, (int)k, (int)n_mid, (int)n_out, s);
     float *part = (float *)((char *)workspace + adapter_h_bytes(m, n_mid));
     const AdapterPlan p = adapter_plan(m, k, n_mid, n_out);
     float *p1 = p.s1 > 1 ? part : nullptr, *p2 = p.s2 > 1 ? part : nullptr;
-    int st = p.wide1 ? launch_gemm_wide<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, p1, (int)m, (int)n_mid, (int)k, p.s1, s)
-                     : launch_gemm_tiled<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, p1, (int)m, (int)n_mid, (int)k, p.s1, s);
+    int st = p.skinny1 ? adapter_skinny_first(w1_q4, x_bf16, h, (int)m, (int)k, (int)n_mid, s)
+             : p.wide1 ? launch_gemm_wide<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, p1, (int)m, (int)n_mid, (int)k, p.s1, s)
+                       : launch_gemm_tiled<T_GELU_OUT>(w1_q4, x_bf16, nullptr, h, p1, (int)m, (int)n_mid, (int)k, p.s1, s);
     if (!st)
-        st = p.wide2 ? launch_gemm_wide<T_PAIR_IN>(w2_q4, h, y, nullptr, p2, (int)m, (int)n_out, (int)(2 * n_mid), p.s2, s)
-                     : launch_gemm_tiled<T_PAIR_IN>(w2_q4, h, y, nullptr, p2, (int)m, (int)n_out, (int)(2 * n_mid),
-                                                    p.s2, s);
+        st = p.skinny2 ? adapter_skinny_second(w2_q4, h, y, (int)m, (int)n_mid, (int)n_out, s)
+             : p.wide2 ? launch_gemm_wide<T_PAIR_IN>(w2_q4, h, y, nullptr, p2, (int)m, (int)n_out, (int)(2 * n_mid), p.s2, s)
+                       : launch_gemm_tiled<T_PAIR_IN>(w2_q4, h, y, nullptr, p2, (int)m, (int)n_out, (int)(2 * n_mid),
+                                                      p.s2, s);
     return st ? st : ok();
 }

@@ -39,7 +39,7 @@ def test_adapter_chunk_rows(vx, orc, m):
 
 @pytest.mark.parametrize("m,k,n_mid,n_out", [(1, 1280, 1280, 64), (17, 1280, 3072, 100), (65, 3072, 1280, 33),
                                              (130, 5120, 1280, 1283), (3, 5120, 3072, 7), (200, 1280, 1280, 1280),
-                                             (16, 3072, 3072, 1283), (11, 5120, 1280, 100)])
+                                             (16, 3072, 3072, 1283), (11, 5120, 1280, 100), (64, 5120, 3072, 1283)])
 def test_adapter_ragged(vx, orc, m, k, n_mid, n_out):
     say(f"adapter ragged m={m} {k}->{n_mid}->{n_out}")
     w1, w2, xb = synth.adapter_inputs(700 + m, m, k, n_mid, n_out)
