@@ -98,6 +98,15 @@ def test_validation_before_device_work(lib):
     assert lib.vox_q4_gemm_workspace(64, 1280, 5120) > 0
     assert lib.vox_q4_gemm_workspace(750, 5120, 1280) == 0
     assert lib.vox_q4_gemm_workspace(4, 4, 48) == 0
+    # 128 x 128 tiles: K in 4 slices of 10 stages for 60 tiles, in 2 of 12 for 80; one slice from
+    # 160 tiles on
+    assert lib.vox_q4_gemm_workspace(750, 1280, 5120) == 4 * 750 * 1280 * 4
+    assert lib.vox_q4_gemm_workspace(600, 2000, 3072) == 2 * 600 * 2000 * 4
+    assert lib.vox_q4_gemm_workspace(750, 3840, 1280) == 0
+    # 16-row tiles with the whole K in LDS: up to 64 rows at K = 1280 / 3072, 16 at K = 5120
+    assert lib.vox_q4_gemm_workspace(16, 1280, 5120) == 0
+    assert lib.vox_q4_gemm_workspace(64, 3840, 1280) == 0
+    assert lib.vox_q4_gemm_workspace(64, 3072, 3072) == 0
     assert lib.vox_w16_gemv(p, 0, p, C.c_void_p(0x800000), 10, 12, None) == vox.VOX_E_INVAL    # k % 8
     assert lib.vox_w16_gemv(p, 2, p, C.c_void_p(0x800000), 10, 16, None) == vox.VOX_E_INVAL    # fmt
     assert lib.vox_w16_gemv(p, 1, p, C.c_void_p(0x800000), 0, 16, None) == vox.VOX_OK          # empty
@@ -115,6 +124,10 @@ def test_validation_before_device_work(lib):
     assert lib.vox_adapter_workspace(16, 4096, 3072, 3072) == 0       # k without compiled stages
     assert lib.vox_adapter_workspace(16, 5120, 5120, 3072) == 0       # n_mid without compiled stages
     assert lib.vox_adapter_workspace(0, 5120, 3072, 3072) == 0
+    # 187 rows: both products on 128 x 128 tiles with K in 4 slices (the GELU pairs, then the
+    # larger product's partial tiles); at most 16 rows: the pairs only
+    assert lib.vox_adapter_workspace(187, 5120, 3072, 3072) == 187 * 3072 * 4 + 4 * 187 * 3072 * 4
+    assert lib.vox_adapter_workspace(16, 5120, 3072, 3072) == 16 * 3072 * 4
     big = C.c_void_p(0x10000000)
     aw = lib.vox_adapter_workspace(4, 1280, 1280, 64)
     assert lib.vox_adapter(p, p, p, p, 4, 48, 1280, 64, big, aw, None) == vox.VOX_E_INVAL          # k % 32
