@@ -871,9 +871,10 @@ __global__ __launch_bounds__(GH_THREADS * KW) __attribute__((amdgpu_waves_per_eu
         acc[i] += dprev * t[i];
 
     if constexpr (KW > 1) {
-        // groups 1.. leave their partial tiles in LDS (the stage buffers are free after the last
-        // barrier); group 0 adds them in group order
+        // groups 1.. leave their partial tiles in LDS, over the stage buffers once every wave has
+        // read the last stage; group 0 adds them in group order
         float *red = reinterpret_cast<float *>(as);
+        __syncthreads();
         if (kg > 0) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
