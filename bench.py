@@ -11,8 +11,9 @@ with HIP events on the stream the steps run on), the decoder at a full, wrapped 
 window, the roofline of the dominant kernel (the Q4_0 GEMV, timed with HIP events at the LM-head
 shape over rotating weight copies so that every launch streams from HBM) next to the read ceiling
 of the streaming probe at the same byte count, a GEMV sweep over row counts at K = 3072, the
-decoder's own dominant kernel from the committed kernel trace, and the CPU oracle timed on
-bounded samples on the host (at all its threads and at one).
+decoder's own dominant kernel from the committed kernel trace, the encoder-chunk GEMM set at 16
+and 750 frames, and the CPU oracle timed on bounded samples on the host (at all its threads and
+at one).
 
 Other modes: --leg kernels (per-kernel timings of the other workloads), --leg gemv (the GEMV leg
 alone, for counter runs), --leg probe (read ceilings and the grid-handoff probe), and
@@ -292,6 +293,42 @@ def timed_all(torch, stream, launch, copies, reps, replays=5):
     return per
 
 
+def gemm_set(torch, synth, vox, dev, stream, m: int, fused: bool) -> dict:
+    """The encoder-chunk GEMM set at M = m: the six linears of one layer back to back (q, k, v, o,
+    ffn_up, ffn_down); fused: q, k and v as one 3840-row product over their concatenated weights
+    (the rows of a Q4_0 matrix are independent, so stacking Wq, Wk, Wv gives q, k, v side by side
+    in one output).  Rotated weight copies (more than 1 GiB), graph replay, HIP events."""
+    GiB = 1 << 30
+    sets = []
+    for name, n, k in synth.ENCODER_LINEARS:
+        w, xb = synth.gemm_inputs(synth.SEED_GEMM, m, n, k)
+        sets.append((name, n, k, w, torch.from_numpy(xb.view(np.int16)).to(dev)))
+    if fused:
+        qkv_w = np.concatenate([sets[0][3], sets[1][3], sets[2][3]], axis=0)
+        sets = [("qkv", 3 * sets[0][1], sets[0][2], qkv_w, sets[0][4])] + sets[3:]
+    wbytes = sum(s_[3].nbytes for s_ in sets)
+    copies = max(2, int(np.ceil(1.1 * GiB / wbytes)))
+    wdev = [[torch.from_numpy(s_[3]).to(dev) for s_ in sets] for _ in range(copies)]
+    ys = [torch.empty(m, s_[1], dtype=torch.float32, device=dev) for s_ in sets]
+    # one workspace serves the set (the launches run one after another on the stream)
+    wsb = max(vox.q4_gemm_workspace(m, n_, k_) for _, n_, k_, _, _ in sets)
+    gws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def launch(i):
+        for j, (name, n, k, _, xd) in enumerate(sets):
+            vox._check(vox.lib().vox_q4_gemm(vox._ptr(wdev[i][j]), vox._ptr(xd), vox._ptr(ys[j]), m, n, k,
+                                             vox._ptr(gws) if wsb else None, wsb, vox._stream(None)))
+    us = timed(torch, stream, launch, copies, 50)
+    flops = 2 * m * sum(n * k for _, n, k in synth.ENCODER_LINEARS)
+    b = wbytes + sum(m * k_ * 2 + m * n_ * 4 for _, n_, k_, _, _ in sets)
+    del wdev
+    torch.cuda.empty_cache()
+    return {"case": f"encoder linears set, M={m}" + (", q/k/v as one 3840-row call" if fused else ""),
+            "us": round(us, 3), "flops": flops, "tflops": round(flops / us / 1e6, 2),
+            "frac_mfma_bf16": round(flops / us / 1e6 / 2500.0, 4), "bytes": b, "gbs": round(b / us / 1e3, 1),
+            "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def kernels_leg(torch, synth, vox, dev, stream):
     """Per-kernel device times of the workloads beside the decoder step: the single 3072x3072
     GEMV, one decoder layer's linears, GQA attention at three ring fills, the encoder-chunk
@@ -343,37 +380,9 @@ def kernels_leg(torch, synth, vox, dev, stream):
     torch.cuda.empty_cache()
 
     # encoder-chunk GEMM set: the six linears of one layer, each M; then the same set with q, k and v
-    # as one 3840-row product over their concatenated weights (the rows of a Q4_0 matrix are
-    # independent, so stacking Wq, Wk, Wv gives q, k, v side by side in one output)
+    # as one 3840-row product over their concatenated weights
     for m, fused in [(m_, f_) for m_ in synth.ENCODER_M for f_ in (False, True)]:
-        sets = []
-        for name, n, k in synth.ENCODER_LINEARS:
-            w, xb = synth.gemm_inputs(synth.SEED_GEMM, m, n, k)
-            sets.append((name, n, k, w, torch.from_numpy(xb.view(np.int16)).to(dev)))
-        if fused:
-            qkv_w = np.concatenate([sets[0][3], sets[1][3], sets[2][3]], axis=0)
-            sets = [("qkv", 3 * sets[0][1], sets[0][2], qkv_w, sets[0][4])] + sets[3:]
-        wbytes = sum(s_[3].nbytes for s_ in sets)
-        copies = max(2, int(np.ceil(1.1 * GiB / wbytes)))
-        wdev = [[torch.from_numpy(s_[3]).to(dev) for s_ in sets] for _ in range(copies)]
-        ys = [torch.empty(m, s_[1], dtype=torch.float32, device=dev) for s_ in sets]
-        # one workspace serves the set (the launches run one after another on the stream)
-        wsb = max(vox.q4_gemm_workspace(m, n_, k_) for _, n_, k_, _, _ in sets)
-        gws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-
-        def launch(i):
-            for j, (name, n, k, _, xd) in enumerate(sets):
-                vox._check(vox.lib().vox_q4_gemm(vox._ptr(wdev[i][j]), vox._ptr(xd), vox._ptr(ys[j]), m, n, k,
-                                                 vox._ptr(gws) if wsb else None, wsb, vox._stream(None)))
-        us = timed(torch, stream, launch, copies, 50)
-        flops = 2 * m * sum(n * k for _, n, k in synth.ENCODER_LINEARS)
-        b = wbytes + sum(m * k_ * 2 + m * n_ * 4 for _, n_, k_, _, _ in sets)
-        emit({"kernel": "q4_gemm", "case": f"encoder linears set, M={m}" + (", q/k/v as one 3840-row call" if fused
-                                                                             else ""), "us": round(us, 3), "flops": flops,
-              "tflops": round(flops / us / 1e6, 2), "frac_mfma_bf16": round(flops / us / 1e6 / 2500.0, 4),
-              "bytes": b, "gbs": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
-        del wdev
-        torch.cuda.empty_cache()
+        emit({"kernel": "q4_gemm", **gemm_set(torch, synth, vox, dev, stream, m, fused)})
 
     # one product per launch at 750 frames (each linear of the set, q/k/v stacked), then the wide
     # product over K at 750 x 5120 (the cost of a stage and of a launch)
@@ -970,6 +979,14 @@ def main():
     sweep = gemv_sweep(torch, synth, vox, dev, stream)
     print(f"[bench] gemv sweep: " + ", ".join(f"{r['n']}:{r['gbs']:.0f}" for r in sweep), file=sys.stderr, flush=True)
 
+    # the encoder-chunk GEMM set (q, k, v stacked) at the shortest and the longest chunk
+    egemm = {}
+    for m in (synth.ENCODER_M[0], synth.ENCODER_M[-1]):
+        r = gemm_set(torch, synth, vox, dev, stream, m, True)
+        egemm[f"M={m}"] = {k_: r[k_] for k_ in ("us", "tflops", "frac_mfma_bf16", "gbs", "frac_hbm")}
+    print(f"[bench] encoder GEMM sets: " + ", ".join(f"{k_} {v_['us']:.1f} us" for k_, v_ in egemm.items()),
+          file=sys.stderr, flush=True)
+
     cpu = None if args.no_cpu else cpu_leg(args, synth, w)
 
     out = {
@@ -1004,6 +1021,7 @@ def main():
         "decoder_w16": w16,
         "decoder_roofline": decoder_trace_roofline(synth),
         "gemv_sweep_k3072": sweep,
+        "encoder_gemm_set_qkv_stacked": egemm,
         "last_token": dm["last_token"],
         "cpu_baseline": cpu,
     }
