@@ -47,10 +47,14 @@ def test_adapter_ragged(vx, orc, m, k, n_mid, n_out):
 
 
 @pytest.mark.parametrize("m,k,n_mid,n_out", [(190, 5120, 3072, 3000), (520, 5120, 1280, 2000),
-                                             (800, 1280, 3072, 3072)])
+                                             (800, 1280, 3072, 3072), (190, 5120, 3072, 3456),
+                                             (400, 1280, 3072, 2560), (800, 5120, 1280, 3000),
+                                             (400, 3072, 3072, 640)])
 def test_adapter_wide(vx, orc, m, k, n_mid, n_out):
     # longer chunks through the 128 x 128 tile product: GELU output with K split over the grid
-    # (through the slice sum) and unsplit (stored by the product), pair input split and unsplit
+    # (through the slice sum) and unsplit (stored by the product), pair input split and unsplit;
+    # stages per workgroup: GELU output 10 (4 slices, unsplit) and 12 (2 slices), pair input 12, 16,
+    # 24 (4, 3, 2 slices), 20 and 48 (unsplit)
     say(f"adapter wide m={m} {k}->{n_mid}->{n_out}")
     w1, w2, xb = synth.adapter_inputs(710 + m, m, k, n_mid, n_out)
     assert_close(_adapter(vx, w1, w2, xb, n_out), orc.adapter(w1, w2, xb), f"adapter {m} {k}->{n_mid}->{n_out}")
