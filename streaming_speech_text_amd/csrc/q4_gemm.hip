@@ -397,8 +397,6 @@ constexpr int GT_STAGE = GT_KC * 32;                        // inputs per stage
 constexpr int GT_WAVES = GT_THREADS / 64;
 constexpr int GT_RAW = GT_KC * 18;                          // weight bytes of one row per stage
 constexpr int GT_WB = 8;                                    // bytes per weight piece (72 = 9 x 8)
-constexpr int GT_W_CHUNKS = GT_BN * GT_RAW / GT_WB;         // weight pieces per stage
-constexpr int GT_WR = (GT_W_CHUNKS + GT_THREADS - 1) / GT_THREADS;   // load rounds per stage
 static_assert(GT_RAW % GT_WB == 0, "a row's stage bytes split into whole pieces");
 static_assert(GT_KC == GT_THREADS / 64, "one block per wave per stage");
 static_assert(GELU_STAGE == GT_STAGE, "a GELU pair stage is one weight stage of the second product");
@@ -416,18 +414,18 @@ __device__ __forceinline__ float ubyte_to_f(uint32_t v, int j)
     return r;
 }
 
-// Reads the bytes of block `blk` (0..GT_KC-1 of the stage) of the four 16-column blocks from the
+// Reads the bytes of block `blk` (0..GT_KC-1 of the stage) of the NJ 16-column blocks from the
 // raw stage copy (GT_RAW bytes per row) with aligned dword reads and unpacks this lane's operand
 // (column 16j + l16, inputs 8*grp .. 8*grp+7) and scale.  ODD: blk is odd, so the block starts
 // at 2 mod 4 and its code bytes are 4-aligned; otherwise the block is 4-aligned and the code
 // bytes are 2 mod 4.
-template <bool ODD>
-__device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, int grp, bf16x8 (&bf)[4],
-                                         float (&d)[4])
+template <bool ODD, int NJ>
+__device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, int grp, bf16x8 (&bf)[NJ],
+                                         float (&d)[NJ])
 {
-    uint32_t dw[4][4];
+    uint32_t dw[NJ][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const uint32_t *p = raw + (((16 * j + l16) * GT_RAW + 18 * blk) >> 2);
         if constexpr (ODD) {
             const uint32_t *q = p + 1 + 2 * (grp & 1);
@@ -443,7 +441,7 @@ __device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, 
         }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         uint32_t d16, lo, hi;
         if constexpr (ODD) {
             d16 = dw[j][0] >> 16;
@@ -465,22 +463,26 @@ __device__ __forceinline__ void unpack_b(const uint32_t *raw, int blk, int l16, 
 // NS: stages (of GT_STAGE inputs) per workgroup, fixed at compile time.  Workgroup z of the grid's
 // third dimension takes stages z*NS .. z*NS+NS-1; with one slice it writes the output itself,
 // otherwise its fp32 partial tile goes to part[z][m][n] and q4_gemm_reduce_kernel adds the
-// slices.  k is the activations' row length.
-template <int NS, int MODE>
+// slices.  k is the activations' row length.  NJ: 16-column blocks per tile (4: 64 x 64 tiles; 2:
+// 64 x 32 tiles, for outputs that reach enough workgroups that way without splitting K).
+template <int NS, int MODE, int NJ = 4>
 __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void q4_gemm_tiled_kernel(const uint8_t *__restrict__ w,
                                                                    const uint16_t *__restrict__ x,
                                                                    float *__restrict__ y, uint16_t *__restrict__ hl,
                                                                    float *__restrict__ part, int m, int n, int k)
 {
-    __shared__ __attribute__((aligned(16))) uint32_t braw[2][GT_BN * GT_RAW / 4];
-    __shared__ f32x4v red[GT_WAVES / 2][16][64];   // tree reduction of the waves' tiles
+    constexpr int BN = 16 * NJ;                                   // tile columns
+    constexpr int W_CHUNKS = BN * GT_RAW / GT_WB;                 // weight pieces per stage
+    constexpr int WR = (W_CHUNKS + GT_THREADS - 1) / GT_THREADS;  // load rounds per stage
+    __shared__ __attribute__((aligned(16))) uint32_t braw[2][BN * GT_RAW / 4];
+    __shared__ f32x4v red[GT_WAVES / 2][4 * NJ][64];   // tree reduction of the waves' tiles
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l16 = lane & 15, grp = lane >> 4;
     const int m0 = blockIdx.y * GT_BM;
-    const int n0 = blockIdx.x * GT_BN;
+    const int n0 = blockIdx.x * BN;
     const int st0 = blockIdx.z * NS, st_end = st0 + NS;
     constexpr int KWS = MODE == T_PAIR_IN ? 1 : 0;   // weight stage = activation stage >> KWS
     const uint32_t row_bytes = (uint32_t)((k >> KWS) / 32) * 18;
@@ -492,11 +494,11 @@ __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
         aoff[i] = (uint32_t)min(m0 + 16 * i + l16, m - 1) * (uint32_t)k + (uint32_t)(32 * wave + 8 * grp);
     // weight pieces: chunk c -> row c / (GT_RAW / GT_WB) of the tile, piece c % (GT_RAW / GT_WB);
     // rounds past the last chunk are clamped to it (a duplicate load and an identical LDS store)
-    uint32_t woff[GT_WR];
-    int wlds[GT_WR];
+    uint32_t woff[WR];
+    int wlds[WR];
 #pragma unroll
-    for (int r = 0; r < GT_WR; ++r) {
-        const int c = min(tid + GT_THREADS * r, GT_W_CHUNKS - 1);
+    for (int r = 0; r < WR; ++r) {
+        const int c = min(tid + GT_THREADS * r, W_CHUNKS - 1);
         const int col = min(n0 + c / (GT_RAW / GT_WB), n - 1);
         woff[r] = (uint32_t)col * row_bytes + (uint32_t)(GT_WB * (c % (GT_RAW / GT_WB)));
         wlds[r] = (GT_WB / 4) * c;
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 
     // two stages of loads in flight: register slots 0 and 1 (compile-time indices)
     u32x4v ar[2][4];
-    u32x2v wr[2][GT_WR];
+    u32x2v wr[2][WR];
     auto load_stage = [&](int st, auto slot) {
         constexpr int S = decltype(slot)::value;
         st = min(st, st_end - 1);   // past the slice: a harmless reload of its last stage
@@ -514,22 +516,22 @@ __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
             ar[S][i] = *reinterpret_cast<const u32x4v *>(xs + aoff[i]);
         const uint8_t *ws = w + (size_t)(st >> KWS) * GT_RAW;
 #pragma unroll
-        for (int r = 0; r < GT_WR; ++r)
+        for (int r = 0; r < WR; ++r)
             wr[S][r] = *reinterpret_cast<const u32x2v *>(ws + woff[r]);
     };
 
-    f32x4v acc[4][4];
+    f32x4v acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
             acc[i][j] = 0.0f;
 
     auto stage = [&](int st, auto slot) {
         constexpr int S = decltype(slot)::value;
         const int b = st & 1;
 #pragma unroll
-        for (int r = 0; r < GT_WR; ++r)
+        for (int r = 0; r < WR; ++r)
             *reinterpret_cast<u32x2v *>(&braw[b][wlds[r]]) = wr[S][r];
         bf16x8 af[4];
 #pragma unroll
@@ -539,26 +541,26 @@ __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
         // B operands of block `wave` for the four 16-column blocks.  The block of column c
         // starts at byte o = c*GT_RAW + 18*wave: 4-aligned for even waves, 2 mod 4 for odd ones
         // (the parity is uniform over a wave, so each wave runs one straight-line path).
-        bf16x8 bf[4];
-        float d[4];
+        bf16x8 bf[NJ];
+        float d[NJ];
         if ((wave & 1) == 0)
-            unpack_b<false>(&braw[b][0], wave, l16, grp, bf, d);
+            unpack_b<false, NJ>(&braw[b][0], wave, l16, grp, bf, d);
         else
-            unpack_b<true>(&braw[b][0], wave, l16, grp, bf, d);
+            unpack_b<true, NJ>(&braw[b][0], wave, l16, grp, bf, d);
         // products in two rounds of 8 with independent result registers, then the scaled sums
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            f32x4v t[2][4];
+            f32x4v t[2][NJ];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
                     t[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[2 * h + i], bf[j], (f32x4v)0.0f, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
                     acc[2 * h + i][j] += d[j] * t[i][j];
         }
         load_stage(st + 2, slot);   // after the products, so the slot's registers are free
@@ -581,16 +583,16 @@ __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    red[wave - half][i * 4 + j][lane] = acc[i][j];
+                for (int j = 0; j < NJ; ++j)
+                    red[wave - half][i * NJ + j][lane] = acc[i][j];
         }
         __syncthreads();
         if (wave < half) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] += red[wave][i * 4 + j][lane];
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] += red[wave][i * NJ + j][lane];
         }
         __syncthreads();
     }
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(GT_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const int col = n0 + 16 * j + l16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -949,18 +951,30 @@ static int tiled_slices(int64_t m, int64_t n, int64_t k)
     return most;
 }
 
+// 64 x 32 tiles at K = 1280 where they alone give GT_TARGET_WGS workgroups and 64 x 64 tiles would
+// need K slices: measured on MI355X, 200 x 1280 x 1280 9.2 us against 11.4 with two slices and
+// their sum; at K = 5120 and 3072 the unsplit chain of 64 x 32 tiles was slower (200 x 1280 x 5120
+// 24.2 against 22.3 us, 100 x 3072 x 3072 17.5 against 17.2), and where 64 x 64 tiles need no
+// slices 64 x 32 ones were 10-20 % slower (750 x 1280 x 1280 15.4 against 12.9 us).
+static bool tiled_narrow(int64_t m, int64_t n, int64_t k)
+{
+    const int64_t rows = (m + GT_BM - 1) / GT_BM;
+    return tiled_shape(m, n, k) && k == 1280 && ((n + GT_BN - 1) / GT_BN) * rows < GT_TARGET_WGS &&
+           ((n + 31) / 32) * rows >= GT_TARGET_WGS;
+}
+
 static size_t tiled_workspace(int64_t m, int64_t n, int slices)
 {
     return slices > 1 ? (size_t)slices * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
-template <int S, int MODE>
+template <int S, int MODE, int NJ = 4>
 static void launch_tiled_slices(const void *w, const uint16_t *x, float *y, uint16_t *hl, float *part, int m, int n,
                                 int k, int slices, hipStream_t s)
 {
-    const dim3 grid((unsigned)((n + GT_BN - 1) / GT_BN), (unsigned)((m + GT_BM - 1) / GT_BM), (unsigned)slices);
-    hipLaunchKernelGGL((q4_gemm_tiled_kernel<S, MODE>), grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y, hl,
-                       part, m, n, k);
+    const dim3 grid((unsigned)((n + 16 * NJ - 1) / (16 * NJ)), (unsigned)((m + GT_BM - 1) / GT_BM), (unsigned)slices);
+    hipLaunchKernelGGL((q4_gemm_tiled_kernel<S, MODE, NJ>), grid, dim3(GT_THREADS), 0, s, (const uint8_t *)w, x, y,
+                       hl, part, m, n, k);
 }
 
 // Output: y (fp32), or for T_GELU_OUT GELU pairs in hl (n a multiple of 256).  part: slices x m x n
@@ -1134,7 +1148,7 @@ extern "C" size_t vox_q4_gemm_workspace(int64_t m, int64_t n, int64_t k)
         return ws > 1 ? tiled_workspace(m, n, ws) : 0;
     if (skinny_shape(m, n, k))
         return 0;
-    if (!tiled_shape(m, n, k))
+    if (!tiled_shape(m, n, k) || tiled_narrow(m, n, k))
         return 0;
     return tiled_workspace(m, n, tiled_slices(m, n, k));
 }
@@ -1172,6 +1186,9 @@ extern "C" int vox_q4_gemm(const void *w_q4, const uint16_t *x_bf16, float *y, i
                                        (int)n, (int)k, wide, s);
     } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && skinny_shape(m, n, k)) {
         st = launch_gemm_skinny(w_q4, x_bf16, y, (int)m, (int)n, (int)k, s);
+    } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_narrow(m, n, k)) {
+        launch_tiled_slices<10, T_PLAIN, 2>(w_q4, x_bf16, y, nullptr, nullptr, (int)m, (int)n, (int)k, 1, s);
+        st = check_launch("q4 tiled product");
     } else if (aligned(x_bf16, 16) && aligned(w_q4, 16) && tiled_shape(m, n, k)) {
         int slices = workspace ? tiled_slices(m, n, k) : 1;
         const size_t need = tiled_workspace(m, n, slices);

@@ -107,6 +107,9 @@ def test_validation_before_device_work(lib):
     assert lib.vox_q4_gemm_workspace(16, 1280, 5120) == 0
     assert lib.vox_q4_gemm_workspace(64, 3840, 1280) == 0
     assert lib.vox_q4_gemm_workspace(64, 3072, 3072) == 0
+    # 64 x 32 tiles at K = 1280 instead of K slices of 64 x 64 tiles; not at K = 5120
+    assert lib.vox_q4_gemm_workspace(200, 1280, 1280) == 0
+    assert lib.vox_q4_gemm_workspace(200, 1280, 5120) == 2 * 200 * 1280 * 4
     assert lib.vox_w16_gemv(p, 0, p, C.c_void_p(0x800000), 10, 12, None) == vox.VOX_E_INVAL    # k % 8
     assert lib.vox_w16_gemv(p, 2, p, C.c_void_p(0x800000), 10, 16, None) == vox.VOX_E_INVAL    # fmt
     assert lib.vox_w16_gemv(p, 1, p, C.c_void_p(0x800000), 0, 16, None) == vox.VOX_OK          # empty

@@ -86,7 +86,7 @@ def test_gemm_ragged(vx, orc, m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [(70, 96, 1280), (64, 1280, 5120), (300, 200, 1280), (257, 130, 5120),
                                    (750, 1280, 1280), (256, 3072, 3072), (260, 10300, 1280), (16, 1280, 5120),
-                                   (750, 1280, 5120), (600, 2000, 3072)])
+                                   (750, 1280, 5120), (600, 2000, 3072), (200, 1283, 1280)])
 def test_gemm_exact_dyadic(vx, orc, m, n, k):
     # small-integer activations and power-of-two scales: every product and partial sum is exact,
     # so the matrix-core result must equal the oracle bit for bit (also when K is split)
@@ -102,6 +102,15 @@ def test_gemm_exact_dyadic(vx, orc, m, n, k):
     assert np.array_equal(_gemm(vx, w, xb, m, n, k).astype(np.float64), ref)
     if vx.q4_gemm_workspace(m, n, k):
         assert np.array_equal(_gemm(vx, w, xb, m, n, k, split=False).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(200, 1280, 1280), (200, 1283, 1280), (129, 2600, 1280)])
+def test_gemm_narrow_tiles(vx, orc, m, n, k):
+    # 64 x 32 tiles at K = 1280 where 64 x 64 tiles would need K slices: one launch, no workspace
+    assert vx.q4_gemm_workspace(m, n, k) == 0
+    w, xb = synth.gemm_inputs(640 + m, m, n, k)
+    say(f"gemm narrow tiles m={m} n={n} k={k}")
+    assert_close(_gemm(vx, w, xb, m, n, k), orc.q4_gemm(w, xb), f"gemm narrow {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,n,k", [(750, 5120, 1280), (770, 5120, 3072), (1023, 3850, 5120), (260, 10300, 1280),
