@@ -188,7 +188,9 @@ __device__ __forceinline__ float block_sum_fixed(float v, float *buf)
 }
 // Issues the 16-byte loads of tile t into the thread's prefetch registers.  The loads are
 // unconditional (chunks past the end of a short tile re-read the tile's first chunk), so no
-// branch separates them and the compiler's wait counts stay exact.
+// branch separates them and the compiler's wait counts stay exact.  They are non-temporal: each
+// weight is read once per call (measured on MI355X: the decoder step 0.871 -> 0.828 ms/token, the
+// 9216 x 3072 GEMV 6.06 -> 5.64 us, results identical).
 template <class Gm, class Policy>
 __device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT])
 {
@@ -210,7 +212,8 @@ __device__ __forceinline__ void gemv_fetch(Policy &P, int t, u32x4 (&pf)[Gm::CPT
         const int p = Gm::NPART == 1 ? 0 : (ch < Gm::PC ? 0 : 1);
         int off = ch - p * Gm::PC;
         off = (ch < Gm::TC && off < valid_chunks[p]) ? off : 0;
-        pf[i] = *reinterpret_cast<const u32x4 *>(base[0] + (p ? delta : (int64_t)0) + (int64_t)off * 16);
+        pf[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(base[0] + (p ? delta : (int64_t)0) + (int64_t)off * 16));
     }
 }
 

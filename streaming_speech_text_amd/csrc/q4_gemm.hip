@@ -301,13 +301,16 @@ __global__ __launch_bounds__(512) void q4_gemm_skinny_kernel(const uint8_t *__re
             xa[b][a] = *reinterpret_cast<const u32x4v *>(xp + 128 * a);
     }
     // the 16 weight rows (rows past n repeat row n - 1): chunk q -> row q / CH, chunk q % CH;
-    // threads past the last chunk reload it (an identical LDS store)
+    // threads past the last chunk reload it (an identical LDS store).  Non-temporal loads: at 16
+    // rows each weight is read once (measured on MI355X: the M = 16 sets 3-4 % faster; the tiled
+    // and wide products, whose row tiles share the weights, were 3-10 % slower with them)
     u32x4v wr[PER];
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
         const int q = min(tid + 512 * p, 16 * CH - 1);
         const int col = min(n0 + q / CH, n - 1);
-        wr[p] = *reinterpret_cast<const u32x4v *>(w + (size_t)col * RB + (size_t)16 * (q % CH));
+        wr[p] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4v *>(w + (size_t)col * RB + (size_t)16 * (q % CH)));
     }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {

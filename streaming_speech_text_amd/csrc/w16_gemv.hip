@@ -63,9 +63,11 @@ __global__ __launch_bounds__(W16_THREADS) void w16_gemv_kernel(const uint16_t *_
         for (int j = 0; j < CH; ++j) {
             const int e = c0 + 512 * j + 8 * lane;
             const int ee = e < k ? e : 0;   // past the row end: read element 0, weigh it by 0
+            // non-temporal: each weight is read once (measured on MI355X: the LM-head shape 126 ->
+            // 113 us, the chain of a decoder step's GEMVs 6.5-7 % faster)
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                wq[j][r] = *reinterpret_cast<const u32x4 *>(wr[r] + ee);
+                wq[j][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr[r] + ee));
             xa[j][0] = *reinterpret_cast<const f32x4w *>(x + ee);
             xa[j][1] = *reinterpret_cast<const f32x4w *>(x + ee + 4);
             if (e >= k) {
