@@ -119,16 +119,18 @@ def probe_lib():
     L = C.CDLL(path)
     L.vox_probe_sink_entries.restype = C.c_int
     L.vox_probe_sink_entries.argtypes = [C.c_int]
-    L.vox_probe_stream_read.restype = C.c_int
-    L.vox_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    for fn in (L.vox_probe_stream_read, L.vox_probe_stream_read_nt):
+        fn.restype = C.c_int
+        fn.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
     return L
 
 
 def probe_ceiling(torch, dev, stream, sizes, reps=100):
-    """Streaming-read rate (GB/s) of a plain 16-byte-load kernel for each byte count in `sizes`:
+    """Streaming-read rate (GB/s) of a 16-byte-load kernel for each byte count in `sizes`:
     launches read consecutive windows of a buffer of more than 1 GiB (so no window is served from
     the 256 MB Infinity Cache), captured in a graph and timed like the kernels; the best over
-    1, 2, 4 and 8 workgroups per compute unit.  Returns {bytes: (us, GB/s, wg_per_cu)}."""
+    plain and non-temporal loads and 1, 2, 4 and 8 workgroups per compute unit.  Returns
+    {bytes: (us, GB/s, wg_per_cu, loads)}."""
     L = probe_lib()
     GiB = 2 ** 30
     out = {}
@@ -139,15 +141,15 @@ def probe_ceiling(torch, dev, stream, sizes, reps=100):
         buf = torch.empty(n_win * size, dtype=torch.uint8, device=dev)
         buf.fill_(1)
         best = None
-        for wg in (1, 2, 4, 8):
-            def launch(i, wg=wg):
-                st = L.vox_probe_stream_read(buf.data_ptr() + i * size, size, sink.data_ptr(), wg,
-                                             torch.cuda.current_stream().cuda_stream)
-                if st:
-                    raise RuntimeError(f"probe launch failed ({st})")
-            us = timed(torch, stream, launch, n_win, reps)
-            if best is None or us < best[0]:
-                best = (us, size / us / 1e3, wg)
+        for fn, loads in ((L.vox_probe_stream_read, "plain"), (L.vox_probe_stream_read_nt, "non-temporal")):
+            for wg in (1, 2, 4, 8):
+                def launch(i, wg=wg, fn=fn):
+                    st = fn(buf.data_ptr() + i * size, size, sink.data_ptr(), wg, torch.cuda.current_stream().cuda_stream)
+                    if st:
+                        raise RuntimeError(f"probe launch failed ({st})")
+                us = timed(torch, stream, launch, n_win, reps)
+                if best is None or us < best[0]:
+                    best = (us, size / us / 1e3, wg, loads)
         out[size] = best
         del buf
         torch.cuda.empty_cache()
@@ -161,9 +163,9 @@ def probe_leg(torch, dev, stream):
     streamed per phase."""
     sizes = [7077888, 10616832, 15925248, 31850496, 226492416, 5308416, 1 << 20, 4 << 20, 16 << 20,
              64 << 20, 256 << 20]
-    for b, (us, gbs, wg) in probe_ceiling(torch, dev, stream, sizes).items():
+    for b, (us, gbs, wg, loads) in probe_ceiling(torch, dev, stream, sizes).items():
         print(json.dumps({"leg": "probe", "bytes": b, "us": round(us, 3), "gbs": round(gbs, 1),
-                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "wg_per_cu": wg}), flush=True)
+                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "wg_per_cu": wg, "loads": loads}), flush=True)
     import ctypes as C
     L = probe_lib()
     L.vox_probe_handoff_work_bytes.restype = C.c_size_t
@@ -975,7 +977,7 @@ def main():
     gemv = gemv_leg(args, torch, synth, vox, dev, stream)
     traffic = measured_traffic(kernel_source_digest(), gemv["bytes"])
     ceil = probe_ceiling(torch, dev, stream, [gemv["bytes"] // 256 * 256], reps=50)
-    c_us, c_gbs, c_wg = next(iter(ceil.values()))
+    c_us, c_gbs, c_wg, c_loads = next(iter(ceil.values()))
     sweep = gemv_sweep(torch, synth, vox, dev, stream)
     print(f"[bench] gemv sweep: " + ", ".join(f"{r['n']}:{r['gbs']:.0f}" for r in sweep), file=sys.stderr, flush=True)
 
@@ -1011,7 +1013,7 @@ def main():
                      "us_per_launch": round(gemv["us"], 3), "us_per_launch_spread": gemv["spread"],
                      "ceiling": {"gbs": round(c_gbs, 1), "frac_hbm": round(c_gbs / HBM_PEAK_GBS, 4),
                                  "us": round(c_us, 3), "probe": "streaming read of the same byte count "
-                                 "(libvox_probe.so)", "workgroups_per_cu": c_wg},
+                                 "(libvox_probe.so)", "workgroups_per_cu": c_wg, "loads": c_loads},
                      "frac_of_ceiling": round(gemv["gbs"] / c_gbs, 4)},
         "decoder_ms_per_token": spread(dm["dev_ms"]),
         "decoder_host_clock_ms_per_token": spread(dm["wall_ms"]),

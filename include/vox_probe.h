@@ -25,6 +25,8 @@ int vox_probe_sink_entries(int wg_per_cu);
  * writes one checksum per workgroup to the device array sink.  Enqueued on `stream` (a
  * hipStream_t; NULL = the null stream).  Returns 0, -1 on a bad argument, -4 if the launch failed. */
 int vox_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream);
+/* The same read with non-temporal loads (the form the GEMVs' weight streams use). */
+int vox_probe_stream_read_nt(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream);
 
 /* Grid-wide handoff probe: the cost of passing a 3072-float vector between phases inside one
  * persistent kernel (one 512-thread workgroup per compute unit, a grid barrier per phase, each

@@ -1,9 +1,9 @@
 // stream_read.hip - streaming-read probe: the HBM read rate a plain kernel reaches on this GPU.
 //
-// Not an operation of the decoder.  It reads a buffer once with 16-byte loads and keeps a
-// checksum per workgroup, so the loads cannot be dropped.  The rate it reaches at a given size
-// is the practical ceiling for a kernel that must stream that many bytes once (the decoder's
-// GEMVs stream their Q4_0 weights exactly once per token).
+// Not an operation of the decoder.  It reads a buffer once with 16-byte loads (plain or
+// non-temporal) and keeps a checksum per workgroup, so the loads cannot be dropped.  The best rate
+// it reaches at a given size is the practical ceiling for a kernel that must stream that many
+// bytes once (the decoder's GEMVs stream their Q4_0 weights exactly once per token).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -16,8 +16,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int PROBE_THREADS = 256;
 constexpr int PROBE_UNROLL = 8;   // 16-byte loads in flight per thread per round
 
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const u32x4 *p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
 // Workgroup i reads 16-byte chunks i*T + t, then every gridDim*T further, PROBE_UNROLL rounds
-// at a time (all loads of a round issued before their first use).
+// at a time (all loads of a round issued before their first use).  NT: non-temporal loads.
+template <bool NT>
 __global__ __launch_bounds__(PROBE_THREADS) void stream_read_kernel(const u32x4 *__restrict__ src, int64_t n16,
                                                                     uint32_t *__restrict__ sink)
 {
@@ -28,13 +38,13 @@ __global__ __launch_bounds__(PROBE_THREADS) void stream_read_kernel(const u32x4 
         u32x4 v[PROBE_UNROLL];
 #pragma unroll
         for (int u = 0; u < PROBE_UNROLL; ++u)
-            v[u] = src[i + u * stride];
+            v[u] = ld16<NT>(src + i + u * stride);
 #pragma unroll
         for (int u = 0; u < PROBE_UNROLL; ++u)
             acc ^= v[u];
     }
     for (; i < n16; i += stride)
-        acc ^= src[i];
+        acc ^= ld16<NT>(src + i);
     __shared__ uint32_t red[PROBE_THREADS];
     red[threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
     __syncthreads();
@@ -57,14 +67,27 @@ extern "C" int vox_probe_sink_entries(int wg_per_cu)
     return wg_per_cu * cus;
 }
 
-extern "C" int vox_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream)
+namespace {
+template <bool NT>
+int stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream)
 {
     if (!buf || !sink || bytes == 0 || bytes % 16 || ((uintptr_t)buf % 16))
         return -1;
     const int grid = vox_probe_sink_entries(wg_per_cu);
     if (grid < 1)
         return -1;
-    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(PROBE_THREADS), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(stream_read_kernel<NT>, dim3(grid), dim3(PROBE_THREADS), 0, (hipStream_t)stream,
                        (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
     return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+}  // namespace
+
+extern "C" int vox_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream)
+{
+    return stream_read<false>(buf, bytes, sink, wg_per_cu, stream);
+}
+
+extern "C" int vox_probe_stream_read_nt(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream)
+{
+    return stream_read<true>(buf, bytes, sink, wg_per_cu, stream);
 }

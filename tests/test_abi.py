@@ -48,13 +48,14 @@ def test_probe_library_exports_its_header():
     fns = header_functions(PROBE_HEADER)
     assert fns == ["vox_probe_handoff_persistent", "vox_probe_handoff_phase", "vox_probe_handoff_reset",
                    "vox_probe_handoff_work_bytes", "vox_probe_mfma_rate", "vox_probe_mfma_rate_entries",
-                   "vox_probe_sink_entries", "vox_probe_stream_read"]
+                   "vox_probe_sink_entries", "vox_probe_stream_read", "vox_probe_stream_read_nt"]
     assert all(hasattr(plib, f) for f in fns)
-    plib.vox_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
-    # bad arguments are refused before any HIP call
-    assert plib.vox_probe_stream_read(None, 16, C.c_void_p(0x1000), 1, None) == -1
-    assert plib.vox_probe_stream_read(C.c_void_p(0x1000), 24, C.c_void_p(0x1000), 1, None) == -1
-    assert plib.vox_probe_stream_read(C.c_void_p(0x1008), 32, C.c_void_p(0x1000), 1, None) == -1
+    for fn in (plib.vox_probe_stream_read, plib.vox_probe_stream_read_nt):
+        fn.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+        # bad arguments are refused before any HIP call
+        assert fn(None, 16, C.c_void_p(0x1000), 1, None) == -1
+        assert fn(C.c_void_p(0x1000), 24, C.c_void_p(0x1000), 1, None) == -1
+        assert fn(C.c_void_p(0x1008), 32, C.c_void_p(0x1000), 1, None) == -1
     plib.vox_probe_mfma_rate.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     out = C.c_void_p(0x1000)
     assert plib.vox_probe_mfma_rate(2, 0, 1, 16, out, None) == -1     # no such product
