@@ -389,7 +389,7 @@ __global__ __launch_bounds__(Gm::NT) __attribute__((amdgpu_waves_per_eu(3))) voi
 
 // LATE_V for the split-window buckets: two resident workgroups per compute unit.
 template <int GROUP, bool LATE_V>
-__global__ __launch_bounds__(ATTN_THREADS) __attribute__((amdgpu_waves_per_eu(LATE_V && GROUP <= 4 ? 4 : 1))) void dec_attn_kernel(AttnArgs a)
+__global__ __launch_bounds__(ATTN_THREADS) __attribute__((amdgpu_waves_per_eu(LATE_V && GROUP == 1 ? 4 : LATE_V && GROUP <= 4 ? 2 : 1))) void dec_attn_kernel(AttnArgs a)
 {
     attn_chunk<GROUP, LATE_V>(a);
 }

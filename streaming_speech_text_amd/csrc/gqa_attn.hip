@@ -11,7 +11,7 @@ namespace vox {
 // LATE_V (split windows), groups up to 4: at least four waves per SIMD, i.e. two resident workgroups per
 // compute unit.
 template <int GROUP, bool LATE_V>
-__global__ __launch_bounds__(ATTN_THREADS) __attribute__((amdgpu_waves_per_eu(LATE_V && GROUP <= 4 ? 4 : 1))) void gqa_attn_kernel(AttnArgs a)
+__global__ __launch_bounds__(ATTN_THREADS) __attribute__((amdgpu_waves_per_eu(LATE_V && GROUP == 1 ? 4 : LATE_V && GROUP <= 4 ? 2 : 1))) void gqa_attn_kernel(AttnArgs a)
 {
     attn_chunk<GROUP, LATE_V>(a);
 }
