@@ -45,11 +45,14 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sequences", type=int, default=5, help="decoder sequences timed (median reported)")
-    ap.add_argument("--leg", choices=["all", "decoder", "decoder_w16", "gemv", "kernels", "probe"], default="all",
+    ap.add_argument("--leg", choices=["all", "decoder", "decoder_full", "decoder_w16", "gemv", "kernels", "probe"],
+                    default="all",
                     help="gemv: only the GEMV roofline leg and a copy of known size (for counter runs); "
                          "kernels: per-kernel timings of the other workloads, one JSON line each; "
                          "probe: read ceilings and the grid-handoff probe; decoder: only the decoder at the "
-                         "bench configuration (for kernel traces); decoder_w16: only the decoder over f16 weights")
+                         "bench configuration (for kernel traces); decoder_full: the decoder at the bench "
+                         "configuration, then at a full, wrapped 8192-position window; decoder_w16: only the "
+                         "decoder over f16 weights")
     ap.add_argument("--summarize-trace", metavar="CSV", help="print per-kernel statistics of a rocprofv3 "
                     "kernel_trace.csv (calls, mean, p10/p50/p90, min, max in us) and exit")
     ap.add_argument("--trace-json", metavar="OUT", help="with --summarize-trace: also write the statistics with "
@@ -965,7 +968,11 @@ def main():
     s = synth.VOXTRAL_DECODER
     print(f"[bench] generating weights ({s.n_layers} layers, vocab {s.vocab})", file=sys.stderr, flush=True)
     w = synth.decoder_weights(synth.SEED_DECODER, s)
-    dm, full = decoder_legs(args, torch, synth, vox, dev, stream, w, full_window=args.leg == "all")
+    dm, full = decoder_legs(args, torch, synth, vox, dev, stream, w, full_window=args.leg in ("all", "decoder_full"))
+    if args.leg == "decoder_full":
+        print(json.dumps({"leg": "decoder_full", "ms_per_token": spread(dm["dev_ms"]), "full_window": full}),
+              flush=True)
+        return
     if args.leg == "decoder":
         n_steps = (args.sequences + 1) * len(dm["prefix"]) + max(args.warmup, args.steps) + args.sequences * args.steps
         print(json.dumps({"leg": "decoder", "ms_per_token": spread(dm["dev_ms"]), "decoder_steps": n_steps}),
