@@ -62,6 +62,22 @@ def test_attention_edge_lengths(vx, orc, n_valid):
     assert_close(got, _oracle(orc, q, kc, vc, np.arange(n_valid)), f"attn L={n_valid}")
 
 
+@pytest.mark.parametrize("nq,nkv,n_slots,n_valid", [
+    (32, 8, 20000, 20000),   # 32 chunks of 625: four full sub-chunks and a partial one each
+    (32, 8, 16384, 16384),   # 32 chunks of 512: four full sub-chunks each
+    (32, 8, 20000, 9000),    # chunks of 282: two full sub-chunks and a partial one (the last: 258)
+    (16, 8, 20000, 20000),   # groups of two query heads
+    (64, 8, 16384, 16000),   # groups of eight query heads
+])
+def test_attention_long_chunks(vx, orc, nq, nkv, n_slots, n_valid):
+    # rings longer than 8192 slots: every chunk walks three to five 128-position sub-chunks, so each
+    # full sub-chunk's K loads are issued during the one before, and a partial one follows them
+    q, kc, vc = synth.attention_inputs(970 + nq, nq, nkv, HD, n_slots)
+    say(f"attention long chunks nq={nq} nkv={nkv} n_slots={n_slots} n_valid={n_valid}")
+    got = _run(vx, q, kc, vc, n_valid)
+    assert_close(got, _oracle(orc, q, kc, vc, np.arange(n_valid)), f"attn {nq}/{nkv} L={n_valid} of {n_slots}")
+
+
 @pytest.mark.parametrize("nq,nkv", [(8, 8), (16, 8), (64, 8), (4, 1), (8, 2)])
 def test_attention_group_sizes(vx, orc, nq, nkv):
     q, kc, vc = synth.attention_inputs(950 + nq + nkv, nq, nkv, HD, 300)
