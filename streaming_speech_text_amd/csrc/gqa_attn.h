@@ -182,7 +182,14 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
     __shared__ float ored[ATTN_WAVES][GROUP][ATTN_HD];    // per-wave partial outputs
     __shared__ float ml[GROUP][2];
 
-    const int g = blockIdx.y;
+    // One chunk per query head (gridDim.x == 1): workgroup y takes query head
+    // (y % 8) * (gridDim.y / 8) + y / 8, so the workgroups of the query heads that share a KV head
+    // have ids eight apart and land on one XCD (workgroups go to the eight XCDs round-robin), whose
+    // L2 then fetches that KV head's rows from HBM once instead of once per query head (measured
+    // on MI355X: the decoder step 0.817 -> 0.808 ms/token at 39-102 positions)
+    const int g = (GROUP == 1 && a.kv_shift > 0 && gridDim.x == 1 && (gridDim.y & 7) == 0)
+                      ? (int)((blockIdx.y & 7) * (gridDim.y >> 3) + (blockIdx.y >> 3))
+                      : (int)blockIdx.y;
     const int s = blockIdx.x;
     int nv = a.n_valid;
     if (a.pos) {
