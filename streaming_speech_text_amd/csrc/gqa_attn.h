@@ -191,12 +191,19 @@ __device__ __forceinline__ void attn_chunk(const AttnArgs &a)
     // L / 8 % G of it: a bijection whenever w n_kv is a multiple of 8.
     int g = blockIdx.y, s = blockIdx.x;
     if constexpr (GROUP == 1) {
-        const int w = gridDim.x, nkv = gridDim.y >> a.kv_shift, G = 1 << a.kv_shift;
-        if (a.kv_shift > 0 && (w * nkv) % 8 == 0) {
+        const int w = gridDim.x, sh = a.kv_shift, nkv = gridDim.y >> sh;
+        if (sh > 0 && (w * nkv) % 8 == 0) {
             const int L = blockIdx.x + w * blockIdx.y;
-            const int grp = (L & 7) * (w * nkv / 8) + (L >> 3) / G;
-            g = (grp / w) * G + (L >> 3) % G;
-            s = grp % w;
+            const int grp = (L & 7) * ((w * nkv) >> 3) + ((L >> 3) >> sh);
+            const int j = (L >> 3) & ((1 << sh) - 1);
+            if ((w & (w - 1)) == 0) {   // the decoder's widths: shifts only
+                const int lw = __builtin_ctz(w);
+                g = ((grp >> lw) << sh) + j;
+                s = grp & (w - 1);
+            } else {
+                g = (grp / w << sh) + j;
+                s = grp % w;
+            }
         }
     }
     int nv = a.n_valid;
