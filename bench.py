@@ -122,18 +122,20 @@ def probe_lib():
     L = C.CDLL(path)
     L.vox_probe_sink_entries.restype = C.c_int
     L.vox_probe_sink_entries.argtypes = [C.c_int]
-    for fn in (L.vox_probe_stream_read, L.vox_probe_stream_read_nt):
+    for fn in (L.vox_probe_stream_read, L.vox_probe_stream_read_nt, L.vox_probe_stream_read_lds,
+               L.vox_probe_stream_read_lds_nt):
         fn.restype = C.c_int
         fn.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
     return L
 
 
-def probe_ceiling(torch, dev, stream, sizes, reps=100):
+def probe_ceiling(torch, dev, stream, sizes, reps=100, lds=False):
     """Streaming-read rate (GB/s) of a 16-byte-load kernel for each byte count in `sizes`:
     launches read consecutive windows of a buffer of more than 1 GiB (so no window is served from
     the 256 MB Infinity Cache), captured in a graph and timed like the kernels; the best over
-    plain and non-temporal loads and 1, 2, 4 and 8 workgroups per compute unit.  Returns
-    {bytes: (us, GB/s, wg_per_cu, loads)}."""
+    plain and non-temporal loads and 1, 2, 4 and 8 workgroups per compute unit (lds: instead the
+    direct-to-LDS forms of the same loads at 1, 2 and 4 workgroups, whose 32 KB of LDS each allow
+    no more).  Returns {bytes: (us, GB/s, wg_per_cu, loads)}."""
     L = probe_lib()
     GiB = 2 ** 30
     out = {}
@@ -144,8 +146,11 @@ def probe_ceiling(torch, dev, stream, sizes, reps=100):
         buf = torch.empty(n_win * size, dtype=torch.uint8, device=dev)
         buf.fill_(1)
         best = None
-        for fn, loads in ((L.vox_probe_stream_read, "plain"), (L.vox_probe_stream_read_nt, "non-temporal")):
-            for wg in (1, 2, 4, 8):
+        forms = (((L.vox_probe_stream_read_lds, "direct-to-LDS"), (L.vox_probe_stream_read_lds_nt,
+                  "direct-to-LDS non-temporal")) if lds else
+                 ((L.vox_probe_stream_read, "plain"), (L.vox_probe_stream_read_nt, "non-temporal")))
+        for fn, loads in forms:
+            for wg in ((1, 2, 4) if lds else (1, 2, 4, 8)):
                 def launch(i, wg=wg, fn=fn):
                     st = fn(buf.data_ptr() + i * size, size, sink.data_ptr(), wg, torch.cuda.current_stream().cuda_stream)
                     if st:
@@ -167,6 +172,11 @@ def probe_leg(torch, dev, stream):
     sizes = [7077888, 10616832, 15925248, 31850496, 226492416, 5308416, 1 << 20, 4 << 20, 16 << 20,
              64 << 20, 256 << 20]
     for b, (us, gbs, wg, loads) in probe_ceiling(torch, dev, stream, sizes).items():
+        print(json.dumps({"leg": "probe", "bytes": b, "us": round(us, 3), "gbs": round(gbs, 1),
+                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "wg_per_cu": wg, "loads": loads}), flush=True)
+    # the same reads with direct-to-LDS loads (the data bypasses the registers) at the decoder
+    # kernels' byte counts
+    for b, (us, gbs, wg, loads) in probe_ceiling(torch, dev, stream, sizes[:6], lds=True).items():
         print(json.dumps({"leg": "probe", "bytes": b, "us": round(us, 3), "gbs": round(gbs, 1),
                           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "wg_per_cu": wg, "loads": loads}), flush=True)
     import ctypes as C

@@ -27,6 +27,10 @@ int vox_probe_sink_entries(int wg_per_cu);
 int vox_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream);
 /* The same read with non-temporal loads (the form the GEMVs' weight streams use). */
 int vox_probe_stream_read_nt(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream);
+/* The same read with direct-to-LDS 16-byte loads (the data lands in LDS without passing through
+ * registers; 32 KB of LDS per workgroup), plain or non-temporal. */
+int vox_probe_stream_read_lds(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream);
+int vox_probe_stream_read_lds_nt(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream);
 
 /* Grid-wide handoff probe: the cost of passing a 3072-float vector between phases inside one
  * persistent kernel (one 512-thread workgroup per compute unit, a grid barrier per phase, each

@@ -56,6 +56,45 @@ __global__ __launch_bounds__(PROBE_THREADS) void stream_read_kernel(const u32x4 
     }
 }
 
+// The same read with direct-to-LDS loads (global_load_lds_dwordx4): the 16 bytes of lane L land
+// in LDS at the wave's slot base + 16 L without passing through registers.  Each round issues
+// PROBE_UNROLL loads per thread into slots of their own, waits for all of them, then reads back the
+// thread's first dword of each slot into the checksum.  NT: non-temporal loads.
+template <bool NT>
+__global__ __launch_bounds__(PROBE_THREADS) void stream_read_lds_kernel(const u32x4 *__restrict__ src, int64_t n16,
+                                                                        uint32_t *__restrict__ sink)
+{
+    __shared__ uint32_t ring[PROBE_UNROLL][PROBE_THREADS * 4];   // slot u: 16 bytes per thread
+    const int wave = threadIdx.x >> 6;
+    const int64_t stride = (int64_t)gridDim.x * PROBE_THREADS;
+    int64_t i = (int64_t)blockIdx.x * PROBE_THREADS + threadIdx.x;
+    uint32_t acc = 0u;
+    for (; i + (PROBE_UNROLL - 1) * stride < n16; i += PROBE_UNROLL * stride) {
+#pragma unroll
+        for (int u = 0; u < PROBE_UNROLL; ++u)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + i + u * stride),
+                                             (__attribute__((address_space(3))) void *)&ring[u][wave * 256], 16, 0,
+                                             NT ? 2 : 0);
+        __builtin_amdgcn_s_waitcnt(0);   // every counter at zero: the round's data is in LDS
+#pragma unroll
+        for (int u = 0; u < PROBE_UNROLL; ++u)
+            acc ^= ring[u][threadIdx.x * 4];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = ld16<NT>(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t red[PROBE_THREADS];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int t = 0; t < PROBE_THREADS; ++t)
+            r ^= red[t];
+        sink[blockIdx.x] = r;
+    }
+}
+
 }  // namespace
 
 extern "C" int vox_probe_sink_entries(int wg_per_cu)
@@ -68,7 +107,7 @@ extern "C" int vox_probe_sink_entries(int wg_per_cu)
 }
 
 namespace {
-template <bool NT>
+template <bool NT, bool LDS = false>
 int stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream)
 {
     if (!buf || !sink || bytes == 0 || bytes % 16 || ((uintptr_t)buf % 16))
@@ -76,8 +115,12 @@ int stream_read(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, vo
     const int grid = vox_probe_sink_entries(wg_per_cu);
     if (grid < 1)
         return -1;
-    hipLaunchKernelGGL(stream_read_kernel<NT>, dim3(grid), dim3(PROBE_THREADS), 0, (hipStream_t)stream,
-                       (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
+    if constexpr (LDS)
+        hipLaunchKernelGGL(stream_read_lds_kernel<NT>, dim3(grid), dim3(PROBE_THREADS), 0, (hipStream_t)stream,
+                           (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
+    else
+        hipLaunchKernelGGL(stream_read_kernel<NT>, dim3(grid), dim3(PROBE_THREADS), 0, (hipStream_t)stream,
+                           (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 }  // namespace
@@ -90,4 +133,15 @@ extern "C" int vox_probe_stream_read(const void *buf, size_t bytes, uint32_t *si
 extern "C" int vox_probe_stream_read_nt(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream)
 {
     return stream_read<true>(buf, bytes, sink, wg_per_cu, stream);
+}
+
+extern "C" int vox_probe_stream_read_lds(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu, void *stream)
+{
+    return stream_read<false, true>(buf, bytes, sink, wg_per_cu, stream);
+}
+
+extern "C" int vox_probe_stream_read_lds_nt(const void *buf, size_t bytes, uint32_t *sink, int wg_per_cu,
+                                            void *stream)
+{
+    return stream_read<true, true>(buf, bytes, sink, wg_per_cu, stream);
 }

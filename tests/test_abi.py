@@ -48,9 +48,11 @@ def test_probe_library_exports_its_header():
     fns = header_functions(PROBE_HEADER)
     assert fns == ["vox_probe_handoff_persistent", "vox_probe_handoff_phase", "vox_probe_handoff_reset",
                    "vox_probe_handoff_work_bytes", "vox_probe_mfma_rate", "vox_probe_mfma_rate_entries",
-                   "vox_probe_sink_entries", "vox_probe_stream_read", "vox_probe_stream_read_nt"]
+                   "vox_probe_sink_entries", "vox_probe_stream_read", "vox_probe_stream_read_lds",
+                   "vox_probe_stream_read_lds_nt", "vox_probe_stream_read_nt"]
     assert all(hasattr(plib, f) for f in fns)
-    for fn in (plib.vox_probe_stream_read, plib.vox_probe_stream_read_nt):
+    for fn in (plib.vox_probe_stream_read, plib.vox_probe_stream_read_nt, plib.vox_probe_stream_read_lds,
+               plib.vox_probe_stream_read_lds_nt):
         fn.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
         # bad arguments are refused before any HIP call
         assert fn(None, 16, C.c_void_p(0x1000), 1, None) == -1
